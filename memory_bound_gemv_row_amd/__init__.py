@@ -1,0 +1,7 @@
+"""Row-major GEMV, y[M] = A[M,N] . x[N], on MI355X (gfx950).
+
+The compute lives in a hand-written HIP library behind a C ABI
+(``include/gemv.h``); ``binding`` is a thin ctypes layer over it.  The
+library is loaded on first use and its absence is an error: there is no CPU
+fallback.
+"""

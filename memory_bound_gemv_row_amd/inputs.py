@@ -1,0 +1,94 @@
+"""Seeded synthetic inputs for row-major GEMV (no GEMV arithmetic here).
+
+This module only draws random operands.  It serves both the HIP path and the
+CPU oracle, and holds none of either side's arithmetic: no products, no
+dequantisation, no packing of values chosen elsewhere.
+
+Workloads (all synthetic; no page uses a dataset):
+  f32 : A and x i.i.d. uniform[-1, 1], cast to float32 (round to nearest even)
+        -- the square FP32 study of "cuda-gemv-optimization".
+  f16 : A ~ N(0, 1/N), x ~ N(0, 1), cast to binary16 -- decode-projection
+        shapes from "membound", section "Results".
+  q8  : A int8 uniform on [-127, 127]; one binary16 scale per row,
+        uniform[0.5, 1.5]/127; x ~ N(0, 1) binary16.
+  q4  : A packed two nibbles per byte, [M, N/2] uint8.  Every byte is drawn
+        uniform on 0..255, so each nibble is independently uniform over its
+        16 codes, i.e. uniform on [-8, 7] read as two's complement; one
+        binary16 scale per row and 128-column group, uniform[0.5, 1.5]/7,
+        stored [M, N/128]; x ~ N(0, 1) binary16.
+Every shape draws from numpy's PCG64 ``default_rng(seed)`` afresh, in the
+order A, scales, x.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+KINDS = ("f32", "f16", "q8", "q4")
+
+
+@dataclass(frozen=True)
+class Workload:
+    kind: str
+    M: int
+    N: int
+
+    @property
+    def name(self) -> str:
+        return f"{self.kind}_{self.M}x{self.N}"
+
+
+# The five workload families, at their full sizes.
+WORKLOADS = {
+    "f32_1024": [Workload("f32", 1024, 1024)],
+    "f32_sweep": [Workload("f32", n, n) for n in (2048, 4096, 8192)],
+    "f16_decode": [Workload("f16", 4096, 4096), Workload("f16", 8192, 8192),
+                   Workload("f16", 14336, 4096), Workload("f16", 4096, 14336)],
+    "q8_decode": [Workload("q8", 8192, 8192), Workload("q8", 14336, 4096)],
+    "q4_decode": [Workload("q4", 4096, 14336), Workload("q4", 14336, 4096)],
+}
+
+
+def all_workloads():
+    return [w for ws in WORKLOADS.values() for w in ws]
+
+
+def make_f32(M: int, N: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    A = rng.uniform(-1.0, 1.0, (M, N)).astype(np.float32)
+    x = rng.uniform(-1.0, 1.0, N).astype(np.float32)
+    return {"A": A, "x": x}
+
+
+def make_f16(M: int, N: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    sigma = 1.0 / np.sqrt(N) if N > 0 else 1.0
+    A = rng.normal(0.0, sigma, (M, N)).astype(np.float16)
+    x = rng.standard_normal(N).astype(np.float16)
+    return {"A": A, "x": x}
+
+
+def make_q8(M: int, N: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    A = rng.integers(-127, 128, (M, N), dtype=np.int8)
+    scale = rng.uniform(0.5 / 127.0, 1.5 / 127.0, M).astype(np.float16)
+    x = rng.standard_normal(N).astype(np.float16)
+    return {"A": A, "scale": scale, "x": x}
+
+
+def make_q4(M: int, N: int, seed: int = 0):
+    if N % 128 != 0:
+        raise ValueError("INT4 rows are made of whole 128-column groups (N % 128 == 0)")
+    rng = np.random.default_rng(seed)
+    A = rng.integers(0, 256, (M, N // 2), dtype=np.uint8)
+    scale = rng.uniform(0.5 / 7.0, 1.5 / 7.0, (M, N // 128)).astype(np.float16)
+    x = rng.standard_normal(N).astype(np.float16)
+    return {"A": A, "scale": scale, "x": x}
+
+
+MAKERS = {"f32": make_f32, "f16": make_f16, "q8": make_q8, "q4": make_q4}
+
+
+def make(kind: str, M: int, N: int, seed: int = 0):
+    return MAKERS[kind](M, N, seed)

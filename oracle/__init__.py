@@ -1,0 +1,18 @@
+"""CPU oracle for row-major GEMV (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding)
+never imports, links or calls it, and it shares no code with them.
+"""
+from .oracle import (  # noqa: F401
+    build,
+    half_to_double,
+    half_to_double_array,
+    gemv_f32,
+    gemv_f16,
+    gemv_q8,
+    gemv_q4,
+    num_threads,
+    library_path,
+)
+from .metrics import parity_error, parity_report, GATES  # noqa: F401

@@ -1,0 +1,69 @@
+"""Parity metric between a GPU result and the oracle (test infrastructure).
+
+The pages compare GPU output with a CPU reference through a relative error,
+so that summation-order differences are absorbed ("cuda-gemv-optimization",
+section "Correctness verification"), report the maximum relative error next
+to every benchmark row ("membound", section "Results"), and floor the
+denominator so that outputs near zero do not raise false alarms ("membound",
+section "Bonus kernel: online softmax", which scores relative to
+max(ref, 1e-4)).
+
+Reading taken here: the floor scales with the row-result magnitude, at 1% of
+the largest |reference| output, because GEMV outputs are sums of random-sign
+terms and some land arbitrarily close to zero:
+
+    err = max_i |y_i - r_i| / max(|r_i|, 0.01 * max_k |r_k|)
+
+Gates: 1e-4 for the FP32 and dequantised INT8/INT4 paths, 2e-3 for FP16
+inputs with FP32 accumulation.  The unfloored elementwise maximum, the
+normwise error and the componentwise error relative to sum_j |w_ij x_j| are
+reported as diagnostics and never gated.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GATES = {"f32": 1e-4, "q8": 1e-4, "q4": 1e-4, "f16": 2e-3}
+FLOOR_FRACTION = 0.01
+
+
+def parity_error(y: np.ndarray, ref: np.ndarray) -> float:
+    """Floored max relative error; NaN/Inf in either input give +inf."""
+    y = np.asarray(y, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    if y.shape != r.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {r.shape}")
+    if y.size == 0:
+        return 0.0
+    if not (np.all(np.isfinite(y)) and np.all(np.isfinite(r))):
+        same = (np.isnan(y) & np.isnan(r)) | (y == r)
+        if not np.all(same):
+            return float("inf")
+        finite = np.isfinite(r)
+        y, r = y[finite], r[finite]
+        if y.size == 0:
+            return 0.0
+    scale = np.max(np.abs(r))
+    denom = np.maximum(np.abs(r), FLOOR_FRACTION * scale)
+    err = np.abs(y - r)
+    if scale == 0.0:
+        return 0.0 if np.all(err == 0.0) else float("inf")
+    return float(np.max(err / denom))
+
+
+def parity_report(y: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray | None = None) -> dict:
+    """Gated metric plus ungated diagnostics."""
+    y64 = np.asarray(y, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    out = {"floored_rel": parity_error(y64, r)}
+    if r.size:
+        err = np.abs(y64 - r)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            out["elementwise_rel"] = float(np.max(np.where(r != 0, err / np.abs(r), np.where(err == 0, 0.0, np.inf))))
+        m = float(np.max(np.abs(r)))
+        out["normwise_rel"] = float(np.max(err) / m) if m > 0 else float(np.max(err))
+        if abs_sum is not None:
+            a = np.asarray(abs_sum, dtype=np.float64).ravel()
+            with np.errstate(divide="ignore", invalid="ignore"):
+                out["componentwise"] = float(np.max(np.where(a > 0, err / a, 0.0)))
+    return out

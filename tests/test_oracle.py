@@ -1,0 +1,280 @@
+"""Pins for the CPU oracle, each against something other than the oracle itself.
+
+Pins used: the IEEE binary16 decoding of numpy (all 65536 codes), the pages'
+worked row-major example (golden fixture), closed forms (identity and
+all-ones matrices, x = 1), exactly rounded sums (math.fsum, fractions), an
+independent vectorised dequantisation followed by BLAS float64 matmul, exact
+integer arithmetic, and one-hot probes of every column.  Each pin is chosen
+so that a plausible slip in the oracle (a transposed index, a dropped term,
+a swapped nibble, a wrong group index, a flushed subnormal) fails it.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from qpack import pack_int4, unpack_int4, f16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+U = 2.0 ** -53
+
+
+def _sum_bound(terms):
+    """Worst-case error of a recursive double sum of n exactly known terms."""
+    n = len(terms)
+    return n * U * math.fsum(abs(t) for t in terms) * 1.0000001
+
+
+# ---------------------------------------------------------------- decoder
+def test_half_decoder_matches_numpy_on_all_codes(oracle_mod):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle_mod.half_to_double_array(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+    # subnormals are honoured, not flushed
+    assert oracle_mod.half_to_double(0x0001) == 2.0 ** -24
+    assert oracle_mod.half_to_double(0x03FF) == 1023 * 2.0 ** -24
+    assert oracle_mod.half_to_double(0x8001) == -(2.0 ** -24)
+
+
+# ---------------------------------------------------------------- layout
+def test_rowmajor_worked_example(oracle_mod):
+    g = json.load(open(os.path.join(GOLDEN, "rowmajor_worked_example.json")))
+    M, N, r, c = g["M"], g["N"], g["row"], g["col"]
+    flat = np.arange(M * N, dtype=np.float32)          # value == linear offset
+    x = np.zeros(N, dtype=np.float32)
+    x[c] = 1.0
+    y = oracle_mod.gemv_f32(flat.reshape(M, N), x)
+    assert y[r] == g["offset"]
+    assert list(y) == [i * N + c for i in range(M)]
+
+
+# ---------------------------------------------------------------- closed forms
+def test_identity_gives_x(oracle_mod):
+    rng = np.random.default_rng(1)
+    n = 300
+    x32 = rng.uniform(-1, 1, n).astype(np.float32)
+    assert np.array_equal(oracle_mod.gemv_f32(np.eye(n, dtype=np.float32), x32), x32.astype(np.float64))
+    # binary16 x including subnormals and a signed zero
+    x16 = f16(rng.standard_normal(n))
+    x16[:4] = np.array([0x0001, 0x03FF, 0x8000, 0x8005], dtype=np.uint16).view(np.float16)
+    y = oracle_mod.gemv_f16(np.eye(n, dtype=np.float16), x16)
+    assert np.array_equal(y, x16.astype(np.float64))
+
+
+def test_identity_quantised_gives_scaled_x(oracle_mod):
+    rng = np.random.default_rng(2)
+    n = 256
+    x = f16(rng.standard_normal(n))
+    s8 = f16(rng.uniform(0.5, 1.5, n) / 127)
+    y8 = oracle_mod.gemv_q8(np.eye(n, dtype=np.int8), s8, x)
+    assert np.array_equal(y8, s8.astype(np.float64) * x.astype(np.float64))
+    s4 = f16(rng.uniform(0.5, 1.5, (n, n // 128)) / 7)
+    y4 = oracle_mod.gemv_q4(pack_int4(np.eye(n, dtype=np.int64)), s4, x)
+    expect = s4.astype(np.float64)[np.arange(n), np.arange(n) // 128] * x.astype(np.float64)
+    assert np.array_equal(y4, expect)
+
+
+def test_all_ones_gives_sum_of_x(oracle_mod):
+    rng = np.random.default_rng(3)
+    M, N = 5, 1000
+    x = rng.uniform(-1, 1, N).astype(np.float32)
+    y = oracle_mod.gemv_f32(np.ones((M, N), dtype=np.float32), x)
+    terms = [float(v) for v in x]
+    exact = math.fsum(terms)
+    assert np.all(y == y[0])
+    assert abs(y[0] - exact) <= _sum_bound(terms)
+
+
+def test_x_ones_gives_row_sums(oracle_mod):
+    rng = np.random.default_rng(4)
+    M, N = 7, 640
+    A = f16(rng.standard_normal((M, N)) / math.sqrt(N))
+    y = oracle_mod.gemv_f16(A, np.ones(N, dtype=np.float16))
+    for i in range(M):
+        terms = [float(v) for v in A[i].astype(np.float64)]
+        assert abs(y[i] - math.fsum(terms)) <= _sum_bound(terms)
+    q = rng.integers(-8, 8, (M, N))
+    s = f16(rng.uniform(0.5, 1.5, (M, N // 128)) / 7)
+    y4 = oracle_mod.gemv_q4(pack_int4(q), s, np.ones(N, dtype=np.float16))
+    for i in range(M):
+        terms = [float(q[i, j]) * float(s[i, j // 128]) for j in range(N)]
+        assert abs(y4[i] - math.fsum(terms)) <= _sum_bound(terms)
+
+
+# ---------------------------------------------------------------- exact sums
+@pytest.mark.parametrize("M,N", [(1, 1), (1, 2), (3, 5), (4, 7), (16, 16), (2, 33), (9, 64)])
+def test_tiny_shapes_against_fsum(oracle_mod, M, N):
+    rng = np.random.default_rng(M * 100 + N)
+    A = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    x = rng.uniform(-1, 1, N).astype(np.float32)
+    y = oracle_mod.gemv_f32(A, x)
+    for i in range(M):
+        terms = [float(A[i, j]) * float(x[j]) for j in range(N)]   # exact products
+        assert abs(y[i] - math.fsum(terms)) <= _sum_bound(terms)
+
+
+def test_exact_rational_4x4(oracle_mod):
+    rng = np.random.default_rng(5)
+    A = f16(rng.standard_normal((4, 4)))
+    x = f16(rng.standard_normal(4))
+    y = oracle_mod.gemv_f16(A, x)
+    for i in range(4):
+        exact = sum(Fraction(float(A[i, j])) * Fraction(float(x[j])) for j in range(4))
+        terms = [float(A[i, j]) * float(x[j]) for j in range(4)]
+        assert abs(Fraction(y[i]) - exact) <= Fraction(_sum_bound(terms))
+        assert math.fsum(terms) == float(exact)     # fsum is correctly rounded
+
+
+def test_integer_inputs_are_exact(oracle_mod):
+    rng = np.random.default_rng(6)
+    M, N = 64, 777
+    Ai = rng.integers(-3, 4, (M, N))
+    xi = rng.integers(-3, 4, N)
+    want = (Ai @ xi).astype(np.float64)
+    assert np.array_equal(oracle_mod.gemv_f32(Ai.astype(np.float32), xi.astype(np.float32)), want)
+    assert np.array_equal(oracle_mod.gemv_f16(Ai.astype(np.float16), xi.astype(np.float16)), want)
+    assert np.array_equal(oracle_mod.gemv_q8(Ai.astype(np.int8), np.ones(M, np.float16), xi.astype(np.float16)), want)
+
+
+# ---------------------------------------------------------------- library routines
+def test_random_against_blas_float64(oracle_mod):
+    rng = np.random.default_rng(7)
+    M, N = 512, 4096
+    A = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    x = rng.uniform(-1, 1, N).astype(np.float32)
+    ref = A.astype(np.float64) @ x.astype(np.float64)
+    y = oracle_mod.gemv_f32(A, x)
+    assert np.max(np.abs(y - ref)) <= 1e-13 * np.max(np.abs(ref))
+    A16 = f16(rng.standard_normal((M, N)) / math.sqrt(N))
+    x16 = f16(rng.standard_normal(N))
+    ref16 = A16.astype(np.float64) @ x16.astype(np.float64)
+    y16 = oracle_mod.gemv_f16(A16, x16)
+    assert np.max(np.abs(y16 - ref16)) <= 1e-13 * np.max(np.abs(ref16))
+
+
+def test_q8_against_vectorised_dequant(oracle_mod):
+    rng = np.random.default_rng(8)
+    M, N = 300, 4000
+    q = rng.integers(-128, 128, (M, N), dtype=np.int8)       # includes -128
+    s = f16(rng.uniform(0.5, 1.5, M) / 127)
+    x = f16(rng.standard_normal(N))
+    W = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    ref = W @ x.astype(np.float64)
+    y = oracle_mod.gemv_q8(q, s, x)
+    assert np.max(np.abs(y - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_q4_against_vectorised_dequant(oracle_mod):
+    rng = np.random.default_rng(9)
+    M, N = 200, 14 * 128
+    packed = rng.integers(0, 256, (M, N // 2), dtype=np.uint8)
+    s = f16(rng.uniform(0.5, 1.5, (M, N // 128)) / 7)
+    x = f16(rng.standard_normal(N))
+    W = unpack_int4(packed).astype(np.float64) * np.repeat(s.astype(np.float64), 128, axis=1)
+    ref = W @ x.astype(np.float64)
+    y = oracle_mod.gemv_q4(packed, s, x)
+    assert np.max(np.abs(y - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------- one-hot probes
+def test_one_hot_columns_f32_f16(oracle_mod):
+    rng = np.random.default_rng(10)
+    M, N = 6, 40
+    A = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    A16 = f16(rng.standard_normal((M, N)))
+    for j in range(N):
+        e32 = np.zeros(N, np.float32)
+        e32[j] = 1
+        assert np.array_equal(oracle_mod.gemv_f32(A, e32), A[:, j].astype(np.float64))
+        assert np.array_equal(oracle_mod.gemv_f16(A16, e32.astype(np.float16)), A16[:, j].astype(np.float64))
+
+
+def test_one_hot_columns_q4_pin_nibble_order_and_group(oracle_mod):
+    rng = np.random.default_rng(11)
+    M, N = 5, 384
+    q = rng.integers(-8, 8, (M, N))
+    q[:, 0], q[:, 1] = -1, -7          # byte 0x9F: low nibble -1 (col 0), high nibble -7 (col 1)
+    packed = pack_int4(q)
+    assert packed[0, 0] == 0x9F
+    # distinct power-of-two scale per group so a group slip changes the value
+    s = np.array([[2.0 ** (g - 2 + i) for g in range(N // 128)] for i in range(M)], dtype=np.float16)
+    swapped = q.copy()
+    swapped[:, 0::2], swapped[:, 1::2] = q[:, 1::2], q[:, 0::2]
+    for j in range(N):
+        e = np.zeros(N, np.float16)
+        e[j] = 1
+        y = oracle_mod.gemv_q4(packed, s, e)
+        want = q[:, j] * s[:, j // 128].astype(np.float64)
+        assert np.array_equal(y, want)
+        if np.any(q[:, j] != swapped[:, j]):
+            assert not np.array_equal(y, swapped[:, j] * s[:, j // 128].astype(np.float64))
+
+
+def test_one_hot_columns_q8(oracle_mod):
+    rng = np.random.default_rng(12)
+    M, N = 4, 70
+    q = rng.integers(-128, 128, (M, N), dtype=np.int8)
+    s = f16(rng.uniform(0.5, 1.5, M) / 127)
+    for j in range(N):
+        e = np.zeros(N, np.float16)
+        e[j] = 1
+        assert np.array_equal(oracle_mod.gemv_q8(q, s, e), q[:, j].astype(np.float64) * s.astype(np.float64))
+
+
+# ---------------------------------------------------------------- degenerate and special values
+def test_empty_shapes(oracle_mod):
+    assert oracle_mod.gemv_f32(np.zeros((0, 5), np.float32), np.zeros(5, np.float32)).shape == (0,)
+    y = oracle_mod.gemv_f16(np.zeros((3, 0), np.float16), np.zeros(0, np.float16))
+    assert np.array_equal(y, np.zeros(3))
+
+
+def test_nan_and_inf_propagate(oracle_mod):
+    A = np.ones((3, 4), np.float32)
+    A[1, 2] = np.nan
+    A[2, 0] = np.inf
+    y = oracle_mod.gemv_f32(A, np.ones(4, np.float32))
+    assert y[0] == 4 and np.isnan(y[1]) and y[2] == np.inf
+
+
+def test_q4_rejects_partial_groups(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.gemv_q4(np.zeros((2, 32), np.uint8), np.zeros((2, 0), np.float16), np.zeros(64, np.float16))
+
+
+# ---------------------------------------------------------------- operation count
+class _Counted:
+    """Float wrapper counting multiplications and additions."""
+    muls = 0
+    adds = 0
+
+    def __init__(self, v):
+        self.v = v
+
+    def __mul__(self, o):
+        _Counted.muls += 1
+        return _Counted(self.v * o.v)
+
+    def __add__(self, o):
+        _Counted.adds += 1
+        return _Counted(self.v + o.v)
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (3, 4), (5, 17), (2, 128)])
+def test_flop_count_by_brute_force(M, N):
+    from memory_bound_gemv_row_amd import accounting
+
+    _Counted.muls = _Counted.adds = 0
+    A = [[_Counted(1.0) for _ in range(N)] for _ in range(M)]
+    x = [_Counted(1.0) for _ in range(N)]
+    for i in range(M):
+        acc = A[i][0] * x[0]                 # a dot product of N terms
+        for j in range(1, N):
+            acc = acc + A[i][j] * x[j]
+    assert _Counted.muls + _Counted.adds == accounting.flops(M, N)
