@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of row-major GEMV on one MI355X.
+
+One step is one GEMV call, y = A . x, on FP16 A[8192, 8192] and x[8192]
+with FP32 accumulation and output: the FP16 decode-projection workload of the
+"membound" page (section "Results").  Weights rotate through >= 1 GiB of
+device copies, so that no launch is served by the 256 MB Infinity Cache or
+the L2 ("membound", section "Two gotchas the numbers caught", gotcha 1); x
+and y stay fixed.  The same run measures a pure-read probe over the same
+ring, before and after the GEMV, and keeps the higher rate as the
+denominator ("membound", section "Why GEMV, and why MBU", and gotcha 2).
+
+Prints ONE JSON line.  ``value`` is the achieved algorithmic HBM bandwidth
+(bytes of A + x + y per call / time per call).  Extra fields:
+``roofline`` (the GEMV kernel against the 8 TB/s datasheet), ``probe``
+(the same-run pure-read ceiling and the %-of-probe), ``cpu_baseline`` (the
+CPU oracle timed on the host cores on the same inputs; its result also
+gates the GPU result, and the run aborts on a parity failure, as the pages
+do), and ``detail`` (the other FP16 shape and the INT8/INT4 speed-ups over
+FP16, timed in interleaved rounds).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMV achieved HBM GB/s and % of pure-read roofline (fp16 8192² and 4096×14336)"
+HBM_PEAK_GBPS = 8000.0
+RING_BYTES = 1 << 30
+KERNEL_SOURCES = ("memory_bound_gemv_row_amd/csrc/gemv_kernels.hpp", "memory_bound_gemv_row_amd/csrc/gemv_api.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--kind", default="f16", choices=["f32", "f16", "q8", "q4"])
+    ap.add_argument("--M", type=int, default=8192)
+    ap.add_argument("--N", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the CPU-baseline leg")
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--rounds", type=int, default=5)
+    ap.add_argument("--profile", action="store_true",
+                    help="launch each kernel exactly once after a cold flush (for counter collection)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- device workload
+class Ring:
+    """>= 1 GiB of identical weight copies in one allocation, plus x and y."""
+
+    def __init__(self, kind, M, N, ops, min_bytes=RING_BYTES):
+        import numpy as np
+        import torch
+
+        from memory_bound_gemv_row_amd import accounting
+
+        self.kind, self.M, self.N = kind, M, N
+        wbytes = accounting.weight_bytes(kind, M, N)
+        abytes = ops["A"].nbytes
+        sbytes = ops["scale"].nbytes if "scale" in ops else 0
+        self.abytes = -(-abytes // 256) * 256          # scales start on a 256-byte boundary
+        self.slot = -(-(self.abytes + sbytes) // 256) * 256
+        assert wbytes == abytes + sbytes
+        self.copies = accounting.ring_copies(kind, M, N, min_bytes)
+        self.buf = torch.empty(self.copies * self.slot, dtype=torch.uint8, device="cuda")
+        src = torch.zeros(self.slot, dtype=torch.uint8, device="cuda")
+        src[:abytes] = torch.from_numpy(np.ascontiguousarray(ops["A"]).view(np.uint8).ravel()).cuda()
+        if sbytes:
+            src[self.abytes:self.abytes + sbytes] = torch.from_numpy(
+                np.ascontiguousarray(ops["scale"]).view(np.uint8).ravel()).cuda()
+        for c in range(self.copies):
+            self.buf[c * self.slot:(c + 1) * self.slot].copy_(src)
+        del src
+        self.x = torch.from_numpy(np.ascontiguousarray(ops["x"]).view(np.uint8).ravel()).cuda()
+        self.y = torch.empty(M, dtype=torch.float32, device="cuda")
+        self.base = self.buf.data_ptr()
+        torch.cuda.synchronize()
+
+    def a_ptr(self, c):
+        return self.base + (c % self.copies) * self.slot
+
+    def s_ptr(self, c):
+        return self.a_ptr(c) + self.abytes
+
+    def launch(self, c, stream):
+        from memory_bound_gemv_row_amd import binding
+
+        k, M, N, y, x = self.kind, self.M, self.N, self.y.data_ptr(), self.x.data_ptr()
+        if k == "f32":
+            rc = binding.gemv_f32_ptr(self.a_ptr(c), x, y, M, N, stream)
+        elif k == "f16":
+            rc = binding.gemv_f16_ptr(self.a_ptr(c), x, y, M, N, stream)
+        elif k == "q8":
+            rc = binding.gemv_q8_ptr(self.a_ptr(c), self.s_ptr(c), x, y, M, N, stream)
+        else:
+            rc = binding.gemv_q4_ptr(self.a_ptr(c), self.s_ptr(c), x, y, M, N, stream)
+        if rc != 0:
+            raise RuntimeError(f"gemv_{k} returned status {rc} ({binding.status_string(rc)})")
+
+    def free(self):
+        self.buf = self.x = self.y = None
+
+
+def time_eager(ring, steps, warmup):
+    """Warm up, then time exactly `steps` launches with HIP events on the
+    stream the kernels run on.  Returns seconds per launch."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for i in range(warmup):
+        ring.launch(i, sh)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        ring.launch(warmup + i, sh)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / steps
+
+
+def graph_of(ring, launches, first=0):
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(launches):
+                ring.launch(first + i, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, launches, replays=1):
+    import torch
+
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / (launches * replays)
+
+
+def probe_gbps(buf, reps=20):
+    """Best pure-read rate over `reps` full passes of `buf`."""
+    import torch
+
+    from memory_bound_gemv_row_amd import binding
+
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nbytes = buf.numel() * buf.element_size()
+    sh = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for r in range(reps + 2):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        rc = binding.probe_read_ptr(buf.data_ptr(), nbytes, sink.data_ptr(), 0xA5A5A5A5, sh)
+        end.record()
+        if rc != 0:
+            raise RuntimeError(f"gemv_probe_read returned {rc}")
+        torch.cuda.synchronize()
+        if r >= 2:
+            best = max(best, nbytes / (start.elapsed_time(end) * 1e-3) / 1e9)
+    return best
+
+
+# ---------------------------------------------------------------- CPU baseline leg
+def cpu_baseline(kind, ops, y_gpu, seconds):
+    """Time the oracle (as it stands) on the host cores and check the GPU result
+    against it.  Returns (record, parity report)."""
+    import numpy as np
+
+    import oracle
+    from memory_bound_gemv_row_amd import accounting
+
+    oracle.build(force=False)
+    fn = {"f32": lambda: oracle.gemv_f32(ops["A"], ops["x"]),
+          "f16": lambda: oracle.gemv_f16(ops["A"], ops["x"]),
+          "q8": lambda: oracle.gemv_q8(ops["A"], ops["scale"], ops["x"]),
+          "q4": lambda: oracle.gemv_q4(ops["A"], ops["scale"], ops["x"])}[kind]
+    ref = fn()
+    times = []
+    t_end = time.perf_counter() + seconds
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 200):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    M, N = ops["A"].shape[0], (ops["A"].shape[1] * (2 if kind == "q4" else 1))
+    rec = {"value": accounting.gbps(accounting.alg_bytes(kind, M, N), t), "unit": "GB/s",
+           "cores": oracle.num_threads(), "kind": "oracle",
+           "ms_per_call": t * 1e3, "calls": len(times),
+           "sample": f"the full {kind} {M}x{N} workload (same seeded inputs), {len(times)} oracle calls, median"}
+    rep = oracle.parity_report(y_gpu, ref)
+    rep["gate"] = oracle.GATES[kind]
+    return rec, rep
+
+
+# ---------------------------------------------------------------- traffic from counters
+def traffic_record(kind, M, N):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    they were taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = t.get("workloads", {}).get(f"{kind}_{M}x{N}")
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- interleaved detail
+DETAIL_SHAPES = [
+    ("8192x8192", 8192, 8192, ("f16", "q8")),
+    ("14336x4096", 14336, 4096, ("f16", "q8", "q4")),
+    ("4096x14336", 4096, 14336, ("f16", "q4")),
+]
+
+
+def detail(rounds, launches=256):
+    import torch
+
+    from memory_bound_gemv_row_amd import accounting, inputs
+
+    out = {}
+    for name, M, N, kinds in DETAIL_SHAPES:
+        rings, graphs = {}, {}
+        for k in kinds:
+            rings[k] = Ring(k, M, N, inputs.make(k, M, N, seed=0))
+            graphs[k] = graph_of(rings[k], launches)
+            graphs[k].replay()
+        probe_buf = rings[kinds[0]].buf
+        torch.cuda.synchronize()
+        best = {k: float("inf") for k in kinds}
+        per_round = {k: [] for k in kinds}
+        probe_best = 0.0
+        for _ in range(rounds):
+            for k in kinds:
+                t = time_graph(graphs[k], launches)
+                per_round[k].append(t)
+                best[k] = min(best[k], t)
+            probe_best = max(probe_best, probe_gbps(probe_buf, reps=3))
+        rec = {"probe_gbps": probe_best}
+        for k in kinds:
+            gb = accounting.gbps(accounting.alg_bytes(k, M, N), best[k])
+            rec[k] = {"us": best[k] * 1e6, "us_median": sorted(per_round[k])[len(per_round[k]) // 2] * 1e6,
+                      "gbps": gb, "pct_of_probe": 100 * gb / max(probe_best, gb),
+                      "pct_of_8tbs": 100 * gb / HBM_PEAK_GBPS}
+        for k in kinds:
+            if k != "f16":
+                rec[k]["x_f16"] = best["f16"] / best[k]
+        out[name] = rec
+        for k in kinds:
+            rings[k].free()
+        del graphs, rings
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- main
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this GEMV library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from memory_bound_gemv_row_amd import accounting, binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    kind, M, N = args.kind, args.M, args.N
+    ops = inputs.make(kind, M, N, seed=0)
+    ring = Ring(kind, M, N, ops)
+    nbytes = accounting.alg_bytes(kind, M, N)
+
+    if args.profile:
+        # one cold launch per kernel, each after a >= 1 GiB flush read
+        flush = torch.empty(RING_BYTES, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        sh = torch.cuda.current_stream().cuda_stream
+        binding.probe_read_ptr(flush.data_ptr(), RING_BYTES, sink.data_ptr(), 0xA5A5A5A5, sh)
+        ring.launch(0, sh)
+        binding.probe_read_ptr(flush.data_ptr(), RING_BYTES, sink.data_ptr(), 0xA5A5A5A5, sh)
+        binding.probe_copy_ptr(ring.buf.data_ptr(), flush.data_ptr(), 256 << 20, sh)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": f"{kind}_{M}x{N}", "launches": 1}), flush=True)
+        return
+
+    probe_before = probe_gbps(ring.buf)
+    t = time_eager(ring, args.steps, args.warmup)
+    probe_after = probe_gbps(ring.buf)
+    y_gpu = ring.y.cpu().numpy()
+    value = accounting.gbps(nbytes, t)
+    probe = max(probe_before, probe_after)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": t * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": kind, "data": "synthetic",
+        "config": {"workload": f"{kind}_{M}x{N}", "M": M, "N": N, "accumulate": "f32", "seed": 0,
+                   "ring_copies": ring.copies, "ring_bytes": ring.copies * ring.slot,
+                   "launch": binding.describe_launch(kind, M, N, True)},
+    }
+    rec["probe"] = {"gbps": round(probe, 2), "before": round(probe_before, 2), "after": round(probe_after, 2),
+                    "pct_of_probe": round(100 * value / max(probe, value), 2),
+                    "pct_of_8tbs": round(100 * probe / HBM_PEAK_GBPS, 2)}
+    traffic = traffic_record(kind, M, N)
+    rec["roofline"] = {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                       "alg_bytes_per_launch": nbytes, "kernel_us": round(t * 1e6, 3),
+                       "gflops": round(accounting.flops(M, N) / t / 1e9, 1)}
+    ring.free()
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(kind, ops, y_gpu, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu
+        rec["parity"] = parity
+        if not parity["floored_rel"] <= parity["gate"]:
+            print(json.dumps({"error": "parity failure: GPU result disagrees with the oracle", "parity": parity}),
+                  flush=True)
+            sys.exit(3)
+    else:
+        rec["cpu_baseline"] = None
+
+    if not args.no_detail:
+        rec["detail"] = detail(args.rounds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

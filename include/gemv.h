@@ -1,0 +1,137 @@
+/*
+ * gemv.h -- C ABI of the MI355X (gfx950) row-major GEMV library.
+ *
+ *     y[M] = A[M, N] . x[N],   y_i = sum_j A_ij x_j
+ *
+ * The operation is the plain matrix-vector product ("Making GEMV Fast",
+ * section "Algorithm"; the llama.cpp FP16 GEMV walkthrough, opening
+ * equation), with A dense and row-major: element (i, j) at linear offset
+ * i*N + j, leading dimension N, no stride argument ("Making GEMV Fast",
+ * section "Row-major indexing refresher").  Four storage formats; every one
+ * accumulates in FP32 and writes FP32 y.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Pointers   Device pointers (hipMalloc'd or any device-accessible
+ *              allocation).  The caller owns every buffer.  The library
+ *              allocates nothing, keeps no pointer after returning, and needs
+ *              no workspace.
+ *   Binary16   FP16 values (x, FP16 A, scales) are passed as IEEE 754
+ *              binary16 bit patterns in uint16_t.  Subnormals are honoured.
+ *   Stream     Work is enqueued on `stream` (0 = the null stream) and the
+ *              call returns without synchronising; y is valid once the
+ *              caller synchronises that stream.
+ *   Semantics  y is overwritten (no alpha/beta, no accumulation into y).
+ *              N == 0 writes y = 0 (the empty sum).  M == 0 is a no-op.
+ *   Aliasing   y must not overlap A, x or scale.
+ *   Alignment  Any alignment is accepted.  The bandwidth path needs
+ *              16-byte-aligned A and x and a row length in bytes that is a
+ *              multiple of 16; other inputs take a slower element-wise path.
+ *   Results    Deterministic: the reduction order depends only on (format,
+ *              M, N, pointer alignment, device), so repeated calls give
+ *              bitwise identical y.  No atomics.
+ *   Errors     Every entry point returns a gemv_status and never prints or
+ *              exits.  Invalid arguments are rejected before anything is
+ *              enqueued.  Faults during execution surface at the caller's
+ *              next synchronisation, as for any HIP kernel.
+ *   Threads    Entry points are thread-safe and may be called concurrently on
+ *              different streams.
+ */
+#ifndef MBGR_GEMV_H
+#define MBGR_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same typedef as the HIP runtime header, so that C callers need no HIP headers. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum gemv_status {
+    GEMV_OK = 0,
+    GEMV_E_INVAL = 1,       /* negative M or N, or a null pointer where data is needed */
+    GEMV_E_UNSUPPORTED = 2, /* format constraint violated (INT4: N % 128 != 0)        */
+    GEMV_E_LAUNCH = 3,      /* the HIP runtime refused the kernel launch             */
+    GEMV_E_DEVICE = 4       /* no current HIP device or its properties are unreadable */
+} gemv_status;
+
+/* FP32: A float[M*N] row-major, x float[N], y float[M].
+ * ("cuda-gemv-optimization", section "Results": FP32 row-major GEMV.) */
+int gemv_f32(const float* A, const float* x, float* y, int M, int N, hipStream_t stream);
+
+/* FP16 weights and activations, FP32 accumulation and output:
+ * A binary16[M*N] row-major, x binary16[N], y float[M].
+ * (llama.cpp FP16 GEMV walkthrough: FP16 weight and hidden state, FP32
+ * accumulation and output; "membound", section "Results".) */
+int gemv_f16(const uint16_t* A, const uint16_t* x, float* y, int M, int N, hipStream_t stream);
+
+/* INT8 weights with one symmetric binary16 scale per row:
+ *   A int8[M*N] row-major, scale binary16[M], x binary16[N], y float[M],
+ *   y_i = sum_j (A_ij * scale_i) * x_j.
+ * Every int8 value, -128 included, is accepted.
+ * ("membound", section "The kernel decode actually runs: dequant GEMV".) */
+int gemv_q8(const int8_t* A, const uint16_t* scale, const uint16_t* x, float* y, int M, int N,
+            hipStream_t stream);
+
+/* INT4 weights, two per byte, with one symmetric binary16 scale per row and
+ * 128-column group:
+ *   A uint8[M*(N/2)] row-major; byte (i, k) holds column 2k in its low
+ *     nibble and column 2k+1 in its high nibble, each a two's-complement
+ *     value in [-8, 7];
+ *   scale binary16[M*(N/128)] row-major, scale[i*(N/128) + j/128] covers
+ *     columns j of row i;
+ *   x binary16[N], y float[M],
+ *   y_i = sum_j (q_ij * scale_{i, j/128}) * x_j.
+ * N must be a multiple of 128 (GEMV_E_UNSUPPORTED otherwise).
+ * ("membound", section "The kernel decode actually runs: dequant GEMV":
+ * symmetric per-group-of-128 scales.) */
+int gemv_q4(const uint8_t* A, const uint16_t* scale, const uint16_t* x, float* y, int M, int N,
+            hipStream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* gemv_status_string(int status);
+
+/* ---- measurement kernels --------------------------------------------------
+ * The pages measure a GEMV against the bandwidth a plain stream achieves on
+ * the same device in the same run: a pure-read probe is the denominator for
+ * GEMV's read-dominated traffic, a streaming copy for balanced read+write
+ * traffic ("membound", section "Why GEMV, and why MBU").  These are those
+ * probes; they are not part of the GEMV computation.
+ */
+
+/* Reads `bytes` bytes of `buf` once with 16-byte loads.  `bytes` must be a
+ * multiple of 16 and `buf` 16-byte aligned (GEMV_E_INVAL otherwise).  The
+ * loaded words are XOR-folded; the fold is written to `sink[0]` only if it
+ * equals `guard`, so the reads cannot be optimised away and nothing is
+ * normally written.  `sink` must point to at least 4 writable bytes. */
+int gemv_probe_read(const void* buf, size_t bytes, uint32_t* sink, uint32_t guard, hipStream_t stream);
+
+/* Copies `bytes` bytes from `src` to `dst` with 16-byte loads and stores.
+ * Same size and alignment rules; the buffers must not overlap. */
+int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+/* Launch geometry the library uses for a call.  kind: 0 f32, 1 f16, 2 q8,
+ * 3 q4.  `aligned` states whether A and x are 16-byte aligned.  Writes
+ * grid size, workgroup size, rows per wave, LDS bytes, and a variant tag
+ * (1 = bandwidth path with x in LDS, 2 = bandwidth path with x read from
+ * global memory, 3 = element-wise path).  Returns GEMV_OK or an error code;
+ * it queries the current device's compute-unit count. */
+typedef struct gemv_launch_info {
+    int variant;
+    int grid;
+    int block;
+    int rows_per_wave;
+    int unroll;          /* 16-byte loads per lane and row issued together */
+    int lds_bytes;
+} gemv_launch_info;
+
+int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBGR_GEMV_H */

@@ -5,3 +5,12 @@ The compute lives in a hand-written HIP library behind a C ABI
 library is loaded on first use and its absence is an error: there is no CPU
 fallback.
 """
+
+from .binding import (  # noqa: F401,E402  (no library load at import time)
+    GemvError,
+    gemv_f32,
+    gemv_f16,
+    gemv_q8,
+    gemv_q4,
+    describe_launch,
+)

@@ -1,0 +1,201 @@
+"""ctypes binding over the C ABI in ``include/gemv.h``.
+
+Argument marshalling only: every step of the product runs in the HIP
+library.  PyTorch supplies device memory and the current stream; no torch
+operator is on the path.  If the library is missing the first call raises:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgemv_amd.so")
+
+KIND = {"f32": 0, "f16": 1, "q8": 2, "q4": 3}
+STATUS = {0: "GEMV_OK", 1: "GEMV_E_INVAL", 2: "GEMV_E_UNSUPPORTED", 3: "GEMV_E_LAUNCH", 4: "GEMV_E_DEVICE"}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GemvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("grid", ctypes.c_int), ("block", ctypes.c_int),
+                ("rows_per_wave", ctypes.c_int), ("unroll", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+
+
+def load():
+    """Load the in-tree library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run python -m memory_bound_gemv_row_amd.build)")
+        lib = ctypes.CDLL(LIB_PATH)
+        p, i = ctypes.c_void_p, ctypes.c_int
+        for name in ("gemv_f32", "gemv_f16"):
+            getattr(lib, name).argtypes = [p, p, p, i, i, p]
+            getattr(lib, name).restype = i
+        for name in ("gemv_q8", "gemv_q4"):
+            getattr(lib, name).argtypes = [p, p, p, p, i, i, p]
+            getattr(lib, name).restype = i
+        lib.gemv_status_string.argtypes = [i]
+        lib.gemv_status_string.restype = ctypes.c_char_p
+        lib.gemv_probe_read.argtypes = [p, ctypes.c_size_t, p, ctypes.c_uint32, p]
+        lib.gemv_probe_read.restype = i
+        lib.gemv_probe_copy.argtypes = [p, p, ctypes.c_size_t, p]
+        lib.gemv_probe_copy.restype = i
+        lib.gemv_describe_launch.argtypes = [i, i, i, i, ctypes.POINTER(LaunchInfo)]
+        lib.gemv_describe_launch.restype = i
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().gemv_status_string(int(status)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise GemvError(rc, where)
+
+
+# ---------------------------------------------------------------- raw pointers
+# Device pointers as integers, stream as an integer handle (0 = null stream).
+def gemv_f32_ptr(A: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_f32(A, x, y, M, N, stream)
+
+
+def gemv_f16_ptr(A: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_f16(A, x, y, M, N, stream)
+
+
+def gemv_q8_ptr(A: int, scale: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_q8(A, scale, x, y, M, N, stream)
+
+
+def gemv_q4_ptr(A: int, scale: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_q4(A, scale, x, y, M, N, stream)
+
+
+def probe_read_ptr(buf: int, nbytes: int, sink: int, guard: int = 0xA5A5A5A5, stream: int = 0) -> int:
+    return load().gemv_probe_read(buf, nbytes, sink, guard, stream)
+
+
+def probe_copy_ptr(src: int, dst: int, nbytes: int, stream: int = 0) -> int:
+    return load().gemv_probe_copy(src, dst, nbytes, stream)
+
+
+def describe_launch(kind: str, M: int, N: int, aligned: bool = True) -> dict:
+    info = LaunchInfo()
+    _check(load().gemv_describe_launch(KIND[kind], M, N, int(aligned), ctypes.byref(info)), "gemv_describe_launch")
+    return {f: getattr(info, f) for f, _ in LaunchInfo._fields_}
+
+
+# ---------------------------------------------------------------- torch tensors
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtypes, shape):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _out(out, M, device):
+    import torch
+
+    if out is None:
+        return torch.empty(M, dtype=torch.float32, device=device)
+    _need(out, "out", (torch.float32,), (M,))
+    return out
+
+
+def gemv_f32(A, x, out=None, stream=None):
+    import torch
+
+    M, N = A.shape
+    a = _need(A, "A", (torch.float32,), (M, N))
+    xp = _need(x, "x", (torch.float32,), (N,))
+    y = _out(out, M, A.device)
+    _check(gemv_f32_ptr(a, xp, y.data_ptr(), M, N, _stream(stream)), "gemv_f32")
+    return y
+
+
+def gemv_f16(A, x, out=None, stream=None):
+    import torch
+
+    h = (torch.float16, torch.int16, torch.uint16)
+    M, N = A.shape
+    a = _need(A, "A", h, (M, N))
+    xp = _need(x, "x", h, (N,))
+    y = _out(out, M, A.device)
+    _check(gemv_f16_ptr(a, xp, y.data_ptr(), M, N, _stream(stream)), "gemv_f16")
+    return y
+
+
+def gemv_q8(A, scale, x, out=None, stream=None):
+    import torch
+
+    h = (torch.float16, torch.int16, torch.uint16)
+    M, N = A.shape
+    a = _need(A, "A", (torch.int8,), (M, N))
+    s = _need(scale, "scale", h, (M,))
+    xp = _need(x, "x", h, (N,))
+    y = _out(out, M, A.device)
+    _check(gemv_q8_ptr(a, s, xp, y.data_ptr(), M, N, _stream(stream)), "gemv_q8")
+    return y
+
+
+def gemv_q4(A, scale, x, out=None, stream=None):
+    """A: uint8 [M, N/2] (two INT4 per byte, low nibble = even column),
+    scale: binary16 [M, N/128], x: binary16 [N]."""
+    import torch
+
+    h = (torch.float16, torch.int16, torch.uint16)
+    M, half = A.shape
+    N = 2 * half
+    a = _need(A, "A", (torch.uint8,), (M, half))
+    if N % 128:
+        raise ValueError("INT4 needs N % 128 == 0")
+    s = _need(scale, "scale", h, (M, N // 128))
+    xp = _need(x, "x", h, (N,))
+    y = _out(out, M, A.device)
+    _check(gemv_q4_ptr(a, s, xp, y.data_ptr(), M, N, _stream(stream)), "gemv_q4")
+    return y
+
+
+def probe_read(buf, sink, guard: int = 0xA5A5A5A5, stream=None):
+    _check(probe_read_ptr(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), guard,
+                          _stream(stream)), "gemv_probe_read")
+
+
+def probe_copy(src, dst, stream=None):
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    _check(probe_copy_ptr(src.data_ptr(), dst.data_ptr(), n, _stream(stream)), "gemv_probe_copy")

@@ -1,0 +1,292 @@
+// gemv_api.hip -- C ABI of the gfx950 GEMV library (declared in include/gemv.h).
+//
+// Host side only: argument validation, choice of kernel variant and launch
+// geometry, and the launch itself on the caller's stream.  The host
+// launcher of the pages picks the grid and block and launches
+// asynchronously ("Making GEMV Fast", the launch_kernel functions); here the
+// grid is sized from the row count and the device's compute-unit count, and
+// a launch failure is returned as a status instead of ending the process.
+#include "gemv.h"
+#include "gemv_kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+namespace gemv {
+namespace {
+
+constexpr int kWaves = 4;                  // waves per workgroup (256 threads)
+constexpr int kMaxLdsBytes = 64 * 1024;    // x staged in LDS up to this size
+constexpr bool kNT = true;                 // stream A with non-temporal loads
+constexpr int kMaxDevices = 64;
+
+std::mutex g_cu_mutex;
+int g_cu_count[kMaxDevices] = {0};
+
+// Compute-unit count of the current device, cached per device.
+int current_cu_count(int* out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMV_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (g_cu_count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return GEMV_E_DEVICE;
+        g_cu_count[dev] = n;
+    }
+    *out = g_cu_count[dev];
+    return GEMV_OK;
+}
+
+int elems_per_chunk(int kind)
+{
+    switch (kind) {
+    case kF32: return Traits<kF32>::kElems;
+    case kF16: return Traits<kF16>::kElems;
+    case kQ8: return Traits<kQ8>::kElems;
+    default: return Traits<kQ4>::kElems;
+    }
+}
+
+int x_granules_per_chunk(int kind)
+{
+    switch (kind) {
+    case kF32: return Traits<kF32>::kXGran;
+    case kF16: return Traits<kF16>::kXGran;
+    case kQ8: return Traits<kQ8>::kXGran;
+    default: return Traits<kQ4>::kXGran;
+    }
+}
+
+struct Plan {
+    int variant;   // 1 rows+LDS x, 2 rows+global x, 3 element-wise
+    int grid;
+    int block;
+    int R;
+    int U;
+    int lds;
+};
+
+// Geometry for one call.  A row of nchunks 16-byte chunks takes
+// passes = ceil(nchunks/64) wave-wide loads.  Long rows: one row per wave
+// and up to 8 loads in flight per lane.  Short rows: several rows per wave,
+// so each wave still has several KiB in flight and x reads are shared.
+Plan make_plan(int kind, int M, int N, bool aligned)
+{
+    Plan p{};
+    const int epc = elems_per_chunk(kind);
+    if (!aligned || N == 0 || N % epc != 0) {
+        p.variant = 3;
+        p.block = 256;
+        p.grid = (M + 3) / 4;
+        p.R = 1;
+        p.U = 1;
+        return p;
+    }
+    const int nchunks = N / epc;
+    const int passes = (nchunks + 63) / 64;
+    p.U = passes >= 5 ? 8 : (passes >= 3 ? 4 : (passes == 2 ? 2 : 1));
+    p.R = passes >= 4 ? 1 : (passes >= 2 ? 2 : 4);
+    const int64_t xbytes = (int64_t)nchunks * x_granules_per_chunk(kind) * 16;
+    if (xbytes <= kMaxLdsBytes) {
+        p.variant = 1;
+        p.lds = (int)xbytes;
+    } else {
+        p.variant = 2;
+        p.lds = 0;
+        p.R = 1;
+        p.U = 8;
+    }
+    p.block = kWaves * 64;
+    const int64_t ngroups = ((int64_t)M + p.R - 1) / p.R;
+    p.grid = (int)((ngroups + kWaves - 1) / kWaves);
+    return p;
+}
+
+template <int F, int R, int U>
+const void* rows_kernel(bool xlds)
+{
+    return xlds ? reinterpret_cast<const void*>(&gemv_rows<F, kWaves, R, U, true, kNT>)
+                : reinterpret_cast<const void*>(&gemv_rows<F, kWaves, R, U, false, kNT>);
+}
+
+template <int F, int R>
+const void* rows_kernel_u(int U, bool xlds)
+{
+    switch (U) {
+    case 1: return rows_kernel<F, R, 1>(xlds);
+    case 2: return rows_kernel<F, R, 2>(xlds);
+    case 4: return rows_kernel<F, R, 4>(xlds);
+    default: return rows_kernel<F, R, 8>(xlds);
+    }
+}
+
+template <int F>
+const void* select_kernel(const Plan& p)
+{
+    if (p.variant == 3)
+        return reinterpret_cast<const void*>(&gemv_elementwise<F>);
+    switch (p.R) {
+    case 1: return rows_kernel_u<F, 1>(p.U, p.variant == 1);
+    case 2: return rows_kernel_u<F, 2>(p.U, p.variant == 1);
+    default: return rows_kernel_u<F, 4>(p.U, p.variant == 1);
+    }
+}
+
+const void* kernel_for(int kind, const Plan& p)
+{
+    switch (kind) {
+    case kF32: return select_kernel<kF32>(p);
+    case kF16: return select_kernel<kF16>(p);
+    case kQ8: return select_kernel<kQ8>(p);
+    default: return select_kernel<kQ4>(p);
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch(int kind, const void* A, const uint16_t* scale, const void* x, float* y, int M, int N,
+           hipStream_t stream)
+{
+    if (M < 0 || N < 0)
+        return GEMV_E_INVAL;
+    if (kind == kQ4 && N % 128 != 0)
+        return GEMV_E_UNSUPPORTED;
+    if (M == 0)
+        return GEMV_OK;
+    if (y == nullptr)
+        return GEMV_E_INVAL;
+    if (N > 0 && (A == nullptr || x == nullptr))
+        return GEMV_E_INVAL;
+    if ((kind == kQ8 || kind == kQ4) && N > 0 && scale == nullptr)
+        return GEMV_E_INVAL;
+    int cus = 0;
+    if (int rc = current_cu_count(&cus); rc != GEMV_OK)
+        return rc;
+    const bool aligned = aligned16(A) && aligned16(x);
+    const Plan p = make_plan(kind, M, N, aligned);
+    const uint8_t* a8 = static_cast<const uint8_t*>(A);
+    const uint8_t* x8 = static_cast<const uint8_t*>(x);
+    void* args[] = {(void*)&a8, (void*)&scale, (void*)&x8, (void*)&y, (void*)&M, (void*)&N};
+    const hipError_t err = hipLaunchKernel(kernel_for(kind, p), dim3(p.grid), dim3(p.block), args,
+                                           (size_t)p.lds, stream);
+    return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
+}
+
+// Probe geometry: enough 256-thread workgroups to give every CU 8 of them.
+constexpr int kProbeU = 4;
+constexpr int kProbeWgPerCu = 8;
+
+int probe_grid(int64_t n16, int* grid)
+{
+    int cus = 0;
+    if (int rc = current_cu_count(&cus); rc != GEMV_OK)
+        return rc;
+    const int64_t per_wg = 256 * kProbeU;
+    const int64_t need = (n16 + per_wg - 1) / per_wg;
+    const int64_t cap = (int64_t)cus * kProbeWgPerCu;
+    *grid = (int)(need < cap ? need : cap);
+    return GEMV_OK;
+}
+
+}  // namespace
+}  // namespace gemv
+
+extern "C" {
+
+int gemv_f32(const float* A, const float* x, float* y, int M, int N, hipStream_t stream)
+{
+    return gemv::launch(gemv::kF32, A, nullptr, x, y, M, N, stream);
+}
+
+int gemv_f16(const uint16_t* A, const uint16_t* x, float* y, int M, int N, hipStream_t stream)
+{
+    return gemv::launch(gemv::kF16, A, nullptr, x, y, M, N, stream);
+}
+
+int gemv_q8(const int8_t* A, const uint16_t* scale, const uint16_t* x, float* y, int M, int N,
+            hipStream_t stream)
+{
+    return gemv::launch(gemv::kQ8, A, scale, x, y, M, N, stream);
+}
+
+int gemv_q4(const uint8_t* A, const uint16_t* scale, const uint16_t* x, float* y, int M, int N,
+            hipStream_t stream)
+{
+    return gemv::launch(gemv::kQ4, A, scale, x, y, M, N, stream);
+}
+
+const char* gemv_status_string(int status)
+{
+    switch (status) {
+    case GEMV_OK: return "ok";
+    case GEMV_E_INVAL: return "invalid argument";
+    case GEMV_E_UNSUPPORTED: return "unsupported shape for this format";
+    case GEMV_E_LAUNCH: return "kernel launch failed";
+    case GEMV_E_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+    }
+}
+
+int gemv_probe_read(const void* buf, size_t bytes, uint32_t* sink, uint32_t guard, hipStream_t stream)
+{
+    if (bytes % 16 != 0 || (bytes > 0 && (buf == nullptr || !gemv::aligned16(buf))) || sink == nullptr)
+        return GEMV_E_INVAL;
+    if (bytes == 0)
+        return GEMV_OK;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    int grid = 0;
+    if (int rc = gemv::probe_grid(n16, &grid); rc != GEMV_OK)
+        return rc;
+    const gemv::u32x4* b = static_cast<const gemv::u32x4*>(buf);
+    void* args[] = {(void*)&b, (void*)&n16, (void*)&sink, (void*)&guard};
+    const hipError_t err = hipLaunchKernel(
+        reinterpret_cast<const void*>(&gemv::probe_read_kernel<gemv::kProbeU, gemv::kNT>), dim3(grid),
+        dim3(256), args, 0, stream);
+    return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
+}
+
+int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream)
+{
+    if (bytes % 16 != 0)
+        return GEMV_E_INVAL;
+    if (bytes == 0)
+        return GEMV_OK;
+    if (src == nullptr || dst == nullptr || !gemv::aligned16(src) || !gemv::aligned16(dst))
+        return GEMV_E_INVAL;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    int grid = 0;
+    if (int rc = gemv::probe_grid(n16, &grid); rc != GEMV_OK)
+        return rc;
+    const gemv::u32x4* s = static_cast<const gemv::u32x4*>(src);
+    gemv::u32x4* d = static_cast<gemv::u32x4*>(dst);
+    void* args[] = {(void*)&s, (void*)&d, (void*)&n16};
+    const hipError_t err = hipLaunchKernel(
+        reinterpret_cast<const void*>(&gemv::probe_copy_kernel<gemv::kProbeU, gemv::kNT>), dim3(grid),
+        dim3(256), args, 0, stream);
+    return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
+}
+
+int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info)
+{
+    if (info == nullptr || kind < 0 || kind > 3 || M < 0 || N < 0)
+        return GEMV_E_INVAL;
+    if (kind == gemv::kQ4 && N % 128 != 0)
+        return GEMV_E_UNSUPPORTED;
+    int cus = 0;
+    if (int rc = gemv::current_cu_count(&cus); rc != GEMV_OK)
+        return rc;
+    const gemv::Plan p = gemv::make_plan(kind, M, N, aligned != 0);
+    info->variant = p.variant;
+    info->grid = p.grid;
+    info->block = p.block;
+    info->rows_per_wave = p.R;
+    info->unroll = p.U;
+    info->lds_bytes = p.lds;
+    return GEMV_OK;
+}
+
+}  // extern "C"

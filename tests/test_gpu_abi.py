@@ -1,0 +1,151 @@
+"""GPU checks of the C-ABI contract: status codes, degenerate sizes, output
+bounds, streams, determinism, unaligned operands and the probes."""
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_gemv_row_amd import binding, inputs
+
+from gpu_util import dev, run_gpu, run_oracle, say
+from oracle.metrics import GATES, parity_error
+
+pytestmark = pytest.mark.gpu
+
+
+def _ptrs(kind, ops):
+    A = dev(ops["A"])
+    x = dev(ops["x"])
+    s = dev(ops["scale"]) if "scale" in ops else None
+    return A, s, x
+
+
+def _call(kind, A, s, x, y, M, N, stream=0):
+    if kind == "f32":
+        return binding.gemv_f32_ptr(A, x, y, M, N, stream)
+    if kind == "f16":
+        return binding.gemv_f16_ptr(A, x, y, M, N, stream)
+    if kind == "q8":
+        return binding.gemv_q8_ptr(A, s, x, y, M, N, stream)
+    return binding.gemv_q4_ptr(A, s, x, y, M, N, stream)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+def test_status_codes(gpu, kind):
+    M, N = 8, 256
+    A, s, x = _ptrs(kind, inputs.make(kind, M, N))
+    y = torch.zeros(M, device="cuda")
+    sp = s.data_ptr() if s is not None else 0
+    a, xp, yp = A.data_ptr(), x.data_ptr(), y.data_ptr()
+    say(f"[status] {kind}")
+    assert _call(kind, a, sp, xp, yp, -1, N) == 1
+    assert _call(kind, a, sp, xp, yp, M, -5) == 1
+    assert _call(kind, a, sp, xp, 0, M, N) == 1
+    assert _call(kind, 0, sp, xp, yp, M, N) == 1
+    assert _call(kind, a, sp, 0, yp, M, N) == 1
+    if kind in ("q8", "q4"):
+        assert _call(kind, a, 0, xp, yp, M, N) == 1
+    assert _call(kind, 0, 0, 0, 0, 0, N) == 0          # M == 0: nothing to do
+    if kind == "q4":
+        assert _call(kind, a, sp, xp, yp, M, 200) == 2   # partial 128-column group
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)                            # rejected calls wrote nothing
+    with pytest.raises(ValueError):     # the binding checks shapes before the call
+        binding.gemv_f32(torch.zeros(4, 4, device="cuda"), torch.zeros(5, device="cuda"))
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+def test_n_zero_writes_zeros(gpu, kind):
+    M = 70
+    y = torch.full((M,), 7.0, device="cuda")
+    A = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    scale = torch.full((M,), float("inf"), dtype=torch.float16, device="cuda")   # must not matter
+    say(f"[N=0] {kind}")
+    assert _call(kind, A.data_ptr(), scale.data_ptr(), A.data_ptr(), y.data_ptr(), M, 0) == 0
+    assert _call(kind, 0, 0, 0, y.data_ptr(), M, 0) == 0      # nothing is read when N == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+def test_writes_only_y_0_to_M(gpu, oracle_mod, kind):
+    M, N = 37, 1024
+    ops = inputs.make(kind, M, N, seed=2)
+    A, s, x = _ptrs(kind, ops)
+    guard = torch.full((M + 128,), 12345.0, device="cuda")
+    y = guard[64:64 + M]
+    say(f"[canary] {kind}")
+    assert _call(kind, A.data_ptr(), s.data_ptr() if s is not None else 0, x.data_ptr(), y.data_ptr(), M, N) == 0
+    torch.cuda.synchronize()
+    g = guard.cpu().numpy()
+    assert np.all(g[:64] == 12345.0) and np.all(g[64 + M:] == 12345.0)
+    assert parity_error(g[64:64 + M], run_oracle(oracle_mod, kind, ops)) <= GATES[kind]
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+def test_repeat_runs_bitwise_identical(gpu, kind):
+    ops = inputs.make(kind, 1000, 4096, seed=4)
+    say(f"[determinism] {kind}")
+    ys = [run_gpu(kind, ops) for _ in range(3)]
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
+def test_non_default_stream(gpu, oracle_mod):
+    ops = inputs.make("f16", 2048, 4096, seed=6)
+    A, _, x = _ptrs("f16", ops)
+    s = torch.cuda.Stream()
+    y = torch.empty(2048, device="cuda")
+    torch.cuda.synchronize()
+    say("[stream]")
+    with torch.cuda.stream(s):
+        binding.gemv_f16(A, x, out=y)          # binding passes the current stream
+    s.synchronize()
+    assert parity_error(y.cpu().numpy(), run_oracle(oracle_mod, "f16", ops)) <= GATES["f16"]
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("offset", [2, 4, 8])
+def test_unaligned_operands(gpu, oracle_mod, kind, offset):
+    """A and x at byte offsets that break 16-byte alignment take the
+    element-wise path and still agree with the oracle."""
+    M, N = 33, 1024
+    ops = inputs.make(kind, M, N, seed=offset)
+    elt = {"f32": 4, "f16": 2, "q8": 1, "q4": 1}[kind]
+    if offset % elt:
+        pytest.skip("offset not a multiple of the element size")
+    Ab = ops["A"].view(np.uint8).ravel()
+    xb = ops["x"].view(np.uint8).ravel()
+    bufA = torch.zeros(Ab.size + 64, dtype=torch.uint8, device="cuda")
+    bufx = torch.zeros(xb.size + 64, dtype=torch.uint8, device="cuda")
+    bufA[offset:offset + Ab.size] = dev(Ab)
+    bufx[offset:offset + xb.size] = dev(xb)
+    s = dev(ops["scale"]) if "scale" in ops else None
+    y = torch.empty(M, device="cuda")
+    say(f"[unaligned] {kind} +{offset}")
+    rc = _call(kind, bufA.data_ptr() + offset, s.data_ptr() if s is not None else 0,
+               bufx.data_ptr() + offset, y.data_ptr(), M, N)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert parity_error(y.cpu().numpy(), run_oracle(oracle_mod, kind, ops)) <= GATES[kind]
+
+
+def test_describe_launch_fills_all_cus(gpu):
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    for kind, M, N in (("f32", 1024, 1024), ("f16", 8192, 8192), ("q4", 4096, 14336), ("q4", 14336, 4096)):
+        info = binding.describe_launch(kind, M, N)
+        assert info["grid"] >= cus, (kind, M, N, info, cus)
+    assert binding.describe_launch("f16", 8, 1001)["variant"] == 3
+
+
+def test_probe_copy_and_read(gpu):
+    n = 64 << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    say("[probe]")
+    binding.probe_copy(src, dst)
+    binding.probe_read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert binding.probe_read_ptr(src.data_ptr() + 4, 1024, sink.data_ptr()) == 1   # misaligned
+    assert binding.probe_read_ptr(src.data_ptr(), 1000, sink.data_ptr()) == 1       # not a multiple of 16

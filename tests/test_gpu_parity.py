@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Full-size workloads are compared element by element on every output (the
+oracle computes them all in seconds), in the same launch configuration the
+benchmark times.  Smaller shapes cover several tiles and ragged tails, both
+kernel variants (16-byte chunks and the element-wise path), every
+rows-per-wave setting, and the degenerate cases.  Integer-valued and
+subnormal inputs make every summation order exact, so those cases must match
+bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_gemv_row_amd import inputs, binding
+from oracle.metrics import GATES, parity_report
+
+from gpu_util import dev, run_gpu, run_oracle, say
+from qpack import pack_int4, f16
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(oracle, kind, ops, label):
+    say(f"[parity] {label}")
+    y = run_gpu(kind, ops)
+    ref = run_oracle(oracle, kind, ops)
+    rep = parity_report(y, ref)
+    assert rep["floored_rel"] <= GATES[kind], (label, rep)
+    return rep
+
+
+# ---------------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("w", inputs.all_workloads(), ids=lambda w: w.name)
+def test_full_size_workload(gpu, oracle_mod, w):
+    ops = inputs.make(w.kind, w.M, w.N, seed=0)
+    info = binding.describe_launch(w.kind, w.M, w.N, aligned=True)
+    assert info["variant"] in (1, 2), info       # the bandwidth path is what runs
+    rep = _check(oracle_mod, w.kind, ops, f"{w.name} seed 0 {info}")
+    print(w.name, rep)
+
+
+# ---------------------------------------------------------------- shapes, tiles, tails
+_MS = [1, 2, 3, 4, 5, 7, 9, 16, 17, 33, 65, 257]
+_NS = {
+    # multiples of the chunk width (bandwidth path) and ragged ones (element-wise)
+    "f32": [1, 3, 4, 8, 60, 64, 252, 256, 260, 1020, 1024, 2052, 4100, 9000, 17000],
+    "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 8200, 14336, 20000],
+    "q8": [1, 15, 16, 32, 1008, 1024, 1040, 5000, 8192, 9232, 20000],
+    "q4": [128, 256, 384, 1024, 2048, 2176, 4096, 7296, 14336],
+}
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+def test_shapes_and_tails(gpu, oracle_mod, kind):
+    for N in _NS[kind]:
+        for M in _MS:
+            ops = inputs.make(kind, M, N, seed=M * 7919 + N)
+            _check(oracle_mod, kind, ops, f"{kind} M={M} N={N}")
+
+
+@pytest.mark.parametrize("kind,N", [("f32", 64 * 4 * 8 * 2 + 4), ("f16", 64 * 8 * 17 + 8), ("q8", 64 * 16 * 9 + 16),
+                                    ("q4", 64 * 32 * 3 + 128)])
+def test_many_passes_and_row_groups(gpu, oracle_mod, kind, N):
+    # enough rows for several workgroups, a partial last workgroup, and rows
+    # whose chunk count leaves a partly filled final pass
+    ops = inputs.make(kind, 4 * 50 + 3, N, seed=5)
+    _check(oracle_mod, kind, ops, f"{kind} tiles N={N}")
+
+
+# ---------------------------------------------------------------- exactness
+def _int_ops(kind, M, N, rng):
+    x = rng.integers(-3, 4, N)
+    if kind == "f32":
+        return {"A": rng.integers(-3, 4, (M, N)).astype(np.float32), "x": x.astype(np.float32)}
+    if kind == "f16":
+        return {"A": rng.integers(-3, 4, (M, N)).astype(np.float16), "x": x.astype(np.float16)}
+    if kind == "q8":
+        return {"A": rng.integers(-128, 128, (M, N), dtype=np.int8),
+                "scale": np.full(M, 2.0 ** -7, np.float16), "x": x.astype(np.float16)}
+    q = rng.integers(-8, 8, (M, N))
+    g = np.arange(N // 128)
+    s = np.tile((2.0 ** (g % 8 - 4)).astype(np.float16), (M, 1))
+    return {"A": pack_int4(q), "scale": s, "x": x.astype(np.float16)}
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("M,N", [(37, 1024), (8, 4096), (300, 256), (5, 1152)])
+def test_integer_inputs_bit_exact(gpu, oracle_mod, kind, M, N):
+    ops = _int_ops(kind, M, N, np.random.default_rng(M + N))
+    say(f"[exact] {kind} M={M} N={N}")
+    y = run_gpu(kind, ops)
+    ref = run_oracle(oracle_mod, kind, ops)
+    assert np.array_equal(y.astype(np.float64), ref), (kind, np.max(np.abs(y - ref)))
+
+
+@pytest.mark.parametrize("N", [512, 4096, 1000])
+def test_f16_subnormal_operands_bit_exact(gpu, oracle_mod, N):
+    # A made only of binary16 subnormals k * 2^-24 (k in [-1023, 1023]) and
+    # integer x: every partial sum is k' * 2^-24 with |k'| < 2^24, exact in FP32.
+    rng = np.random.default_rng(N)
+    M = 40
+    k = rng.integers(-1023, 1024, (M, N))
+    A = (np.where(k < 0, 0x8000, 0) | np.abs(k)).astype(np.uint16).view(np.float16)
+    x = rng.integers(-3, 4, N).astype(np.float16)
+    ops = {"A": A, "x": x}
+    say(f"[subnormal A] N={N}")
+    y = run_gpu("f16", ops)
+    ref = run_oracle(oracle_mod, "f16", ops)
+    assert np.array_equal(y.astype(np.float64), ref)
+    # the same with the roles swapped: subnormal x, integer A
+    ops = {"A": rng.integers(-3, 4, (M, N)).astype(np.float16), "x": A[0].copy()}
+    say(f"[subnormal x] N={N}")
+    assert np.array_equal(run_gpu("f16", ops).astype(np.float64), run_oracle(oracle_mod, "f16", ops))
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_quantised_subnormal_x_bit_exact(gpu, oracle_mod, kind):
+    rng = np.random.default_rng(3)
+    M, N = 24, 2048
+    ops = _int_ops(kind, M, N, rng)
+    # |k| <= 15 keeps every partial sum below 2^24 units of its finest term
+    k = rng.integers(-15, 16, N)
+    ops["x"] = (np.where(k < 0, 0x8000, 0) | np.abs(k)).astype(np.uint16).view(np.float16)
+    say(f"[subnormal x] {kind}")
+    y = run_gpu(kind, ops)
+    assert np.array_equal(y.astype(np.float64), run_oracle(oracle_mod, kind, ops))
+
+
+# ---------------------------------------------------------------- layout probes
+def test_q4_one_hot_columns(gpu, oracle_mod):
+    # x = e_j recovers column j: pins nibble order, sign and group index
+    rng = np.random.default_rng(11)
+    M, N = 9, 512
+    q = rng.integers(-8, 8, (M, N))
+    s = np.array([[2.0 ** (g - 2 + (i % 3)) for g in range(N // 128)] for i in range(M)], np.float16)
+    A, S = dev(pack_int4(q)), dev(s)
+    for j in range(N):
+        e = np.zeros(N, np.float16)
+        e[j] = 1
+        y = binding.gemv_q4(A, S, dev(e)).cpu().numpy()
+        assert np.array_equal(y.astype(np.float64), q[:, j] * s[:, j // 128].astype(np.float64)), j
+
+
+def test_rowmajor_one_hot_f32(gpu, oracle_mod):
+    M, N = 3, 4 * 64
+    A = np.arange(M * N, dtype=np.float32).reshape(M, N)
+    Ad = dev(A)
+    for j in (0, 1, 2, 3, 4, 255):
+        e = np.zeros(N, np.float32)
+        e[j] = 1
+        y = binding.gemv_f32(Ad, dev(e)).cpu().numpy()
+        assert list(y) == [i * N + j for i in range(M)]
+
+
+# ---------------------------------------------------------------- degenerate cases
+@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+def test_extreme_int_values_and_identity(gpu, oracle_mod, kind):
+    n = 256
+    rng = np.random.default_rng(0)
+    xv = f16(rng.standard_normal(n))
+    if kind == "f32":
+        ops = {"A": np.eye(n, dtype=np.float32), "x": rng.uniform(-1, 1, n).astype(np.float32)}
+        want = ops["x"].astype(np.float64)
+    elif kind == "f16":
+        ops = {"A": np.eye(n, dtype=np.float16), "x": xv}
+        want = xv.astype(np.float64)
+    elif kind == "q8":
+        A = np.full((n, n), -128, np.int8)        # the most negative code everywhere
+        ops = {"A": A, "scale": np.full(n, 2.0 ** -7, np.float16), "x": np.ones(n, np.float16)}
+        want = np.full(n, -128.0 * n * 2 ** -7)
+    else:
+        q = np.full((n, n), -8)
+        ops = {"A": pack_int4(q), "scale": np.full((n, n // 128), 0.5, np.float16), "x": np.ones(n, np.float16)}
+        want = np.full(n, -8.0 * 0.5 * n)
+    say(f"[degenerate] {kind}")
+    y = run_gpu(kind, ops)
+    assert np.array_equal(y.astype(np.float64), want)
+    assert np.array_equal(y.astype(np.float64), run_oracle(oracle_mod, kind, ops))
+
+
+def test_nan_propagates(gpu, oracle_mod):
+    A = np.ones((8, 1024), np.float32)
+    A[3, 100] = np.nan
+    y = run_gpu("f32", {"A": A, "x": np.ones(1024, np.float32)})
+    assert np.isnan(y[3]) and np.all(y[[0, 1, 2, 4, 5, 6, 7]] == 1024)

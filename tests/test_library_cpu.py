@@ -1,0 +1,48 @@
+"""Host-side checks of the C-ABI library that need no GPU: it builds, loads,
+and exports every function that include/gemv.h declares."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from memory_bound_gemv_row_amd import binding, build
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gemv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemv_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if build.stale():
+        build.build()
+    return ctypes.CDLL(binding.LIB_PATH)
+
+
+def test_header_declares_the_four_paths():
+    names = _declared_functions()
+    for n in ("gemv_f32", "gemv_f16", "gemv_q8", "gemv_q4", "gemv_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    binding.load()
+    assert binding.status_string(0) == "ok"
+    assert binding.status_string(1) == "invalid argument"
+    assert binding.status_string(2).startswith("unsupported")
+    assert binding.status_string(99) == "unknown status"
+
+
+def test_gfx950_code_object_is_embedded():
+    blob = open(binding.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
