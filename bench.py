@@ -22,7 +22,6 @@ FP16, timed in interleaved rounds).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,17 +33,6 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMV achieved HBM GB/s and % of pure-read roofline (fp16 8192² and 4096×14336)"
 HBM_PEAK_GBPS = 8000.0
 RING_BYTES = 1 << 30
-KERNEL_SOURCES = ("memory_bound_gemv_row_amd/csrc/gemv_kernels.hpp", "memory_bound_gemv_row_amd/csrc/gemv_api.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -224,17 +212,14 @@ def cpu_baseline(kind, ops, y_gpu, seconds):
 
 # ---------------------------------------------------------------- traffic from counters
 def traffic_record(kind, M, N):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
-    they were taken on other kernel sources."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or it was taken on other kernel sources."""
+    from memory_bound_gemv_row_amd import profiling
+
+    got = profiling.read_traffic(os.path.join(ROOT, "profiles", f"gemv_{kind}_{M}x{N}_traffic.txt"))
+    if got is None or got[1] != profiling.kernel_source_hash():
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    entry = t.get("workloads", {}).get(f"{kind}_{M}x{N}")
-    return None if entry is None else entry.get("bytes_per_launch")
+    return got[0]
 
 
 # ---------------------------------------------------------------- interleaved detail

@@ -114,17 +114,18 @@ int gemv_probe_read(const void* buf, size_t bytes, uint32_t* sink, uint32_t guar
 int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 /* Launch geometry the library uses for a call.  kind: 0 f32, 1 f16, 2 q8,
- * 3 q4.  `aligned` states whether A and x are 16-byte aligned.  Writes
- * grid size, workgroup size, rows per wave, LDS bytes, and a variant tag
- * (1 = bandwidth path with x in LDS, 2 = bandwidth path with x read from
- * global memory, 3 = element-wise path).  Returns GEMV_OK or an error code;
- * it queries the current device's compute-unit count. */
+ * 3 q4.  `aligned` states whether A and x are 16-byte aligned.  Fills
+ * `info` with the variant (1 = streaming kernel with x staged in LDS,
+ * 2 = streaming kernel with x read from global memory, 3 = element-wise
+ * kernel), grid and workgroup sizes, rows per wave, 1-KiB loads in flight
+ * per wave, and dynamic LDS bytes.  Returns GEMV_OK or an error code; it
+ * queries the current device's compute-unit count and launches nothing. */
 typedef struct gemv_launch_info {
     int variant;
     int grid;
     int block;
     int rows_per_wave;
-    int unroll;          /* 16-byte loads per lane and row issued together */
+    int units_in_flight;
     int lds_bytes;
 } gemv_launch_info;
 

@@ -29,7 +29,7 @@ class GemvError(RuntimeError):
 
 class LaunchInfo(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("grid", ctypes.c_int), ("block", ctypes.c_int),
-                ("rows_per_wave", ctypes.c_int), ("unroll", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+                ("rows_per_wave", ctypes.c_int), ("units_in_flight", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
 
 
 def load():

@@ -16,9 +16,13 @@
 namespace gemv {
 namespace {
 
-constexpr int kWaves = 4;                  // waves per workgroup (256 threads)
 constexpr int kMaxLdsBytes = 64 * 1024;    // x staged in LDS up to this size
 constexpr bool kNT = true;                 // stream A with non-temporal loads
+// INT8: offset-code decode (fewer instructions); INT4: exponent-bias decode,
+// whose error stays within the INT4 tolerance (the offset-code form's bias
+// cancellation does not, at 14336-wide rows).
+constexpr int kQ8Decode = 1;
+constexpr int kQ4Decode = 0;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_cu_mutex;
@@ -51,77 +55,77 @@ int elems_per_chunk(int kind)
     }
 }
 
-int x_granules_per_chunk(int kind)
+int lds_bytes(int kind, int nchunks)
 {
     switch (kind) {
-    case kF32: return Traits<kF32>::kXGran;
-    case kF16: return Traits<kF16>::kXGran;
-    case kQ8: return Traits<kQ8>::kXGran;
-    default: return Traits<kQ4>::kXGran;
+    case kF32: return 4 * stream_lds_words<kF32, true, 0>(nchunks);
+    case kF16: return 4 * stream_lds_words<kF16, true, 0>(nchunks);
+    case kQ8: return 4 * stream_lds_words<kQ8, false, kQ8Decode>(nchunks);
+    default: return 4 * stream_lds_words<kQ4, false, kQ4Decode>(nchunks);
     }
 }
 
 struct Plan {
-    int variant;   // 1 rows+LDS x, 2 rows+global x, 3 element-wise
+    int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise
     int grid;
     int block;
-    int R;
-    int U;
+    int waves;     // per workgroup
+    int rows;      // rows per wave (upper bound)
+    int D;         // units in flight per wave
     int lds;
 };
 
-// Geometry for one call.  A row of nchunks 16-byte chunks takes
-// passes = ceil(nchunks/64) wave-wide loads.  Long rows: one row per wave
-// and up to 8 loads in flight per lane.  Short rows: several rows per wave,
-// so each wave still has several KiB in flight and x reads are shared.
-Plan make_plan(int kind, int M, int N, bool aligned)
+// Geometry for one call.  A row of nchunks 16-byte chunks is
+// P = ceil(nchunks / 64) units (one 1-KiB wave load each).
+//   FP32/FP16: x read with each unit (no staging); one row per wave, or two
+//     for very long rows; 8 units in flight when rows have at least 8 units.
+//   INT8/INT4: x staged in LDS with its sums; INT4 rows are short in bytes,
+//     so waves take two rows and workgroups are 8 waves wide.
+// Every launch gives each of the device's CUs work when M >= CUs.
+Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
 {
     Plan p{};
     const int epc = elems_per_chunk(kind);
-    if (!aligned || N == 0 || N % epc != 0) {
+    if (!aligned || N == 0 || N % epc != 0 || ((kind == kQ8 || kind == kQ4) && lds_bytes(kind, N / epc) > kMaxLdsBytes)) {
         p.variant = 3;
         p.block = 256;
+        p.waves = 4;
         p.grid = (M + 3) / 4;
-        p.R = 1;
-        p.U = 1;
+        p.rows = 1;
+        p.D = 1;
         return p;
     }
     const int nchunks = N / epc;
-    const int passes = (nchunks + 63) / 64;
-    p.U = passes >= 5 ? 8 : (passes >= 3 ? 4 : (passes == 2 ? 2 : 1));
-    p.R = passes >= 4 ? 1 : (passes >= 2 ? 2 : 4);
-    const int64_t xbytes = (int64_t)nchunks * x_granules_per_chunk(kind) * 16;
-    if (xbytes <= kMaxLdsBytes) {
-        p.variant = 1;
-        p.lds = (int)xbytes;
-    } else {
+    const int P = (nchunks + 63) / 64;
+    if (kind == kF32 || kind == kF16) {
         p.variant = 2;
-        p.lds = 0;
-        p.R = 1;
-        p.U = 8;
+        p.waves = P >= 16 ? 8 : 4;
+        p.D = P >= 8 ? 8 : 4;
+        p.rows = P >= 24 ? 2 : 1;
+    } else if (kind == kQ8) {
+        p.variant = 1;
+        p.waves = 4;
+        p.D = 4;
+        p.rows = 1;
+    } else {
+        p.variant = 1;
+        p.waves = 8;
+        p.D = P >= 4 ? 4 : 2;
+        p.rows = 2;
     }
-    p.block = kWaves * 64;
-    const int64_t ngroups = ((int64_t)M + p.R - 1) / p.R;
-    p.grid = (int)((ngroups + kWaves - 1) / kWaves);
+    p.lds = lds_bytes(kind, nchunks);
+    p.block = p.waves * 64;
+    const int64_t waves_needed = ((int64_t)M + p.rows - 1) / p.rows;
+    p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
     return p;
 }
 
-template <int F, int R, int U>
-const void* rows_kernel(bool xlds)
+template <int F, int W, int D>
+const void* stream_kernel()
 {
-    return xlds ? reinterpret_cast<const void*>(&gemv_rows<F, kWaves, R, U, true, kNT>)
-                : reinterpret_cast<const void*>(&gemv_rows<F, kWaves, R, U, false, kNT>);
-}
-
-template <int F, int R>
-const void* rows_kernel_u(int U, bool xlds)
-{
-    switch (U) {
-    case 1: return rows_kernel<F, R, 1>(xlds);
-    case 2: return rows_kernel<F, R, 2>(xlds);
-    case 4: return rows_kernel<F, R, 4>(xlds);
-    default: return rows_kernel<F, R, 8>(xlds);
-    }
+    constexpr bool xg = (F == kF32 || F == kF16);
+    constexpr int dec = F == kQ8 ? kQ8Decode : (F == kQ4 ? kQ4Decode : 0);
+    return reinterpret_cast<const void*>(&gemv_stream<F, W, D, kNT, xg, dec>);
 }
 
 template <int F>
@@ -129,11 +133,9 @@ const void* select_kernel(const Plan& p)
 {
     if (p.variant == 3)
         return reinterpret_cast<const void*>(&gemv_elementwise<F>);
-    switch (p.R) {
-    case 1: return rows_kernel_u<F, 1>(p.U, p.variant == 1);
-    case 2: return rows_kernel_u<F, 2>(p.U, p.variant == 1);
-    default: return rows_kernel_u<F, 4>(p.U, p.variant == 1);
-    }
+    if (p.waves == 8)
+        return p.D == 8 ? stream_kernel<F, 8, 8>() : (p.D == 4 ? stream_kernel<F, 8, 4>() : stream_kernel<F, 8, 2>());
+    return p.D == 8 ? stream_kernel<F, 4, 8>() : (p.D == 4 ? stream_kernel<F, 4, 4>() : stream_kernel<F, 4, 2>());
 }
 
 const void* kernel_for(int kind, const Plan& p)
@@ -167,7 +169,7 @@ int launch(int kind, const void* A, const uint16_t* scale, const void* x, float*
     if (int rc = current_cu_count(&cus); rc != GEMV_OK)
         return rc;
     const bool aligned = aligned16(A) && aligned16(x);
-    const Plan p = make_plan(kind, M, N, aligned);
+    const Plan p = make_plan(kind, M, N, aligned, cus);
     const uint8_t* a8 = static_cast<const uint8_t*>(A);
     const uint8_t* x8 = static_cast<const uint8_t*>(x);
     void* args[] = {(void*)&a8, (void*)&scale, (void*)&x8, (void*)&y, (void*)&M, (void*)&N};
@@ -279,12 +281,12 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
     int cus = 0;
     if (int rc = gemv::current_cu_count(&cus); rc != GEMV_OK)
         return rc;
-    const gemv::Plan p = gemv::make_plan(kind, M, N, aligned != 0);
+    const gemv::Plan p = gemv::make_plan(kind, M, N, aligned != 0, cus);
     info->variant = p.variant;
     info->grid = p.grid;
     info->block = p.block;
-    info->rows_per_wave = p.R;
-    info->unroll = p.U;
+    info->rows_per_wave = p.rows;
+    info->units_in_flight = p.D;
     info->lds_bytes = p.lds;
     return GEMV_OK;
 }

@@ -172,6 +172,54 @@ __device__ __forceinline__ float chunk_q4(u32x4 a, const u32x4 (&xp)[4], float s
     return __builtin_fmaf(s, __builtin_fmaf(acc_16, 0.0625f, acc_1), acc);
 }
 
+// Cheaper decode (fewer VALU instructions per weight).  The offset code
+// q + 8 (INT4) or q + 128 (INT8) is placed straight into the low mantissa
+// bits of a binary16 with a zero exponent field, i.e. read as the subnormal
+// (q + bias) * 2^-24, exact, and v_dot2_f32_f16 multiplies it by x exactly
+// (at most 4 + 11 or 8 + 11 significant bits).  The bias is removed once:
+// sum_j q_j x_j = 2^24 * sum_j ((q_j + bias) 2^-24) x_j - bias * sum_j x_j,
+// with sum_j x_j taken per 32-column chunk (INT4, whose scale changes per
+// group) or per row (INT8, whose scale is per row) when x is staged.
+
+// INT4 chunk, offset-code form: returns 2^-24 * sum (q + 8) x over 32 columns.
+// Column pairs (c, c+4) and (c+1, c+5) as in q4_word; the high pair sits four
+// bits up, i.e. carries an extra factor 16, removed by the final FMA.
+__device__ __forceinline__ float q4_sub_chunk(u32x4 a, const u32x4 (&xp)[4])
+{
+    float lo = 0.0f, hi = 0.0f;
+    const unsigned ws[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned w = ws[k] ^ 0x88888888u;
+        const unsigned w8 = w >> 8;
+        lo = __builtin_amdgcn_fdot2(as_h2(w & 0x000F000Fu), as_h2(xp[k].x), lo, false);
+        hi = __builtin_amdgcn_fdot2(as_h2(w & 0x00F000F0u), as_h2(xp[k].y), hi, false);
+        lo = __builtin_amdgcn_fdot2(as_h2(w8 & 0x000F000Fu), as_h2(xp[k].z), lo, false);
+        hi = __builtin_amdgcn_fdot2(as_h2(w8 & 0x00F000F0u), as_h2(xp[k].w), hi, false);
+    }
+    return __builtin_fmaf(hi, 0.0625f, lo);
+}
+
+// INT8 chunk, offset-code form: acc + 2^-24 * sum (q + 128) x over 16
+// columns.  A byte permute places bytes 0,1 (and 2,3) of the XOR-ed word
+// under zero high bytes, giving the subnormal pairs (c, c+1) that match x's
+// natural pairs.
+__device__ __forceinline__ float q8_sub_chunk(u32x4 a, u32x4 x0, u32x4 x1, float acc)
+{
+    const unsigned ws[4] = {a.x, a.y, a.z, a.w};
+    const unsigned xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const unsigned w = ws[k] ^ 0x80808080u;
+        // v_perm_b32 selector: byte value 12 yields 0x00; 0..3 pick bytes of w
+        const unsigned p01 = __builtin_amdgcn_perm(0u, w, 0x0C010C00u);
+        const unsigned p23 = __builtin_amdgcn_perm(0u, w, 0x0C030C02u);
+        acc = __builtin_amdgcn_fdot2(as_h2(p01), as_h2(xs[2 * k]), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_h2(p23), as_h2(xs[2 * k + 1]), acc, false);
+    }
+    return acc;
+}
+
 // Reorder one 8-column block of binary16 x from (x0..x7) to
 // (x0,x4), (x1,x5), (x2,x6), (x3,x7), the pairing q4_word expects.
 __device__ __forceinline__ u32x4 q4_pair_x(u32x4 v)
@@ -184,116 +232,217 @@ __device__ __forceinline__ u32x4 q4_pair_x(u32x4 v)
     return r;
 }
 
-// ---------------------------------------------------------------- bandwidth kernel
+// Copy the nxg 16-byte granules of x into LDS (INT4: reordered for q4_word).
+// Each thread issues up to 8 loads before the first wait, so staging costs
+// about one cache round trip per 8 granules.
+template <int F, int NT>
+__device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds, int nxg)
+{
+    for (int g0 = threadIdx.x; g0 < nxg; g0 += 8 * NT) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int g = g0 + k * NT;
+            v[k] = xg[g < nxg ? g : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int g = g0 + k * NT;
+            if (g < nxg)
+                lds[g] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+        }
+    }
+}
+
+// Staging for the offset-code decode: thread t stages whole chunks
+// t, t + NT, ... and also records, per chunk, 8 * sum of its 32 x values
+// (INT4, in lds_f[chunk]) or accumulates the sum of all x (INT8: one partial
+// per wave in lds_f[wave]).  Sums use v_dot2_f32_f16 against (1, 1): FP32
+// accumulation of exact binary16 values.
+template <int F, int WAVES>
+__device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4* lds, float* lds_f, int nchunks)
+{
+    constexpr int NT = WAVES * 64;
+    constexpr int G = Traits<F>::kXGran;
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float part = 0.0f;
+    for (int c = threadIdx.x; c < nchunks; c += NT) {
+        u32x4 v[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            v[k] = xg[c * G + k];
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].x), ones, sum, false);
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].y), ones, sum, false);
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].z), ones, sum, false);
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].w), ones, sum, false);
+            lds[c * G + k] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+        }
+        if constexpr (F == kQ4)
+            lds_f[c] = 8.0f * sum;
+        else
+            part += sum;
+    }
+    if constexpr (F == kQ8) {
+        const float w = wave_sum(part);
+        if ((threadIdx.x & 63) == 0)
+            lds_f[threadIdx.x >> 6] = w;
+    }
+}
+
+// ---------------------------------------------------------------- streaming kernel
 // Preconditions (checked by the host): N is a multiple of Traits<F>::kElems,
-// A and x are 16-byte aligned, M >= 1.  For XLDS the launch provides
-// N * sizeof(x element) bytes of dynamic LDS.
-template <int F, int WAVES, int R, int U, bool XLDS, bool NT>
+// A and x are 16-byte aligned, M >= 1, and the launch provides
+// stream_lds_bytes<F, XG, DEC>(N) bytes of dynamic LDS.
+//
+// Each wave owns the rows wave_id, wave_id + nwaves, ... and walks them as
+// one linear sequence of units; a unit is one pass over a row (one 16-byte
+// chunk per lane, 1 KiB per wave).  Loads run D units ahead of the
+// arithmetic in straight-line code, so the wait before each unit only needs
+// the oldest of D outstanding loads.  The first D loads are issued before x
+// is staged, so HBM traffic starts with the kernel.  A row's last pass may
+// be ragged (fewer than 64 chunks): lanes past the row end re-read chunk 0
+// of the same row and contribute exactly zero.  The unit count is padded to
+// a multiple of D; padded units re-read the wave's last row and are never
+// stored.
+//
+//   XG  (FP32/FP16 only): x granules are loaded from global memory with each
+//       unit instead of being staged in LDS (no staging, no barrier).
+//   DEC (INT8/INT4 only): 0 = exponent-bias decode (q8_word / q4_word),
+//       1 = offset-code decode (q8_sub_chunk / q4_sub_chunk) with the bias
+//       term from sums of x taken while staging.
+template <int F, bool XG, int DEC>
+__host__ __device__ constexpr int stream_lds_words(int nchunks)
+{
+    // 16-byte granules of x, then (offset-code INT4) one float per chunk, or
+    // (offset-code INT8) one float per wave for the sum of x.
+    return XG ? 0 : nchunks * Traits<F>::kXGran * 4 + (DEC == 1 ? (F == kQ4 ? nchunks : 16) : 0);
+}
+
+template <int F, int WAVES, int D, bool NT, bool XG, int DEC>
 __global__ void __launch_bounds__(WAVES * 64)
-gemv_rows(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
-          const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
+gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
+            const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
     using T = Traits<F>;
+    static_assert(!XG || F == kF32 || F == kF16, "x from global memory: FP32/FP16 only");
+    static_assert(DEC == 0 || F == kQ8 || F == kQ4, "offset-code decode: INT8/INT4 only");
     extern __shared__ u32x4 lds_x[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int nchunks = N / T::kElems;
+    const int P = (nchunks + 63) >> 6;
     const int64_t row_bytes = (int64_t)nchunks * 16;
+    const int groups = N / 128;   // INT4 scales per row
+    const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_id = blockIdx.x * WAVES + wave_in_wg;
+    const int nwaves = gridDim.x * WAVES;
+    const int my_rows = wave_id < M ? (M - 1 - wave_id) / nwaves + 1 : 0;
+    const int units = my_rows * P;
+    const int units_pad = (units + D - 1) / D * D;
+    const int last_row = wave_id + (my_rows - 1) * nwaves;
     const u32x4* xg = reinterpret_cast<const u32x4*>(x);
+    float* lds_f = reinterpret_cast<float*>(lds_x + nchunks * T::kXGran);   // after the x granules
 
-    if constexpr (XLDS) {
-        const int nxg = nchunks * T::kXGran;
-        for (int g = threadIdx.x; g < nxg; g += WAVES * 64) {
-            u32x4 v = xg[g];
-            if constexpr (F == kQ4)
-                v = q4_pair_x(v);
-            lds_x[g] = v;
-        }
-        __syncthreads();
-    }
-
-    auto xgran = [&](int g) -> u32x4 {
-        if constexpr (XLDS) {
-            return lds_x[g];
-        } else {
-            u32x4 v = xg[g];
-            if constexpr (F == kQ4)
-                v = q4_pair_x(v);
-            return v;
+    u32x4 buf[D];
+    u32x4 xbuf[XG ? D : 1];
+    uint16_t sbuf[D];
+    int l_row = wave_id, l_pass = 0;
+    auto issue = [&](int d) {
+        const int row = l_row <= last_row ? l_row : last_row;
+        const int c = l_pass * 64 + lane;
+        const int cc = c < nchunks ? c : 0;
+        buf[d] = load16<NT>(reinterpret_cast<const u32x4*>(A + (int64_t)row * row_bytes) + cc);
+        if constexpr (XG)
+            xbuf[d] = xg[cc];
+        if constexpr (F == kQ4)
+            sbuf[d] = scale[(int64_t)row * groups + (cc >> 2)];
+        if (++l_pass == P) {
+            l_pass = 0;
+            l_row += nwaves;
         }
     };
 
-    const int ngroups = (M + R - 1) / R;
-    const int groups_per_row_scale = N / 128;   // INT4 scales per row
-    for (int grp = blockIdx.x * WAVES + wave; grp < ngroups; grp += gridDim.x * WAVES) {
-        const int row0 = grp * R;
-        const u32x4* arow[R];
-        int rclamp[R];
+    if (units > 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            // rows past M re-read row M-1 (in bounds); their sums are dropped
-            rclamp[r] = min(row0 + r, M - 1);
-            arow[r] = reinterpret_cast<const u32x4*>(A + (int64_t)rclamp[r] * row_bytes);
-        }
-        float acc[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            acc[r] = 0.0f;
+        for (int d = 0; d < D; ++d)
+            issue(d);
+    }
 
-        for (int c0 = 0; c0 < nchunks; c0 += 64 * U) {
-            u32x4 a[U][R];
-            float s[U][R];
+    float xsum = 0.0f;   // offset-code INT8: sum of x over the row
+    if constexpr (!XG) {
+        if constexpr (DEC == 1)
+            stage_x_sums<F, WAVES>(xg, lds_x, lds_f, nchunks);
+        else
+            stage_x<F, WAVES * 64>(xg, lds_x, nchunks * T::kXGran);
+        __syncthreads();
+        if constexpr (F == kQ8 && DEC == 1) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * 64 + lane;
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    a[u][r] = (c < nchunks) ? load16<NT>(arow[r] + c) : u32x4{0u, 0u, 0u, 0u};
-                    if constexpr (F == kQ4)
-                        s[u][r] = (c < nchunks)
-                            ? half_bits_to_float(scale[(int64_t)rclamp[r] * groups_per_row_scale + (c >> 2)])
-                            : 0.0f;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * 64 + lane;
-                if (c < nchunks) {
-                    if constexpr (F == kF32) {
-                        const u32x4 xv = xgran(c);
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            acc[r] = chunk_f32(a[u][r], xv, acc[r]);
-                    } else if constexpr (F == kF16) {
-                        const u32x4 xv = xgran(c);
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            acc[r] = chunk_f16(a[u][r], xv, acc[r]);
-                    } else if constexpr (F == kQ8) {
-                        const u32x4 x0 = xgran(2 * c), x1 = xgran(2 * c + 1);
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            acc[r] = chunk_q8(a[u][r], x0, x1, acc[r]);
-                    } else {
-                        const u32x4 xp[4] = {xgran(4 * c), xgran(4 * c + 1), xgran(4 * c + 2), xgran(4 * c + 3)};
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            acc[r] = chunk_q4(a[u][r], xp, s[u][r], acc[r]);
-                    }
-                }
-            }
-        }
-
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float t = wave_sum(acc[r]);
-            if (lane == 0 && row0 + r < M) {
-                if constexpr (F == kQ8)
-                    t *= half_bits_to_float(scale[row0 + r]);
-                y[row0 + r] = t;
-            }
+            for (int w = 0; w < WAVES; ++w)
+                xsum += lds_f[w];
         }
     }
+    if (units == 0)
+        return;
+
+    float acc = 0.0f;
+    int c_row = wave_id, c_pass = 0;
+    auto consume = [&](int d) {
+        const int c = c_pass * 64 + lane;
+        const bool live = c < nchunks;
+        const int cc = live ? c : 0;
+        u32x4 a = buf[d];
+        if (!live) {
+            // codes that decode to exactly zero in every form
+            const unsigned z = (F == kQ4 && DEC == 1) ? 0x88888888u : ((F == kQ8 && DEC == 1) ? 0x80808080u : 0u);
+            a = u32x4{z, z, z, z};
+        }
+        if constexpr (F == kF32) {
+            acc = chunk_f32(a, XG ? xbuf[XG ? d : 0] : lds_x[cc], acc);
+        } else if constexpr (F == kF16) {
+            acc = chunk_f16(a, XG ? xbuf[XG ? d : 0] : lds_x[cc], acc);
+        } else if constexpr (F == kQ8) {
+            if constexpr (DEC == 1)
+                acc = q8_sub_chunk(a, lds_x[2 * cc], lds_x[2 * cc + 1], acc);
+            else
+                acc = chunk_q8(a, lds_x[2 * cc], lds_x[2 * cc + 1], acc);
+        } else {
+            const u32x4 xp[4] = {lds_x[4 * cc], lds_x[4 * cc + 1], lds_x[4 * cc + 2], lds_x[4 * cc + 3]};
+            const float s = half_bits_to_float(sbuf[d]);
+            if constexpr (DEC == 1) {
+                const float bias = live ? lds_f[cc] : 0.0f;     // 8 * sum of the chunk's x
+                acc = __builtin_fmaf(s, __builtin_fmaf(q4_sub_chunk(a, xp), 16777216.0f, -bias), acc);
+            } else {
+                acc = chunk_q4(a, xp, s, acc);
+            }
+        }
+        if (++c_pass == P) {
+            float t = wave_sum(acc);
+            if (lane == 0 && c_row < M) {
+                if constexpr (F == kQ8) {
+                    if constexpr (DEC == 1)
+                        t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);
+                    t *= half_bits_to_float(scale[c_row]);
+                }
+                y[c_row] = t;
+            }
+            acc = 0.0f;
+            c_pass = 0;
+            c_row += nwaves;
+        }
+    };
+
+    for (int k0 = D; k0 < units_pad; k0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            consume(d);
+            issue(d);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        consume(d);
 }
 
 // ---------------------------------------------------------------- element-wise kernel
