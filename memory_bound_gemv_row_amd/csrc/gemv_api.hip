@@ -79,8 +79,8 @@ struct Plan {
 // P = ceil(nchunks / 64) units (one 1-KiB wave load each).
 //   FP32/FP16: x read with each unit (no staging); one row per wave, or two
 //     for very long rows; 8 units in flight when rows have at least 8 units.
-//   INT8/INT4: x staged in LDS with its sums; INT4 rows are short in bytes,
-//     so waves take two rows and workgroups are 8 waves wide.
+//   INT8/INT4: x staged in LDS (INT8 with its sum); short rows (INT4 in
+//     particular) put several rows on each wave.
 // Every launch gives each of the device's CUs work when M >= CUs.
 Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
 {
@@ -99,19 +99,25 @@ Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
     const int P = (nchunks + 63) / 64;
     if (kind == kF32 || kind == kF16) {
         p.variant = 2;
-        p.waves = P >= 16 ? 8 : 4;
-        p.D = P >= 8 ? 8 : 4;
-        p.rows = P >= 24 ? 2 : 1;
+        if (P >= 24) {            // very long rows: two per wave, fewer in flight each
+            p.waves = 4;
+            p.D = 4;
+            p.rows = 2;
+        } else {
+            p.waves = P >= 16 ? 8 : 4;
+            p.D = P >= 8 ? 8 : 4;
+            p.rows = 1;
+        }
     } else if (kind == kQ8) {
         p.variant = 1;
         p.waves = 4;
         p.D = 4;
-        p.rows = 1;
+        p.rows = P <= 4 ? 4 : 1;  // short INT8 rows: more rows per wave
     } else {
         p.variant = 1;
-        p.waves = 8;
+        p.waves = 4;
         p.D = P >= 4 ? 4 : 2;
-        p.rows = 2;
+        p.rows = P >= 4 ? 2 : 4;  // short INT4 rows: more rows per wave
     }
     p.lds = lds_bytes(kind, nchunks);
     p.block = p.waves * 64;

@@ -153,12 +153,14 @@ __device__ __forceinline__ void q4_word(unsigned w, u32x4 xp, float& acc_1, floa
 {
     const f16x2 b1 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const f16x2 b16 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-    w ^= 0x88888888u;
+    // (w ^ 0x88888888) & mask | 0x64006400 written as one AND and one XOR:
+    // the XOR constant flips the nibble's sign bit (bit 3 or bit 7 of each
+    // half) and sets the exponent bits 0x6400, which the mask has cleared.
     const unsigned w8 = w >> 8;
-    acc_1 = __builtin_amdgcn_fdot2(as_h2((w & 0x000F000Fu) | 0x64006400u) + b1, as_h2(xp.x), acc_1, false);
-    acc_16 = __builtin_amdgcn_fdot2(as_h2((w & 0x00F000F0u) | 0x64006400u) + b16, as_h2(xp.y), acc_16, false);
-    acc_1 = __builtin_amdgcn_fdot2(as_h2((w8 & 0x000F000Fu) | 0x64006400u) + b1, as_h2(xp.z), acc_1, false);
-    acc_16 = __builtin_amdgcn_fdot2(as_h2((w8 & 0x00F000F0u) | 0x64006400u) + b16, as_h2(xp.w), acc_16, false);
+    acc_1 = __builtin_amdgcn_fdot2(as_h2((w & 0x000F000Fu) ^ 0x64086408u) + b1, as_h2(xp.x), acc_1, false);
+    acc_16 = __builtin_amdgcn_fdot2(as_h2((w & 0x00F000F0u) ^ 0x64806480u) + b16, as_h2(xp.y), acc_16, false);
+    acc_1 = __builtin_amdgcn_fdot2(as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + b1, as_h2(xp.z), acc_1, false);
+    acc_16 = __builtin_amdgcn_fdot2(as_h2((w8 & 0x00F000F0u) ^ 0x64806480u) + b16, as_h2(xp.w), acc_16, false);
 }
 
 // INT4: 32 columns (all inside one 128-column group) and their group scale.
@@ -236,9 +238,9 @@ __device__ __forceinline__ u32x4 q4_pair_x(u32x4 v)
 // Each thread issues up to 8 loads before the first wait, so staging costs
 // about one cache round trip per 8 granules.
 template <int F, int NT>
-__device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds, int nxg)
+__device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds, int nxg, int nxg_pad)
 {
-    for (int g0 = threadIdx.x; g0 < nxg; g0 += 8 * NT) {
+    for (int g0 = threadIdx.x; g0 < nxg_pad; g0 += 8 * NT) {
         u32x4 v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -250,6 +252,8 @@ __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds
             const int g = g0 + k * NT;
             if (g < nxg)
                 lds[g] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+            else if (g < nxg_pad)
+                lds[g] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 }
@@ -260,13 +264,22 @@ __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds
 // per wave in lds_f[wave]).  Sums use v_dot2_f32_f16 against (1, 1): FP32
 // accumulation of exact binary16 values.
 template <int F, int WAVES>
-__device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4* lds, float* lds_f, int nchunks)
+__device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4* lds, float* lds_f, int nchunks,
+                                             int nchunks_pad)
 {
     constexpr int NT = WAVES * 64;
     constexpr int G = Traits<F>::kXGran;
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     float part = 0.0f;
-    for (int c = threadIdx.x; c < nchunks; c += NT) {
+    for (int c = threadIdx.x; c < nchunks_pad; c += NT) {
+        if (c >= nchunks) {          // whole-pass padding: zero x, zero sums
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+                lds[c * G + k] = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (F == kQ4)
+                lds_f[c] = 0.0f;
+            continue;
+        }
         u32x4 v[G];
 #pragma unroll
         for (int k = 0; k < G; ++k)
@@ -301,10 +314,12 @@ __device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4
 // one linear sequence of units; a unit is one pass over a row (one 16-byte
 // chunk per lane, 1 KiB per wave).  Loads run D units ahead of the
 // arithmetic in straight-line code, so the wait before each unit only needs
-// the oldest of D outstanding loads.  The first D loads are issued before x
-// is staged, so HBM traffic starts with the kernel.  A row's last pass may
-// be ragged (fewer than 64 chunks): lanes past the row end re-read chunk 0
-// of the same row and contribute exactly zero.  The unit count is padded to
+// the oldest of D outstanding loads.  The first D loads are issued at
+// kernel start (INT4: right after x is staged).  A ragged last pass
+// (fewer than 64 chunks) contributes exactly zero in the lanes past the row
+// end: with global loads (FP32/FP16) those lanes load chunk 0 and zero it
+// before use; with buffer loads (INT8/INT4) the row-sized resource returns
+// zeros and meets zero-padded x.  The unit count is padded to
 // a multiple of D; padded units re-read the wave's last row and are never
 // stored.
 //
@@ -316,9 +331,19 @@ __device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4
 template <int F, bool XG, int DEC>
 __host__ __device__ constexpr int stream_lds_words(int nchunks)
 {
-    // 16-byte granules of x, then (offset-code INT4) one float per chunk, or
-    // (offset-code INT8) one float per wave for the sum of x.
-    return XG ? 0 : nchunks * Traits<F>::kXGran * 4 + (DEC == 1 ? (F == kQ4 ? nchunks : 16) : 0);
+    // 16-byte granules of x for whole passes (zero past the row end), then
+    // (offset-code INT4) one float per chunk, or (offset-code INT8) one float
+    // per wave for the sum of x.
+    return XG ? 0
+              : ((nchunks + 63) / 64) * 64 * Traits<F>::kXGran * 4 +
+                    (DEC == 1 ? (F == kQ4 ? ((nchunks + 63) / 64) * 64 : 16) : 0);
+}
+
+// Buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes
+// return zero, which is how lanes past a row's end contribute nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 template <int F, int WAVES, int D, bool NT, bool XG, int DEC>
@@ -327,55 +352,82 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
     using T = Traits<F>;
-    static_assert(!XG || F == kF32 || F == kF16, "x from global memory: FP32/FP16 only");
+    static_assert(!XG || DEC == 0, "x from global memory: exponent-bias decode only");
     static_assert(DEC == 0 || F == kQ8 || F == kQ4, "offset-code decode: INT8/INT4 only");
+    constexpr int kAux = NT ? 2 : 0;   // buffer-load cache policy: non-temporal
+    constexpr int NT_ = WAVES * 64;
+    constexpr int G = T::kXGran;       // x granules per unit
     extern __shared__ u32x4 lds_x[];
     const int lane = threadIdx.x & 63;
     const int nchunks = N / T::kElems;
-    const int P = (nchunks + 63) >> 6;
-    const int64_t row_bytes = (int64_t)nchunks * 16;
-    const int groups = N / 128;   // INT4 scales per row
-    const int wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wave_id = blockIdx.x * WAVES + wave_in_wg;
+    const int P = (nchunks + 63) >> 6;          // units per row
+    const uint32_t row_bytes = (uint32_t)nchunks * 16;
+    const int groups = N / 128;                 // INT4 scales per row
+    const int wave_id = blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwaves = gridDim.x * WAVES;
     const int my_rows = wave_id < M ? (M - 1 - wave_id) / nwaves + 1 : 0;
     const int units = my_rows * P;
     const int units_pad = (units + D - 1) / D * D;
     const int last_row = wave_id + (my_rows - 1) * nwaves;
+    const int nxg = nchunks * G;
+    const int nxg_pad = P * 64 * G;             // staged granules, zero past the row end
     const u32x4* xg = reinterpret_cast<const u32x4*>(x);
-    float* lds_f = reinterpret_cast<float*>(lds_x + nchunks * T::kXGran);   // after the x granules
+    float* lds_f = reinterpret_cast<float*>(lds_x + nxg_pad);
 
+    // A unit's loads: the row's resource (wave-uniform), the pass offset
+    // (wave-uniform) and the lane's fixed offset.
+    const int lane_off = lane * 16;
+    constexpr int XGR = XG ? G : 1;   // x granules per unit held in registers
     u32x4 buf[D];
-    u32x4 xbuf[XG ? D : 1];
+    u32x4 xbuf[XG ? D : 1][XGR];
     uint16_t sbuf[D];
     int l_row = wave_id, l_pass = 0;
     auto issue = [&](int d) {
         const int row = l_row <= last_row ? l_row : last_row;
         const int c = l_pass * 64 + lane;
-        const int cc = c < nchunks ? c : 0;
-        buf[d] = load16<NT>(reinterpret_cast<const u32x4*>(A + (int64_t)row * row_bytes) + cc);
-        if constexpr (XG)
-            xbuf[d] = xg[cc];
-        if constexpr (F == kQ4)
-            sbuf[d] = scale[(int64_t)row * groups + (cc >> 2)];
+        if constexpr (XG) {
+            // FP32/FP16: plain global loads; a lane past the row end loads
+            // chunk 0 of the row, which consume() replaces by zero.
+            const int cc = c < nchunks ? c : 0;
+            buf[d] = load16<NT>(reinterpret_cast<const u32x4*>(A + (int64_t)row * row_bytes) + cc);
+#pragma unroll
+            for (int k = 0; k < XGR; ++k)
+                xbuf[d][k] = xg[cc * XGR + k];
+        } else {
+            // INT8/INT4: buffer loads through a resource of exactly the row's
+            // bytes.  The whole offset goes in the VGPR operand, which is what
+            // the range check covers (the SGPR offset stays 0), so lanes past
+            // the row end read zeros.
+            const int voff = lane_off + l_pass * 1024;
+            const auto rsrc = make_rsrc(A + (int64_t)row * row_bytes, row_bytes);
+            buf[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, kAux));
+        }
+        if constexpr (F == kQ4) {
+            const auto srsrc = make_rsrc(scale + (int64_t)row * groups, (uint32_t)groups * 2);
+            sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (lane >> 2) * 2 + l_pass * 32, 0, 0);
+        }
         if (++l_pass == P) {
             l_pass = 0;
             l_row += nwaves;
         }
     };
 
-    if (units > 0) {
+    // With x staged in LDS the order of the prologue and the staging matters:
+    // INT4 stages first (its staging loads are then the oldest in the wave's
+    // in-order load counter, so the LDS writes need not wait for A), INT8
+    // issues its first D units of A first (each measured faster).
+    constexpr bool kStageFirst = (F == kQ4);
+    if (!kStageFirst && units > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d)
             issue(d);
     }
-
     float xsum = 0.0f;   // offset-code INT8: sum of x over the row
     if constexpr (!XG) {
         if constexpr (DEC == 1)
-            stage_x_sums<F, WAVES>(xg, lds_x, lds_f, nchunks);
+            stage_x_sums<F, WAVES>(xg, lds_x, lds_f, nchunks, P * 64);
         else
-            stage_x<F, WAVES * 64>(xg, lds_x, nchunks * T::kXGran);
+            stage_x<F, NT_>(xg, lds_x, nxg, nxg_pad);
         __syncthreads();
         if constexpr (F == kQ8 && DEC == 1) {
 #pragma unroll
@@ -385,37 +437,34 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     }
     if (units == 0)
         return;
+    if (kStageFirst) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            issue(d);
+    }
 
     float acc = 0.0f;
     int c_row = wave_id, c_pass = 0;
-    auto consume = [&](int d) {
-        const int c = c_pass * 64 + lane;
-        const bool live = c < nchunks;
-        const int cc = live ? c : 0;
-        u32x4 a = buf[d];
-        if (!live) {
-            // codes that decode to exactly zero in every form
-            const unsigned z = (F == kQ4 && DEC == 1) ? 0x88888888u : ((F == kQ8 && DEC == 1) ? 0x80808080u : 0u);
-            a = u32x4{z, z, z, z};
-        }
+    // One unit of arithmetic: a = the unit's 16 bytes of A per lane, xv = its
+    // x granules in staged layout (INT4: pair-reordered).
+    auto compute = [&](u32x4 a, const u32x4 (&xv)[G], uint16_t sraw) {
         if constexpr (F == kF32) {
-            acc = chunk_f32(a, XG ? xbuf[XG ? d : 0] : lds_x[cc], acc);
+            acc = chunk_f32(a, xv[0], acc);
         } else if constexpr (F == kF16) {
-            acc = chunk_f16(a, XG ? xbuf[XG ? d : 0] : lds_x[cc], acc);
+            acc = chunk_f16(a, xv[0], acc);
         } else if constexpr (F == kQ8) {
             if constexpr (DEC == 1)
-                acc = q8_sub_chunk(a, lds_x[2 * cc], lds_x[2 * cc + 1], acc);
+                acc = q8_sub_chunk(a, xv[0], xv[G - 1], acc);
             else
-                acc = chunk_q8(a, lds_x[2 * cc], lds_x[2 * cc + 1], acc);
+                acc = chunk_q8(a, xv[0], xv[G - 1], acc);
         } else {
-            const u32x4 xp[4] = {lds_x[4 * cc], lds_x[4 * cc + 1], lds_x[4 * cc + 2], lds_x[4 * cc + 3]};
-            const float s = half_bits_to_float(sbuf[d]);
-            if constexpr (DEC == 1) {
-                const float bias = live ? lds_f[cc] : 0.0f;     // 8 * sum of the chunk's x
-                acc = __builtin_fmaf(s, __builtin_fmaf(q4_sub_chunk(a, xp), 16777216.0f, -bias), acc);
-            } else {
+            const u32x4 xp[4] = {xv[0], xv[1 % G], xv[2 % G], xv[3 % G]};
+            const float s = half_bits_to_float(sraw);
+            if constexpr (DEC == 1)
+                acc = __builtin_fmaf(s, __builtin_fmaf(q4_sub_chunk(a, xp), 16777216.0f,
+                                                       -lds_f[c_pass * 64 + lane]), acc);
+            else
                 acc = chunk_q4(a, xp, s, acc);
-            }
         }
         if (++c_pass == P) {
             float t = wave_sum(acc);
@@ -431,6 +480,23 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             c_pass = 0;
             c_row += nwaves;
         }
+    };
+    auto consume = [&](int d) {
+        const int cc = c_pass * 64 + lane;       // < P * 64: staged (possibly zero) x
+        u32x4 a = buf[d];
+        u32x4 xv[G];
+        if constexpr (XG) {
+            if (cc >= nchunks)                   // past the row end: chunk 0 was loaded
+                a = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+                xv[k] = (F == kQ4) ? q4_pair_x(xbuf[d][k % XGR]) : xbuf[d][k % XGR];
+        } else {
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+                xv[k] = lds_x[cc * G + k];
+        }
+        compute(a, xv, sbuf[d]);
     };
 
     for (int k0 = D; k0 < units_pad; k0 += D) {
