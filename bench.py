@@ -230,21 +230,54 @@ DETAIL_SHAPES = [
 ]
 
 
+def probe_slice_graph(ring, launches):
+    """HIP graph of `launches` pure-read probes, each over one ring slot's
+    weight bytes (rotating slots): a pure read of exactly what one GEMV
+    launch streams, launched the same way."""
+    import torch
+
+    from memory_bound_gemv_row_amd import accounting, binding
+
+    nbytes = accounting.weight_bytes(ring.kind, ring.M, ring.N) // 16 * 16
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(launches):
+                rc = binding.probe_read_ptr(ring.a_ptr(i), nbytes, sink.data_ptr(), 0xA5A5A5A5,
+                                            torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"gemv_probe_read returned {rc}")
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g._sink = sink
+    return g, nbytes
+
+
 def detail(rounds, launches=256):
+    """Other shapes and formats, in interleaved rounds (best round per
+    kernel).  Besides each GEMV, a pure-read probe over the same weight bytes
+    is timed the same way; its time is the floor for that launch, and the
+    ratio of those floors bounds the INT8/INT4 speed-ups over FP16."""
     import torch
 
     from memory_bound_gemv_row_amd import accounting, inputs
 
     out = {}
     for name, M, N, kinds in DETAIL_SHAPES:
-        rings, graphs = {}, {}
+        rings, graphs, pgraphs = {}, {}, {}
         for k in kinds:
             rings[k] = Ring(k, M, N, inputs.make(k, M, N, seed=0))
             graphs[k] = graph_of(rings[k], launches)
             graphs[k].replay()
+            pgraphs[k] = probe_slice_graph(rings[k], launches)
+            pgraphs[k][0].replay()
         probe_buf = rings[kinds[0]].buf
         torch.cuda.synchronize()
         best = {k: float("inf") for k in kinds}
+        pbest = {k: float("inf") for k in kinds}
         per_round = {k: [] for k in kinds}
         probe_best = 0.0
         for _ in range(rounds):
@@ -252,20 +285,24 @@ def detail(rounds, launches=256):
                 t = time_graph(graphs[k], launches)
                 per_round[k].append(t)
                 best[k] = min(best[k], t)
+                pbest[k] = min(pbest[k], time_graph(pgraphs[k][0], launches))
             probe_best = max(probe_best, probe_gbps(probe_buf, reps=3))
         rec = {"probe_gbps": probe_best}
         for k in kinds:
             gb = accounting.gbps(accounting.alg_bytes(k, M, N), best[k])
             rec[k] = {"us": best[k] * 1e6, "us_median": sorted(per_round[k])[len(per_round[k]) // 2] * 1e6,
                       "gbps": gb, "pct_of_probe": 100 * gb / max(probe_best, gb),
-                      "pct_of_8tbs": 100 * gb / HBM_PEAK_GBPS}
+                      "pct_of_8tbs": 100 * gb / HBM_PEAK_GBPS,
+                      "same_size_probe_us": pbest[k] * 1e6,
+                      "pct_of_same_size_probe": 100 * pbest[k] / best[k]}
         for k in kinds:
             if k != "f16":
                 rec[k]["x_f16"] = best["f16"] / best[k]
+                rec[k]["x_f16_same_size_probe_ceiling"] = pbest["f16"] / pbest[k]
         out[name] = rec
         for k in kinds:
             rings[k].free()
-        del graphs, rings
+        del graphs, rings, pgraphs
         torch.cuda.empty_cache()
     return out
 
