@@ -110,7 +110,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
         }
     } else if (kind == kQ8) {
         p.variant = 1;
-        p.waves = 4;
+        p.waves = P >= 8 ? 8 : 4;
         p.D = 4;
         p.rows = P <= 4 ? 4 : 1;  // short INT8 rows: more rows per wave
     } else {

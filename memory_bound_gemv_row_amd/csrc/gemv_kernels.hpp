@@ -405,6 +405,11 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         if constexpr (F == kQ4) {
             const auto srsrc = make_rsrc(scale + (int64_t)row * groups, (uint32_t)groups * 2);
             sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (lane >> 2) * 2 + l_pass * 32, 0, 0);
+        } else if constexpr (F == kQ8) {
+            // the row scale travels with every unit of the row, in load order,
+            // so the row end needs no load of its own (which would have to
+            // wait for every A load in flight)
+            sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(scale + row, 2), 0, 0, 0);
         }
         if (++l_pass == P) {
             l_pass = 0;
@@ -472,7 +477,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
                 if constexpr (F == kQ8) {
                     if constexpr (DEC == 1)
                         t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);
-                    t *= half_bits_to_float(scale[c_row]);
+                    t *= half_bits_to_float(sraw);   // this row's scale (see issue)
                 }
                 y[c_row] = t;
             }
