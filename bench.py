@@ -16,7 +16,7 @@ Prints ONE JSON line.  ``value`` is the achieved algorithmic HBM bandwidth
 (the same-run pure-read ceiling and the %-of-probe), ``cpu_baseline`` (the
 CPU oracle timed on the host cores on the same inputs; its result also
 gates the GPU result, and the run aborts on a parity failure, as the pages
-do), and ``detail`` (the other FP16 shape and the INT8/INT4 speed-ups over
+do), and ``detail`` (the other FP16 shapes, FP16 weights with FP32 x, and the INT8/INT4 speed-ups over
 FP16, timed in interleaved rounds).
 """
 from __future__ import annotations
@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--kind", default="f16", choices=["f32", "f16", "q8", "q4"])
+    ap.add_argument("--kind", default="f16", choices=["f32", "f16", "f16x32", "q8", "q4"])
     ap.add_argument("--M", type=int, default=8192)
     ap.add_argument("--N", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -97,6 +97,8 @@ class Ring:
             rc = binding.gemv_f32_ptr(self.a_ptr(c), x, y, M, N, stream)
         elif k == "f16":
             rc = binding.gemv_f16_ptr(self.a_ptr(c), x, y, M, N, stream)
+        elif k == "f16x32":
+            rc = binding.gemv_f16x32_ptr(self.a_ptr(c), x, y, M, N, stream)
         elif k == "q8":
             rc = binding.gemv_q8_ptr(self.a_ptr(c), self.s_ptr(c), x, y, M, N, stream)
         else:
@@ -190,6 +192,7 @@ def cpu_baseline(kind, ops, y_gpu, seconds):
     oracle.build(force=False)
     fn = {"f32": lambda: oracle.gemv_f32(ops["A"], ops["x"]),
           "f16": lambda: oracle.gemv_f16(ops["A"], ops["x"]),
+          "f16x32": lambda: oracle.gemv_f16x32(ops["A"], ops["x"]),
           "q8": lambda: oracle.gemv_q8(ops["A"], ops["scale"], ops["x"]),
           "q4": lambda: oracle.gemv_q4(ops["A"], ops["scale"], ops["x"])}[kind]
     ref = fn()
@@ -224,9 +227,9 @@ def traffic_record(kind, M, N):
 
 # ---------------------------------------------------------------- interleaved detail
 DETAIL_SHAPES = [
-    ("8192x8192", 8192, 8192, ("f16", "q8")),
-    ("14336x4096", 14336, 4096, ("f16", "q8", "q4")),
-    ("4096x14336", 4096, 14336, ("f16", "q4")),
+    ("8192x8192", 8192, 8192, ("f16", "q8", "f16x32")),
+    ("14336x4096", 14336, 4096, ("f16", "q8", "q4", "f16x32")),
+    ("4096x14336", 4096, 14336, ("f16", "q4", "f16x32")),
 ]
 
 

@@ -7,8 +7,9 @@
  * section "Algorithm"; the llama.cpp FP16 GEMV walkthrough, opening
  * equation), with A dense and row-major: element (i, j) at linear offset
  * i*N + j, leading dimension N, no stride argument ("Making GEMV Fast",
- * section "Row-major indexing refresher").  Four storage formats; every one
- * accumulates in FP32 and writes FP32 y.
+ * section "Row-major indexing refresher").  Four storage formats for A, with
+ * binary16 or (for FP16 A) FP32 x; every entry point accumulates in FP32
+ * and writes FP32 y.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -24,9 +25,11 @@
  *   Semantics  y is overwritten (no alpha/beta, no accumulation into y).
  *              N == 0 writes y = 0 (the empty sum).  M == 0 is a no-op.
  *   Aliasing   y must not overlap A, x or scale.
- *   Alignment  Any alignment is accepted.  The bandwidth path needs
- *              16-byte-aligned A and x and a row length in bytes that is a
- *              multiple of 16; other inputs take a slower element-wise path.
+ *   Alignment  Each pointer needs only its element's natural alignment
+ *              (4 bytes for float, 2 for binary16, 1 for int8/uint8).  The
+ *              bandwidth path needs 16-byte-aligned A and x and a row length
+ *              in bytes that is a multiple of 16; other inputs take a slower
+ *              element-wise path.
  *   Results    Deterministic: the reduction order depends only on (format,
  *              M, N, pointer alignment, device), so repeated calls give
  *              bitwise identical y.  No atomics.
@@ -67,6 +70,15 @@ int gemv_f32(const float* A, const float* x, float* y, int M, int N, hipStream_t
  * (llama.cpp FP16 GEMV walkthrough: FP16 weight and hidden state, FP32
  * accumulation and output; "membound", section "Results".) */
 int gemv_f16(const uint16_t* A, const uint16_t* x, float* y, int M, int N, hipStream_t stream);
+
+/* FP16 weights with an FP32 hidden state, FP32 accumulation and output:
+ *   A binary16[M*N] row-major, x float[N], y float[M].
+ * Each weight is widened to FP32 exactly and multiplied by x_j exactly, so
+ * only the FP32 additions round, as in gemv_f32.  x takes 4N bytes against
+ * gemv_f16's 2N; A's traffic is the same.
+ * (llama.cpp FP16 GEMV walkthrough, implementation note: the original
+ * kernel keeps the hidden state in FP32.) */
+int gemv_f16x32(const uint16_t* A, const float* x, float* y, int M, int N, hipStream_t stream);
 
 /* INT8 weights with one symmetric binary16 scale per row:
  *   A int8[M*N] row-major, scale binary16[M], x binary16[N], y float[M],
@@ -114,11 +126,14 @@ int gemv_probe_read(const void* buf, size_t bytes, uint32_t* sink, uint32_t guar
 int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 /* Launch geometry the library uses for a call.  kind: 0 f32, 1 f16, 2 q8,
- * 3 q4.  `aligned` states whether A and x are 16-byte aligned.  Fills
- * `info` with the variant (1 = streaming kernel with x staged in LDS,
+ * 3 q4, 4 f16x32 (FP16 A, FP32 x).  `aligned` states whether A and x are
+ * 16-byte aligned.  Fills `info` with the variant (1 = streaming kernel with x staged in LDS,
  * 2 = streaming kernel with x read from global memory, 3 = element-wise
  * kernel), grid and workgroup sizes, rows per wave, 1-KiB loads in flight
- * per wave, and dynamic LDS bytes.  Returns GEMV_OK or an error code; it
+ * per wave, and dynamic LDS bytes.  The geometry is chosen per shape:
+ * workgroups of 4 or 8 waves, 2 to 8 loads in flight, 1 to 4 rows per wave
+ * (the llama.cpp walkthrough's implementation note: the original kernel
+ * selects its block size at run time).  Returns GEMV_OK or an error code; it
  * queries the current device's compute-unit count and launches nothing. */
 typedef struct gemv_launch_info {
     int variant;

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401,E402  (no library load at import time)
     GemvError,
     gemv_f32,
     gemv_f16,
+    gemv_f16x32,
     gemv_q8,
     gemv_q4,
     describe_launch,

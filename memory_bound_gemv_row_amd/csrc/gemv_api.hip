@@ -51,6 +51,7 @@ int elems_per_chunk(int kind)
     case kF32: return Traits<kF32>::kElems;
     case kF16: return Traits<kF16>::kElems;
     case kQ8: return Traits<kQ8>::kElems;
+    case kF16X32: return Traits<kF16X32>::kElems;
     default: return Traits<kQ4>::kElems;
     }
 }
@@ -61,6 +62,7 @@ int lds_bytes(int kind, int nchunks)
     case kF32: return 4 * stream_lds_words<kF32, true, 0>(nchunks);
     case kF16: return 4 * stream_lds_words<kF16, true, 0>(nchunks);
     case kQ8: return 4 * stream_lds_words<kQ8, false, kQ8Decode>(nchunks);
+    case kF16X32: return 4 * stream_lds_words<kF16X32, false, 0>(nchunks);
     default: return 4 * stream_lds_words<kQ4, false, kQ4Decode>(nchunks);
     }
 }
@@ -81,6 +83,11 @@ struct Plan {
 //     for very long rows; 8 units in flight when rows have at least 8 units.
 //   INT8/INT4: x staged in LDS (INT8 with its sum); short rows (INT4 in
 //     particular) put several rows on each wave.
+//   FP16 with FP32 x: x is twice the bytes of FP16 x, and reading it with
+//     every unit costs more cache bandwidth than staging it, once the staging
+//     (4N bytes per workgroup) is spread over enough rows: staged for rows of
+//     at least 12 units, or for 8192 rows and more; read with each unit
+//     otherwise, and whenever the staged x would exceed the LDS budget.
 // Every launch gives each of the device's CUs work when M >= CUs.
 Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
 {
@@ -108,6 +115,29 @@ Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
             p.D = P >= 8 ? 8 : 4;
             p.rows = 1;
         }
+    } else if (kind == kF16X32) {
+        const bool fits = lds_bytes(kind, nchunks) <= kMaxLdsBytes;
+        if (fits && P >= 24) {
+            p.variant = 1;
+            p.waves = 8;
+            p.D = 4;
+            p.rows = 2;
+        } else if (fits && P >= 12) {
+            p.variant = 1;
+            p.waves = 8;
+            p.D = 8;
+            p.rows = 2;
+        } else if (fits && M >= 8192) {
+            p.variant = 1;
+            p.waves = 4;
+            p.D = 8;
+            p.rows = 4;
+        } else {
+            p.variant = 2;
+            p.waves = 4;
+            p.D = P >= 8 ? 8 : 4;
+            p.rows = P >= 8 ? 2 : 1;
+        }
     } else if (kind == kQ8) {
         p.variant = 1;
         p.waves = P >= 8 ? 8 : 4;
@@ -119,29 +149,39 @@ Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
         p.D = P >= 4 ? 4 : 2;
         p.rows = P >= 4 ? 2 : 4;  // short INT4 rows: more rows per wave
     }
-    p.lds = lds_bytes(kind, nchunks);
+    p.lds = p.variant == 1 ? lds_bytes(kind, nchunks) : 0;
     p.block = p.waves * 64;
     const int64_t waves_needed = ((int64_t)M + p.rows - 1) / p.rows;
     p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
     return p;
 }
 
-template <int F, int W, int D>
+template <int F, int W, int D, bool XG>
 const void* stream_kernel()
 {
-    constexpr bool xg = (F == kF32 || F == kF16);
     constexpr int dec = F == kQ8 ? kQ8Decode : (F == kQ4 ? kQ4Decode : 0);
-    return reinterpret_cast<const void*>(&gemv_stream<F, W, D, kNT, xg, dec>);
+    return reinterpret_cast<const void*>(&gemv_stream<F, W, D, kNT, XG, dec>);
 }
 
+template <int F, bool XG>
+const void* select_stream(const Plan& p)
+{
+    if (p.waves == 8)
+        return p.D == 8 ? stream_kernel<F, 8, 8, XG>() : (p.D == 4 ? stream_kernel<F, 8, 4, XG>() : stream_kernel<F, 8, 2, XG>());
+    return p.D == 8 ? stream_kernel<F, 4, 8, XG>() : (p.D == 4 ? stream_kernel<F, 4, 4, XG>() : stream_kernel<F, 4, 2, XG>());
+}
+
+// Variant 1 stages x in LDS, variant 2 reads it with each unit; FP32 and
+// FP16 always take variant 2, INT8 and INT4 variant 1.
 template <int F>
 const void* select_kernel(const Plan& p)
 {
     if (p.variant == 3)
         return reinterpret_cast<const void*>(&gemv_elementwise<F>);
-    if (p.waves == 8)
-        return p.D == 8 ? stream_kernel<F, 8, 8>() : (p.D == 4 ? stream_kernel<F, 8, 4>() : stream_kernel<F, 8, 2>());
-    return p.D == 8 ? stream_kernel<F, 4, 8>() : (p.D == 4 ? stream_kernel<F, 4, 4>() : stream_kernel<F, 4, 2>());
+    if constexpr (F == kF16X32)
+        return p.variant == 2 ? select_stream<F, true>(p) : select_stream<F, false>(p);
+    else
+        return select_stream<F, F == kF32 || F == kF16>(p);
 }
 
 const void* kernel_for(int kind, const Plan& p)
@@ -150,6 +190,7 @@ const void* kernel_for(int kind, const Plan& p)
     case kF32: return select_kernel<kF32>(p);
     case kF16: return select_kernel<kF16>(p);
     case kQ8: return select_kernel<kQ8>(p);
+    case kF16X32: return select_kernel<kF16X32>(p);
     default: return select_kernel<kQ4>(p);
     }
 }
@@ -213,6 +254,11 @@ int gemv_f32(const float* A, const float* x, float* y, int M, int N, hipStream_t
 int gemv_f16(const uint16_t* A, const uint16_t* x, float* y, int M, int N, hipStream_t stream)
 {
     return gemv::launch(gemv::kF16, A, nullptr, x, y, M, N, stream);
+}
+
+int gemv_f16x32(const uint16_t* A, const float* x, float* y, int M, int N, hipStream_t stream)
+{
+    return gemv::launch(gemv::kF16X32, A, nullptr, x, y, M, N, stream);
 }
 
 int gemv_q8(const int8_t* A, const uint16_t* scale, const uint16_t* x, float* y, int M, int N,
@@ -280,7 +326,7 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
 
 int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info)
 {
-    if (info == nullptr || kind < 0 || kind > 3 || M < 0 || N < 0)
+    if (info == nullptr || kind < 0 || kind > 4 || M < 0 || N < 0)
         return GEMV_E_INVAL;
     if (kind == gemv::kQ4 && N % 128 != 0)
         return GEMV_E_UNSUPPORTED;

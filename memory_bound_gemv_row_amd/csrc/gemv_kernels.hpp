@@ -39,7 +39,8 @@ namespace gemv {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-enum Format : int { kF32 = 0, kF16 = 1, kQ8 = 2, kQ4 = 3 };
+// kF16X32: binary16 A with an FP32 x (the hidden state kept in FP32).
+enum Format : int { kF32 = 0, kF16 = 1, kQ8 = 2, kQ4 = 3, kF16X32 = 4 };
 
 // Per-format geometry of one 16-byte chunk of A.
 //   kElems : matrix elements per chunk
@@ -47,6 +48,7 @@ enum Format : int { kF32 = 0, kF16 = 1, kQ8 = 2, kQ4 = 3 };
 template <int F> struct Traits;
 template <> struct Traits<kF32> { static constexpr int kElems = 4;  static constexpr int kXGran = 1; };
 template <> struct Traits<kF16> { static constexpr int kElems = 8;  static constexpr int kXGran = 1; };
+template <> struct Traits<kF16X32> { static constexpr int kElems = 8; static constexpr int kXGran = 2; };
 template <> struct Traits<kQ8>  { static constexpr int kElems = 16; static constexpr int kXGran = 2; };
 template <> struct Traits<kQ4>  { static constexpr int kElems = 32; static constexpr int kXGran = 4; };
 
@@ -90,8 +92,9 @@ __device__ __forceinline__ float wave_sum(float v)
 
 // ---------------------------------------------------------------- chunk products
 // Each returns acc plus the dot product of one 16-byte chunk of A with the
-// matching x elements.  Products are exact in FP32 for every format (at most
-// 24 significant bits); only the additions round.
+// matching x elements.  Only the additions round: FP32 and FP16-with-FP32-x
+// products are formed inside an FMA, which rounds once after the add, and
+// the other formats' products have at most 24 significant bits.
 
 // FP32: 4 columns.
 __device__ __forceinline__ float chunk_f32(u32x4 a, u32x4 xv, float acc)
@@ -110,6 +113,23 @@ __device__ __forceinline__ float chunk_f16(u32x4 a, u32x4 xv, float acc)
     acc = __builtin_amdgcn_fdot2(as_h2(a.y), as_h2(xv.y), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(a.z), as_h2(xv.z), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(xv.w), acc, false);
+    return acc;
+}
+
+// FP16 A with FP32 x: 8 columns; x0 holds columns 0..3, x1 columns 4..7.
+// Each binary16 weight is widened exactly and meets its FP32 x in one FMA
+// (v_fma_mix_f32 selects the low or high half of the A register), so every
+// product is exact and only the additions round, as in the FP32 path.
+__device__ __forceinline__ float chunk_f16x32(u32x4 a, u32x4 x0, u32x4 x1, float acc)
+{
+    const unsigned ws[4] = {a.x, a.y, a.z, a.w};
+    const unsigned xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f16x2 h = as_h2(ws[k]);
+        acc = __builtin_fmaf((float)h.x, as_f(xs[2 * k]), acc);
+        acc = __builtin_fmaf((float)h.y, as_f(xs[2 * k + 1]), acc);
+    }
     return acc;
 }
 
@@ -234,12 +254,29 @@ __device__ __forceinline__ u32x4 q4_pair_x(u32x4 v)
     return r;
 }
 
-// Copy the nxg 16-byte granules of x into LDS (INT4: reordered for q4_word).
-// Each thread issues up to 8 loads before the first wait, so staging costs
-// about one cache round trip per 8 granules.
+// Where granule k (of kXGran) of chunk c sits in staged x.  FP16-with-FP32-x
+// stores each of its two granules as its own plane of nchunks_pad granules,
+// so that a wave's LDS read of granule k covers 1 KiB of consecutive bytes;
+// the other formats keep x's natural order (one granule per chunk, or INT8's
+// and INT4's consecutive granules of one chunk).
+template <int F>
+__device__ __forceinline__ int staged_index(int c, int k, int nchunks_pad)
+{
+    if constexpr (F == kF16X32)
+        return k * nchunks_pad + c;
+    else
+        return c * Traits<F>::kXGran + k;
+}
+
+// Copy the nxg 16-byte granules of x into LDS (INT4: reordered for q4_word;
+// FP16 with FP32 x: split into granule planes).  Each thread issues up to 8
+// loads before the first wait, so staging costs about one cache round trip
+// per 8 granules.
 template <int F, int NT>
 __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds, int nxg, int nxg_pad)
 {
+    constexpr int G = Traits<F>::kXGran;
+    const int nchunks_pad = nxg_pad / G;
     for (int g0 = threadIdx.x; g0 < nxg_pad; g0 += 8 * NT) {
         u32x4 v[8];
 #pragma unroll
@@ -250,10 +287,13 @@ __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int g = g0 + k * NT;
+            if (g >= nxg_pad)
+                continue;
+            const int dst = staged_index<F>(g / G, g % G, nchunks_pad);
             if (g < nxg)
-                lds[g] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
-            else if (g < nxg_pad)
-                lds[g] = u32x4{0u, 0u, 0u, 0u};
+                lds[dst] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+            else
+                lds[dst] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 }
@@ -317,13 +357,13 @@ __device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4
 // the oldest of D outstanding loads.  The first D loads are issued at
 // kernel start (INT4: right after x is staged).  A ragged last pass
 // (fewer than 64 chunks) contributes exactly zero in the lanes past the row
-// end: with global loads (FP32/FP16) those lanes load chunk 0 and zero it
+// end: with global loads (unquantised A) those lanes load chunk 0 and zero it
 // before use; with buffer loads (INT8/INT4) the row-sized resource returns
 // zeros and meets zero-padded x.  The unit count is padded to
 // a multiple of D; padded units re-read the wave's last row and are never
 // stored.
 //
-//   XG  (FP32/FP16 only): x granules are loaded from global memory with each
+//   XG  x granules are loaded from global memory with each
 //       unit instead of being staged in LDS (no staging, no barrier).
 //   DEC (INT8/INT4 only): 0 = exponent-bias decode (q8_word / q4_word),
 //       1 = offset-code decode (q8_sub_chunk / q4_sub_chunk) with the bias
@@ -457,6 +497,8 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             acc = chunk_f32(a, xv[0], acc);
         } else if constexpr (F == kF16) {
             acc = chunk_f16(a, xv[0], acc);
+        } else if constexpr (F == kF16X32) {
+            acc = chunk_f16x32(a, xv[0], xv[1 % G], acc);
         } else if constexpr (F == kQ8) {
             if constexpr (DEC == 1)
                 acc = q8_sub_chunk(a, xv[0], xv[G - 1], acc);
@@ -499,7 +541,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         } else {
 #pragma unroll
             for (int k = 0; k < G; ++k)
-                xv[k] = lds_x[cc * G + k];
+                xv[k] = lds_x[staged_index<F>(cc, k, P * 64)];
         }
         compute(a, xv, sbuf[d]);
     };
@@ -540,6 +582,11 @@ gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sca
         const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
         for (int j = lane; j < N; j += 64)
             acc = __builtin_fmaf(half_bits_to_float(a[j]), half_bits_to_float(xh[j]), acc);
+    } else if constexpr (F == kF16X32) {
+        const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
+        const float* xf = reinterpret_cast<const float*>(x);
+        for (int j = lane; j < N; j += 64)
+            acc = __builtin_fmaf(half_bits_to_float(a[j]), xf[j], acc);
     } else if constexpr (F == kQ8) {
         const int8_t* a = reinterpret_cast<const int8_t*>(A) + (int64_t)row * N;
         const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);

@@ -9,6 +9,8 @@ Workloads (all synthetic; no page uses a dataset):
         -- the square FP32 study of "cuda-gemv-optimization".
   f16 : A ~ N(0, 1/N), x ~ N(0, 1), cast to binary16 -- decode-projection
         shapes from "membound", section "Results".
+  f16x32 : A ~ N(0, 1/N) as binary16, x ~ N(0, 1) kept in float32 (FP16
+        weights with an FP32 hidden state, as the llama.cpp original keeps it).
   q8  : A int8 uniform on [-127, 127]; one binary16 scale per row,
         uniform[0.5, 1.5]/127; x ~ N(0, 1) binary16.
   q4  : A packed two nibbles per byte, [M, N/2] uint8.  Every byte is drawn
@@ -25,7 +27,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-KINDS = ("f32", "f16", "q8", "q4")
+KINDS = ("f32", "f16", "f16x32", "q8", "q4")
 
 
 @dataclass(frozen=True)
@@ -46,6 +48,7 @@ WORKLOADS = {
     "f16_decode": [Workload("f16", 4096, 4096), Workload("f16", 8192, 8192),
                    Workload("f16", 14336, 4096), Workload("f16", 4096, 14336)],
     "q8_decode": [Workload("q8", 8192, 8192), Workload("q8", 14336, 4096)],
+    "f16x32_decode": [Workload("f16x32", 8192, 8192), Workload("f16x32", 4096, 14336)],
     "q4_decode": [Workload("q4", 4096, 14336), Workload("q4", 14336, 4096)],
 }
 
@@ -69,6 +72,14 @@ def make_f16(M: int, N: int, seed: int = 0):
     return {"A": A, "x": x}
 
 
+def make_f16x32(M: int, N: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    sigma = 1.0 / np.sqrt(N) if N > 0 else 1.0
+    A = rng.normal(0.0, sigma, (M, N)).astype(np.float16)
+    x = rng.standard_normal(N).astype(np.float32)
+    return {"A": A, "x": x}
+
+
 def make_q8(M: int, N: int, seed: int = 0):
     rng = np.random.default_rng(seed)
     A = rng.integers(-127, 128, (M, N), dtype=np.int8)
@@ -87,7 +98,7 @@ def make_q4(M: int, N: int, seed: int = 0):
     return {"A": A, "scale": scale, "x": x}
 
 
-MAKERS = {"f32": make_f32, "f16": make_f16, "q8": make_q8, "q4": make_q4}
+MAKERS = {"f32": make_f32, "f16": make_f16, "f16x32": make_f16x32, "q8": make_q8, "q4": make_q4}
 
 
 def make(kind: str, M: int, N: int, seed: int = 0):

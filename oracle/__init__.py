@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     half_to_double_array,
     gemv_f32,
     gemv_f16,
+    gemv_f16x32,
     gemv_q8,
     gemv_q4,
     num_threads,

@@ -116,6 +116,25 @@ int oracle_gemv_f16(const uint16_t* A, const uint16_t* x, double* y, int64_t M, 
     return 0;
 }
 
+/* FP16 A (binary16 bit patterns) with an FP32 x: the hidden state kept in
+ * FP32 (llama.cpp FP16 GEMV walkthrough, implementation note on the
+ * original kernel).  Each product (11 x 24 significant bits) is exact in
+ * double. */
+int oracle_gemv_f16x32(const uint16_t* A, const float* x, double* y, int64_t M, int64_t N)
+{
+    if (M < 0 || N < 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        const uint16_t* row = A + i * N;
+        double acc = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            acc += half_bits_to_double(row[j]) * (double)x[j];
+        y[i] = acc;
+    }
+    return 0;
+}
+
 /* INT8 A with one binary16 scale per row; w_ij = q_ij * s_i. */
 int oracle_gemv_q8(const int8_t* A, const uint16_t* scale, const uint16_t* x, double* y,
                    int64_t M, int64_t N)

@@ -15,7 +15,8 @@ terms and some land arbitrarily close to zero:
     err = max_i |y_i - r_i| / max(|r_i|, 0.01 * max_k |r_k|)
 
 Gates: 1e-4 for the FP32 and dequantised INT8/INT4 paths, 2e-3 for FP16
-inputs with FP32 accumulation.  The unfloored elementwise maximum, the
+inputs with FP32 accumulation, and 1e-4 for FP16 weights with FP32
+activations (each product rounds once, like the FP32 path).  The unfloored elementwise maximum, the
 normwise error and the componentwise error relative to sum_j |w_ij x_j| are
 reported as diagnostics and never gated.
 """
@@ -23,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-GATES = {"f32": 1e-4, "q8": 1e-4, "q4": 1e-4, "f16": 2e-3}
+GATES = {"f32": 1e-4, "q8": 1e-4, "q4": 1e-4, "f16": 2e-3, "f16x32": 1e-4}
 FLOOR_FRACTION = 0.01
 
 

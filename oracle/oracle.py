@@ -61,9 +61,11 @@ def _load():
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_gemv_f32.argtypes = [p, p, p, i64, i64]
         lib.oracle_gemv_f16.argtypes = [p, p, p, i64, i64]
+        lib.oracle_gemv_f16x32.argtypes = [p, p, p, i64, i64]
         lib.oracle_gemv_q8.argtypes = [p, p, p, p, i64, i64]
         lib.oracle_gemv_q4.argtypes = [p, p, p, p, i64, i64]
-        for f in (lib.oracle_gemv_f32, lib.oracle_gemv_f16, lib.oracle_gemv_q8, lib.oracle_gemv_q4):
+        for f in (lib.oracle_gemv_f32, lib.oracle_gemv_f16, lib.oracle_gemv_f16x32, lib.oracle_gemv_q8,
+                  lib.oracle_gemv_q4):
             f.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -125,6 +127,20 @@ def gemv_f16(A: np.ndarray, x: np.ndarray) -> np.ndarray:
     rc = _load().oracle_gemv_f16(_ptr(A), _ptr(x), _ptr(y), M, N)
     if rc != 0:
         raise ValueError("oracle_gemv_f16 rejected its arguments")
+    return y
+
+
+def gemv_f16x32(A: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """FP16 A (binary16) with FP32 x."""
+    A = _f16_bits(A, "A")
+    x = _as(x, np.float32, "x")
+    M, N = A.shape
+    if x.shape != (N,):
+        raise ValueError("x must have shape (N,)")
+    y = np.empty(M, dtype=np.float64)
+    rc = _load().oracle_gemv_f16x32(_ptr(A), _ptr(x), _ptr(y), M, N)
+    if rc != 0:
+        raise ValueError("oracle_gemv_f16x32 rejected its arguments")
     return y
 
 

@@ -18,6 +18,8 @@ def run_gpu(kind: str, ops: dict) -> np.ndarray:
         y = binding.gemv_f32(A, x)
     elif kind == "f16":
         y = binding.gemv_f16(A, x)
+    elif kind == "f16x32":
+        y = binding.gemv_f16x32(A, x)
     elif kind == "q8":
         y = binding.gemv_q8(A, dev(ops["scale"]), x)
     else:
@@ -31,6 +33,8 @@ def run_oracle(oracle, kind: str, ops: dict) -> np.ndarray:
         return oracle.gemv_f32(ops["A"], ops["x"])
     if kind == "f16":
         return oracle.gemv_f16(ops["A"], ops["x"])
+    if kind == "f16x32":
+        return oracle.gemv_f16x32(ops["A"], ops["x"])
     if kind == "q8":
         return oracle.gemv_q8(ops["A"], ops["scale"], ops["x"])
     return oracle.gemv_q4(ops["A"], ops["scale"], ops["x"])

@@ -24,12 +24,14 @@ def _call(kind, A, s, x, y, M, N, stream=0):
         return binding.gemv_f32_ptr(A, x, y, M, N, stream)
     if kind == "f16":
         return binding.gemv_f16_ptr(A, x, y, M, N, stream)
+    if kind == "f16x32":
+        return binding.gemv_f16x32_ptr(A, x, y, M, N, stream)
     if kind == "q8":
         return binding.gemv_q8_ptr(A, s, x, y, M, N, stream)
     return binding.gemv_q4_ptr(A, s, x, y, M, N, stream)
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_status_codes(gpu, kind):
     M, N = 8, 256
     A, s, x = _ptrs(kind, inputs.make(kind, M, N))
@@ -53,7 +55,7 @@ def test_status_codes(gpu, kind):
         binding.gemv_f32(torch.zeros(4, 4, device="cuda"), torch.zeros(5, device="cuda"))
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_n_zero_writes_zeros(gpu, kind):
     M = 70
     y = torch.full((M,), 7.0, device="cuda")
@@ -66,7 +68,7 @@ def test_n_zero_writes_zeros(gpu, kind):
     assert torch.all(y == 0)
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_writes_only_y_0_to_M(gpu, oracle_mod, kind):
     M, N = 37, 1024
     ops = inputs.make(kind, M, N, seed=2)
@@ -81,7 +83,7 @@ def test_writes_only_y_0_to_M(gpu, oracle_mod, kind):
     assert parity_error(g[64:64 + M], run_oracle(oracle_mod, kind, ops)) <= GATES[kind]
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_repeat_runs_bitwise_identical(gpu, kind):
     ops = inputs.make(kind, 1000, 4096, seed=4)
     say(f"[determinism] {kind}")
@@ -102,14 +104,14 @@ def test_non_default_stream(gpu, oracle_mod):
     assert parity_error(y.cpu().numpy(), run_oracle(oracle_mod, "f16", ops)) <= GATES["f16"]
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 @pytest.mark.parametrize("offset", [2, 4, 8])
 def test_unaligned_operands(gpu, oracle_mod, kind, offset):
     """A and x at byte offsets that break 16-byte alignment take the
     element-wise path and still agree with the oracle."""
     M, N = 33, 1024
     ops = inputs.make(kind, M, N, seed=offset)
-    elt = {"f32": 4, "f16": 2, "q8": 1, "q4": 1}[kind]
+    elt = {"f32": 4, "f16": 2, "f16x32": 4, "q8": 1, "q4": 1}[kind]   # natural alignment of x
     if offset % elt:
         pytest.skip("offset not a multiple of the element size")
     Ab = ops["A"].view(np.uint8).ravel()
@@ -131,10 +133,18 @@ def test_unaligned_operands(gpu, oracle_mod, kind, offset):
 def test_describe_launch_fills_all_cus(gpu):
     props = torch.cuda.get_device_properties(0)
     cus = props.multi_processor_count
-    for kind, M, N in (("f32", 1024, 1024), ("f16", 8192, 8192), ("q4", 4096, 14336), ("q4", 14336, 4096)):
+    for kind, M, N in (("f32", 1024, 1024), ("f16", 8192, 8192), ("q4", 4096, 14336), ("q4", 14336, 4096),
+                       ("f16x32", 8192, 8192), ("f16x32", 4096, 14336), ("f16x32", 14336, 4096),
+                       ("f16x32", 4096, 4096)):
         info = binding.describe_launch(kind, M, N)
         assert info["grid"] >= cus, (kind, M, N, info, cus)
     assert binding.describe_launch("f16", 8, 1001)["variant"] == 3
+    # FP16 A with FP32 x: x staged in LDS for long rows or many rows, read
+    # with each unit otherwise, and never staged beyond the LDS budget
+    assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 1
+    assert binding.describe_launch("f16x32", 14336, 4096)["variant"] == 1
+    assert binding.describe_launch("f16x32", 4096, 4096)["variant"] == 2
+    assert binding.describe_launch("f16x32", 64, 32768)["variant"] == 2
 
 
 def test_probe_copy_and_read(gpu):

@@ -47,11 +47,13 @@ _NS = {
     "f32": [1, 3, 4, 8, 60, 64, 252, 256, 260, 1020, 1024, 2052, 4100, 9000, 17000],
     "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 8200, 14336, 20000],
     "q8": [1, 15, 16, 32, 1008, 1024, 1040, 5000, 8192, 9232, 20000],
+    # 5632 | 6144 straddle the staged-x threshold, 16392 is just past the LDS budget
+    "f16x32": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 5632, 6144, 8200, 14336, 16384, 16392, 20000],
     "q4": [128, 256, 384, 1024, 2048, 2176, 4096, 7296, 14336],
 }
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_shapes_and_tails(gpu, oracle_mod, kind):
     for N in _NS[kind]:
         for M in _MS:
@@ -60,7 +62,7 @@ def test_shapes_and_tails(gpu, oracle_mod, kind):
 
 
 @pytest.mark.parametrize("kind,N", [("f32", 64 * 4 * 8 * 2 + 4), ("f16", 64 * 8 * 17 + 8), ("q8", 64 * 16 * 9 + 16),
-                                    ("q4", 64 * 32 * 3 + 128)])
+                                    ("q4", 64 * 32 * 3 + 128), ("f16x32", 64 * 8 * 17 + 8), ("f16x32", 64 * 8 * 3 + 8)])
 def test_many_passes_and_row_groups(gpu, oracle_mod, kind, N):
     # enough rows for several workgroups, a partial last workgroup, and rows
     # whose chunk count leaves a partly filled final pass
@@ -75,6 +77,8 @@ def _int_ops(kind, M, N, rng):
         return {"A": rng.integers(-3, 4, (M, N)).astype(np.float32), "x": x.astype(np.float32)}
     if kind == "f16":
         return {"A": rng.integers(-3, 4, (M, N)).astype(np.float16), "x": x.astype(np.float16)}
+    if kind == "f16x32":
+        return {"A": rng.integers(-3, 4, (M, N)).astype(np.float16), "x": x.astype(np.float32)}
     if kind == "q8":
         return {"A": rng.integers(-128, 128, (M, N), dtype=np.int8),
                 "scale": np.full(M, 2.0 ** -7, np.float16), "x": x.astype(np.float16)}
@@ -84,7 +88,7 @@ def _int_ops(kind, M, N, rng):
     return {"A": pack_int4(q), "scale": s, "x": x.astype(np.float16)}
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 @pytest.mark.parametrize("M,N", [(37, 1024), (8, 4096), (300, 256), (5, 1152)])
 def test_integer_inputs_bit_exact(gpu, oracle_mod, kind, M, N):
     ops = _int_ops(kind, M, N, np.random.default_rng(M + N))
@@ -112,6 +116,38 @@ def test_f16_subnormal_operands_bit_exact(gpu, oracle_mod, N):
     ops = {"A": rng.integers(-3, 4, (M, N)).astype(np.float16), "x": A[0].copy()}
     say(f"[subnormal x] N={N}")
     assert np.array_equal(run_gpu("f16", ops).astype(np.float64), run_oracle(oracle_mod, "f16", ops))
+
+
+@pytest.mark.parametrize("M,N", [(40, 1024), (9000, 1024), (24, 8192)])
+def test_f16x32_full_precision_x_bit_exact(gpu, oracle_mod, M, N):
+    # x = k * 2^-8 with |k| < 2^12 (up to 12 significant bits, so many values
+    # are not binary16) and integer A: every product and partial sum is a
+    # multiple of 2^-8 whose magnitude stays below sum_j |A_ij k_j| < 2^24
+    # units, exact in FP32 in any order.  Covers x read per unit (N = 1024),
+    # staged for many rows (M = 9000) and staged for long rows (N = 8192,
+    # where A is drawn from {-1, 0, 1} to keep the bound).
+    rng = np.random.default_rng(M + N)
+    k = rng.integers(-4095, 4096, N)
+    x = (k * 2.0 ** -8).astype(np.float32)
+    assert np.any(x.astype(np.float16).astype(np.float32) != x)
+    amax = 3 if N <= 1024 else 1
+    A = rng.integers(-amax, amax + 1, (M, N))
+    assert np.max(np.abs(A) @ np.abs(k)) < 2 ** 24
+    ops = {"A": A.astype(np.float16), "x": x}
+    say(f"[exact f16x32] M={M} N={N} {binding.describe_launch('f16x32', M, N)}")
+    y = run_gpu("f16x32", ops)
+    assert np.array_equal(y.astype(np.float64), run_oracle(oracle_mod, "f16x32", ops))
+
+
+def test_f16x32_subnormal_weights_bit_exact(gpu, oracle_mod):
+    # binary16 subnormal A (k * 2^-24) must be widened, not flushed
+    rng = np.random.default_rng(17)
+    M, N = 40, 4096
+    k = rng.integers(-1023, 1024, (M, N))
+    A = (np.where(k < 0, 0x8000, 0) | np.abs(k)).astype(np.uint16).view(np.float16)
+    ops = {"A": A, "x": rng.integers(-3, 4, N).astype(np.float32)}
+    say("[subnormal A] f16x32")
+    assert np.array_equal(run_gpu("f16x32", ops).astype(np.float64), run_oracle(oracle_mod, "f16x32", ops))
 
 
 @pytest.mark.parametrize("kind", ["q8", "q4"])
@@ -154,7 +190,7 @@ def test_rowmajor_one_hot_f32(gpu, oracle_mod):
 
 
 # ---------------------------------------------------------------- degenerate cases
-@pytest.mark.parametrize("kind", ["f32", "f16", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_extreme_int_values_and_identity(gpu, oracle_mod, kind):
     n = 256
     rng = np.random.default_rng(0)
@@ -165,6 +201,12 @@ def test_extreme_int_values_and_identity(gpu, oracle_mod, kind):
     elif kind == "f16":
         ops = {"A": np.eye(n, dtype=np.float16), "x": xv}
         want = xv.astype(np.float64)
+    elif kind == "f16x32":
+        # x with 24 significant bits and outside the binary16 range: y = x
+        # exactly only if x reaches the products unrounded
+        x32 = (rng.uniform(-1, 1, n) * np.float32(2.0) ** rng.integers(-30, 30, n)).astype(np.float32)
+        ops = {"A": np.eye(n, dtype=np.float16), "x": x32}
+        want = x32.astype(np.float64)
     elif kind == "q8":
         A = np.full((n, n), -128, np.int8)        # the most negative code everywhere
         ops = {"A": A, "scale": np.full(n, 2.0 ** -7, np.float16), "x": np.ones(n, np.float16)}

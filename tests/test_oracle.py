@@ -228,11 +228,62 @@ def test_one_hot_columns_q8(oracle_mod):
         assert np.array_equal(oracle_mod.gemv_q8(q, s, e), q[:, j].astype(np.float64) * s.astype(np.float64))
 
 
+# ---------------------------------------------------------------- FP16 weights, FP32 activations
+def test_f16x32_identity_keeps_full_x(oracle_mod):
+    # x values with more than 11 significant bits, beyond the binary16 range
+    # and below its subnormals: any cast of x to binary16 changes them.
+    rng = np.random.default_rng(13)
+    n = 200
+    x = rng.uniform(-1, 1, n).astype(np.float32)
+    x[:4] = np.array([1.0 + 2.0 ** -20, 1.0e6, -3.0e-9, 65520.0], dtype=np.float32)
+    assert np.any(x.astype(np.float16).astype(np.float32) != x)
+    y = oracle_mod.gemv_f16x32(np.eye(n, dtype=np.float16), x)
+    assert np.array_equal(y, x.astype(np.float64))
+
+
+def test_f16x32_one_hot_columns(oracle_mod):
+    rng = np.random.default_rng(14)
+    M, N = 5, 48
+    A = f16(rng.standard_normal((M, N)))
+    A[0, :3] = np.array([0x0001, 0x83FF, 0x7BFF], dtype=np.uint16).view(np.float16)   # subnormals, max
+    for j in range(N):
+        e = np.zeros(N, np.float32)
+        e[j] = 3.0
+        assert np.array_equal(oracle_mod.gemv_f16x32(A, e), 3.0 * A[:, j].astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (3, 5), (2, 33), (9, 64)])
+def test_f16x32_tiny_shapes_exact_rational(oracle_mod, M, N):
+    rng = np.random.default_rng(M * 1000 + N)
+    A = f16(rng.standard_normal((M, N)))
+    x = rng.standard_normal(N).astype(np.float32)
+    y = oracle_mod.gemv_f16x32(A, x)
+    for i in range(M):
+        exact = sum(Fraction(float(A[i, j])) * Fraction(float(x[j])) for j in range(N))
+        terms = [float(A[i, j]) * float(x[j]) for j in range(N)]     # 11 x 24 bits: exact
+        assert abs(Fraction(y[i]) - exact) <= Fraction(_sum_bound(terms))
+
+
+def test_f16x32_against_blas_float64(oracle_mod):
+    rng = np.random.default_rng(15)
+    M, N = 300, 4096
+    A = f16(rng.standard_normal((M, N)) / math.sqrt(N))
+    x = rng.standard_normal(N).astype(np.float32)
+    ref = A.astype(np.float64) @ x.astype(np.float64)
+    y = oracle_mod.gemv_f16x32(A, x)
+    assert np.max(np.abs(y - ref)) <= 1e-13 * np.max(np.abs(ref))
+    # the FP16-activation result differs once x is rounded to binary16
+    y16 = oracle_mod.gemv_f16(A, x.astype(np.float16))
+    assert np.max(np.abs(y16 - ref)) > 1e-6 * np.max(np.abs(ref))
+
+
 # ---------------------------------------------------------------- degenerate and special values
 def test_empty_shapes(oracle_mod):
     assert oracle_mod.gemv_f32(np.zeros((0, 5), np.float32), np.zeros(5, np.float32)).shape == (0,)
     y = oracle_mod.gemv_f16(np.zeros((3, 0), np.float16), np.zeros(0, np.float16))
     assert np.array_equal(y, np.zeros(3))
+    y = oracle_mod.gemv_f16x32(np.zeros((2, 0), np.float16), np.zeros(0, np.float32))
+    assert np.array_equal(y, np.zeros(2))
 
 
 def test_nan_and_inf_propagate(oracle_mod):
