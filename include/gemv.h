@@ -8,8 +8,8 @@
  * equation), with A dense and row-major: element (i, j) at linear offset
  * i*N + j, leading dimension N, no stride argument ("Making GEMV Fast",
  * section "Row-major indexing refresher").  Four storage formats for A, with
- * binary16 or (for FP16 A) FP32 x; every entry point accumulates in FP32
- * and writes FP32 y.
+ * binary16 or (for FP16 A) FP32 x; every entry point but the lossy
+ * gemv_f16_acc16 accumulates in FP32, and all write FP32 y.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -80,6 +80,22 @@ int gemv_f16(const uint16_t* A, const uint16_t* x, float* y, int M, int N, hipSt
  * kernel keeps the hidden state in FP32.) */
 int gemv_f16x32(const uint16_t* A, const float* x, float* y, int M, int N, hipStream_t stream);
 
+/* FP16 weights and activations with FP16 ACCUMULATION -- LOSSY:
+ *   A binary16[M*N] row-major, x binary16[N], y float[M].
+ * Each lane of the kernel keeps its running sums in binary16 (one rounding
+ * to binary16 per term, at most k = max(ceil(N/64), 4) terms per sum); only
+ * the final cross-lane reduction and y are FP32.  For every row,
+ *   |y_i - sum_j A_ij x_j| <= ((1 + g16(k)) (1 + g32(8)) - 1) * sum_j |A_ij x_j|
+ *                             + N * 2^-24,
+ * with gB(k) = k*uB / (1 - k*uB), u16 = 2^-11, u32 = 2^-24 (the N*2^-24
+ * term covers roundings of sums in binary16's subnormal range, spacing
+ * 2^-24).  A partial sum beyond binary16's
+ * range (65504) gives an infinite y_i.  Use gemv_f16 unless this rounding is
+ * acceptable.
+ * (llama.cpp FP16 GEMV walkthrough, implementation note: the original
+ * kernel can accumulate in FP16 or FP32.) */
+int gemv_f16_acc16(const uint16_t* A, const uint16_t* x, float* y, int M, int N, hipStream_t stream);
+
 /* INT8 weights with one symmetric binary16 scale per row:
  *   A int8[M*N] row-major, scale binary16[M], x binary16[N], y float[M],
  *   y_i = sum_j (A_ij * scale_i) * x_j.
@@ -126,7 +142,8 @@ int gemv_probe_read(const void* buf, size_t bytes, uint32_t* sink, uint32_t guar
 int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 /* Launch geometry the library uses for a call.  kind: 0 f32, 1 f16, 2 q8,
- * 3 q4, 4 f16x32 (FP16 A, FP32 x).  `aligned` states whether A and x are
+ * 3 q4, 4 f16x32 (FP16 A, FP32 x), 5 f16_acc16 (FP16 accumulation).
+ * `aligned` states whether A and x are
  * 16-byte aligned.  Fills `info` with the variant (1 = streaming kernel with x staged in LDS,
  * 2 = streaming kernel with x read from global memory, 3 = element-wise
  * kernel), grid and workgroup sizes, rows per wave, 1-KiB loads in flight

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401,E402  (no library load at import time)
     gemv_f32,
     gemv_f16,
     gemv_f16x32,
+    gemv_f16_acc16,
     gemv_q8,
     gemv_q4,
     describe_launch,

@@ -11,6 +11,7 @@ add 2/128 byte per weight):
     f32 : 4MN            + 4N + 4M
     f16 : 2MN            + 2N + 4M
     f16x32 : 2MN         + 4N + 4M      (FP16 weights, FP32 activations)
+    f16_acc16 : as f16                  (FP16 accumulation changes no byte)
     q8  :  MN + 2M       + 2N + 4M      (one binary16 scale per row)
     q4  : MN/2 + 2M(N/128) + 2N + 4M    (one binary16 scale per 128-column group)
 
@@ -20,14 +21,14 @@ multiplies are not counted as FLOPs.
 """
 from __future__ import annotations
 
-X_BYTES = {"f32": 4, "f16": 2, "f16x32": 4, "q8": 2, "q4": 2}
+X_BYTES = {"f32": 4, "f16": 2, "f16x32": 4, "f16_acc16": 2, "q8": 2, "q4": 2}
 
 
 def weight_bytes(kind: str, M: int, N: int) -> int:
     """Bytes of A plus its scales: the streamed, read-once part."""
     if kind == "f32":
         return 4 * M * N
-    if kind in ("f16", "f16x32"):
+    if kind in ("f16", "f16x32", "f16_acc16"):
         return 2 * M * N
     if kind == "q8":
         return M * N + 2 * M

@@ -14,7 +14,7 @@ import threading
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgemv_amd.so")
 
-KIND = {"f32": 0, "f16": 1, "q8": 2, "q4": 3, "f16x32": 4}
+KIND = {"f32": 0, "f16": 1, "q8": 2, "q4": 3, "f16x32": 4, "f16_acc16": 5}
 STATUS = {0: "GEMV_OK", 1: "GEMV_E_INVAL", 2: "GEMV_E_UNSUPPORTED", 3: "GEMV_E_LAUNCH", 4: "GEMV_E_DEVICE"}
 
 _lock = threading.Lock()
@@ -43,7 +43,7 @@ def load():
                                "(run python -m memory_bound_gemv_row_amd.build)")
         lib = ctypes.CDLL(LIB_PATH)
         p, i = ctypes.c_void_p, ctypes.c_int
-        for name in ("gemv_f32", "gemv_f16", "gemv_f16x32"):
+        for name in ("gemv_f32", "gemv_f16", "gemv_f16x32", "gemv_f16_acc16"):
             getattr(lib, name).argtypes = [p, p, p, i, i, p]
             getattr(lib, name).restype = i
         for name in ("gemv_q8", "gemv_q4"):
@@ -82,6 +82,10 @@ def gemv_f16_ptr(A: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int
 
 def gemv_f16x32_ptr(A: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
     return load().gemv_f16x32(A, x, y, M, N, stream)
+
+
+def gemv_f16_acc16_ptr(A: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_f16_acc16(A, x, y, M, N, stream)
 
 
 def gemv_q8_ptr(A: int, scale: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
@@ -172,6 +176,20 @@ def gemv_f16x32(A, x, out=None, stream=None):
     xp = _need(x, "x", (torch.float32,), (N,))
     y = _out(out, M, A.device)
     _check(gemv_f16x32_ptr(a, xp, y.data_ptr(), M, N, _stream(stream)), "gemv_f16x32")
+    return y
+
+
+def gemv_f16_acc16(A, x, out=None, stream=None):
+    """LOSSY: binary16 running sums (see gemv_f16_acc16 in include/gemv.h).
+    A: binary16 [M, N], x: binary16 [N]."""
+    import torch
+
+    h = (torch.float16, torch.int16, torch.uint16)
+    M, N = A.shape
+    a = _need(A, "A", h, (M, N))
+    xp = _need(x, "x", h, (N,))
+    y = _out(out, M, A.device)
+    _check(gemv_f16_acc16_ptr(a, xp, y.data_ptr(), M, N, _stream(stream)), "gemv_f16_acc16")
     return y
 
 

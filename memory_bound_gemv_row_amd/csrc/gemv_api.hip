@@ -52,6 +52,7 @@ int elems_per_chunk(int kind)
     case kF16: return Traits<kF16>::kElems;
     case kQ8: return Traits<kQ8>::kElems;
     case kF16X32: return Traits<kF16X32>::kElems;
+    case kF16H: return Traits<kF16H>::kElems;
     default: return Traits<kQ4>::kElems;
     }
 }
@@ -63,6 +64,7 @@ int lds_bytes(int kind, int nchunks)
     case kF16: return 4 * stream_lds_words<kF16, true, 0>(nchunks);
     case kQ8: return 4 * stream_lds_words<kQ8, false, kQ8Decode>(nchunks);
     case kF16X32: return 4 * stream_lds_words<kF16X32, false, 0>(nchunks);
+    case kF16H: return 4 * stream_lds_words<kF16H, true, 0>(nchunks);
     default: return 4 * stream_lds_words<kQ4, false, kQ4Decode>(nchunks);
     }
 }
@@ -79,7 +81,7 @@ struct Plan {
 
 // Geometry for one call.  A row of nchunks 16-byte chunks is
 // P = ceil(nchunks / 64) units (one 1-KiB wave load each).
-//   FP32/FP16: x read with each unit (no staging); one row per wave, or two
+//   FP32/FP16 (either accumulation): x read with each unit (no staging); one row per wave, or two
 //     for very long rows; 8 units in flight when rows have at least 8 units.
 //   INT8/INT4: x staged in LDS (INT8 with its sum); short rows (INT4 in
 //     particular) put several rows on each wave.
@@ -104,7 +106,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
     }
     const int nchunks = N / epc;
     const int P = (nchunks + 63) / 64;
-    if (kind == kF32 || kind == kF16) {
+    if (kind == kF32 || kind == kF16 || kind == kF16H) {
         p.variant = 2;
         if (P >= 24) {            // very long rows: two per wave, fewer in flight each
             p.waves = 4;
@@ -181,7 +183,7 @@ const void* select_kernel(const Plan& p)
     if constexpr (F == kF16X32)
         return p.variant == 2 ? select_stream<F, true>(p) : select_stream<F, false>(p);
     else
-        return select_stream<F, F == kF32 || F == kF16>(p);
+        return select_stream<F, F == kF32 || F == kF16 || F == kF16H>(p);
 }
 
 const void* kernel_for(int kind, const Plan& p)
@@ -191,6 +193,7 @@ const void* kernel_for(int kind, const Plan& p)
     case kF16: return select_kernel<kF16>(p);
     case kQ8: return select_kernel<kQ8>(p);
     case kF16X32: return select_kernel<kF16X32>(p);
+    case kF16H: return select_kernel<kF16H>(p);
     default: return select_kernel<kQ4>(p);
     }
 }
@@ -261,6 +264,11 @@ int gemv_f16x32(const uint16_t* A, const float* x, float* y, int M, int N, hipSt
     return gemv::launch(gemv::kF16X32, A, nullptr, x, y, M, N, stream);
 }
 
+int gemv_f16_acc16(const uint16_t* A, const uint16_t* x, float* y, int M, int N, hipStream_t stream)
+{
+    return gemv::launch(gemv::kF16H, A, nullptr, x, y, M, N, stream);
+}
+
 int gemv_q8(const int8_t* A, const uint16_t* scale, const uint16_t* x, float* y, int M, int N,
             hipStream_t stream)
 {
@@ -326,7 +334,7 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
 
 int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info)
 {
-    if (info == nullptr || kind < 0 || kind > 4 || M < 0 || N < 0)
+    if (info == nullptr || kind < 0 || kind > 5 || M < 0 || N < 0)
         return GEMV_E_INVAL;
     if (kind == gemv::kQ4 && N % 128 != 0)
         return GEMV_E_UNSUPPORTED;

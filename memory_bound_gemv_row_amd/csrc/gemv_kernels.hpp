@@ -40,7 +40,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // kF16X32: binary16 A with an FP32 x (the hidden state kept in FP32).
-enum Format : int { kF32 = 0, kF16 = 1, kQ8 = 2, kQ4 = 3, kF16X32 = 4 };
+// kF16H: binary16 A and x with binary16 running sums (lossy; see chunk_f16h).
+enum Format : int { kF32 = 0, kF16 = 1, kQ8 = 2, kQ4 = 3, kF16X32 = 4, kF16H = 5 };
 
 // Per-format geometry of one 16-byte chunk of A.
 //   kElems : matrix elements per chunk
@@ -49,6 +50,7 @@ template <int F> struct Traits;
 template <> struct Traits<kF32> { static constexpr int kElems = 4;  static constexpr int kXGran = 1; };
 template <> struct Traits<kF16> { static constexpr int kElems = 8;  static constexpr int kXGran = 1; };
 template <> struct Traits<kF16X32> { static constexpr int kElems = 8; static constexpr int kXGran = 2; };
+template <> struct Traits<kF16H> { static constexpr int kElems = 8;  static constexpr int kXGran = 1; };
 template <> struct Traits<kQ8>  { static constexpr int kElems = 16; static constexpr int kXGran = 2; };
 template <> struct Traits<kQ4>  { static constexpr int kElems = 32; static constexpr int kXGran = 4; };
 
@@ -113,6 +115,21 @@ __device__ __forceinline__ float chunk_f16(u32x4 a, u32x4 xv, float acc)
     acc = __builtin_amdgcn_fdot2(as_h2(a.y), as_h2(xv.y), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(a.z), as_h2(xv.z), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(xv.w), acc, false);
+    return acc;
+}
+
+// FP16 with FP16 accumulation: 8 columns into one pair of binary16 running
+// sums (even columns in .x, odd in .y), one v_pk_fma_f16 per column pair,
+// so each term costs one binary16 rounding.  The caller widens the pair to
+// FP32 at the row end; the cross-lane reduction and y are FP32.  Lossy: a
+// lane's sums carry N/128 terms each at binary16 precision and overflow
+// past 65504.
+__device__ __forceinline__ f16x2 chunk_f16h(u32x4 a, u32x4 xv, f16x2 acc)
+{
+    acc = __builtin_elementwise_fma(as_h2(a.x), as_h2(xv.x), acc);
+    acc = __builtin_elementwise_fma(as_h2(a.y), as_h2(xv.y), acc);
+    acc = __builtin_elementwise_fma(as_h2(a.z), as_h2(xv.z), acc);
+    acc = __builtin_elementwise_fma(as_h2(a.w), as_h2(xv.w), acc);
     return acc;
 }
 
@@ -489,6 +506,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     }
 
     float acc = 0.0f;
+    f16x2 acch = {(_Float16)0.0f, (_Float16)0.0f};   // FP16 accumulation only
     int c_row = wave_id, c_pass = 0;
     // One unit of arithmetic: a = the unit's 16 bytes of A per lane, xv = its
     // x granules in staged layout (INT4: pair-reordered).
@@ -499,6 +517,8 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             acc = chunk_f16(a, xv[0], acc);
         } else if constexpr (F == kF16X32) {
             acc = chunk_f16x32(a, xv[0], xv[1 % G], acc);
+        } else if constexpr (F == kF16H) {
+            acch = chunk_f16h(a, xv[0], acch);
         } else if constexpr (F == kQ8) {
             if constexpr (DEC == 1)
                 acc = q8_sub_chunk(a, xv[0], xv[G - 1], acc);
@@ -514,6 +534,10 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
                 acc = chunk_q4(a, xp, s, acc);
         }
         if (++c_pass == P) {
+            if constexpr (F == kF16H) {
+                acc = (float)acch.x + (float)acch.y;
+                acch = f16x2{(_Float16)0.0f, (_Float16)0.0f};
+            }
             float t = wave_sum(acc);
             if (lane == 0 && c_row < M) {
                 if constexpr (F == kQ8) {
@@ -587,6 +611,14 @@ gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sca
         const float* xf = reinterpret_cast<const float*>(x);
         for (int j = lane; j < N; j += 64)
             acc = __builtin_fmaf(half_bits_to_float(a[j]), xf[j], acc);
+    } else if constexpr (F == kF16H) {
+        // one binary16 running sum per lane (ceil(N/64) terms)
+        const _Float16* a = reinterpret_cast<const _Float16*>(A) + (int64_t)row * N;
+        const _Float16* xh = reinterpret_cast<const _Float16*>(x);
+        _Float16 h = (_Float16)0.0f;
+        for (int j = lane; j < N; j += 64)
+            h = __builtin_fmaf16(a[j], xh[j], h);
+        acc = (float)h;
     } else if constexpr (F == kQ8) {
         const int8_t* a = reinterpret_cast<const int8_t*>(A) + (int64_t)row * N;
         const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);

@@ -11,6 +11,7 @@ Workloads (all synthetic; no page uses a dataset):
         shapes from "membound", section "Results".
   f16x32 : A ~ N(0, 1/N) as binary16, x ~ N(0, 1) kept in float32 (FP16
         weights with an FP32 hidden state, as the llama.cpp original keeps it).
+  f16_acc16 : the f16 operands (the lossy FP16-accumulation entry point).
   q8  : A int8 uniform on [-127, 127]; one binary16 scale per row,
         uniform[0.5, 1.5]/127; x ~ N(0, 1) binary16.
   q4  : A packed two nibbles per byte, [M, N/2] uint8.  Every byte is drawn
@@ -27,7 +28,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-KINDS = ("f32", "f16", "f16x32", "q8", "q4")
+KINDS = ("f32", "f16", "f16x32", "f16_acc16", "q8", "q4")
 
 
 @dataclass(frozen=True)
@@ -41,7 +42,7 @@ class Workload:
         return f"{self.kind}_{self.M}x{self.N}"
 
 
-# The five workload families, at their full sizes.
+# The workload families, at their full sizes.
 WORKLOADS = {
     "f32_1024": [Workload("f32", 1024, 1024)],
     "f32_sweep": [Workload("f32", n, n) for n in (2048, 4096, 8192)],
@@ -49,6 +50,7 @@ WORKLOADS = {
                    Workload("f16", 14336, 4096), Workload("f16", 4096, 14336)],
     "q8_decode": [Workload("q8", 8192, 8192), Workload("q8", 14336, 4096)],
     "f16x32_decode": [Workload("f16x32", 8192, 8192), Workload("f16x32", 4096, 14336)],
+    "f16_acc16_decode": [Workload("f16_acc16", 8192, 8192), Workload("f16_acc16", 4096, 14336)],
     "q4_decode": [Workload("q4", 4096, 14336), Workload("q4", 14336, 4096)],
 }
 
@@ -98,7 +100,8 @@ def make_q4(M: int, N: int, seed: int = 0):
     return {"A": A, "scale": scale, "x": x}
 
 
-MAKERS = {"f32": make_f32, "f16": make_f16, "f16x32": make_f16x32, "q8": make_q8, "q4": make_q4}
+MAKERS = {"f32": make_f32, "f16": make_f16, "f16x32": make_f16x32, "f16_acc16": make_f16, "q8": make_q8,
+          "q4": make_q4}
 
 
 def make(kind: str, M: int, N: int, seed: int = 0):

@@ -16,4 +16,4 @@ from .oracle import (  # noqa: F401
     num_threads,
     library_path,
 )
-from .metrics import parity_error, parity_report, GATES  # noqa: F401
+from .metrics import parity_error, parity_report, GATES, acc16_bound, acc16_ratio  # noqa: F401

@@ -16,7 +16,9 @@ terms and some land arbitrarily close to zero:
 
 Gates: 1e-4 for the FP32 and dequantised INT8/INT4 paths, 2e-3 for FP16
 inputs with FP32 accumulation, and 1e-4 for FP16 weights with FP32
-activations (each product rounds once, like the FP32 path).  The unfloored elementwise maximum, the
+activations (each product rounds once, like the FP32 path).  The lossy
+FP16-accumulation path is gated instead by a componentwise bound derived from
+its arithmetic (``acc16_bound``).  The unfloored elementwise maximum, the
 normwise error and the componentwise error relative to sum_j |w_ij x_j| are
 reported as diagnostics and never gated.
 """
@@ -26,6 +28,51 @@ import numpy as np
 
 GATES = {"f32": 1e-4, "q8": 1e-4, "q4": 1e-4, "f16": 2e-3, "f16x32": 1e-4}
 FLOOR_FRACTION = 0.01
+
+U16 = 2.0 ** -11
+U32 = 2.0 ** -24
+
+
+def _gamma(k: int, u: float) -> float:
+    return k * u / (1.0 - k * u) if k * u < 1.0 else float("inf")
+
+
+def acc16_bound(abs_sum: np.ndarray, N: int) -> np.ndarray:
+    """Componentwise error bound of the FP16-accumulation path.
+
+    The llama.cpp walkthrough's implementation note says the original kernel
+    may accumulate in FP16; the pages give no precision for that mode, so the
+    bound is derived from the arithmetic.  Each lane keeps running sums in
+    binary16, at most k = max(ceil(N/64), 4) terms per sum (one column per
+    lane and pass in the element-wise kernel; four pairs per 16-byte chunk
+    in the streaming kernel, whose 64 lanes cover 512 columns per pass, so
+    that its 4 ceil(N/512) terms never exceed k), one rounding per term
+    (relative u16 = 2^-11 for normal results; absolute at most 2^-25 in the
+    subnormal range).  The sums are widened exactly and combined in FP32 in
+    at most 8 levels.  The standard recursive-summation bound (Higham,
+    "Accuracy and Stability of Numerical Algorithms", section 4.2) gives
+
+        |y_i - r_i| <= ((1 + g16(k)) (1 + g32(8)) - 1) * sum_j |A_ij x_j|
+                       + N * 2^-24,
+
+    g(k) = k u / (1 - k u), with the subnormal terms (at most 2^-25 per
+    column, before later roundings) bounded generously by 2^-24 per column.
+    """
+    k = max(-(-int(N) // 64), 4)
+    a = np.asarray(abs_sum, dtype=np.float64)
+    g16, g32 = _gamma(k, U16), _gamma(8, U32)
+    return (g16 + g32 + g16 * g32) * a + N * 2.0 ** -24
+
+
+def acc16_ratio(y: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray, N: int) -> float:
+    """max_i |y_i - r_i| / bound_i; at most 1 when the bound holds."""
+    y = np.asarray(y, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    if y.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    return float(np.max(np.abs(y - r) / acc16_bound(abs_sum, N).ravel()))
 
 
 def parity_error(y: np.ndarray, ref: np.ndarray) -> float:

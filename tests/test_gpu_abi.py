@@ -6,7 +6,7 @@ import torch
 
 from memory_bound_gemv_row_amd import binding, inputs
 
-from gpu_util import dev, run_gpu, run_oracle, say
+from gpu_util import dev, run_gpu, run_oracle, say, within_gate
 from oracle.metrics import GATES, parity_error
 
 pytestmark = pytest.mark.gpu
@@ -26,12 +26,14 @@ def _call(kind, A, s, x, y, M, N, stream=0):
         return binding.gemv_f16_ptr(A, x, y, M, N, stream)
     if kind == "f16x32":
         return binding.gemv_f16x32_ptr(A, x, y, M, N, stream)
+    if kind == "f16_acc16":
+        return binding.gemv_f16_acc16_ptr(A, x, y, M, N, stream)
     if kind == "q8":
         return binding.gemv_q8_ptr(A, s, x, y, M, N, stream)
     return binding.gemv_q4_ptr(A, s, x, y, M, N, stream)
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "f16_acc16", "q8", "q4"])
 def test_status_codes(gpu, kind):
     M, N = 8, 256
     A, s, x = _ptrs(kind, inputs.make(kind, M, N))
@@ -55,7 +57,7 @@ def test_status_codes(gpu, kind):
         binding.gemv_f32(torch.zeros(4, 4, device="cuda"), torch.zeros(5, device="cuda"))
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "f16_acc16", "q8", "q4"])
 def test_n_zero_writes_zeros(gpu, kind):
     M = 70
     y = torch.full((M,), 7.0, device="cuda")
@@ -68,7 +70,7 @@ def test_n_zero_writes_zeros(gpu, kind):
     assert torch.all(y == 0)
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "f16_acc16", "q8", "q4"])
 def test_writes_only_y_0_to_M(gpu, oracle_mod, kind):
     M, N = 37, 1024
     ops = inputs.make(kind, M, N, seed=2)
@@ -80,10 +82,10 @@ def test_writes_only_y_0_to_M(gpu, oracle_mod, kind):
     torch.cuda.synchronize()
     g = guard.cpu().numpy()
     assert np.all(g[:64] == 12345.0) and np.all(g[64 + M:] == 12345.0)
-    assert parity_error(g[64:64 + M], run_oracle(oracle_mod, kind, ops)) <= GATES[kind]
+    assert within_gate(oracle_mod, kind, ops, g[64:64 + M], run_oracle(oracle_mod, kind, ops))["ok"]
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "f16_acc16", "q8", "q4"])
 def test_repeat_runs_bitwise_identical(gpu, kind):
     ops = inputs.make(kind, 1000, 4096, seed=4)
     say(f"[determinism] {kind}")
@@ -104,14 +106,14 @@ def test_non_default_stream(gpu, oracle_mod):
     assert parity_error(y.cpu().numpy(), run_oracle(oracle_mod, "f16", ops)) <= GATES["f16"]
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "f16_acc16", "q8", "q4"])
 @pytest.mark.parametrize("offset", [2, 4, 8])
 def test_unaligned_operands(gpu, oracle_mod, kind, offset):
     """A and x at byte offsets that break 16-byte alignment take the
     element-wise path and still agree with the oracle."""
     M, N = 33, 1024
     ops = inputs.make(kind, M, N, seed=offset)
-    elt = {"f32": 4, "f16": 2, "f16x32": 4, "q8": 1, "q4": 1}[kind]   # natural alignment of x
+    elt = {"f32": 4, "f16": 2, "f16x32": 4, "f16_acc16": 2, "q8": 1, "q4": 1}[kind]   # natural alignment of x
     if offset % elt:
         pytest.skip("offset not a multiple of the element size")
     Ab = ops["A"].view(np.uint8).ravel()
@@ -127,7 +129,7 @@ def test_unaligned_operands(gpu, oracle_mod, kind, offset):
                bufx.data_ptr() + offset, y.data_ptr(), M, N)
     assert rc == 0
     torch.cuda.synchronize()
-    assert parity_error(y.cpu().numpy(), run_oracle(oracle_mod, kind, ops)) <= GATES[kind]
+    assert within_gate(oracle_mod, kind, ops, y.cpu().numpy(), run_oracle(oracle_mod, kind, ops))["ok"]
 
 
 def test_describe_launch_fills_all_cus(gpu):

@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_the_four_paths():
     names = _declared_functions()
-    for n in ("gemv_f32", "gemv_f16", "gemv_f16x32", "gemv_q8", "gemv_q4", "gemv_status_string"):
+    for n in ("gemv_f32", "gemv_f16", "gemv_f16x32", "gemv_f16_acc16", "gemv_q8", "gemv_q4", "gemv_status_string"):
         assert n in names
 
 

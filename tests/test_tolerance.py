@@ -84,3 +84,107 @@ def test_gate_rejects_a_dropped_term():
     ref = A.astype(np.float64) @ x.astype(np.float64)
     y = ref - A[:, 17].astype(np.float64) * x[17]
     assert parity_error(y, ref) > GATES["f32"]
+
+
+# ---------------------------------------------------------------- FP16 accumulation bound
+def _fma16(a, x, s):
+    """One binary16 FMA: a*x + s formed exactly (in float64 at these
+    magnitudes), then rounded once to binary16."""
+    return (a.astype(np.float64) * x.astype(np.float64) + s.astype(np.float64)).astype(np.float16)
+
+
+def _butterfly_f32(acc):
+    acc = acc.astype(np.float32)
+    width = acc.shape[1]
+    while width > 1:
+        width //= 2
+        acc = (acc[:, :width] + acc[:, width:2 * width]).astype(np.float32)
+    return acc[:, 0]
+
+
+def _acc16_stream_order(A, x):
+    """Emulate the streaming kernel: lane l owns the 8-column chunks l, l+64,
+    ... of a row and keeps two binary16 running sums (even and odd columns);
+    the pair is widened and added in FP32, then a 64-lane FP32 butterfly."""
+    M, N = A.shape
+    assert N % 8 == 0
+    pad = -N % 512                # lanes past the row end add exact zeros
+    A = np.concatenate([A, np.zeros((M, pad), np.float16)], axis=1)
+    x = np.concatenate([x, np.zeros(pad, np.float16)])
+    P = (N + pad) // 512
+    Ar = A.reshape(M, P, 64, 4, 2)
+    xr = x.reshape(P, 64, 4, 2)
+    acc = np.zeros((M, 64, 2), np.float16)
+    for p in range(P):
+        for w in range(4):
+            acc = _fma16(Ar[:, p, :, w, :], xr[p, :, w, :], acc)
+    lane = acc[:, :, 0].astype(np.float32) + acc[:, :, 1].astype(np.float32)
+    return _butterfly_f32(lane)
+
+
+def _acc16_elementwise_order(A, x):
+    """Emulate the element-wise kernel: one binary16 sum per lane over the
+    columns l, l+64, ... (ceil(N/64) terms)."""
+    M, N = A.shape
+    pad = -N % 64
+    Ap = np.concatenate([A, np.zeros((M, pad), np.float16)], axis=1).reshape(M, -1, 64)
+    xp = np.concatenate([x, np.zeros(pad, np.float16)]).reshape(-1, 64)
+    acc = np.zeros((M, 64), np.float16)
+    for p in range(Ap.shape[1]):
+        acc = _fma16(Ap[:, p, :], xp[p], acc)
+    return _butterfly_f32(acc)
+
+
+def _abs_sum(A, x):
+    return np.abs(A.astype(np.float64)) @ np.abs(x.astype(np.float64))
+
+
+@pytest.mark.parametrize("dist", ["workload", "positive"])
+@pytest.mark.parametrize("N", [8, 64, 200, 520, 8192])
+def test_acc16_bound_holds_for_both_kernel_orders(dist, N):
+    from oracle.metrics import acc16_ratio
+
+    rng = np.random.default_rng(31 + N)
+    M = 128 if N > 512 else 4096
+    if dist == "workload":      # the FP16 decode workload's distribution
+        A = (rng.standard_normal((M, N)) / np.sqrt(N)).astype(np.float16)
+        x = rng.standard_normal(N).astype(np.float16)
+    else:                       # all terms positive: the roundings cannot cancel
+        A = rng.uniform(0, 1, (M, N)).astype(np.float16)
+        x = rng.uniform(0, 1, N).astype(np.float16)
+    ref = A.astype(np.float64) @ x.astype(np.float64)
+    for order in (_acc16_stream_order, _acc16_elementwise_order):
+        r = acc16_ratio(order(A, x), ref, _abs_sum(A, x), N)
+        assert r <= 1.0, (order.__name__, dist, r)
+    if dist == "positive" and N == 8192:
+        # the bound is not vacuous: a same-direction pile-up uses about 1 % of it
+        assert acc16_ratio(_acc16_elementwise_order(A, x), ref, _abs_sum(A, x), N) > 0.004
+
+
+def test_acc16_bound_rejects_one_running_sum_per_row():
+    # one binary16 sum over the whole row (k = N, not ceil(N/64)) stagnates
+    # once the sum's spacing exceeds the terms, far outside the bound
+    from oracle.metrics import acc16_ratio
+
+    rng = np.random.default_rng(32)
+    M, N = 16, 8192
+    A = rng.uniform(0, 1, (M, N)).astype(np.float16)
+    x = rng.uniform(0, 1, N).astype(np.float16)
+    acc = np.zeros(M, np.float16)
+    for j in range(N):
+        acc = _fma16(A[:, j], x[j:j + 1], acc)
+    ref = A.astype(np.float64) @ x.astype(np.float64)
+    assert acc16_ratio(acc, ref, _abs_sum(A, x), N) > 1.0
+
+
+def test_acc16_bound_closed_form():
+    from oracle.metrics import acc16_bound
+
+    # N = 8192: k = 128 binary16 terms per sum, g16 = 1/15, g32(8) = 8u/(1-8u)
+    g16 = 128 * 2.0 ** -11 / (1 - 128 * 2.0 ** -11)
+    g32 = 8 * 2.0 ** -24 / (1 - 8 * 2.0 ** -24)
+    assert g16 == pytest.approx(1 / 15)
+    want = (1 + g16) * (1 + g32) - 1 + 8192 * 2.0 ** -24
+    assert acc16_bound(np.array([1.0]), 8192)[0] == pytest.approx(want, rel=1e-12)
+    # the bound is finite only while k * u16 < 1
+    assert np.isinf(acc16_bound(np.array([1.0]), 64 * 2048)[0])
