@@ -1,4 +1,5 @@
-"""CPU oracle for row-major GEMV (test infrastructure only).
+"""CPU oracle for row-major GEMV and its weight quantiser (test
+infrastructure only).
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The product path (the HIP library and its binding)
@@ -15,5 +16,9 @@ from .oracle import (  # noqa: F401
     gemv_q4,
     num_threads,
     library_path,
+    double_to_half,
+    quantize_q8,
+    quantize_q4,
+    quant_rmse,
 )
 from .metrics import parity_error, parity_report, GATES, acc16_bound, acc16_ratio  # noqa: F401

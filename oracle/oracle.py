@@ -1,12 +1,13 @@
-"""ctypes wrapper over the C oracle (``gemv_oracle.c``).
+"""ctypes wrapper over the C oracle (``gemv_oracle.c``, ``quant_oracle.c``).
 
 Test infrastructure only: the product path never imports this module.
 
 Every function takes numpy arrays, checks dtypes and shapes, and returns the
-oracle's float64 result.  The arithmetic lives entirely in the C file, which
+oracle's result.  The arithmetic lives entirely in the C files: the GEMV
 follows the plain definition y_i = sum_j A_ij x_j ("Making GEMV Fast",
 section "Algorithm") with the INT8/INT4 reference weights taken as exactly
-q*s ("membound", section "The kernel decode actually runs: dequant GEMV").
+q*s, and the quantiser makes those operands from FP32 weights ("membound",
+section "The kernel decode actually runs: dequant GEMV").
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "gemv_oracle.c")
+_SRCS = [os.path.join(_HERE, "gemv_oracle.c"), os.path.join(_HERE, "quant_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -30,17 +31,21 @@ def library_path() -> str:
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+    if not force and not _stale():
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = [
         "gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
         "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-Werror",
-        _SRC, "-o", tmp, "-lm",
+        *_SRCS, "-o", tmp, "-lm",
     ]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
+
+
+def _stale() -> bool:
+    return not os.path.exists(_LIB) or any(os.path.getmtime(p) > os.path.getmtime(_LIB) for p in _SRCS)
 
 
 def _load():
@@ -48,7 +53,7 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if _stale():
             build()
         lib = ctypes.CDLL(_LIB)
         p = ctypes.c_void_p
@@ -66,6 +71,11 @@ def _load():
         lib.oracle_gemv_q4.argtypes = [p, p, p, p, i64, i64]
         for f in (lib.oracle_gemv_f32, lib.oracle_gemv_f16, lib.oracle_gemv_f16x32, lib.oracle_gemv_q8,
                   lib.oracle_gemv_q4):
+            f.restype = ctypes.c_int
+        lib.oracle_double_to_half.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_half.restype = ctypes.c_uint16
+        for f in (lib.oracle_quantize_q8, lib.oracle_quantize_q4):
+            f.argtypes = [p, p, p, p, i64, i64]
             f.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -172,3 +182,42 @@ def gemv_q4(A: np.ndarray, scale: np.ndarray, x: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_gemv_q4 rejected its arguments")
     return y
+
+
+# ---------------------------------------------------------------- quantiser
+def double_to_half(v: float) -> int:
+    """binary16 bit pattern of v, round to nearest, ties to even."""
+    return int(_load().oracle_double_to_half(float(v)))
+
+
+def quantize_q8(W: np.ndarray):
+    """FP32 W [M, N] -> (q int8 [M, N], scale binary16 bits uint16 [M],
+    row_sse float64 [M])."""
+    W = _as(W, np.float32, "W")
+    M, N = W.shape
+    q = np.empty((M, N), dtype=np.int8)
+    s = np.empty(M, dtype=np.uint16)
+    e = np.empty(M, dtype=np.float64)
+    if _load().oracle_quantize_q8(_ptr(W), _ptr(q), _ptr(s), _ptr(e), M, N) != 0:
+        raise ValueError("oracle_quantize_q8 rejected its arguments")
+    return q, s, e
+
+
+def quantize_q4(W: np.ndarray):
+    """FP32 W [M, N], N % 128 == 0 -> (packed uint8 [M, N/2], scale binary16
+    bits uint16 [M, N/128], row_sse float64 [M])."""
+    W = _as(W, np.float32, "W")
+    M, N = W.shape
+    if N % 128:
+        raise ValueError("INT4 quantisation needs N % 128 == 0")
+    q = np.zeros((M, N // 2), dtype=np.uint8)
+    s = np.empty((M, N // 128), dtype=np.uint16)
+    e = np.empty(M, dtype=np.float64)
+    if _load().oracle_quantize_q4(_ptr(W), _ptr(q), _ptr(s), _ptr(e), M, N) != 0:
+        raise ValueError("oracle_quantize_q4 rejected its arguments")
+    return q, s, e
+
+
+def quant_rmse(row_sse: np.ndarray, M: int, N: int) -> float:
+    """sqrt(sum of squared quantisation errors / number of weights)."""
+    return float(np.sqrt(np.sum(np.asarray(row_sse, dtype=np.float64)) / (M * N))) if M * N else 0.0
