@@ -16,8 +16,10 @@ Prints ONE JSON line.  ``value`` is the achieved algorithmic HBM bandwidth
 (the same-run pure-read ceiling and the %-of-probe), ``cpu_baseline`` (the
 CPU oracle timed on the host cores on the same inputs; its result also
 gates the GPU result, and the run aborts on a parity failure, as the pages
-do), and ``detail`` (the other FP16 shapes, FP16 weights with FP32 x, and the INT8/INT4 speed-ups over
-FP16, timed in interleaved rounds).
+do), ``detail`` (the other FP16 shapes, FP16 weights with FP32 x, FP16
+accumulation, and the INT8/INT4 speed-ups over FP16, timed in interleaved
+rounds) and ``quantiser`` (the FP32 -> INT8/INT4 weight quantiser and the
+RMSE of its codes).
 """
 from __future__ import annotations
 
@@ -320,6 +322,78 @@ def detail(rounds, launches=256):
     return out
 
 
+# ---------------------------------------------------------------- quantiser
+def quant_bytes(kind, M, N):
+    """Algorithmic bytes of one quantiser call: FP32 weights read once; codes,
+    binary16 scales and the per-row squared error written once."""
+    if kind == "q8":
+        return 4 * M * N + M * N + 2 * M + 4 * M
+    return 4 * M * N + M * N // 2 + 2 * M * (N // 128) + 4 * M
+
+
+def quant_detail(rounds, launches=64):
+    """The weight quantiser (FP32 -> INT8 / INT4 + per-row squared error) on
+    the INT8/INT4 GEMV shapes: weights rotate through >= 1 GiB of copies,
+    launches captured in a HIP graph, best of `rounds`; a pure-read probe over
+    the same weight bytes is timed the same way.  Also reports the RMSE of the
+    GPU's codes ("membound", dequant section: 2.3e-3 / 4.1e-2 on U[-1,1])."""
+    import numpy as np
+    import torch
+
+    from memory_bound_gemv_row_amd import binding, inputs
+
+    out = {}
+    for kind, M, N in inputs.QUANT_WORKLOADS:
+        W = torch.from_numpy(inputs.make_weights(M, N, seed=0)).cuda()
+        wbytes = 4 * M * N
+        copies = max(1, -(-RING_BYTES // wbytes))
+        ring = torch.empty((copies, M, N), dtype=torch.float32, device="cuda")
+        ring[:] = W
+        del W
+        q = torch.empty((M, N if kind == "q8" else N // 2), dtype=torch.int8 if kind == "q8" else torch.uint8,
+                        device="cuda")
+        sc = torch.empty(M if kind == "q8" else M * (N // 128), dtype=torch.float16, device="cuda")
+        e = torch.empty(M, dtype=torch.float32, device="cuda")
+        fn = binding.quantize_q8_ptr if kind == "q8" else binding.quantize_q4_ptr
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        graphs = []
+        for which in ("quant", "probe"):
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    for i in range(launches):
+                        h = torch.cuda.current_stream().cuda_stream
+                        src = ring[i % copies].data_ptr()
+                        if which == "quant":
+                            rc = fn(src, q.data_ptr(), sc.data_ptr(), e.data_ptr(), M, N, h)
+                        else:
+                            rc = binding.probe_read_ptr(src, wbytes, sink.data_ptr(), 0xA5A5A5A5, h)
+                        if rc != 0:
+                            raise RuntimeError(f"{which} returned {rc}")
+            torch.cuda.current_stream().wait_stream(st)
+            torch.cuda.synchronize()
+            g.replay()
+            graphs.append(g)
+        best = [float("inf"), float("inf")]
+        for _ in range(rounds):
+            for j in range(2):
+                best[j] = min(best[j], time_graph(graphs[j], launches))
+        nbytes = quant_bytes(kind, M, N)
+        gb = nbytes / best[0] / 1e9
+        rmse = float(np.sqrt(e.double().sum().item() / (M * N)))
+        out[f"{kind}_{M}x{N}"] = {
+            "us": best[0] * 1e6, "alg_bytes": nbytes, "gbps": gb, "pct_of_8tbs": 100 * gb / HBM_PEAK_GBPS,
+            "read_probe_us": best[1] * 1e6,
+            "pct_of_read_probe_time": 100 * best[1] / best[0],
+            "rmse": rmse,
+        }
+        del graphs, ring, q, sc, e
+        torch.cuda.empty_cache()
+    return out
+
+
 # ---------------------------------------------------------------- main
 def main():
     args = parse()
@@ -397,6 +471,7 @@ def main():
 
     if not args.no_detail:
         rec["detail"] = detail(args.rounds)
+        rec["quantiser"] = quant_detail(args.rounds)
     print(json.dumps(rec), flush=True)
 
 

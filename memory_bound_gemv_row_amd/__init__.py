@@ -15,4 +15,6 @@ from .binding import (  # noqa: F401,E402  (no library load at import time)
     gemv_q8,
     gemv_q4,
     describe_launch,
+    quantize_q8,
+    quantize_q4,
 )

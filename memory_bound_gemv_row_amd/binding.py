@@ -1,4 +1,5 @@
-"""ctypes binding over the C ABI in ``include/gemv.h``.
+"""ctypes binding over the C ABI in ``include/gemv.h`` and
+``include/gemv_quant.h``.
 
 Argument marshalling only: every step of the product runs in the HIP
 library.  PyTorch supplies device memory and the current stream; no torch
@@ -49,6 +50,9 @@ def load():
         for name in ("gemv_q8", "gemv_q4"):
             getattr(lib, name).argtypes = [p, p, p, p, i, i, p]
             getattr(lib, name).restype = i
+        for name in ("gemv_quantize_q8", "gemv_quantize_q4"):
+            getattr(lib, name).argtypes = [p, p, p, p, i, i, p]
+            getattr(lib, name).restype = i
         lib.gemv_status_string.argtypes = [i]
         lib.gemv_status_string.restype = ctypes.c_char_p
         lib.gemv_probe_read.argtypes = [p, ctypes.c_size_t, p, ctypes.c_uint32, p]
@@ -94,6 +98,14 @@ def gemv_q8_ptr(A: int, scale: int, x: int, y: int, M: int, N: int, stream: int 
 
 def gemv_q4_ptr(A: int, scale: int, x: int, y: int, M: int, N: int, stream: int = 0) -> int:
     return load().gemv_q4(A, scale, x, y, M, N, stream)
+
+
+def quantize_q8_ptr(W: int, q: int, scale: int, row_sse: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_quantize_q8(W, q, scale, row_sse, M, N, stream)
+
+
+def quantize_q4_ptr(W: int, q: int, scale: int, row_sse: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_quantize_q4(W, q, scale, row_sse, M, N, stream)
 
 
 def probe_read_ptr(buf: int, nbytes: int, sink: int, guard: int = 0xA5A5A5A5, stream: int = 0) -> int:
@@ -222,6 +234,39 @@ def gemv_q4(A, scale, x, out=None, stream=None):
     y = _out(out, M, A.device)
     _check(gemv_q4_ptr(a, s, xp, y.data_ptr(), M, N, _stream(stream)), "gemv_q4")
     return y
+
+
+def quantize_q8(W, with_error=True, stream=None):
+    """FP32 W [M, N] -> (q int8 [M, N], scale float16 [M], row_sse float32 [M]
+    or None).  RMSE = sqrt(row_sse.sum() / (M * N))."""
+    import torch
+
+    M, N = W.shape
+    w = _need(W, "W", (torch.float32,), (M, N))
+    q = torch.empty((M, N), dtype=torch.int8, device=W.device)
+    s = torch.empty(M, dtype=torch.float16, device=W.device)
+    e = torch.empty(M, dtype=torch.float32, device=W.device) if with_error else None
+    _check(quantize_q8_ptr(w, q.data_ptr(), s.data_ptr(), e.data_ptr() if e is not None else 0, M, N,
+                           _stream(stream)), "gemv_quantize_q8")
+    return q, s, e
+
+
+def quantize_q4(W, with_error=True, stream=None):
+    """FP32 W [M, N], N % 128 == 0 -> (q uint8 [M, N/2] two INT4 per byte,
+    low nibble = even column; scale float16 [M, N/128]; row_sse float32 [M]
+    or None)."""
+    import torch
+
+    M, N = W.shape
+    if N % 128:
+        raise ValueError("INT4 quantisation needs N % 128 == 0")
+    w = _need(W, "W", (torch.float32,), (M, N))
+    q = torch.empty((M, N // 2), dtype=torch.uint8, device=W.device)
+    s = torch.empty((M, N // 128), dtype=torch.float16, device=W.device)
+    e = torch.empty(M, dtype=torch.float32, device=W.device) if with_error else None
+    _check(quantize_q4_ptr(w, q.data_ptr(), s.data_ptr(), e.data_ptr() if e is not None else 0, M, N,
+                           _stream(stream)), "gemv_quantize_q4")
+    return q, s, e
 
 
 def probe_read(buf, sink, guard: int = 0xA5A5A5A5, stream=None):

@@ -1,7 +1,8 @@
 """Build the gfx950 HIP library in-tree with hipcc.
 
 ``python -m memory_bound_gemv_row_amd.build`` compiles
-``csrc/gemv_api.hip`` (which includes the kernels) into
+``csrc/gemv_api.hip`` (GEMV, which includes its kernels) and
+``csrc/quant_api.hip`` (the weight quantiser) into one library,
 ``memory_bound_gemv_row_amd/libgemv_amd.so``.
 """
 from __future__ import annotations
@@ -15,8 +16,9 @@ ROOT = os.path.dirname(PKG)
 SRC_DIR = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemv_amd.so")
-SOURCES = [os.path.join(SRC_DIR, "gemv_api.hip")]
-DEPENDS = SOURCES + [os.path.join(SRC_DIR, "gemv_kernels.hpp"), os.path.join(INCLUDE, "gemv.h")]
+SOURCES = [os.path.join(SRC_DIR, "gemv_api.hip"), os.path.join(SRC_DIR, "quant_api.hip")]
+DEPENDS = SOURCES + [os.path.join(SRC_DIR, "gemv_kernels.hpp"), os.path.join(SRC_DIR, "quant_kernels.hpp"),
+                     os.path.join(INCLUDE, "gemv.h"), os.path.join(INCLUDE, "gemv_quant.h")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

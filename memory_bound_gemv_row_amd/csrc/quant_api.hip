@@ -1,0 +1,109 @@
+// quant_api.hip -- C ABI of the weight quantiser (declared in
+// include/gemv_quant.h): validation, geometry and launch.
+#include "gemv_quant.h"
+#include "quant_kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+namespace gquant {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mutex;
+int g_cus[kMaxDevices] = {0};
+
+int cu_count(int* out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMV_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return GEMV_E_DEVICE;
+        g_cus[dev] = n;
+    }
+    *out = g_cus[dev];
+    return GEMV_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int launch(const void* fn, int grid, int block, const float* W, void* q, uint16_t* scale, float* row_sse, int M,
+           int N, hipStream_t stream)
+{
+    void* args[] = {(void*)&W, (void*)&q, (void*)&scale, (void*)&row_sse, (void*)&M, (void*)&N};
+    return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream) == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
+}
+
+template <bool SSE>
+const void* q8_kernel(int P)
+{
+    return P <= 16 ? reinterpret_cast<const void*>(&quantize_q8_kernel<4, 4, SSE>)
+         : P <= 32 ? reinterpret_cast<const void*>(&quantize_q8_kernel<4, 8, SSE>)
+                   : reinterpret_cast<const void*>(&quantize_q8_kernel<4, 16, SSE>);
+}
+
+int check(const float* W, const void* q, const uint16_t* scale, int M, int N)
+{
+    if (M < 0 || N < 0)
+        return GEMV_E_INVAL;
+    if (M > 0 && (scale == nullptr || (N > 0 && (W == nullptr || q == nullptr))))
+        return GEMV_E_INVAL;
+    return GEMV_OK;
+}
+
+}  // namespace
+}  // namespace gquant
+
+extern "C" {
+
+int gemv_quantize_q8(const float* W, int8_t* q, uint16_t* scale, float* row_sse, int M, int N,
+                     hipStream_t stream)
+{
+    using namespace gquant;
+    if (int rc = check(W, q, scale, M, N); rc != GEMV_OK)
+        return rc;
+    if (M == 0)
+        return GEMV_OK;
+    int cus = 0;
+    if (int rc = cu_count(&cus); rc != GEMV_OK)
+        return rc;
+    if (N == 0 || N % 4 != 0 || !aligned(W, 16) || !aligned(q, 4))
+        return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<127>), (M + 3) / 4, 256, W, q,
+                      scale, row_sse, M, N, stream);
+    // a workgroup of 4 waves per row; units per wave sized so that rows up
+    // to 64 units (N <= 16384) stay in registers
+    const int P = (N / 4 + 63) / 64;
+    const void* fn = row_sse != nullptr ? q8_kernel<true>(P) : q8_kernel<false>(P);
+    const int grid = M < cus * 8 ? M : cus * 8;
+    return launch(fn, grid, 256, W, q, scale, row_sse, M, N, stream);
+}
+
+int gemv_quantize_q4(const float* W, uint8_t* q, uint16_t* scale, float* row_sse, int M, int N,
+                     hipStream_t stream)
+{
+    using namespace gquant;
+    if (int rc = check(W, q, scale, M, N); rc != GEMV_OK)
+        return rc;
+    if (N % 128 != 0)
+        return GEMV_E_UNSUPPORTED;
+    if (M == 0)
+        return GEMV_OK;
+    int cus = 0;
+    if (int rc = cu_count(&cus); rc != GEMV_OK)
+        return rc;
+    (void)cus;
+    if (N == 0 || !aligned(W, 16) || !aligned(q, 2))
+        return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<7>), (M + 3) / 4, 256, W, q,
+                      scale, row_sse, M, N, stream);
+    // one wave per row, 4 waves per workgroup, 4 units in flight per wave
+    const void* fn = row_sse != nullptr ? reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, true>)
+                                        : reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, false>);
+    return launch(fn, (M + 3) / 4, 256, W, q, scale, row_sse, M, N, stream);
+}
+
+}  // extern "C"

@@ -100,6 +100,17 @@ def make_q4(M: int, N: int, seed: int = 0):
     return {"A": A, "scale": scale, "x": x}
 
 
+def make_weights(M: int, N: int, seed: int = 0) -> np.ndarray:
+    """FP32 weights uniform on [-1, 1]: the quantiser's input, the
+    distribution on which the "membound" page reports its quantisation RMSE."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(-1.0, 1.0, (M, N)).astype(np.float32)
+
+
+# Quantiser workloads: the INT8 and INT4 GEMV shapes, from FP32 weights.
+QUANT_WORKLOADS = [("q8", 8192, 8192), ("q8", 14336, 4096), ("q4", 4096, 14336), ("q4", 14336, 4096)]
+
+
 MAKERS = {"f32": make_f32, "f16": make_f16, "f16x32": make_f16x32, "f16_acc16": make_f16, "q8": make_q8,
           "q4": make_q4}
 

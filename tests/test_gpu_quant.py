@@ -1,0 +1,173 @@
+"""GPU parity of the weight quantiser against the CPU oracle, through the C ABI.
+
+Codes and binary16 scales are integer decisions taken in binary32 on both
+sides, so they must match bit for bit; the per-row squared error is an FP32
+sum on the GPU and is compared within the bound of that sum
+((k + 16) * 2^-24 relative, k = ceil(N/64) terms per lane at most, all terms
+non-negative).
+"""
+import numpy as np
+import pytest
+import torch
+
+from memory_bound_gemv_row_amd import binding, inputs
+from oracle.metrics import GATES, parity_error
+
+from gpu_util import dev, say
+from qpack import unpack_int4
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quant(kind, W, with_error=True):
+    Wd = dev(W)
+    fn = binding.quantize_q8 if kind == "q8" else binding.quantize_q4
+    q, s, e = fn(Wd, with_error=with_error)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy().view(np.uint16), (e.cpu().numpy() if e is not None else None)
+
+
+def _sse_tol(N):
+    k = -(-N // 64) + 16
+    return k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
+
+
+def _compare(oracle, kind, W, label):
+    say(f"[quant] {label}")
+    q, s, e = _gpu_quant(kind, W)
+    oq, os_, oe = (oracle.quantize_q8 if kind == "q8" else oracle.quantize_q4)(W)
+    assert np.array_equal(s, os_), (label, "scales")
+    if not np.array_equal(q, oq):
+        bad = np.argwhere(q != oq)[:5]
+        raise AssertionError((label, "codes differ at", bad.tolist()))
+    denom = np.maximum(oe, 1e-30)
+    rel = np.max(np.abs(e.astype(np.float64) - oe) / denom) if oe.size else 0.0
+    assert rel <= _sse_tol(W.shape[1]) or np.all(np.abs(e - oe) <= 1e-30), (label, rel)
+    return q, s, e, oe
+
+
+@pytest.mark.parametrize("kind,M,N", inputs.QUANT_WORKLOADS, ids=lambda v: str(v))
+def test_full_size_quantiser(gpu, oracle_mod, kind, M, N):
+    W = inputs.make_weights(M, N, seed=0)
+    q, s, e, oe = _compare(oracle_mod, kind, W, f"{kind} {M}x{N} seed 0")
+    rmse_gpu = np.sqrt(e.astype(np.float64).sum() / (M * N))
+    rmse_ref = oracle_mod.quant_rmse(oe, M, N)
+    assert abs(rmse_gpu - rmse_ref) / rmse_ref < 1e-5
+    # the page's printed figure, two significant digits
+    assert float(f"{rmse_gpu:.1e}") == (2.3e-3 if kind == "q8" else 4.1e-2)
+
+
+_MS = [1, 2, 5, 33, 257]
+_NS = {
+    # 16384 is the longest row held in registers, 16388 the first read twice;
+    # N % 4 != 0 takes the element-wise path
+    "q8": [1, 3, 4, 8, 252, 256, 260, 1000, 1024, 4100, 16384, 16388, 20000, 40000],
+    "q4": [128, 256, 384, 1024, 2176, 7296, 14336, 16384, 16512],
+}
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_shapes_and_tails(gpu, oracle_mod, kind):
+    for N in _NS[kind]:
+        for M in _MS:
+            rng = np.random.default_rng(M * 7919 + N)
+            W = (rng.standard_normal((M, N)) * np.exp(rng.uniform(-4, 4, (M, 1)))).astype(np.float32)
+            _compare(oracle_mod, kind, W, f"{kind} M={M} N={N}")
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_unaligned_weights_take_the_elementwise_path(gpu, oracle_mod, kind):
+    M, N = 9, 1024
+    W = inputs.make_weights(M, N, seed=3)
+    buf = torch.zeros(M * N + 16, dtype=torch.float32, device="cuda")
+    buf[1:1 + M * N] = dev(W.ravel())
+    q = torch.empty(M * N if kind == "q8" else M * N // 2, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M if kind == "q8" else M * N // 128, dtype=torch.float16, device="cuda")
+    e = torch.empty(M, dtype=torch.float32, device="cuda")
+    fn = binding.quantize_q8_ptr if kind == "q8" else binding.quantize_q4_ptr
+    say(f"[quant unaligned] {kind}")
+    assert fn(buf.data_ptr() + 4, q.data_ptr(), s.data_ptr(), e.data_ptr(), M, N) == 0
+    torch.cuda.synchronize()
+    oq, os_, oe = (oracle_mod.quantize_q8 if kind == "q8" else oracle_mod.quantize_q4)(W)
+    assert np.array_equal(q.cpu().numpy().view(np.int8 if kind == "q8" else np.uint8).reshape(oq.shape), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint16).reshape(os_.shape), os_)
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_near_ties_match_the_correctly_rounded_division(gpu, oracle_mod, kind):
+    # weights within a few ulp of (k + 1/2) * scale: the kernels' fast
+    # multiply-by-inverse path must hand these to the exact division
+    rng = np.random.default_rng(7)
+    qmax = 127 if kind == "q8" else 7
+    M, N = 64, 1024
+    W = np.zeros((M, N), np.float32)
+    for i in range(M):
+        scale = np.float32(np.float16(rng.uniform(0.01, 2.0)))
+        k = rng.integers(-qmax, qmax, N).astype(np.float64) + 0.5
+        ulps = rng.integers(-3, 4, N)
+        w = (k * np.float64(scale)).astype(np.float32)
+        W[i] = np.nextafter(w, np.where(ulps > 0, np.inf, -np.inf)).astype(np.float32)
+        W[i] = np.where(ulps == 0, w, W[i])
+        # pin each row's or group's absmax so that the scale is exactly `scale`
+        W[i, ::128] = np.float32(qmax * np.float64(scale))
+    _compare(oracle_mod, kind, W, f"{kind} near ties")
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_degenerate_rows(gpu, oracle_mod, kind):
+    M, N = 6, 512
+    W = np.zeros((M, N), np.float32)
+    W[1] = 1.0e7                                   # scale saturates at 65504, codes clip
+    W[2, :] = np.linspace(-1e-4, 1e-4, N)          # binary16-subnormal scales
+    W[3, 5] = 1.0e-9                               # scale rounds to zero
+    W[4] = inputs.make_weights(1, N, seed=1)[0]
+    W[5] = -W[4]
+    _compare(oracle_mod, kind, W, f"{kind} degenerate")
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_without_error_output(gpu, oracle_mod, kind):
+    W = inputs.make_weights(100, 2048, seed=5)
+    q, s, e = _gpu_quant(kind, W, with_error=False)
+    assert e is None
+    oq, os_, _ = (oracle_mod.quantize_q8 if kind == "q8" else oracle_mod.quantize_q4)(W)
+    assert np.array_equal(q, oq) and np.array_equal(s, os_)
+
+
+def test_status_codes(gpu):
+    W = torch.zeros(4, 256, device="cuda")
+    q = torch.zeros(4 * 256, dtype=torch.int8, device="cuda")
+    s = torch.zeros(16, dtype=torch.float16, device="cuda")
+    w, qp, sp = W.data_ptr(), q.data_ptr(), s.data_ptr()
+    say("[quant status]")
+    for fn in (binding.quantize_q8_ptr, binding.quantize_q4_ptr):
+        assert fn(w, qp, sp, 0, -1, 256) == 1
+        assert fn(w, qp, sp, 0, 4, -1) == 1
+        assert fn(0, qp, sp, 0, 4, 256) == 1
+        assert fn(w, 0, sp, 0, 4, 256) == 1
+        assert fn(w, qp, 0, 0, 4, 256) == 1
+        assert fn(0, 0, 0, 0, 0, 256) == 0                 # M == 0: nothing to do
+    assert binding.quantize_q4_ptr(w, qp, sp, 0, 4, 200) == 2
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kind,M,N", [("q8", 1000, 4096), ("q4", 1000, 4096)])
+def test_quantise_then_gemv(gpu, oracle_mod, kind, M, N):
+    # the quantiser's output is the GEMV's input: end to end on the GPU,
+    # against the oracle GEMV on the oracle's codes
+    W = inputs.make_weights(M, N, seed=9)
+    x = inputs.make_f16(1, N, seed=9)["x"]
+    Wd, xd = dev(W), dev(x)
+    say(f"[quant+gemv] {kind}")
+    if kind == "q8":
+        q, s, _ = binding.quantize_q8(Wd, with_error=False)
+        y = binding.gemv_q8(q, s, xd)
+        oq, os_, _ = oracle_mod.quantize_q8(W)
+        ref = oracle_mod.gemv_q8(oq, os_, x)
+    else:
+        q, s, _ = binding.quantize_q4(Wd, with_error=False)
+        y = binding.gemv_q4(q, s, xd)
+        oq, os_, _ = oracle_mod.quantize_q4(W)
+        ref = oracle_mod.gemv_q4(oq, os_, x)
+    torch.cuda.synchronize()
+    assert parity_error(y.cpu().numpy(), ref) <= GATES[kind]

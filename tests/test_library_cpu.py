@@ -8,13 +8,16 @@ import pytest
 
 from memory_bound_gemv_row_amd import binding, build
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gemv.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemv_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemv_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +29,8 @@ def lib():
 
 def test_header_declares_the_four_paths():
     names = _declared_functions()
-    for n in ("gemv_f32", "gemv_f16", "gemv_f16x32", "gemv_f16_acc16", "gemv_q8", "gemv_q4", "gemv_status_string"):
+    for n in ("gemv_f32", "gemv_f16", "gemv_f16x32", "gemv_f16_acc16", "gemv_q8", "gemv_q4", "gemv_status_string",
+              "gemv_quantize_q8", "gemv_quantize_q4"):
         assert n in names
 
 
