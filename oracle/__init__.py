@@ -1,5 +1,5 @@
-"""CPU oracle for row-major GEMV and its weight quantiser (test
-infrastructure only).
+"""CPU oracle for row-major GEMV, its weight quantiser and the row softmax
+(test infrastructure only).
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The product path (the HIP library and its binding)
@@ -20,5 +20,14 @@ from .oracle import (  # noqa: F401
     quantize_q8,
     quantize_q4,
     quant_rmse,
+    softmax_f16,
 )
-from .metrics import parity_error, parity_report, GATES, acc16_bound, acc16_ratio  # noqa: F401
+from .metrics import (  # noqa: F401
+    parity_error,
+    parity_report,
+    GATES,
+    acc16_bound,
+    acc16_ratio,
+    softmax_error,
+    SOFTMAX_GATE,
+)

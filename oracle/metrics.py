@@ -115,3 +115,31 @@ def parity_report(y: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray | None = N
             with np.errstate(divide="ignore", invalid="ignore"):
                 out["componentwise"] = float(np.max(np.where(a > 0, err / a, 0.0)))
     return out
+
+
+# ---------------------------------------------------------------- softmax
+SOFTMAX_FLOOR = 1e-4
+SOFTMAX_GATE = 2e-3
+
+
+def softmax_error(y: np.ndarray, ref: np.ndarray) -> float:
+    """max |y - r| / max(|r|, 1e-4): the "membound" page scores its FP16
+    softmax relative to max(ref, 1e-4) so that binary16-subnormal outputs
+    (below about 6e-5, where relative precision collapses) raise no false
+    alarms (section "Bonus kernel: online softmax").  Gate 2e-3, as for the
+    other binary16 results: binary16 output rounding alone is up to 2^-11
+    (4.9e-4) relative, or 2^-25 absolute (3e-4 against the floor) for
+    subnormal outputs.  NaN must meet NaN."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if y.shape != r.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {r.shape}")
+    if y.size == 0:
+        return 0.0
+    nan_r, nan_y = np.isnan(r), np.isnan(y)
+    if np.any(nan_r != nan_y):
+        return float("inf")
+    ok = ~nan_r
+    if not np.any(ok):
+        return 0.0
+    return float(np.max(np.abs(y[ok] - r[ok]) / np.maximum(np.abs(r[ok]), SOFTMAX_FLOOR)))

@@ -1,4 +1,5 @@
-"""ctypes wrapper over the C oracle (``gemv_oracle.c``, ``quant_oracle.c``).
+"""ctypes wrapper over the C oracle (``gemv_oracle.c``, ``quant_oracle.c``,
+``softmax_oracle.c``).
 
 Test infrastructure only: the product path never imports this module.
 
@@ -19,7 +20,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "gemv_oracle.c"), os.path.join(_HERE, "quant_oracle.c")]
+_SRCS = [os.path.join(_HERE, f) for f in ("gemv_oracle.c", "quant_oracle.c", "softmax_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -77,6 +78,8 @@ def _load():
         for f in (lib.oracle_quantize_q8, lib.oracle_quantize_q4):
             f.argtypes = [p, p, p, p, i64, i64]
             f.restype = ctypes.c_int
+        lib.oracle_softmax_f16.argtypes = [p, p, i64, i64]
+        lib.oracle_softmax_f16.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -221,3 +224,14 @@ def quantize_q4(W: np.ndarray):
 def quant_rmse(row_sse: np.ndarray, M: int, N: int) -> float:
     """sqrt(sum of squared quantisation errors / number of weights)."""
     return float(np.sqrt(np.sum(np.asarray(row_sse, dtype=np.float64)) / (M * N))) if M * N else 0.0
+
+
+# ---------------------------------------------------------------- softmax
+def softmax_f16(x: np.ndarray) -> np.ndarray:
+    """Row-wise softmax of binary16 x [M, N], in float64 (not rounded)."""
+    x = _f16_bits(x, "x")
+    M, N = x.shape
+    y = np.empty((M, N), dtype=np.float64)
+    if _load().oracle_softmax_f16(_ptr(x), _ptr(y), M, N) != 0:
+        raise ValueError("oracle_softmax_f16 rejected its arguments")
+    return y
