@@ -18,8 +18,9 @@ CPU oracle timed on the host cores on the same inputs; its result also
 gates the GPU result, and the run aborts on a parity failure, as the pages
 do), ``detail`` (the other FP16 shapes, FP16 weights with FP32 x, FP16
 accumulation, and the INT8/INT4 speed-ups over FP16, timed in interleaved
-rounds) and ``quantiser`` (the FP32 -> INT8/INT4 weight quantiser and the
-RMSE of its codes).
+rounds), ``quantiser`` (the FP32 -> INT8/INT4 weight quantiser and the
+RMSE of its codes) and ``softmax`` (the row softmax against the
+streaming-copy ceiling).
 """
 from __future__ import annotations
 
@@ -333,31 +334,44 @@ def quant_bytes(kind, M, N):
 
 def quant_detail(rounds, launches=64):
     """The weight quantiser (FP32 -> INT8 / INT4 + per-row squared error) on
-    the INT8/INT4 GEMV shapes: weights rotate through >= 1 GiB of copies,
-    launches captured in a HIP graph, best of `rounds`; a pure-read probe over
-    the same weight bytes is timed the same way.  Also reports the RMSE of the
-    GPU's codes ("membound", dequant section: 2.3e-3 / 4.1e-2 on U[-1,1])."""
+    the INT8/INT4 GEMV shapes.  Each slot of a >= 1 GiB ring holds a copy of
+    the weights and its own outputs (codes, scales, row errors), so that
+    neither the reads nor the writes of one launch can be served by a cache
+    that the previous launch filled; launches are captured in a HIP graph,
+    best of `rounds`.  Two floors are timed the same way: a pure read of the
+    FP32 weights (the bytes that must be read), and a streaming copy moving
+    the same total bytes (half read, half written, into a rotating
+    destination); the quantiser's mix (8:1 or 4:1 read:write) lies between.
+    Also reports the RMSE of the GPU's codes ("membound", dequant section:
+    2.3e-3 / 4.1e-2 on U[-1,1])."""
     import numpy as np
     import torch
 
     from memory_bound_gemv_row_amd import binding, inputs
 
+    def up(n):
+        return -(-n // 256) * 256
+
     out = {}
     for kind, M, N in inputs.QUANT_WORKLOADS:
-        W = torch.from_numpy(inputs.make_weights(M, N, seed=0)).cuda()
         wbytes = 4 * M * N
-        copies = max(1, -(-RING_BYTES // wbytes))
-        ring = torch.empty((copies, M, N), dtype=torch.float32, device="cuda")
-        ring[:] = W
+        qbytes = M * N if kind == "q8" else M * N // 2
+        sbytes = 2 * M if kind == "q8" else 2 * M * (N // 128)
+        offs = [0, up(wbytes), up(wbytes) + up(qbytes), up(wbytes) + up(qbytes) + up(sbytes)]
+        slot = offs[3] + up(4 * M)
+        copies = max(1, -(-RING_BYTES // slot))
+        ring = torch.empty((copies, slot), dtype=torch.uint8, device="cuda")
+        W = torch.from_numpy(inputs.make_weights(M, N, seed=0).view(np.uint8).ravel()).cuda()
+        for c in range(copies):
+            ring[c, :wbytes].copy_(W)
         del W
-        q = torch.empty((M, N if kind == "q8" else N // 2), dtype=torch.int8 if kind == "q8" else torch.uint8,
-                        device="cuda")
-        sc = torch.empty(M if kind == "q8" else M * (N // 128), dtype=torch.float16, device="cuda")
-        e = torch.empty(M, dtype=torch.float32, device="cuda")
+        nbytes = quant_bytes(kind, M, N)
+        half = nbytes // 2 // 16 * 16             # a copy of this many bytes moves nbytes in total
+        cdst = torch.empty((copies, up(half)), dtype=torch.uint8, device="cuda")
         fn = binding.quantize_q8_ptr if kind == "q8" else binding.quantize_q4_ptr
         sink = torch.zeros(4, dtype=torch.int32, device="cuda")
         graphs = []
-        for which in ("quant", "probe"):
+        for which in ("quant", "probe", "copy"):
             g = torch.cuda.CUDAGraph()
             st = torch.cuda.Stream()
             st.wait_stream(torch.cuda.current_stream())
@@ -365,11 +379,72 @@ def quant_detail(rounds, launches=64):
                 with torch.cuda.graph(g, stream=st):
                     for i in range(launches):
                         h = torch.cuda.current_stream().cuda_stream
-                        src = ring[i % copies].data_ptr()
+                        base = ring[i % copies].data_ptr()
                         if which == "quant":
-                            rc = fn(src, q.data_ptr(), sc.data_ptr(), e.data_ptr(), M, N, h)
+                            rc = fn(base, base + offs[1], base + offs[2], base + offs[3], M, N, h)
+                        elif which == "probe":
+                            rc = binding.probe_read_ptr(base, wbytes, sink.data_ptr(), 0xA5A5A5A5, h)
                         else:
-                            rc = binding.probe_read_ptr(src, wbytes, sink.data_ptr(), 0xA5A5A5A5, h)
+                            rc = binding.probe_copy_ptr(base, cdst[i % copies].data_ptr(), half, h)
+                        if rc != 0:
+                            raise RuntimeError(f"{which} returned {rc}")
+            torch.cuda.current_stream().wait_stream(st)
+            torch.cuda.synchronize()
+            g.replay()
+            graphs.append(g)
+        best = [float("inf")] * 3
+        for _ in range(rounds):
+            for j in range(3):
+                best[j] = min(best[j], time_graph(graphs[j], launches))
+        gb = nbytes / best[0] / 1e9
+        e = ring[0, offs[3]:offs[3] + 4 * M].view(torch.float32)
+        rmse = float(np.sqrt(e.double().sum().item() / (M * N)))
+        out[f"{kind}_{M}x{N}"] = {
+            "us": best[0] * 1e6, "alg_bytes": nbytes, "gbps": gb, "pct_of_8tbs": 100 * gb / HBM_PEAK_GBPS,
+            "read_probe_us": best[1] * 1e6,
+            "pct_of_read_probe_time": 100 * best[1] / best[0],
+            "equal_bytes_copy_us": best[2] * 1e6,
+            "pct_of_equal_bytes_copy_time": 100 * best[2] / best[0],
+            "rmse": rmse,
+        }
+        del graphs, ring, cdst
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- softmax
+def softmax_detail(rounds, launches=32):
+    """Row softmax on the "membound" softmax shapes (binary16 in and out):
+    (x, y) slot pairs rotate through >= 1 GiB, launches captured in a HIP
+    graph, best of `rounds`.  The ceiling is the streaming-copy probe moving
+    the same bytes (read 2MN, write 2MN) the same way: the traffic mix of
+    softmax is one read and one write per element, so a pure-read ceiling
+    would flatter it (section "Bonus kernel: online softmax")."""
+    import torch
+
+    from memory_bound_gemv_row_amd import binding, inputs
+
+    out = {}
+    for M, N in inputs.SOFTMAX_WORKLOADS:
+        nbytes = 2 * M * N
+        slots = max(1, -(-RING_BYTES // (2 * nbytes)))
+        x = torch.from_numpy(inputs.make_logits(M, N, seed=0)).cuda()
+        xs = torch.empty((slots, M, N), dtype=torch.float16, device="cuda")
+        xs[:] = x
+        ys = torch.empty((slots, M, N), dtype=torch.float16, device="cuda")
+        del x
+        graphs = []
+        for which in ("softmax", "copy"):
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    for i in range(launches):
+                        h = torch.cuda.current_stream().cuda_stream
+                        a, b = xs[i % slots].data_ptr(), ys[i % slots].data_ptr()
+                        rc = (binding.softmax_f16_ptr(a, b, M, N, h) if which == "softmax"
+                              else binding.probe_copy_ptr(a, b, nbytes, h))
                         if rc != 0:
                             raise RuntimeError(f"{which} returned {rc}")
             torch.cuda.current_stream().wait_stream(st)
@@ -380,16 +455,12 @@ def quant_detail(rounds, launches=64):
         for _ in range(rounds):
             for j in range(2):
                 best[j] = min(best[j], time_graph(graphs[j], launches))
-        nbytes = quant_bytes(kind, M, N)
-        gb = nbytes / best[0] / 1e9
-        rmse = float(np.sqrt(e.double().sum().item() / (M * N)))
-        out[f"{kind}_{M}x{N}"] = {
-            "us": best[0] * 1e6, "alg_bytes": nbytes, "gbps": gb, "pct_of_8tbs": 100 * gb / HBM_PEAK_GBPS,
-            "read_probe_us": best[1] * 1e6,
-            "pct_of_read_probe_time": 100 * best[1] / best[0],
-            "rmse": rmse,
-        }
-        del graphs, ring, q, sc, e
+        gb = 2 * nbytes / best[0] / 1e9
+        out[f"{M}x{N}"] = {"us": best[0] * 1e6, "alg_bytes": 2 * nbytes, "gbps": gb,
+                           "pct_of_8tbs": 100 * gb / HBM_PEAK_GBPS,
+                           "copy_probe_us": best[1] * 1e6, "copy_probe_gbps": 2 * nbytes / best[1] / 1e9,
+                           "pct_of_copy_ceiling": 100 * best[1] / best[0]}
+        del graphs, xs, ys
         torch.cuda.empty_cache()
     return out
 
@@ -472,6 +543,7 @@ def main():
     if not args.no_detail:
         rec["detail"] = detail(args.rounds)
         rec["quantiser"] = quant_detail(args.rounds)
+        rec["softmax"] = softmax_detail(args.rounds)
     print(json.dumps(rec), flush=True)
 
 

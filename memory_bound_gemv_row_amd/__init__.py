@@ -17,4 +17,5 @@ from .binding import (  # noqa: F401,E402  (no library load at import time)
     describe_launch,
     quantize_q8,
     quantize_q4,
+    softmax_f16,
 )

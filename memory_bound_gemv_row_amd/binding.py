@@ -1,5 +1,5 @@
-"""ctypes binding over the C ABI in ``include/gemv.h`` and
-``include/gemv_quant.h``.
+"""ctypes binding over the C ABI in ``include/gemv.h``,
+``include/gemv_quant.h`` and ``include/gemv_softmax.h``.
 
 Argument marshalling only: every step of the product runs in the HIP
 library.  PyTorch supplies device memory and the current stream; no torch
@@ -53,6 +53,8 @@ def load():
         for name in ("gemv_quantize_q8", "gemv_quantize_q4"):
             getattr(lib, name).argtypes = [p, p, p, p, i, i, p]
             getattr(lib, name).restype = i
+        lib.gemv_softmax_f16.argtypes = [p, p, i, i, p]
+        lib.gemv_softmax_f16.restype = i
         lib.gemv_status_string.argtypes = [i]
         lib.gemv_status_string.restype = ctypes.c_char_p
         lib.gemv_probe_read.argtypes = [p, ctypes.c_size_t, p, ctypes.c_uint32, p]
@@ -106,6 +108,10 @@ def quantize_q8_ptr(W: int, q: int, scale: int, row_sse: int, M: int, N: int, st
 
 def quantize_q4_ptr(W: int, q: int, scale: int, row_sse: int, M: int, N: int, stream: int = 0) -> int:
     return load().gemv_quantize_q4(W, q, scale, row_sse, M, N, stream)
+
+
+def softmax_f16_ptr(x: int, y: int, M: int, N: int, stream: int = 0) -> int:
+    return load().gemv_softmax_f16(x, y, M, N, stream)
 
 
 def probe_read_ptr(buf: int, nbytes: int, sink: int, guard: int = 0xA5A5A5A5, stream: int = 0) -> int:
@@ -267,6 +273,21 @@ def quantize_q4(W, with_error=True, stream=None):
     _check(quantize_q4_ptr(w, q.data_ptr(), s.data_ptr(), e.data_ptr() if e is not None else 0, M, N,
                            _stream(stream)), "gemv_quantize_q4")
     return q, s, e
+
+
+def softmax_f16(x, out=None, stream=None):
+    """Row-wise softmax of binary16 x [M, N] -> binary16 [M, N]."""
+    import torch
+
+    h = (torch.float16, torch.int16, torch.uint16)
+    M, N = x.shape
+    xp = _need(x, "x", h, (M, N))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, "out", h, (M, N))
+    _check(softmax_f16_ptr(xp, out.data_ptr(), M, N, _stream(stream)), "gemv_softmax_f16")
+    return out
 
 
 def probe_read(buf, sink, guard: int = 0xA5A5A5A5, stream=None):

@@ -2,7 +2,8 @@
 
 ``python -m memory_bound_gemv_row_amd.build`` compiles
 ``csrc/gemv_api.hip`` (GEMV, which includes its kernels) and
-``csrc/quant_api.hip`` (the weight quantiser) into one library,
+``csrc/quant_api.hip`` (the weight quantiser) and ``csrc/softmax_api.hip``
+(the row softmax) into one library,
 ``memory_bound_gemv_row_amd/libgemv_amd.so``.
 """
 from __future__ import annotations
@@ -16,9 +17,9 @@ ROOT = os.path.dirname(PKG)
 SRC_DIR = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemv_amd.so")
-SOURCES = [os.path.join(SRC_DIR, "gemv_api.hip"), os.path.join(SRC_DIR, "quant_api.hip")]
-DEPENDS = SOURCES + [os.path.join(SRC_DIR, "gemv_kernels.hpp"), os.path.join(SRC_DIR, "quant_kernels.hpp"),
-                     os.path.join(INCLUDE, "gemv.h"), os.path.join(INCLUDE, "gemv_quant.h")]
+SOURCES = [os.path.join(SRC_DIR, f) for f in ("gemv_api.hip", "quant_api.hip", "softmax_api.hip")]
+DEPENDS = SOURCES + [os.path.join(SRC_DIR, f) for f in ("gemv_kernels.hpp", "quant_kernels.hpp", "softmax_kernels.hpp")] \
+    + [os.path.join(INCLUDE, f) for f in ("gemv.h", "gemv_quant.h", "gemv_softmax.h")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

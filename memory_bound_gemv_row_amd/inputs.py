@@ -111,6 +111,17 @@ def make_weights(M: int, N: int, seed: int = 0) -> np.ndarray:
 QUANT_WORKLOADS = [("q8", 8192, 8192), ("q8", 14336, 4096), ("q4", 4096, 14336), ("q4", 14336, 4096)]
 
 
+def make_logits(M: int, N: int, seed: int = 0) -> np.ndarray:
+    """Softmax input: binary16 logits ~ N(0, 1) (the page does not print its
+    distribution; the GEMV's own x recipe is reused)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((M, N)).astype(np.float16)
+
+
+# Softmax workloads: the row shapes of the "membound" softmax table.
+SOFTMAX_WORKLOADS = [(8192, 8192), (4096, 32768), (1024, 131072)]
+
+
 MAKERS = {"f32": make_f32, "f16": make_f16, "f16x32": make_f16x32, "f16_acc16": make_f16, "q8": make_q8,
           "q4": make_q4}
 
