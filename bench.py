@@ -19,8 +19,10 @@ gates the GPU result, and the run aborts on a parity failure, as the pages
 do), ``detail`` (the other FP16 shapes, FP16 weights with FP32 x, FP16
 accumulation, and the INT8/INT4 speed-ups over FP16, timed in interleaved
 rounds), ``quantiser`` (the FP32 -> INT8/INT4 weight quantiser and the
-RMSE of its codes) and ``softmax`` (the row softmax against the
-streaming-copy ceiling).
+RMSE of its codes), ``softmax`` (the row softmax against the
+streaming-copy ceiling) and ``roofline_study`` (every GEMV point and a
+library GEMM reference against min(peak, AI x bandwidth);
+``--plot-roofline FILE`` draws it).
 """
 from __future__ import annotations
 
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the CPU-baseline leg")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--rounds", type=int, default=5)
+    ap.add_argument("--plot-roofline", metavar="BENCH_JSON",
+                    help="print an ASCII roofline chart from a saved bench line and exit (no GPU needed)")
     ap.add_argument("--profile", action="store_true",
                     help="launch each kernel exactly once after a cold flush (for counter collection)")
     return ap.parse_args()
@@ -465,9 +469,119 @@ def softmax_detail(rounds, launches=32):
     return out
 
 
+# ---------------------------------------------------------------- roofline study
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0}     # MI355X dense: FP32 vector/MFMA, FP16 MFMA
+
+
+def gemm_reference(n=8192, reps=20):
+    """Library GEMM reference points (torch.matmul -> hipBLASLt / rocBLAS) on
+    square n x n x n operands, FP16 and FP32: the compute-bound end of the
+    roofline that "cuda-gemv-optimization" names as its next comparison
+    (section "What I'd explore next").  Returns one point per dtype."""
+    import torch
+
+    pts = []
+    for name, dt in (("f16", torch.float16), ("f32", torch.float32)):
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn((n, n), dtype=dt, device="cuda", generator=g)
+        b = torch.randn((n, n), dtype=dt, device="cuda", generator=g)
+        for _ in range(3):
+            c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            c = torch.matmul(a, b)
+        end.record()
+        torch.cuda.synchronize()
+        t = start.elapsed_time(end) * 1e-3 / reps
+        elt = a.element_size()
+        flops = 2 * n ** 3
+        nbytes = elt * 3 * n * n                    # A, B read once, C written once
+        pts.append({"kernel": f"gemm_{name}_{n}^3 (library)", "dtype": name, "ai": flops / nbytes,
+                    "tflops": flops / t / 1e12, "us": t * 1e6, "peak_tflops": PEAK_TFLOPS[name]})
+        del a, b, c
+    torch.cuda.empty_cache()
+    return pts
+
+
+def roofline_study(rec):
+    """Points (arithmetic intensity, achieved TFLOP/s) for every GEMV kernel
+    the bench timed and for the GEMM reference, with the attainable bound
+    min(P_peak, AI * B) ("Making GEMV Fast", section "Arithmetic
+    intensity"), B = the same-run pure-read probe."""
+    from memory_bound_gemv_row_amd import accounting
+
+    bw = rec["probe"]["gbps"] * 1e9
+    pts = []
+
+    def gemv_point(kind, M, N, us):
+        f = accounting.flops(M, N)
+        ai = f / accounting.alg_bytes(kind, M, N)
+        peak = PEAK_TFLOPS["f32"]                    # GEMV arithmetic is FP32 (or FP16-in, FP32-out dot2)
+        tf = f / (us * 1e-6) / 1e12
+        return {"kernel": f"gemv_{kind}_{M}x{N}", "dtype": kind, "ai": ai, "tflops": tf, "us": us,
+                "peak_tflops": peak}
+
+    M, N, kind = rec["config"]["M"], rec["config"]["N"], rec["dtype"]
+    pts.append(gemv_point(kind, M, N, rec["roofline"]["kernel_us"]))
+    for shape, d in rec.get("detail", {}).items():
+        m, n = (int(v) for v in shape.split("x"))
+        for k, v in d.items():
+            if isinstance(v, dict) and not (k == kind and m == M and n == N):
+                pts.append(gemv_point(k, m, n, v["us"]))
+    pts.extend(gemm_reference())
+    for p in pts:
+        p["attainable_tflops"] = min(p["peak_tflops"], p["ai"] * bw / 1e12)
+        p["pct_of_attainable"] = 100 * p["tflops"] / p["attainable_tflops"]
+        p["bound"] = "hbm" if p["ai"] * bw / 1e12 < p["peak_tflops"] else "compute"
+    return {"bandwidth_gbps": bw / 1e9, "points": pts}
+
+
+def ascii_roofline(study, width=72, height=22):
+    """Log-log text chart: the FP16-MFMA and FP32 roofs against the measured
+    bandwidth, and every point of the study (G = GEMV, M = GEMM)."""
+    import math
+
+    bw = study["bandwidth_gbps"] * 1e9
+    x0, x1, y0, y1 = -1.0, 4.0, -1.0, 3.6          # log10 AI (FLOP/B) and log10 TFLOP/s
+    grid = [[" "] * width for _ in range(height)]
+
+    def cell(ai, tf):
+        cx = int(round((math.log10(ai) - x0) / (x1 - x0) * (width - 1)))
+        cy = int(round((math.log10(tf) - y0) / (y1 - y0) * (height - 1)))
+        return min(max(cx, 0), width - 1), min(max(height - 1 - cy, 0), height - 1)
+
+    for peak, ch in ((PEAK_TFLOPS["f16"], "="), (PEAK_TFLOPS["f32"], "-")):
+        for i in range(width):
+            ai = 10 ** (x0 + (x1 - x0) * i / (width - 1))
+            cx, cy = cell(ai, min(peak, ai * bw / 1e12))
+            if grid[cy][cx] == " ":
+                grid[cy][cx] = ch
+    for p in study["points"]:
+        cx, cy = cell(p["ai"], p["tflops"])
+        grid[cy][cx] = "M" if p["kernel"].startswith("gemm") else "G"
+    lines = [f"TFLOP/s (log)  roofs: '=' FP16 MFMA {PEAK_TFLOPS['f16']:.0f}, '-' FP32 {PEAK_TFLOPS['f32']:.0f}, "
+             f"slope = {study['bandwidth_gbps']:.0f} GB/s"]
+    for r, row in enumerate(grid):
+        ylab = 10 ** (y1 - (y1 - y0) * r / (height - 1))
+        lines.append(f"{ylab:9.1f} |" + "".join(row))
+    lines.append(" " * 10 + "+" + "-" * width)
+    lines.append(" " * 11 + "".join(f"{10 ** (x0 + i):<{width // 5}g}" for i in range(5)) + "  AI (FLOP/byte, log)")
+    return "\n".join(lines)
+
+
 # ---------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.plot_roofline:
+        with open(args.plot_roofline) as f:
+            rec = json.loads(f.read().strip().splitlines()[-1])
+        print(ascii_roofline(rec["roofline_study"]))
+        for p in rec["roofline_study"]["points"]:
+            print(f"{p['kernel']:<34} AI {p['ai']:8.2f}  {p['tflops']:8.2f} TFLOP/s  "
+                  f"attainable {p['attainable_tflops']:8.2f}  ({p['pct_of_attainable']:5.1f} %, {p['bound']})")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -544,6 +658,7 @@ def main():
         rec["detail"] = detail(args.rounds)
         rec["quantiser"] = quant_detail(args.rounds)
         rec["softmax"] = softmax_detail(args.rounds)
+        rec["roofline_study"] = roofline_study(rec)
     print(json.dumps(rec), flush=True)
 
 
