@@ -146,8 +146,9 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
  * `aligned` states whether A and x are
  * 16-byte aligned.  Fills `info` with the variant (1 = streaming kernel with x staged in LDS,
  * 2 = streaming kernel with x read from global memory, 3 = element-wise
- * kernel), grid and workgroup sizes, rows per wave, 1-KiB loads in flight
- * per wave, and dynamic LDS bytes.  The geometry is chosen per shape:
+ * kernel), grid and workgroup sizes, rows per wave (at most), 1-KiB loads
+ * in flight per wave, dynamic LDS bytes, and the order in which x is staged
+ * relative to the first loads of A.  The geometry is chosen per shape:
  * workgroups of 4 or 8 waves, 2 to 8 loads in flight, 1 to 4 rows per wave
  * (the llama.cpp walkthrough's implementation note: the original kernel
  * selects its block size at run time).  Returns GEMV_OK or an error code; it
@@ -159,6 +160,7 @@ typedef struct gemv_launch_info {
     int rows_per_wave;
     int units_in_flight;
     int lds_bytes;
+    int stage_order;   /* variant 1: 0 A first, 1 x first, 2 x loads / A / x writes; else -1 */
 } gemv_launch_info;
 
 int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info);

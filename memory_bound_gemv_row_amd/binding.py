@@ -30,7 +30,8 @@ class GemvError(RuntimeError):
 
 class LaunchInfo(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("grid", ctypes.c_int), ("block", ctypes.c_int),
-                ("rows_per_wave", ctypes.c_int), ("units_in_flight", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+                ("rows_per_wave", ctypes.c_int), ("units_in_flight", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("stage_order", ctypes.c_int)]
 
 
 def load():

@@ -77,21 +77,29 @@ struct Plan {
     int rows;      // rows per wave (upper bound)
     int D;         // units in flight per wave
     int lds;
+    int stg;       // order of A prologue and x staging (default_stage_order)
+    int cap;       // at most cap workgroups per CU (0: no cap)
 };
 
-// Geometry for one call.  A row of nchunks 16-byte chunks is
-// P = ceil(nchunks / 64) units (one 1-KiB wave load each).
-//   FP32/FP16 (either accumulation): x read with each unit (no staging); one row per wave, or two
-//     for very long rows; 8 units in flight when rows have at least 8 units.
-//   INT8/INT4: x staged in LDS (INT8 with its sum); short rows (INT4 in
-//     particular) put several rows on each wave.
+// Geometry for one call, chosen from sweeps on MI355X.  A row of nchunks
+// 16-byte chunks is P = ceil(nchunks / 64) units (one 1-KiB wave load each).
+//   FP32/FP16 (either accumulation): x read with each unit (no staging); one
+//     row per wave, or two for very long rows; 8 units in flight when rows
+//     have at least 8 units.
+//   INT8: 4 units in flight; rows of 8 units or more: 8 waves, A first,
+//     a row per wave; shorter rows: 4 waves, x staged with split order
+//     (staging loads, A prologue, LDS writes), at most 3 workgroups per CU.
+//   INT4: rows under 4 units: 8 waves, 2 in flight, split staging; longer
+//     rows: 4 waves, 4 in flight, x staged before A; at most 3 workgroups
+//     per CU.
 //   FP16 with FP32 x: x is twice the bytes of FP16 x, and reading it with
 //     every unit costs more cache bandwidth than staging it, once the staging
 //     (4N bytes per workgroup) is spread over enough rows: staged for rows of
 //     at least 12 units, or for 8192 rows and more; read with each unit
 //     otherwise, and whenever the staged x would exceed the LDS budget.
-// Every launch gives each of the device's CUs work when M >= CUs.
-Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
+// With a cap the grid stays below the row count and waves walk several
+// rows; otherwise every launch gives each CU work once M >= CUs.
+Plan make_plan(int kind, int M, int N, bool aligned, int cus)
 {
     Plan p{};
     const int epc = elems_per_chunk(kind);
@@ -119,21 +127,22 @@ Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
         }
     } else if (kind == kF16X32) {
         const bool fits = lds_bytes(kind, nchunks) <= kMaxLdsBytes;
+        p.rows = 1;
         if (fits && P >= 24) {
             p.variant = 1;
             p.waves = 8;
             p.D = 4;
-            p.rows = 2;
+            p.stg = 2;
         } else if (fits && P >= 12) {
             p.variant = 1;
             p.waves = 8;
             p.D = 8;
-            p.rows = 2;
+            p.cap = 3;
         } else if (fits && M >= 8192) {
             p.variant = 1;
             p.waves = 4;
             p.D = 8;
-            p.rows = 4;
+            p.cap = 4;
         } else {
             p.variant = 2;
             p.waves = 4;
@@ -142,35 +151,62 @@ Plan make_plan(int kind, int M, int N, bool aligned, int /*cus*/)
         }
     } else if (kind == kQ8) {
         p.variant = 1;
-        p.waves = P >= 8 ? 8 : 4;
         p.D = 4;
-        p.rows = P <= 4 ? 4 : 1;  // short INT8 rows: more rows per wave
+        p.rows = 1;
+        if (P >= 8) {
+            // long rows: 8 waves, A first, one row per wave
+            p.waves = 8;
+        } else {
+            // short rows: 4 waves, split staging, at most 3 workgroups per CU
+            p.waves = 4;
+            p.stg = 2;
+            p.cap = 3;
+        }
     } else {
+        // short INT4 rows: 8 waves, 2 units in flight, split staging;
+        // longer rows: 4 waves, 4 units, x staged before A
         p.variant = 1;
-        p.waves = 4;
-        p.D = P >= 4 ? 4 : 2;
-        p.rows = P >= 4 ? 2 : 4;  // short INT4 rows: more rows per wave
+        p.waves = P < 4 ? 8 : 4;
+        p.D = P < 4 ? 2 : 4;
+        p.rows = 1;
+        p.stg = P < 4 ? 2 : 1;
+        p.cap = 3;
     }
     p.lds = p.variant == 1 ? lds_bytes(kind, nchunks) : 0;
     p.block = p.waves * 64;
     const int64_t waves_needed = ((int64_t)M + p.rows - 1) / p.rows;
-    p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
+    int64_t grid = (waves_needed + p.waves - 1) / p.waves;
+    if (p.cap > 0 && grid > (int64_t)p.cap * cus)
+        grid = (int64_t)p.cap * cus;
+    p.grid = (int)grid;
     return p;
 }
 
-template <int F, int W, int D, bool XG>
+template <int F, int W, int D, bool XG, int STG>
 const void* stream_kernel()
 {
     constexpr int dec = F == kQ8 ? kQ8Decode : (F == kQ4 ? kQ4Decode : 0);
-    return reinterpret_cast<const void*>(&gemv_stream<F, W, D, kNT, XG, dec>);
+    return reinterpret_cast<const void*>(&gemv_stream<F, W, D, kNT, XG, dec, STG>);
+}
+
+template <int F, bool XG, int STG>
+const void* select_stream_stg(const Plan& p)
+{
+    if (p.waves == 8)
+        return p.D == 8 ? stream_kernel<F, 8, 8, XG, STG>()
+                        : (p.D == 4 ? stream_kernel<F, 8, 4, XG, STG>() : stream_kernel<F, 8, 2, XG, STG>());
+    return p.D == 8 ? stream_kernel<F, 4, 8, XG, STG>()
+                    : (p.D == 4 ? stream_kernel<F, 4, 4, XG, STG>() : stream_kernel<F, 4, 2, XG, STG>());
 }
 
 template <int F, bool XG>
 const void* select_stream(const Plan& p)
 {
-    if (p.waves == 8)
-        return p.D == 8 ? stream_kernel<F, 8, 8, XG>() : (p.D == 4 ? stream_kernel<F, 8, 4, XG>() : stream_kernel<F, 8, 2, XG>());
-    return p.D == 8 ? stream_kernel<F, 4, 8, XG>() : (p.D == 4 ? stream_kernel<F, 4, 4, XG>() : stream_kernel<F, 4, 2, XG>());
+    if constexpr (XG)
+        return select_stream_stg<F, XG, 0>(p);   // nothing is staged
+    else
+        return p.stg == 2 ? select_stream_stg<F, XG, 2>(p)
+                          : (p.stg == 1 ? select_stream_stg<F, XG, 1>(p) : select_stream_stg<F, XG, 0>(p));
 }
 
 // Variant 1 stages x in LDS, variant 2 reads it with each unit; FP32 and
@@ -345,9 +381,11 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
     info->variant = p.variant;
     info->grid = p.grid;
     info->block = p.block;
-    info->rows_per_wave = p.rows;
+    const int64_t waves = (int64_t)p.grid * p.waves;
+    info->rows_per_wave = waves > 0 ? (int)(((int64_t)M + waves - 1) / waves) : 0;
     info->units_in_flight = p.D;
     info->lds_bytes = p.lds;
+    info->stage_order = p.variant == 1 ? p.stg : -1;
     return GEMV_OK;
 }
 

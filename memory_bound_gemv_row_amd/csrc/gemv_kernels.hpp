@@ -362,6 +362,34 @@ __device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4
     }
 }
 
+// One thread's part of stage_x_sums when a single chunk per thread covers x:
+// v holds chunk c's granules (zero past the row end).
+template <int F, int WAVES>
+__device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<F>::kXGran], int c, u32x4* lds, float* lds_f,
+                                                 int nchunks_pad)
+{
+    constexpr int G = Traits<F>::kXGran;
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float sum = 0.0f;
+    if (c < nchunks_pad) {
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].x), ones, sum, false);
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].y), ones, sum, false);
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].z), ones, sum, false);
+            sum = __builtin_amdgcn_fdot2(as_h2(v[k].w), ones, sum, false);
+            lds[c * G + k] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+        }
+        if constexpr (F == kQ4)
+            lds_f[c] = 8.0f * sum;
+    }
+    if constexpr (F == kQ8) {
+        const float w = wave_sum(sum);
+        if ((threadIdx.x & 63) == 0)
+            lds_f[threadIdx.x >> 6] = w;
+    }
+}
+
 // ---------------------------------------------------------------- streaming kernel
 // Preconditions (checked by the host): N is a multiple of Traits<F>::kElems,
 // A and x are 16-byte aligned, M >= 1, and the launch provides
@@ -403,7 +431,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int F, int WAVES, int D, bool NT, bool XG, int DEC>
+// Order of the A prologue and the staging of x (with x in LDS):
+//   0  the first D units of A, then the staging (loads, LDS writes);
+//   1  the staging, then the first D units of A;
+//   2  the staging loads, then the first D units of A, then the LDS writes:
+//      the staging loads are the older ones in the wave's in-order load
+//      counter, so the LDS writes wait only for them while A is in flight
+//      (when one round of at most 8 granules per thread stages all of x;
+//      otherwise as 1).
+template <int F>
+__host__ __device__ constexpr int default_stage_order()
+{
+    return F == kQ4 ? 1 : 0;
+}
+
+template <int F, int WAVES, int D, bool NT, bool XG, int DEC, int STG = default_stage_order<F>()>
 __global__ void __launch_bounds__(WAVES * 64)
 gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
@@ -474,22 +516,60 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         }
     };
 
-    // With x staged in LDS the order of the prologue and the staging matters:
-    // INT4 stages first (its staging loads are then the oldest in the wave's
-    // in-order load counter, so the LDS writes need not wait for A), INT8
-    // issues its first D units of A first (each measured faster).
-    constexpr bool kStageFirst = (F == kQ4);
-    if (!kStageFirst && units > 0) {
+    // With x staged in LDS the order of the prologue and the staging
+    // matters (see default_stage_order).
+    constexpr int kRound = 8;                   // granules per thread in one staging round
+    const bool split = !XG && STG == 2 &&
+                       (DEC == 1 ? P * 64 <= NT_ : nxg_pad <= kRound * NT_);
+    bool issued = false;
+    if ((XG || STG == 0) && units > 0) {
 #pragma unroll
         for (int d = 0; d < D; ++d)
             issue(d);
+        issued = true;
     }
     float xsum = 0.0f;   // offset-code INT8: sum of x over the row
     if constexpr (!XG) {
-        if constexpr (DEC == 1)
+        if (split) {
+            if constexpr (DEC == 1) {
+                // one chunk (G granules) per thread: load, prologue, sum and write
+                const int c = threadIdx.x;
+                u32x4 v[G];
+#pragma unroll
+                for (int k = 0; k < G; ++k)
+                    v[k] = c < nchunks ? xg[c * G + k] : u32x4{0u, 0u, 0u, 0u};
+                if (units > 0) {
+#pragma unroll
+                    for (int d = 0; d < D; ++d)
+                        issue(d);
+                    issued = true;
+                }
+                stage_chunk_sums<F, WAVES>(v, c, lds_x, lds_f, P * 64);
+            } else {
+                u32x4 v[kRound];
+#pragma unroll
+                for (int k = 0; k < kRound; ++k) {
+                    const int g = threadIdx.x + k * NT_;
+                    v[k] = g < nxg ? xg[g] : u32x4{0u, 0u, 0u, 0u};
+                }
+                if (units > 0) {
+#pragma unroll
+                    for (int d = 0; d < D; ++d)
+                        issue(d);
+                    issued = true;
+                }
+#pragma unroll
+                for (int k = 0; k < kRound; ++k) {
+                    const int g = threadIdx.x + k * NT_;
+                    if (g < nxg_pad)
+                        lds_x[staged_index<F>(g / G, g % G, P * 64)] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+                }
+            }
+        } else if constexpr (DEC == 1) {
             stage_x_sums<F, WAVES>(xg, lds_x, lds_f, nchunks, P * 64);
-        else
+        } else {
             stage_x<F, NT_>(xg, lds_x, nxg, nxg_pad);
+        }
         __syncthreads();
         if constexpr (F == kQ8 && DEC == 1) {
 #pragma unroll
@@ -499,7 +579,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     }
     if (units == 0)
         return;
-    if (kStageFirst) {
+    if (!issued) {
 #pragma unroll
         for (int d = 0; d < D; ++d)
             issue(d);

@@ -70,6 +70,19 @@ def test_many_passes_and_row_groups(gpu, oracle_mod, kind, N):
     _check(oracle_mod, kind, ops, f"{kind} tiles N={N}")
 
 
+@pytest.mark.parametrize("kind,N", [("q8", 1024), ("q8", 4096 + 16), ("q4", 2048 + 128), ("q4", 14336),
+                                    ("f16x32", 1024), ("f16x32", 8192 + 8)])
+def test_waves_walk_several_rows(gpu, oracle_mod, kind, N):
+    # grids capped per CU: each wave walks two or three rows, the last ones
+    # ragged across waves
+    probe = binding.describe_launch(kind, 1 << 20, N)
+    M = probe["grid"] * probe["block"] // 64 * 2 + 37
+    info = binding.describe_launch(kind, M, N)
+    assert info["rows_per_wave"] >= 3, info
+    ops = inputs.make(kind, M, N, seed=11)
+    _check(oracle_mod, kind, ops, f"{kind} multi-row M={M} N={N} {info}")
+
+
 # ---------------------------------------------------------------- exactness
 def _int_ops(kind, M, N, rng):
     x = rng.integers(-3, 4, N)
