@@ -166,6 +166,29 @@ def time_graph(g, launches, replays=1):
     return start.elapsed_time(end) * 1e-3 / (launches * replays)
 
 
+def launch_floor_us(launches=1000):
+    """Per-launch floor: back-to-back launches of the pure-read probe over 16
+    bytes (one workgroup), eager, between events on the launch stream."""
+    import torch
+
+    from memory_bound_gemv_row_amd import binding
+
+    buf = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for _ in range(50):
+        binding.probe_read_ptr(buf.data_ptr(), 16, sink.data_ptr(), 0xA5A5A5A5, sh)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(launches):
+        binding.probe_read_ptr(buf.data_ptr(), 16, sink.data_ptr(), 0xA5A5A5A5, sh)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / launches
+
+
 def probe_gbps(buf, reps=20):
     """Best pure-read rate over `reps` full passes of `buf`."""
     import torch
@@ -190,6 +213,16 @@ def probe_gbps(buf, reps=20):
 
 
 # ---------------------------------------------------------------- CPU baseline leg
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
 def cpu_baseline(kind, ops, y_gpu, seconds):
     """Time the oracle (as it stands) on the host cores and check the GPU result
     against it.  Returns (record, parity report)."""
@@ -205,19 +238,30 @@ def cpu_baseline(kind, ops, y_gpu, seconds):
           "f16_acc16": lambda: oracle.gemv_f16(ops["A"], ops["x"]),
           "q8": lambda: oracle.gemv_q8(ops["A"], ops["scale"], ops["x"]),
           "q4": lambda: oracle.gemv_q4(ops["A"], ops["scale"], ops["x"])}[kind]
-    ref = fn()
-    times = []
-    t_end = time.perf_counter() + seconds
-    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 200):
-        t0 = time.perf_counter()
-        fn()
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
+    def timed(budget):
+        times = []
+        t_end = time.perf_counter() + budget
+        while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 200):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times)
+
+    ref = fn()                                    # warm run; also the parity reference
+    cores = oracle.num_threads()
+    t, calls = timed(seconds)
+    oracle.set_threads(1)
+    t1, calls1 = timed(min(seconds, 5.0))
+    oracle.set_threads(cores)
     M, N = ops["A"].shape[0], (ops["A"].shape[1] * (2 if kind == "q4" else 1))
-    rec = {"value": accounting.gbps(accounting.alg_bytes(kind, M, N), t), "unit": "GB/s",
-           "cores": oracle.num_threads(), "kind": "oracle",
-           "ms_per_call": t * 1e3, "calls": len(times),
-           "sample": f"the full {kind} {M}x{N} workload (same seeded inputs), {len(times)} oracle calls, median"}
+    nbytes = accounting.alg_bytes(kind, M, N)
+    rec = {"value": accounting.gbps(nbytes, t), "unit": "GB/s",
+           "cores": cores, "kind": "oracle",
+           "ms_per_call": t * 1e3, "calls": calls, "gflops": accounting.flops(M, N) / t / 1e9,
+           "one_thread": {"value": accounting.gbps(nbytes, t1), "ms_per_call": t1 * 1e3, "calls": calls1},
+           "cpu_model": cpu_model(),
+           "sample": f"the full {kind} {M}x{N} workload (same seeded inputs), {calls} oracle calls on "
+                     f"{cores} threads, median (then {calls1} calls on one thread)"}
     rep = oracle.parity_report(y_gpu, ref)
     if kind == "f16_acc16":
         # lossy path: gated by its derived componentwise bound (ratio <= 1)
@@ -615,6 +659,7 @@ def main():
         print(json.dumps({"profile": f"{kind}_{M}x{N}", "launches": 1}), flush=True)
         return
 
+    launch_floor = launch_floor_us()
     probe_before = probe_gbps(ring.buf)
     t = time_eager(ring, args.steps, args.warmup)
     probe_after = probe_gbps(ring.buf)
@@ -633,6 +678,7 @@ def main():
                    "launch": binding.describe_launch(kind, M, N, True)},
     }
     rec["probe"] = {"gbps": round(probe, 2), "before": round(probe_before, 2), "after": round(probe_after, 2),
+                    "launch_floor_us": round(launch_floor, 3),
                     "pct_of_probe": round(100 * value / max(probe, value), 2),
                     "pct_of_8tbs": round(100 * probe / HBM_PEAK_GBPS, 2)}
     traffic = traffic_record(kind, M, N)

@@ -15,6 +15,7 @@ from .oracle import (  # noqa: F401
     gemv_q8,
     gemv_q4,
     num_threads,
+    set_threads,
     library_path,
     double_to_half,
     quantize_q8,

@@ -84,6 +84,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the following parallel regions (benchmark leg: all host
+ * threads, then one).  Does not change any result. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* FP32 A and x. */
 int oracle_gemv_f32(const float* A, const float* x, double* y, int64_t M, int64_t N)
 {

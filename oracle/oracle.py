@@ -65,6 +65,8 @@ def _load():
         lib.oracle_half_to_double_array.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         lib.oracle_gemv_f32.argtypes = [p, p, p, i64, i64]
         lib.oracle_gemv_f16.argtypes = [p, p, p, i64, i64]
         lib.oracle_gemv_f16x32.argtypes = [p, p, p, i64, i64]
@@ -97,6 +99,11 @@ def _as(a, dtype, name):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for later oracle calls (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def half_to_double(bits: int) -> float:
