@@ -43,10 +43,37 @@ def run_oracle(oracle, kind: str, ops: dict) -> np.ndarray:
     return oracle.gemv_q4(ops["A"], ops["scale"], ops["x"])
 
 
-def abs_products(ops: dict) -> np.ndarray:
-    """sum_j |A_ij x_j| in float64 (the scale of the FP16-accumulation bound)."""
-    A = np.abs(np.asarray(ops["A"]).astype(np.float64))
-    return A @ np.abs(np.asarray(ops["x"]).astype(np.float64))
+def abs_products(ops: dict, kind: str = "f16") -> np.ndarray:
+    """sum_j |w_ij x_j| in float64, w the weights as the oracle reads them
+    (INT8/INT4 dequantised with their scales)."""
+    x = np.abs(np.asarray(ops["x"]).astype(np.float64))
+    if kind == "q8":
+        W = np.abs(ops["A"].astype(np.float64)) * ops["scale"].astype(np.float64)[:, None]
+    elif kind == "q4":
+        from qpack import unpack_int4
+
+        W = np.abs(unpack_int4(ops["A"]).astype(np.float64)) * np.repeat(
+            ops["scale"].astype(np.float64), 128, axis=1)
+    else:
+        W = np.abs(np.asarray(ops["A"]).astype(np.float64))
+    return W @ x
+
+
+def within_fp32_bound(kind: str, ops: dict, y: np.ndarray, ref: np.ndarray) -> float:
+    """max_i |y_i - r_i| / (g(2N + 8) sum_j |w_ij x_j|), g(n) = n u / (1 - n u),
+    u = 2^-24: the recursive-summation bound of an FP32 dot product of N exact
+    products in any order, with room for v_dot2_f32_f16's two roundings per
+    step and the scale multiplications.  At most 1 for a correct FP32-
+    accumulating kernel, whatever the cancellation (unlike a relative error
+    when M is too small for the floor to act)."""
+    N = np.asarray(ops["x"]).shape[0]
+    n = 2 * N + 8
+    g = n * 2.0 ** -24 / (1 - n * 2.0 ** -24)
+    bound = g * abs_products(ops, kind) + 1e-300
+    y = np.asarray(y, dtype=np.float64)
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    return float(np.max(np.abs(y - ref) / bound)) if y.size else 0.0
 
 
 def within_gate(oracle, kind: str, ops: dict, y: np.ndarray, ref: np.ndarray) -> dict:
@@ -58,7 +85,7 @@ def within_gate(oracle, kind: str, ops: dict, y: np.ndarray, ref: np.ndarray) ->
     rep = parity_report(y, ref)
     if kind == "f16_acc16":
         N = np.asarray(ops["A"]).shape[1]
-        rep["acc16_ratio"] = acc16_ratio(y, ref, abs_products(ops), N)
+        rep["acc16_ratio"] = acc16_ratio(y, ref, abs_products(ops, kind), N)
         rep["ok"] = rep["acc16_ratio"] <= 1.0
     else:
         rep["ok"] = rep["floored_rel"] <= GATES[kind]

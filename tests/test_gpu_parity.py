@@ -261,3 +261,24 @@ def test_nan_propagates(gpu, oracle_mod):
     A[3, 100] = np.nan
     y = run_gpu("f32", {"A": A, "x": np.ones(1024, np.float32)})
     assert np.isnan(y[3]) and np.all(y[[0, 1, 2, 4, 5, 6, 7]] == 1024)
+
+
+# ---------------------------------------------------------------- brute force over small shapes
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
+def test_brute_force_small_shapes(gpu, oracle_mod, kind):
+    # every N in 1..300 (odd, below one wave's width, not a multiple of the
+    # chunk width) for several M up to 17; INT4 takes its whole-group N only
+    # With M this small the floored relative error cannot absorb cancellation
+    # in a single output, so the gate here is the componentwise FP32 bound;
+    # a dropped or misplaced term exceeds it.
+    from gpu_util import within_fp32_bound
+
+    Ns = [128, 256] if kind == "q4" else list(range(1, 301))
+    say(f"[brute force] {kind} N=1..300")
+    for N in Ns:
+        for M in (1, 2, 3, 5, 8, 13, 17):
+            ops = inputs.make(kind, M, N, seed=M * 1000 + N)
+            y = run_gpu(kind, ops)
+            ref = run_oracle(oracle_mod, kind, ops)
+            r = within_fp32_bound(kind, ops, y, ref)
+            assert r <= 1.0, (kind, M, N, r)

@@ -188,3 +188,25 @@ def test_acc16_bound_closed_form():
     assert acc16_bound(np.array([1.0]), 8192)[0] == pytest.approx(want, rel=1e-12)
     # the bound is finite only while k * u16 < 1
     assert np.isinf(acc16_bound(np.array([1.0]), 64 * 2048)[0])
+
+
+def test_componentwise_fp32_bound_accepts_orders_and_catches_a_dropped_term():
+    # the brute-force GPU test's gate: g(2N+8) * sum |w x|
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_util import within_fp32_bound
+
+    rng = np.random.default_rng(9)
+    for N in (1, 7, 126, 300):
+        A = rng.uniform(-1, 1, (17, N)).astype(np.float32)
+        x = rng.uniform(-1, 1, N).astype(np.float32)
+        ops = {"A": A, "x": x}
+        ref = A.astype(np.float64) @ x.astype(np.float64)
+        # a sequential FP32 sum and a 64-lane wave order both pass
+        seq = np.array([np.float32(0)] * 17)
+        for j in range(N):
+            seq = (seq + (A[:, j] * x[j]).astype(np.float32)).astype(np.float32)
+        assert within_fp32_bound("f32", ops, seq, ref) <= 1.0
+        if N > 1:
+            bad = ref - A[:, N // 2].astype(np.float64) * x[N // 2]
+            assert within_fp32_bound("f32", ops, bad, ref) > 1.0
