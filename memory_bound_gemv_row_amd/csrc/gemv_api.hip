@@ -18,11 +18,6 @@ namespace {
 
 constexpr int kMaxLdsBytes = 64 * 1024;    // x staged in LDS up to this size
 constexpr bool kNT = true;                 // stream A with non-temporal loads
-// INT8: offset-code decode (fewer instructions); INT4: exponent-bias decode,
-// whose error stays within the INT4 tolerance (the offset-code form's bias
-// cancellation does not, at 14336-wide rows).
-constexpr int kQ8Decode = 1;
-constexpr int kQ4Decode = 0;
 constexpr int kMaxDevices = 64;
 
 std::mutex g_cu_mutex;
@@ -60,12 +55,12 @@ int elems_per_chunk(int kind)
 int lds_bytes(int kind, int nchunks)
 {
     switch (kind) {
-    case kF32: return 4 * stream_lds_words<kF32, true, 0>(nchunks);
-    case kF16: return 4 * stream_lds_words<kF16, true, 0>(nchunks);
-    case kQ8: return 4 * stream_lds_words<kQ8, false, kQ8Decode>(nchunks);
-    case kF16X32: return 4 * stream_lds_words<kF16X32, false, 0>(nchunks);
-    case kF16H: return 4 * stream_lds_words<kF16H, true, 0>(nchunks);
-    default: return 4 * stream_lds_words<kQ4, false, kQ4Decode>(nchunks);
+    case kF32: return 4 * stream_lds_words<kF32, true>(nchunks);
+    case kF16: return 4 * stream_lds_words<kF16, true>(nchunks);
+    case kQ8: return 4 * stream_lds_words<kQ8, false>(nchunks);
+    case kF16X32: return 4 * stream_lds_words<kF16X32, false>(nchunks);
+    case kF16H: return 4 * stream_lds_words<kF16H, true>(nchunks);
+    default: return 4 * stream_lds_words<kQ4, false>(nchunks);
     }
 }
 
@@ -185,8 +180,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
 template <int F, int W, int D, bool XG, int STG>
 const void* stream_kernel()
 {
-    constexpr int dec = F == kQ8 ? kQ8Decode : (F == kQ4 ? kQ4Decode : 0);
-    return reinterpret_cast<const void*>(&gemv_stream<F, W, D, kNT, XG, dec, STG>);
+    return reinterpret_cast<const void*>(&gemv_stream<F, W, D, kNT, XG, STG>);
 }
 
 template <int F, bool XG, int STG>

@@ -17,11 +17,13 @@
 //     shared memory), or, when it does not fit, read through the caches.
 //   * Accumulation is FP32 in registers.  FP16 operands enter through
 //     v_dot2_f32_f16; INT8/INT4 codes are unpacked in registers to exact
-//     binary16 integers (exponent-bias trick, below) and enter the same way;
-//     the INT8 row scale multiplies the finished row sum, the INT4 group scale
-//     multiplies each 32-column partial (the reference weight is exactly
-//     q*s: "membound", section "The kernel decode actually runs: dequant
-//     GEMV").
+//     binary16 values (INT8 as offset subnormals, INT4 as exponent-biased
+//     integers, below) and enter the same way; the INT8 row scale multiplies
+//     the finished row sum, the INT4 group scale multiplies each 32-column
+//     partial (the reference weight is exactly q*s: "membound", section "The
+//     kernel decode actually runs: dequant GEMV").  FP16 weights with FP32 x
+//     use v_fma_mix_f32; the FP16-accumulation entry point keeps binary16
+//     running sums (v_pk_fma_f16).
 //   * The 64 lane partials are combined with DPP and ds_swizzle steps; no
 //     LDS round trip and no atomics ("Making GEMV Fast", section "How does
 //     warpReduceSum work?", and the llama.cpp walkthrough's butterfly, both
@@ -150,32 +152,6 @@ __device__ __forceinline__ float chunk_f16x32(u32x4 a, u32x4 x0, u32x4 x1, float
     return acc;
 }
 
-// INT8 -> exact binary16 integer.  Flipping the sign bit turns the
-// two's-complement code q into the unsigned byte q + 128; placed under the
-// binary16 exponent of 1024 (bits 0x64xx) that byte becomes the value
-// 1024 + q + 128, exactly, since binary16 spacing in [1024, 2048) is 1.
-// Subtracting 1152 leaves q.  Two columns per 32-bit register.
-__device__ __forceinline__ float q8_word(unsigned w, unsigned x01, unsigned x23, float acc)
-{
-    const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-    w ^= 0x80808080u;
-    const unsigned b01 = (w & 0x000000FFu) | ((w << 8) & 0x00FF0000u) | 0x64006400u;
-    const unsigned b23 = ((w >> 16) & 0x000000FFu) | ((w >> 8) & 0x00FF0000u) | 0x64006400u;
-    acc = __builtin_amdgcn_fdot2(as_h2(b01) + bias, as_h2(x01), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2(b23) + bias, as_h2(x23), acc, false);
-    return acc;
-}
-
-// INT8: 16 columns; x0 holds columns 0..7, x1 columns 8..15 (binary16).
-__device__ __forceinline__ float chunk_q8(u32x4 a, u32x4 x0, u32x4 x1, float acc)
-{
-    acc = q8_word(a.x, x0.x, x0.y, acc);
-    acc = q8_word(a.y, x0.z, x0.w, acc);
-    acc = q8_word(a.z, x1.x, x1.y, acc);
-    acc = q8_word(a.w, x1.z, x1.w, acc);
-    return acc;
-}
-
 // INT4 -> exact binary16 integers.  One 32-bit word holds columns c..c+7,
 // column c+k in bits [4k, 4k+4).  XOR with 0x8 per nibble turns a
 // two's-complement code q into q + 8 in 0..15.  Masking with 0x000F000F
@@ -211,35 +187,18 @@ __device__ __forceinline__ float chunk_q4(u32x4 a, const u32x4 (&xp)[4], float s
     return __builtin_fmaf(s, __builtin_fmaf(acc_16, 0.0625f, acc_1), acc);
 }
 
-// Cheaper decode (fewer VALU instructions per weight).  The offset code
-// q + 8 (INT4) or q + 128 (INT8) is placed straight into the low mantissa
-// bits of a binary16 with a zero exponent field, i.e. read as the subnormal
-// (q + bias) * 2^-24, exact, and v_dot2_f32_f16 multiplies it by x exactly
-// (at most 4 + 11 or 8 + 11 significant bits).  The bias is removed once:
-// sum_j q_j x_j = 2^24 * sum_j ((q_j + bias) 2^-24) x_j - bias * sum_j x_j,
-// with sum_j x_j taken per 32-column chunk (INT4, whose scale changes per
-// group) or per row (INT8, whose scale is per row) when x is staged.
+// INT8 decode (offset code).  Flipping the sign bit turns the
+// two's-complement code q into the unsigned byte q + 128, which placed in
+// the low mantissa bits of a binary16 with a zero exponent field reads as the
+// subnormal (q + 128) * 2^-24, exactly; v_dot2_f32_f16 multiplies it by x
+// exactly (at most 8 + 11 significant bits).  The offset is removed once
+// per row: sum_j q_j x_j = 2^24 * sum_j ((q_j + 128) 2^-24) x_j - 128 * sum_j x_j,
+// with sum_j x_j taken while x is staged.  (INT4 keeps its exponent-bias
+// decode: the same offset form for INT4 cancels a bias of 8 per weight
+// against per-chunk sums, and v_dot2_f32_f16, which is not correctly
+// rounded, then misses the 1e-4 gate at 14336-wide rows.)
 
-// INT4 chunk, offset-code form: returns 2^-24 * sum (q + 8) x over 32 columns.
-// Column pairs (c, c+4) and (c+1, c+5) as in q4_word; the high pair sits four
-// bits up, i.e. carries an extra factor 16, removed by the final FMA.
-__device__ __forceinline__ float q4_sub_chunk(u32x4 a, const u32x4 (&xp)[4])
-{
-    float lo = 0.0f, hi = 0.0f;
-    const unsigned ws[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const unsigned w = ws[k] ^ 0x88888888u;
-        const unsigned w8 = w >> 8;
-        lo = __builtin_amdgcn_fdot2(as_h2(w & 0x000F000Fu), as_h2(xp[k].x), lo, false);
-        hi = __builtin_amdgcn_fdot2(as_h2(w & 0x00F000F0u), as_h2(xp[k].y), hi, false);
-        lo = __builtin_amdgcn_fdot2(as_h2(w8 & 0x000F000Fu), as_h2(xp[k].z), lo, false);
-        hi = __builtin_amdgcn_fdot2(as_h2(w8 & 0x00F000F0u), as_h2(xp[k].w), hi, false);
-    }
-    return __builtin_fmaf(hi, 0.0625f, lo);
-}
-
-// INT8 chunk, offset-code form: acc + 2^-24 * sum (q + 128) x over 16
+// INT8 chunk: acc + 2^-24 * sum (q + 128) x over 16
 // columns.  A byte permute places bytes 0,1 (and 2,3) of the XOR-ed word
 // under zero high bytes, giving the subnormal pairs (c, c+1) that match x's
 // natural pairs.
@@ -315,60 +274,50 @@ __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds
     }
 }
 
-// Staging for the offset-code decode: thread t stages whole chunks
-// t, t + NT, ... and also records, per chunk, 8 * sum of its 32 x values
-// (INT4, in lds_f[chunk]) or accumulates the sum of all x (INT8: one partial
-// per wave in lds_f[wave]).  Sums use v_dot2_f32_f16 against (1, 1): FP32
-// accumulation of exact binary16 values.
-template <int F, int WAVES>
+// Staging for the INT8 decode: thread t stages whole chunks t, t + NT, ...
+// and accumulates the sum of all x (one partial per wave in lds_f[wave]).
+// Sums use v_dot2_f32_f16 against (1, 1): FP32 accumulation of exact
+// binary16 values.
+template <int WAVES>
 __device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4* lds, float* lds_f, int nchunks,
                                              int nchunks_pad)
 {
     constexpr int NT = WAVES * 64;
-    constexpr int G = Traits<F>::kXGran;
+    constexpr int G = Traits<kQ8>::kXGran;
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     float part = 0.0f;
     for (int c = threadIdx.x; c < nchunks_pad; c += NT) {
-        if (c >= nchunks) {          // whole-pass padding: zero x, zero sums
+        if (c >= nchunks) {          // whole-pass padding: zero x
 #pragma unroll
             for (int k = 0; k < G; ++k)
                 lds[c * G + k] = u32x4{0u, 0u, 0u, 0u};
-            if constexpr (F == kQ4)
-                lds_f[c] = 0.0f;
             continue;
         }
         u32x4 v[G];
 #pragma unroll
         for (int k = 0; k < G; ++k)
             v[k] = xg[c * G + k];
-        float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < G; ++k) {
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].x), ones, sum, false);
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].y), ones, sum, false);
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].z), ones, sum, false);
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].w), ones, sum, false);
-            lds[c * G + k] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+            part = __builtin_amdgcn_fdot2(as_h2(v[k].x), ones, part, false);
+            part = __builtin_amdgcn_fdot2(as_h2(v[k].y), ones, part, false);
+            part = __builtin_amdgcn_fdot2(as_h2(v[k].z), ones, part, false);
+            part = __builtin_amdgcn_fdot2(as_h2(v[k].w), ones, part, false);
+            lds[c * G + k] = v[k];
         }
-        if constexpr (F == kQ4)
-            lds_f[c] = 8.0f * sum;
-        else
-            part += sum;
     }
-    if constexpr (F == kQ8) {
-        const float w = wave_sum(part);
-        if ((threadIdx.x & 63) == 0)
-            lds_f[threadIdx.x >> 6] = w;
-    }
+    const float w = wave_sum(part);
+    if ((threadIdx.x & 63) == 0)
+        lds_f[threadIdx.x >> 6] = w;
 }
 
 // One thread's part of stage_x_sums when a single chunk per thread covers x:
 // v holds chunk c's granules (zero past the row end).
-template <int F, int WAVES>
-__device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<F>::kXGran], int c, u32x4* lds, float* lds_f,
-                                                 int nchunks_pad)
+template <int WAVES>
+__device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<kQ8>::kXGran], int c, u32x4* lds,
+                                                 float* lds_f, int nchunks_pad)
 {
-    constexpr int G = Traits<F>::kXGran;
+    constexpr int G = Traits<kQ8>::kXGran;
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     float sum = 0.0f;
     if (c < nchunks_pad) {
@@ -378,22 +327,18 @@ __device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<F>::kXG
             sum = __builtin_amdgcn_fdot2(as_h2(v[k].y), ones, sum, false);
             sum = __builtin_amdgcn_fdot2(as_h2(v[k].z), ones, sum, false);
             sum = __builtin_amdgcn_fdot2(as_h2(v[k].w), ones, sum, false);
-            lds[c * G + k] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
+            lds[c * G + k] = v[k];
         }
-        if constexpr (F == kQ4)
-            lds_f[c] = 8.0f * sum;
     }
-    if constexpr (F == kQ8) {
-        const float w = wave_sum(sum);
-        if ((threadIdx.x & 63) == 0)
-            lds_f[threadIdx.x >> 6] = w;
-    }
+    const float w = wave_sum(sum);
+    if ((threadIdx.x & 63) == 0)
+        lds_f[threadIdx.x >> 6] = w;
 }
 
 // ---------------------------------------------------------------- streaming kernel
 // Preconditions (checked by the host): N is a multiple of Traits<F>::kElems,
 // A and x are 16-byte aligned, M >= 1, and the launch provides
-// stream_lds_bytes<F, XG, DEC>(N) bytes of dynamic LDS.
+// 4 * stream_lds_words<F, XG>(N / Traits<F>::kElems) bytes of dynamic LDS.
 //
 // Each wave owns the rows wave_id, wave_id + nwaves, ... and walks them as
 // one linear sequence of units; a unit is one pass over a row (one 16-byte
@@ -408,20 +353,16 @@ __device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<F>::kXG
 // a multiple of D; padded units re-read the wave's last row and are never
 // stored.
 //
-//   XG  x granules are loaded from global memory with each
-//       unit instead of being staged in LDS (no staging, no barrier).
-//   DEC (INT8/INT4 only): 0 = exponent-bias decode (q8_word / q4_word),
-//       1 = offset-code decode (q8_sub_chunk / q4_sub_chunk) with the bias
-//       term from sums of x taken while staging.
-template <int F, bool XG, int DEC>
+//   XG  (unquantised A only) x granules are loaded from global memory with
+//       each unit instead of being staged in LDS (no staging, no barrier).
+//       INT8 and INT4 always stage x: INT8 also needs the sum of x for its
+//       offset-code decode, and INT4 reads four granules per unit.
+template <int F, bool XG>
 __host__ __device__ constexpr int stream_lds_words(int nchunks)
 {
     // 16-byte granules of x for whole passes (zero past the row end), then
-    // (offset-code INT4) one float per chunk, or (offset-code INT8) one float
-    // per wave for the sum of x.
-    return XG ? 0
-              : ((nchunks + 63) / 64) * 64 * Traits<F>::kXGran * 4 +
-                    (DEC == 1 ? (F == kQ4 ? ((nchunks + 63) / 64) * 64 : 16) : 0);
+    // (INT8) one float per wave (at most 16) for the partial sums of x.
+    return XG ? 0 : ((nchunks + 63) / 64) * 64 * Traits<F>::kXGran * 4 + (F == kQ8 ? 16 : 0);
 }
 
 // Buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes
@@ -445,14 +386,14 @@ __host__ __device__ constexpr int default_stage_order()
     return F == kQ4 ? 1 : 0;
 }
 
-template <int F, int WAVES, int D, bool NT, bool XG, int DEC, int STG = default_stage_order<F>()>
+template <int F, int WAVES, int D, bool NT, bool XG, int STG = default_stage_order<F>()>
 __global__ void __launch_bounds__(WAVES * 64)
 gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
     using T = Traits<F>;
-    static_assert(!XG || DEC == 0, "x from global memory: exponent-bias decode only");
-    static_assert(DEC == 0 || F == kQ8 || F == kQ4, "offset-code decode: INT8/INT4 only");
+    static_assert(!XG || (F != kQ8 && F != kQ4), "INT8 and INT4 stage x in LDS");
+    static_assert(WAVES <= 16, "the INT8 sum of x keeps one partial per wave");
     constexpr int kAux = NT ? 2 : 0;   // buffer-load cache policy: non-temporal
     constexpr int NT_ = WAVES * 64;
     constexpr int G = T::kXGran;       // x granules per unit
@@ -520,7 +461,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     // matters (see default_stage_order).
     constexpr int kRound = 8;                   // granules per thread in one staging round
     const bool split = !XG && STG == 2 &&
-                       (DEC == 1 ? P * 64 <= NT_ : nxg_pad <= kRound * NT_);
+                       (F == kQ8 ? P * 64 <= NT_ : nxg_pad <= kRound * NT_);
     bool issued = false;
     if ((XG || STG == 0) && units > 0) {
 #pragma unroll
@@ -528,10 +469,10 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             issue(d);
         issued = true;
     }
-    float xsum = 0.0f;   // offset-code INT8: sum of x over the row
+    float xsum = 0.0f;   // INT8: sum of x over the row
     if constexpr (!XG) {
         if (split) {
-            if constexpr (DEC == 1) {
+            if constexpr (F == kQ8) {
                 // one chunk (G granules) per thread: load, prologue, sum and write
                 const int c = threadIdx.x;
                 u32x4 v[G];
@@ -544,7 +485,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
                         issue(d);
                     issued = true;
                 }
-                stage_chunk_sums<F, WAVES>(v, c, lds_x, lds_f, P * 64);
+                stage_chunk_sums<WAVES>(v, c, lds_x, lds_f, P * 64);
             } else {
                 u32x4 v[kRound];
 #pragma unroll
@@ -565,13 +506,13 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
                         lds_x[staged_index<F>(g / G, g % G, P * 64)] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
                 }
             }
-        } else if constexpr (DEC == 1) {
-            stage_x_sums<F, WAVES>(xg, lds_x, lds_f, nchunks, P * 64);
+        } else if constexpr (F == kQ8) {
+            stage_x_sums<WAVES>(xg, lds_x, lds_f, nchunks, P * 64);
         } else {
             stage_x<F, NT_>(xg, lds_x, nxg, nxg_pad);
         }
         __syncthreads();
-        if constexpr (F == kQ8 && DEC == 1) {
+        if constexpr (F == kQ8) {
 #pragma unroll
             for (int w = 0; w < WAVES; ++w)
                 xsum += lds_f[w];
@@ -600,18 +541,10 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         } else if constexpr (F == kF16H) {
             acch = chunk_f16h(a, xv[0], acch);
         } else if constexpr (F == kQ8) {
-            if constexpr (DEC == 1)
-                acc = q8_sub_chunk(a, xv[0], xv[G - 1], acc);
-            else
-                acc = chunk_q8(a, xv[0], xv[G - 1], acc);
+            acc = q8_sub_chunk(a, xv[0], xv[G - 1], acc);
         } else {
             const u32x4 xp[4] = {xv[0], xv[1 % G], xv[2 % G], xv[3 % G]};
-            const float s = half_bits_to_float(sraw);
-            if constexpr (DEC == 1)
-                acc = __builtin_fmaf(s, __builtin_fmaf(q4_sub_chunk(a, xp), 16777216.0f,
-                                                       -lds_f[c_pass * 64 + lane]), acc);
-            else
-                acc = chunk_q4(a, xp, s, acc);
+            acc = chunk_q4(a, xp, half_bits_to_float(sraw), acc);
         }
         if (++c_pass == P) {
             if constexpr (F == kF16H) {
@@ -621,8 +554,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             float t = wave_sum(acc);
             if (lane == 0 && c_row < M) {
                 if constexpr (F == kQ8) {
-                    if constexpr (DEC == 1)
-                        t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);
+                    t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);   // remove the offset
                     t *= half_bits_to_float(sraw);   // this row's scale (see issue)
                 }
                 y[c_row] = t;
