@@ -291,6 +291,15 @@ DETAIL_SHAPES = [
     ("8192x8192", 8192, 8192, ("f16", "q8", "f16x32", "f16_acc16")),
     ("14336x4096", 14336, 4096, ("f16", "q8", "q4", "f16x32")),
     ("4096x14336", 4096, 14336, ("f16", "q4", "f16x32")),
+    ("4096x4096", 4096, 4096, ("f16",)),
+    # the FP32 square sweep: small-M grid fill against large-n bandwidth
+    ("1024x1024", 1024, 1024, ("f32",)),
+    ("2048x2048", 2048, 2048, ("f32",)),
+    ("4096x4096", 4096, 4096, ("f32",)),
+    ("8192x8192", 8192, 8192, ("f32",)),
+    # one GPU's share of 14336x4096 split over 8 GPUs: by rows, by columns
+    ("1792x4096", 1792, 4096, ("f16", "q8", "q4")),
+    ("14336x512", 14336, 512, ("f16", "q8", "q4")),
 ]
 
 
@@ -360,10 +369,11 @@ def detail(rounds, launches=256):
                       "same_size_probe_us": pbest[k] * 1e6,
                       "pct_of_same_size_probe": 100 * pbest[k] / best[k]}
         for k in kinds:
-            if k != "f16":
+            if k != "f16" and "f16" in kinds:
                 rec[k]["x_f16"] = best["f16"] / best[k]
                 rec[k]["x_f16_same_size_probe_ceiling"] = pbest["f16"] / pbest[k]
-        out[name] = rec
+        out.setdefault(name, {}).update(rec)
+        out[name]["probe_gbps"] = max(out[name].get("probe_gbps", 0.0), probe_best)
         for k in kinds:
             rings[k].free()
         del graphs, rings, pgraphs

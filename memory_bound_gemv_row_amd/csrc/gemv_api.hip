@@ -80,10 +80,13 @@ struct Plan {
 // 16-byte chunks is P = ceil(nchunks / 64) units (one 1-KiB wave load each).
 //   FP32/FP16 (either accumulation): x read with each unit (no staging); one
 //     row per wave, or two for very long rows; 8 units in flight when rows
-//     have at least 8 units.
-//   INT8: 4 units in flight; rows of 8 units or more: 8 waves, A first,
-//     a row per wave; shorter rows: 4 waves, x staged with split order
-//     (staging loads, A prologue, LDS writes), at most 3 workgroups per CU.
+//     have at least 8 units; rows of 1-3 units put ceil(4 / P) rows on each
+//     wave so that 4 units are in flight without padding.
+//   INT8: rows of 8 units or more: 8 waves, 4 in flight, A first, a row per
+//     wave; rows of 1-2 units: 8 waves, 2 in flight, split staging (staging
+//     loads, A prologue, LDS writes), at most 3 workgroups per CU; other
+//     short rows: 8 waves, x first, a row per wave when M <= 8 x CUs, else
+//     4 waves, split staging, at most 3 workgroups per CU.
 //   INT4: rows under 4 units: 8 waves, 2 in flight, split staging; longer
 //     rows: 4 waves, 4 in flight, x staged before A; at most 3 workgroups
 //     per CU.
@@ -115,10 +118,16 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.waves = 4;
             p.D = 4;
             p.rows = 2;
-        } else {
+        } else if (P >= 4) {
             p.waves = P >= 16 ? 8 : 4;
             p.D = P >= 8 ? 8 : 4;
             p.rows = 1;
+        } else {
+            // rows of 1-3 units: enough rows per wave for 4 units in flight
+            // (one row per wave would pad each wave's stream with re-reads)
+            p.waves = P == 1 ? 8 : 4;
+            p.D = 4;
+            p.rows = (4 + P - 1) / P;
         }
     } else if (kind == kF16X32) {
         const bool fits = lds_bytes(kind, nchunks) <= kMaxLdsBytes;
@@ -142,7 +151,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.variant = 2;
             p.waves = 4;
             p.D = P >= 8 ? 8 : 4;
-            p.rows = P >= 8 ? 2 : 1;
+            p.rows = P >= 8 ? 2 : (P >= 4 ? 1 : (4 + P - 1) / P);
         }
     } else if (kind == kQ8) {
         p.variant = 1;
@@ -151,8 +160,21 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         if (P >= 8) {
             // long rows: 8 waves, A first, one row per wave
             p.waves = 8;
+        } else if (P <= 2) {
+            // rows of at most 2 units: 8 waves, 2 in flight, split staging,
+            // at most 3 workgroups per CU (waves walk several rows)
+            p.waves = 8;
+            p.D = 2;
+            p.stg = 2;
+            p.cap = 3;
+        } else if (M <= 8 * cus) {
+            // few rows (one GPU's share of a row-split matrix): a row per
+            // wave, x staged first
+            p.waves = 8;
+            p.stg = 1;
         } else {
-            // short rows: 4 waves, split staging, at most 3 workgroups per CU
+            // short rows, many of them: 4 waves, split staging, at most 3
+            // workgroups per CU
             p.waves = 4;
             p.stg = 2;
             p.cap = 3;
