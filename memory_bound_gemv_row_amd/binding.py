@@ -144,6 +144,9 @@ def _need(t, name, dtypes, shape):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        # the C ABI launches on the current device's stream
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
     if tuple(t.shape) != tuple(shape):

@@ -101,7 +101,12 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
 {
     Plan p{};
     const int epc = elems_per_chunk(kind);
-    if (!aligned || N == 0 || N % epc != 0 || ((kind == kQ8 || kind == kQ4) && lds_bytes(kind, N / epc) > kMaxLdsBytes)) {
+    // The streaming kernel addresses a row through a 32-bit byte count (the
+    // INT8/INT4 buffer resource's range, the row stride): rows of 2 GiB or
+    // more take the element-wise kernel, which uses 64-bit offsets.
+    const bool huge_row = (int64_t)(N / epc) * 16 >= ((int64_t)1 << 31);
+    if (!aligned || N == 0 || N % epc != 0 || huge_row ||
+        ((kind == kQ8 || kind == kQ4) && lds_bytes(kind, N / epc) > kMaxLdsBytes)) {
         p.variant = 3;
         p.block = 256;
         p.waves = 4;

@@ -611,30 +611,30 @@ gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sca
     if constexpr (F == kF32) {
         const float* a = reinterpret_cast<const float*>(A) + (int64_t)row * N;
         const float* xf = reinterpret_cast<const float*>(x);
-        for (int j = lane; j < N; j += 64)
+        for (int64_t j = lane; j < N; j += 64)
             acc = __builtin_fmaf(a[j], xf[j], acc);
     } else if constexpr (F == kF16) {
         const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
         const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
-        for (int j = lane; j < N; j += 64)
+        for (int64_t j = lane; j < N; j += 64)
             acc = __builtin_fmaf(half_bits_to_float(a[j]), half_bits_to_float(xh[j]), acc);
     } else if constexpr (F == kF16X32) {
         const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
         const float* xf = reinterpret_cast<const float*>(x);
-        for (int j = lane; j < N; j += 64)
+        for (int64_t j = lane; j < N; j += 64)
             acc = __builtin_fmaf(half_bits_to_float(a[j]), xf[j], acc);
     } else if constexpr (F == kF16H) {
         // one binary16 running sum per lane (ceil(N/64) terms)
         const _Float16* a = reinterpret_cast<const _Float16*>(A) + (int64_t)row * N;
         const _Float16* xh = reinterpret_cast<const _Float16*>(x);
         _Float16 h = (_Float16)0.0f;
-        for (int j = lane; j < N; j += 64)
+        for (int64_t j = lane; j < N; j += 64)
             h = __builtin_fmaf16(a[j], xh[j], h);
         acc = (float)h;
     } else if constexpr (F == kQ8) {
         const int8_t* a = reinterpret_cast<const int8_t*>(A) + (int64_t)row * N;
         const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
-        for (int j = lane; j < N; j += 64)
+        for (int64_t j = lane; j < N; j += 64)
             acc = __builtin_fmaf((float)a[j], half_bits_to_float(xh[j]), acc);
     } else {
         const int half_n = N / 2;
