@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the CPU-baseline leg")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--rounds", type=int, default=5)
+    ap.add_argument("--op", choices=["quant_q8", "quant_q4", "softmax"],
+                    help="time (or, with --profile, launch once) the quantiser or the softmax at --M x --N "
+                         "instead of the GEMV bench line")
     ap.add_argument("--plot-roofline", metavar="BENCH_JSON",
                     help="print an ASCII roofline chart from a saved bench line and exit (no GPU needed)")
     ap.add_argument("--profile", action="store_true",
@@ -382,15 +385,7 @@ def detail(rounds, launches=256):
 
 
 # ---------------------------------------------------------------- quantiser
-def quant_bytes(kind, M, N):
-    """Algorithmic bytes of one quantiser call: FP32 weights read once; codes,
-    binary16 scales and the per-row squared error written once."""
-    if kind == "q8":
-        return 4 * M * N + M * N + 2 * M + 4 * M
-    return 4 * M * N + M * N // 2 + 2 * M * (N // 128) + 4 * M
-
-
-def quant_detail(rounds, launches=64):
+def quant_detail(rounds, launches=64, shapes=None):
     """The weight quantiser (FP32 -> INT8 / INT4 + per-row squared error) on
     the INT8/INT4 GEMV shapes.  Each slot of a >= 1 GiB ring holds a copy of
     the weights and its own outputs (codes, scales, row errors), so that
@@ -405,13 +400,13 @@ def quant_detail(rounds, launches=64):
     import numpy as np
     import torch
 
-    from memory_bound_gemv_row_amd import binding, inputs
+    from memory_bound_gemv_row_amd import accounting, binding, inputs
 
     def up(n):
         return -(-n // 256) * 256
 
     out = {}
-    for kind, M, N in inputs.QUANT_WORKLOADS:
+    for kind, M, N in (shapes or inputs.QUANT_WORKLOADS):
         wbytes = 4 * M * N
         qbytes = M * N if kind == "q8" else M * N // 2
         sbytes = 2 * M if kind == "q8" else 2 * M * (N // 128)
@@ -423,7 +418,7 @@ def quant_detail(rounds, launches=64):
         for c in range(copies):
             ring[c, :wbytes].copy_(W)
         del W
-        nbytes = quant_bytes(kind, M, N)
+        nbytes = accounting.quant_bytes(kind, M, N)
         half = nbytes // 2 // 16 * 16             # a copy of this many bytes moves nbytes in total
         cdst = torch.empty((copies, up(half)), dtype=torch.uint8, device="cuda")
         fn = binding.quantize_q8_ptr if kind == "q8" else binding.quantize_q4_ptr
@@ -471,7 +466,7 @@ def quant_detail(rounds, launches=64):
 
 
 # ---------------------------------------------------------------- softmax
-def softmax_detail(rounds, launches=32):
+def softmax_detail(rounds, launches=32, shapes=None):
     """Row softmax on the "membound" softmax shapes (binary16 in and out):
     (x, y) slot pairs rotate through >= 1 GiB, launches captured in a HIP
     graph, best of `rounds`.  The ceiling is the streaming-copy probe moving
@@ -483,7 +478,7 @@ def softmax_detail(rounds, launches=32):
     from memory_bound_gemv_row_amd import binding, inputs
 
     out = {}
-    for M, N in inputs.SOFTMAX_WORKLOADS:
+    for M, N in (shapes or inputs.SOFTMAX_WORKLOADS):
         nbytes = 2 * M * N
         slots = max(1, -(-RING_BYTES // (2 * nbytes)))
         x = torch.from_numpy(inputs.make_logits(M, N, seed=0)).cuda()
@@ -625,6 +620,49 @@ def ascii_roofline(study, width=72, height=22):
     return "\n".join(lines)
 
 
+# ---------------------------------------------------------------- quantiser / softmax on their own
+def op_main(args):
+    """--op: the quantiser or the softmax at one shape.  With --profile: one
+    cold launch after a >= 1 GiB flush read, then the calibration probes
+    (1 GiB read, 256 MiB copy), for counter collection; otherwise the timed
+    record of quant_detail / softmax_detail for that shape."""
+    import torch
+
+    from memory_bound_gemv_row_amd import binding, inputs
+
+    M, N = args.M, args.N
+    if not args.profile:
+        if args.op == "softmax":
+            rec = softmax_detail(args.rounds, shapes=[(M, N)])
+        else:
+            rec = quant_detail(args.rounds, shapes=[(args.op[-2:], M, N)])
+        print(json.dumps({"op": args.op, "M": M, "N": N, "record": rec}), flush=True)
+        return
+    flush = torch.empty(RING_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    if args.op == "softmax":
+        x = torch.from_numpy(inputs.make_logits(M, N, seed=0)).cuda()
+        y = torch.empty_like(x)
+        launch = lambda: binding.softmax_f16_ptr(x.data_ptr(), y.data_ptr(), M, N, sh)
+    else:
+        W = torch.from_numpy(inputs.make_weights(M, N, seed=0)).cuda()
+        q8 = args.op == "quant_q8"
+        q = torch.empty((M, N if q8 else N // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(M if q8 else M * (N // 128), dtype=torch.float16, device="cuda")
+        e = torch.empty(M, dtype=torch.float32, device="cuda")
+        fn = binding.quantize_q8_ptr if q8 else binding.quantize_q4_ptr
+        launch = lambda: fn(W.data_ptr(), q.data_ptr(), sc.data_ptr(), e.data_ptr(), M, N, sh)
+    torch.cuda.synchronize()
+    binding.probe_read_ptr(flush.data_ptr(), RING_BYTES, sink.data_ptr(), 0xA5A5A5A5, sh)
+    if launch() != 0:
+        raise RuntimeError(f"{args.op} launch failed")
+    binding.probe_read_ptr(flush.data_ptr(), RING_BYTES, sink.data_ptr(), 0xA5A5A5A5, sh)
+    binding.probe_copy_ptr(flush.data_ptr(), flush.data_ptr() + (512 << 20), 256 << 20, sh)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": f"{args.op}_{M}x{N}", "launches": 1}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 def main():
     args = parse()
@@ -651,6 +689,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.load()
+    if args.op:
+        return op_main(args)
     kind, M, N = args.kind, args.M, args.N
     ops = inputs.make(kind, M, N, seed=0)
     ring = Ring(kind, M, N, ops)

@@ -60,6 +60,22 @@ def ratio(t_ref: float, t_other: float) -> float:
     return t_ref / t_other
 
 
+def quant_bytes(kind: str, M: int, N: int) -> int:
+    """Algorithmic bytes of one quantiser call: FP32 weights read once; codes,
+    binary16 scales and the per-row squared error (FP32) written once."""
+    if kind == "q8":
+        return 4 * M * N + M * N + 2 * M + 4 * M
+    if kind == "q4":
+        return 4 * M * N + M * N // 2 + 2 * M * (N // 128) + 4 * M
+    raise ValueError(kind)
+
+
+def softmax_bytes(M: int, N: int) -> int:
+    """One read and one write of every binary16 element ("membound", online
+    softmax section: a balanced stream)."""
+    return 4 * M * N
+
+
 def ring_copies(kind: str, M: int, N: int, min_bytes: int = 1 << 30) -> int:
     """Weight copies needed so that a rotation streams >= min_bytes."""
     wb = weight_bytes(kind, M, N)

@@ -23,13 +23,20 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ("memory_bound_gemv_row_amd/csrc/gemv_kernels.hpp", "memory_bound_gemv_row_amd/csrc/gemv_api.hip")
+OP_SOURCES = {
+    "gemv": KERNEL_SOURCES,
+    "quant": ("memory_bound_gemv_row_amd/csrc/quant_kernels.hpp", "memory_bound_gemv_row_amd/csrc/quant_api.hip"),
+    "softmax": ("memory_bound_gemv_row_amd/csrc/softmax_kernels.hpp", "memory_bound_gemv_row_amd/csrc/softmax_api.hip"),
+}
 PROBE_READ_BYTES = 1 << 30
 PROBE_COPY_BYTES = 256 << 20
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(op: str = "gemv") -> str:
+    """Hash of the sources of one operation's kernels (the GEMV by default):
+    a traffic summary is valid only for the sources it was taken on."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in OP_SOURCES[op]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -48,16 +55,21 @@ def _counter(rows, name, kernel_substr):
     return vals
 
 
-def traffic(fetch_csv, write_csv):
-    """Per-launch HBM bytes of the GEMV kernel, with the calibration used."""
+# kernel-name substring of each profiled operation's kernels
+KERNEL_MATCH = {"gemv": "gemv_", "quant": "quantize_", "softmax": "softmax_f16"}
+
+
+def traffic(fetch_csv, write_csv, match="gemv_"):
+    """Per-launch HBM bytes of the profiled kernel (the GEMV unless `match`
+    names another), with the calibration used."""
     fr, wr = _rows(fetch_csv), _rows(write_csv)
     probe_fetch_kib = max(_counter(fr, "FETCH_SIZE", "probe_read_kernel"))
     copy_write_kib = _counter(wr, "WRITE_SIZE", "probe_copy_kernel")[0]
     fetch_factor = PROBE_READ_BYTES / (probe_fetch_kib * 1024)
     write_factor = PROBE_COPY_BYTES / (copy_write_kib * 1024)
-    g_fetch = _counter(fr, "FETCH_SIZE", "gemv_")
-    g_write = _counter(wr, "WRITE_SIZE", "gemv_")
-    kname = next(r["Kernel_Name"] for r in fr if "gemv_" in r["Kernel_Name"] and r["Counter_Name"] == "FETCH_SIZE")
+    g_fetch = _counter(fr, "FETCH_SIZE", match)
+    g_write = _counter(wr, "WRITE_SIZE", match)
+    kname = next(r["Kernel_Name"] for r in fr if match in r["Kernel_Name"] and r["Counter_Name"] == "FETCH_SIZE")
     fetch_b = sum(g_fetch) / len(g_fetch) * 1024 * fetch_factor
     write_b = sum(g_write) / len(g_write) * 1024 * write_factor
     return {"kernel": kname, "fetch_kib_raw": sum(g_fetch) / len(g_fetch), "write_kib_raw": sum(g_write) / len(g_write),
@@ -67,22 +79,34 @@ def traffic(fetch_csv, write_csv):
 
 
 def write_traffic_summary(fetch_csv, write_csv, workload, out, fetch_cmd, write_cmd):
+    """workload: '<kind>_<M>x<N>' for a GEMV kind, 'quant_q8_<M>x<N>',
+    'quant_q4_<M>x<N>' or 'softmax_<M>x<N>'."""
     from memory_bound_gemv_row_amd import accounting
 
-    t = traffic(fetch_csv, write_csv)
-    kind, shape = workload.split("_")
+    name, shape = workload.rsplit("_", 1)
     M, N = (int(v) for v in shape.split("x"))
-    alg = accounting.alg_bytes(kind, M, N)
+    if name.startswith("quant_"):
+        op = "quant"
+        t = traffic(fetch_csv, write_csv, KERNEL_MATCH[op])
+        alg, what = accounting.quant_bytes(name[-2:], M, N), "quantiser"
+    elif name == "softmax":
+        op = "softmax"
+        t = traffic(fetch_csv, write_csv, KERNEL_MATCH[op])
+        alg, what = accounting.softmax_bytes(M, N), "softmax"
+    else:
+        op = "gemv"
+        t = traffic(fetch_csv, write_csv)
+        alg, what = accounting.alg_bytes(name, M, N), "GEMV"
     lines = [
-        f"# HBM traffic of one {workload} GEMV launch (rocprofv3 counters)",
+        f"# HBM traffic of one {workload} {what} launch (rocprofv3 counters)",
         f"fetch command: {fetch_cmd}",
         f"write command: {write_cmd}",
         f"kernel: {t['kernel']}",
-        f"kernel_source_hash: {kernel_source_hash()}",
+        f"kernel_source_hash: {kernel_source_hash(op)}",
         f"probe_read 1 GiB FETCH_SIZE raw KiB: {t['probe_fetch_kib_raw']:.1f} -> fetch factor {t['fetch_factor']:.4f}",
         f"probe_copy 256 MiB WRITE_SIZE raw KiB: {t['copy_write_kib_raw']:.1f} -> write factor {t['write_factor']:.4f}",
-        f"gemv FETCH_SIZE raw KiB: {t['fetch_kib_raw']:.3f} -> {t['fetch_bytes']:.0f} bytes",
-        f"gemv WRITE_SIZE raw KiB: {t['write_kib_raw']:.3f} -> {t['write_bytes']:.0f} bytes",
+        f"kernel FETCH_SIZE raw KiB: {t['fetch_kib_raw']:.3f} -> {t['fetch_bytes']:.0f} bytes",
+        f"kernel WRITE_SIZE raw KiB: {t['write_kib_raw']:.3f} -> {t['write_bytes']:.0f} bytes",
         f"bytes_per_launch: {t['bytes_per_launch']:.0f}",
         f"algorithmic_bytes: {alg}",
         f"traffic / algorithmic: {t['bytes_per_launch'] / alg:.4f}",
