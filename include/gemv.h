@@ -143,16 +143,18 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
 
 /* Launch geometry the library uses for a call.  kind: 0 f32, 1 f16, 2 q8,
  * 3 q4, 4 f16x32 (FP16 A, FP32 x), 5 f16_acc16 (FP16 accumulation).
- * `aligned` states whether A and x are
- * 16-byte aligned.  Fills `info` with the variant (1 = streaming kernel with x staged in LDS,
- * 2 = streaming kernel with x read from global memory, 3 = element-wise
- * kernel), grid and workgroup sizes, rows per wave (at most), 1-KiB loads
+ * `aligned` states whether A and x are 16-byte aligned.  Fills `info` with
+ * the variant (1 = streaming kernel with x staged in LDS, 2 = streaming
+ * kernel with x read from global memory, 3 = element-wise kernel, 4 = packed
+ * kernel for INT8/INT4 rows of at most 32 16-byte chunks, several rows per
+ * wave load), grid and workgroup sizes, rows per wave (at most), 1-KiB loads
  * in flight per wave, dynamic LDS bytes, and the order in which x is staged
  * relative to the first loads of A.  The geometry is chosen per shape:
- * workgroups of 4 or 8 waves, 2 to 8 loads in flight, 1 to 4 rows per wave
- * (the llama.cpp walkthrough's implementation note: the original kernel
- * selects its block size at run time).  Returns GEMV_OK or an error code; it
- * queries the current device's compute-unit count and launches nothing. */
+ * workgroups of 4 or 8 waves, 1 to 8 loads in flight, 1 to 4 rows (packed:
+ * row groups) per wave (the llama.cpp walkthrough's implementation note: the
+ * original kernel selects its block size at run time).  Returns GEMV_OK or an
+ * error code; it queries the current device's compute-unit count and
+ * launches nothing. */
 typedef struct gemv_launch_info {
     int variant;
     int grid;
@@ -160,7 +162,7 @@ typedef struct gemv_launch_info {
     int rows_per_wave;
     int units_in_flight;
     int lds_bytes;
-    int stage_order;   /* variant 1: 0 A first, 1 x first, 2 x loads / A / x writes; else -1 */
+    int stage_order;   /* variants 1, 4: 0 A first, 1 x first, 2 x loads / A / x writes; else -1 */
 } gemv_launch_info;
 
 int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info);

@@ -64,12 +64,24 @@ int lds_bytes(int kind, int nchunks)
     }
 }
 
+// Packed short rows: INT8/INT4 rows of at most this many chunks share wave
+// loads; 64 / L rows per load, L the power of two at or above the chunk count.
+constexpr int kPackedMaxChunks = 32;
+
+int packed_rows_per_load(int nchunks) { return 64 / packed_lanes<kQ8>(nchunks); }
+
+int packed_lds(int kind, int nchunks)
+{
+    return 4 * (kind == kQ8 ? packed_lds_words<kQ8>(nchunks) : packed_lds_words<kQ4>(nchunks));
+}
+
 struct Plan {
-    int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise
+    int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise,
+                   // 4 packed short rows (INT8/INT4)
     int grid;
     int block;
     int waves;     // per workgroup
-    int rows;      // rows per wave (upper bound)
+    int rows;      // rows per wave (upper bound); variant 4: row groups per wave
     int D;         // units in flight per wave
     int lds;
     int stg;       // order of A prologue and x staging (default_stage_order)
@@ -90,6 +102,10 @@ struct Plan {
 //   INT4: rows under 4 units: 8 waves, 2 in flight, split staging; longer
 //     rows: 4 waves, 4 in flight, x staged before A; at most 3 workgroups
 //     per CU.
+//   INT8/INT4 rows of at most 32 chunks (half a wave load): the packed
+//     kernel, 64 / L rows per wave load, 8 waves; with up to 16 row groups
+//     per CU one group per wave, up to 32 two (both in flight), beyond that
+//     four, two in flight.
 //   FP16 with FP32 x: x is twice the bytes of FP16 x, and reading it with
 //     every unit costs more cache bandwidth than staging it, once the staging
 //     (4N bytes per workgroup) is spread over enough rows: staged for rows of
@@ -103,9 +119,12 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
     const int epc = elems_per_chunk(kind);
     // The streaming kernel addresses a row through a 32-bit byte count (the
     // INT8/INT4 buffer resource's range, the row stride): rows of 2 GiB or
-    // more take the element-wise kernel, which uses 64-bit offsets.
+    // more take the element-wise kernel, which uses 64-bit offsets.  Its row
+    // cursors (and the packed kernel's group cursors) run up to about twice
+    // M in int: more than 2^30 rows also take the element-wise kernel.
     const bool huge_row = (int64_t)(N / epc) * 16 >= ((int64_t)1 << 31);
-    if (!aligned || N == 0 || N % epc != 0 || huge_row ||
+    const bool huge_m = M > (1 << 30);
+    if (!aligned || N == 0 || N % epc != 0 || huge_row || huge_m ||
         ((kind == kQ8 || kind == kQ4) && lds_bytes(kind, N / epc) > kMaxLdsBytes)) {
         p.variant = 3;
         p.block = 256;
@@ -117,6 +136,21 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
     }
     const int nchunks = N / epc;
     const int P = (nchunks + 63) / 64;
+    if ((kind == kQ8 || kind == kQ4) && nchunks <= kPackedMaxChunks) {
+        const int R = packed_rows_per_load(nchunks);
+        const int64_t groups = ((int64_t)M + R - 1) / R;
+        const int64_t per_cu = (groups + cus - 1) / cus;
+        p.variant = 4;
+        p.waves = 8;
+        p.D = per_cu <= 16 ? 1 : 2;
+        p.rows = per_cu <= 32 ? p.D : 4;
+        p.stg = 1;
+        p.lds = packed_lds(kind, nchunks);
+        p.block = p.waves * 64;
+        const int64_t waves_needed = (groups + p.rows - 1) / p.rows;
+        p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
+        return p;
+    }
     if (kind == kF32 || kind == kF16 || kind == kF16H) {
         p.variant = 2;
         if (P >= 24) {            // very long rows: two per wave, fewer in flight each
@@ -204,6 +238,13 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
     return p;
 }
 
+template <int F>
+const void* select_packed(const Plan& p)
+{
+    return p.D == 1 ? reinterpret_cast<const void*>(&gemv_packed<F, 8, 1>)
+                    : reinterpret_cast<const void*>(&gemv_packed<F, 8, 2>);
+}
+
 template <int F, int W, int D, bool XG, int STG>
 const void* stream_kernel()
 {
@@ -237,6 +278,10 @@ const void* select_kernel(const Plan& p)
 {
     if (p.variant == 3)
         return reinterpret_cast<const void*>(&gemv_elementwise<F>);
+    if constexpr (F == kQ8 || F == kQ4) {
+        if (p.variant == 4)
+            return select_packed<F>(p);
+    }
     if constexpr (F == kF16X32)
         return p.variant == 2 ? select_stream<F, true>(p) : select_stream<F, false>(p);
     else
@@ -403,10 +448,17 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
     info->grid = p.grid;
     info->block = p.block;
     const int64_t waves = (int64_t)p.grid * p.waves;
-    info->rows_per_wave = waves > 0 ? (int)(((int64_t)M + waves - 1) / waves) : 0;
+    if (p.variant == 4) {
+        // row groups of 64 / L rows, walked grid-stride by the waves
+        const int64_t R = gemv::packed_rows_per_load(N / gemv::elems_per_chunk(kind));
+        const int64_t groups = ((int64_t)M + R - 1) / R;
+        info->rows_per_wave = waves > 0 ? (int)((groups + waves - 1) / waves * R) : 0;
+    } else {
+        info->rows_per_wave = waves > 0 ? (int)(((int64_t)M + waves - 1) / waves) : 0;
+    }
     info->units_in_flight = p.D;
     info->lds_bytes = p.lds;
-    info->stage_order = p.variant == 1 ? p.stg : -1;
+    info->stage_order = (p.variant == 1 || p.variant == 4) ? p.stg : -1;
     return GEMV_OK;
 }
 

@@ -594,6 +594,151 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         consume(d);
 }
 
+// ---------------------------------------------------------------- packed short rows (INT8/INT4)
+// Rows shorter than half a wave load (at most 32 chunks): a wave load takes
+// R = 64 / L rows at once, L = the power of two >= the chunk count, and
+// lane l works on chunk l % L of row g * R + l / L of row group g.  A lane's
+// chunk, and so its x, is the same in every group: x is staged once and kept
+// in registers.  Each group's partial sums meet in a segmented butterfly of
+// L lanes.  Groups stream D ahead as in gemv_stream.
+//
+// Preconditions (checked by the host): F is kQ8 or kQ4, 1 <= N / kElems <= 32,
+// A and x 16-byte aligned, 1 <= M <= 2^30 (row and group indices stay in
+// int), and 4 * packed_lds_words<F>(N / kElems) bytes of dynamic LDS.
+template <int F>
+__host__ __device__ constexpr int packed_lanes(int nchunks)
+{
+    int L = 1;
+    while (L < nchunks)
+        L <<= 1;
+    return L;
+}
+
+template <int F>
+__host__ __device__ constexpr int packed_lds_words(int nchunks)
+{
+    return packed_lanes<F>(nchunks) * Traits<F>::kXGran * 4 + (F == kQ8 ? 16 : 0);
+}
+
+// Sum over aligned groups of L lanes (L a power of two, at most 32); the
+// result is valid in every lane of the group.
+__device__ __forceinline__ float segment_sum(float v, int L)
+{
+    if (L >= 2)
+        v += dpp_mov<0xB1>(v);   // lane ^ 1
+    if (L >= 4)
+        v += dpp_mov<0x4E>(v);   // lane ^ 2
+    if (L >= 8)
+        v += dpp_mov<0x141>(v);  // other quad of the 8-lane half row
+    if (L >= 16)
+        v += dpp_mov<0x140>(v);  // other half of the 16-lane row
+    if (L >= 32)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    return v;
+}
+
+template <int F, int WAVES, int D>
+__global__ void __launch_bounds__(WAVES * 64)
+gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
+            const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
+{
+    static_assert(F == kQ8 || F == kQ4, "packed short rows: INT8/INT4 only");
+    using T = Traits<F>;
+    constexpr int G = T::kXGran;
+    constexpr int NT_ = WAVES * 64;
+    extern __shared__ u32x4 lds_x[];
+    const int lane = threadIdx.x & 63;
+    const int nchunks = N / T::kElems;
+    const int L = packed_lanes<F>(nchunks);
+    const int R = 64 / L;
+    const int sub = lane / L;                    // row within the group
+    const int c = lane & (L - 1);                // this lane's chunk
+    const uint32_t row_bytes = (uint32_t)nchunks * 16;
+    const int sgroups = N / 128;                 // INT4 scales per row
+    const int groups = (M + R - 1) / R;
+    const int wave_id = blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = gridDim.x * WAVES;
+    const int mine = wave_id < groups ? (groups - 1 - wave_id) / nwaves + 1 : 0;
+    const int mine_pad = (mine + D - 1) / D * D;
+    const int last = wave_id + (mine - 1) * nwaves;
+    const u32x4* xg = reinterpret_cast<const u32x4*>(x);
+    float* lds_f = reinterpret_cast<float*>(lds_x + L * G);
+
+    float xsum = 0.0f;   // INT8: sum of x over the row
+    if constexpr (F == kQ8)
+        stage_x_sums<WAVES>(xg, lds_x, lds_f, nchunks, L);
+    else
+        stage_x<F, NT_>(xg, lds_x, nchunks * G, L * G);
+    __syncthreads();
+    if constexpr (F == kQ8) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w)
+            xsum += lds_f[w];
+    }
+    if (mine == 0)
+        return;
+    u32x4 xv[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+        xv[k] = lds_x[c * G + k];
+
+    // One resource per row group (wave-uniform, so the loads need no
+    // per-lane descriptors) covering the group's rows below M; a lane's
+    // offset selects its row and chunk.  Lanes past the row end get an
+    // offset beyond every range and so read zeros, as do rows past M.
+    constexpr uint32_t kOutside = 0x7FFFFFF0u;
+    const bool live = c < nchunks;
+    const uint32_t a_off = live ? (uint32_t)sub * row_bytes + (uint32_t)c * 16 : kOutside;
+    const uint32_t s_off = live ? (uint32_t)(F == kQ4 ? sub * sgroups + (c >> 2) : sub) * 2 : kOutside;
+    u32x4 buf[D];
+    uint16_t sbuf[D];
+    int l_g = wave_id;
+    auto issue = [&](int d) {
+        const int g = l_g <= last ? l_g : last;
+        const int r0 = g * R;
+        const uint32_t nrows = (uint32_t)(M - r0 < R ? M - r0 : R);
+        const auto rsrc = make_rsrc(A + (int64_t)r0 * row_bytes, nrows * row_bytes);
+        buf[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, a_off, 0, 2));
+        const uint32_t srow = F == kQ4 ? (uint32_t)sgroups : 1u;
+        const auto srsrc = make_rsrc(scale + (int64_t)r0 * srow, nrows * srow * 2);
+        sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, s_off, 0, 0);
+        l_g += nwaves;
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        issue(d);
+
+    int c_g = wave_id;
+    auto consume = [&](int d) {
+        float acc;
+        if constexpr (F == kQ4) {
+            acc = chunk_q4(buf[d], xv, half_bits_to_float(sbuf[d]), 0.0f);
+        } else {
+            acc = q8_sub_chunk(buf[d], xv[0], xv[G - 1], 0.0f);
+        }
+        float t = segment_sum(acc, L);
+        if (c == 0 && c_g <= last && c_g * R + sub < M) {
+            const int row = c_g * R + sub;
+            if constexpr (F == kQ8) {
+                t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);   // remove the offset
+                t *= half_bits_to_float(sbuf[d]);
+            }
+            y[row] = t;
+        }
+        c_g += nwaves;
+    };
+    for (int k0 = D; k0 < mine_pad; k0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            consume(d);
+            issue(d);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        consume(d);
+}
+
 // ---------------------------------------------------------------- element-wise kernel
 // Any N >= 0 and any alignment: one wave per row, lane l takes columns
 // l, l+64, ... with scalar loads (INT4: bytes l, l+64, ..., two columns

@@ -141,6 +141,11 @@ def test_describe_launch_fills_all_cus(gpu):
         info = binding.describe_launch(kind, M, N)
         assert info["grid"] >= cus, (kind, M, N, info, cus)
     assert binding.describe_launch("f16", 8, 1001)["variant"] == 3
+    # INT8/INT4 rows of at most 32 chunks: the packed short-row kernel
+    assert binding.describe_launch("q8", 14336, 512)["variant"] == 4
+    assert binding.describe_launch("q4", 14336, 1024)["variant"] == 4
+    assert binding.describe_launch("q8", 14336, 528)["variant"] == 1
+    assert binding.describe_launch("q4", 14336, 1152)["variant"] == 1
     # FP16 A with FP32 x: x staged in LDS for long rows or many rows, read
     # with each unit otherwise, and never staged beyond the LDS budget
     assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 1

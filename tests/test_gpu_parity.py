@@ -45,11 +45,14 @@ _NS = {
     # multiples of the chunk width (bandwidth path) and ragged ones (element-wise)
     "f32": [1, 3, 4, 8, 60, 64, 252, 256, 260, 1020, 1024, 2052, 4100, 9000, 17000],
     "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 8200, 14336, 20000],
-    "q8": [1, 15, 16, 32, 1008, 1024, 1040, 5000, 8192, 9232, 20000],
+    # 16..512 (1-32 chunks) take the packed short-row kernel, 528 is the
+    # first streaming width
+    "q8": [1, 15, 16, 32, 48, 272, 512, 528, 1008, 1024, 1040, 5000, 8192, 9232, 20000],
     # 5632 | 6144 straddle the staged-x threshold, 16392 is just past the LDS budget
     "f16x32": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 5632, 6144, 8200, 14336, 16384, 16392, 20000],
     "f16_acc16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 8200, 14336, 20000],
-    "q4": [128, 256, 384, 1024, 2048, 2176, 4096, 7296, 14336],
+    # up to 1024 (32 chunks) packed; 640 and 896 fill 20 and 28 of 32 lanes
+    "q4": [128, 256, 384, 640, 896, 1024, 1152, 2048, 2176, 4096, 7296, 14336],
 }
 
 
@@ -81,6 +84,31 @@ def test_waves_walk_several_rows(gpu, oracle_mod, kind, N):
     assert info["rows_per_wave"] >= 3, info
     ops = inputs.make(kind, M, N, seed=11)
     _check(oracle_mod, kind, ops, f"{kind} multi-row M={M} N={N} {info}")
+
+
+@pytest.mark.parametrize("kind,N", [("q8", 16), ("q8", 48), ("q8", 272), ("q8", 512),
+                                    ("q4", 128), ("q4", 384), ("q4", 640), ("q4", 1024)])
+def test_packed_short_rows_many_groups(gpu, oracle_mod, kind, N):
+    # rows of at most 32 chunks share wave loads: enough rows for every wave
+    # of a full grid, and a last group only partly filled
+    M = 14336 + 3
+    info = binding.describe_launch(kind, M, N)
+    assert info["variant"] == 4, info
+    ops = inputs.make(kind, M, N, seed=N)
+    _check(oracle_mod, kind, ops, f"{kind} packed M={M} N={N} {info}")
+
+
+@pytest.mark.parametrize("kind,N,M", [("q8", 512, 40000 + 1), ("q4", 1024, 40000 + 1), ("q4", 128, 140000 + 5),
+                                      ("q8", 16, 600000 + 7)])
+def test_packed_waves_walk_several_groups(gpu, oracle_mod, kind, N, M):
+    # more than 32 row groups per CU: each wave walks four groups with two
+    # loads in flight (the steady-state loop), the last groups ragged
+    nchunks = N // (16 if kind == "q8" else 32)
+    R = 64 // (1 << (nchunks - 1).bit_length())
+    info = binding.describe_launch(kind, M, N)
+    assert info["variant"] == 4 and info["units_in_flight"] == 2 and info["rows_per_wave"] == 4 * R, info
+    ops = inputs.make(kind, M, N, seed=M)
+    _check(oracle_mod, kind, ops, f"{kind} packed multi-group M={M} N={N} {info}")
 
 
 # ---------------------------------------------------------------- exactness
