@@ -284,6 +284,80 @@ def test_extreme_int_values_and_identity(gpu, oracle_mod, kind):
     assert np.array_equal(y.astype(np.float64), run_oracle(oracle_mod, kind, ops))
 
 
+def _finite_rows_close(ops, kind, y, ref, rows):
+    from gpu_util import abs_products
+
+    bound = 1e-5 * abs_products(ops, kind)[rows] + 1e-30
+    return np.all(np.abs(y[rows].astype(np.float64) - ref[rows]) <= bound)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "f16x32"])
+def test_special_values_follow_ieee(gpu, oracle_mod, kind):
+    # NaN and infinities in A or x give exactly the definition's NaN / +-inf
+    # per row (IEEE products and sums, in any order); other rows unaffected
+    rng = np.random.default_rng(9)
+    M, N = 8, 1024
+    A = rng.uniform(-1, 1, (M, N))
+    A[A == 0] = 0.5
+    x = rng.uniform(0.25, 1, N)
+    x[300] = 0.0
+    A[1, 100] = np.nan                        # NaN
+    A[2, 100] = np.inf                        # +inf
+    A[3, 100], A[3, 200] = np.inf, -np.inf    # +inf - inf = NaN
+    A[4, 100] = -np.inf                       # -inf
+    A[5, 300] = np.inf                        # inf * 0 = NaN
+    adt = np.float32 if kind == "f32" else np.float16
+    xdt = np.float16 if kind == "f16" else np.float32
+    cases = [("A special", {"A": A.astype(adt), "x": x.astype(xdt)}, [0, 6, 7])]
+    x2 = x.copy()
+    x2[400] = np.inf
+    A2 = rng.uniform(-1, 1, (M, N))
+    A2[A2 == 0] = 0.5
+    A2[6, 400] = 0.0                          # 0 * inf = NaN; other rows +-inf
+    cases.append(("x special", {"A": A2.astype(adt), "x": x2.astype(xdt)}, []))
+    for label, ops, finite in cases:
+        say(f"[special values] {kind} {label}")
+        y = run_gpu(kind, ops)
+        ref = run_oracle(oracle_mod, kind, ops)
+        assert np.array_equal(np.isnan(y), np.isnan(ref)), (label, y, ref)
+        inf = np.isinf(ref)
+        assert np.array_equal(y[inf].astype(np.float64), ref[inf]), (label, y, ref)
+        assert np.array_equal(np.isfinite(y), np.isfinite(ref)), (label, y, ref)
+        assert _finite_rows_close(ops, kind, y, ref, finite), (label, y, ref)
+
+
+@pytest.mark.parametrize("kind,N", [("q8", 256), ("q8", 1024), ("q4", 512), ("q4", 2048)])
+def test_quantised_special_values_are_not_finite(gpu, oracle_mod, kind, N):
+    # The INT kernels factor scales out of FP32 partials, and INT8 removes a
+    # 128 * sum(x) offset, so a non-finite scale or x gives a non-finite row,
+    # though not always the definition's own choice between NaN and inf
+    # (an infinite x entry meets the offset as inf - inf); a NaN always
+    # stays NaN, and rows without special values are unaffected.
+    M = 8
+    ops = inputs.make(kind, M, N, seed=N)
+    if kind == "q8":
+        ops["scale"][2] = np.inf
+        ops["scale"][3] = np.nan
+    else:
+        ops["scale"][2, 1] = np.inf
+        ops["scale"][3, 0] = np.nan
+    say(f"[special scales] {kind} N={N}")
+    y = run_gpu(kind, ops)
+    ref = run_oracle(oracle_mod, kind, ops)
+    assert not np.isfinite(y[2]) and not np.isfinite(ref[2])
+    assert np.isnan(y[3]) and np.isnan(ref[3])
+    rows = [0, 1, 4, 5, 6, 7]
+    assert np.all(np.isfinite(y[rows])) and _finite_rows_close(ops, kind, y, ref, rows)
+    for v, want_nan in ((np.inf, False), (np.nan, True)):
+        ops = inputs.make(kind, M, N, seed=N + 1)
+        ops["x"][10] = v
+        say(f"[special x] {kind} N={N} x={v}")
+        y = run_gpu(kind, ops)
+        assert not np.any(np.isfinite(y)), y
+        if want_nan:
+            assert np.all(np.isnan(y)) and np.all(np.isnan(run_oracle(oracle_mod, kind, ops)))
+
+
 def test_nan_propagates(gpu, oracle_mod):
     A = np.ones((8, 1024), np.float32)
     A[3, 100] = np.nan
