@@ -129,7 +129,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.variant = 3;
         p.block = 256;
         p.waves = 4;
-        p.grid = (M + 3) / 4;
+        p.grid = (int)(((int64_t)M + 3) / 4);
         p.rows = 1;
         p.D = 1;
         return p;

@@ -749,7 +749,7 @@ gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sca
                  const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M)
         return;   // whole wave leaves together
     float acc = 0.0f;

@@ -72,9 +72,12 @@ int gemv_quantize_q8(const float* W, int8_t* q, uint16_t* scale, float* row_sse,
     int cus = 0;
     if (int rc = cu_count(&cus); rc != GEMV_OK)
         return rc;
-    if (N == 0 || N % 4 != 0 || !aligned(W, 16) || !aligned(q, 4))
-        return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<127>), (M + 3) / 4, 256, W, q,
-                      scale, row_sse, M, N, stream);
+    // more than 2^30 rows: the row-walking kernels' int row cursors could
+    // pass INT_MAX; the element-wise kernel indexes rows in 64 bits
+    const int grid4 = (int)(((int64_t)M + 3) / 4);
+    if (N == 0 || N % 4 != 0 || !aligned(W, 16) || !aligned(q, 4) || M > (1 << 30))
+        return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<127>), grid4, 256, W, q, scale,
+                      row_sse, M, N, stream);
     // a workgroup of 4 waves per row; units per wave sized so that rows up
     // to 64 units (N <= 16384) stay in registers
     const int P = (N / 4 + 63) / 64;
@@ -97,13 +100,14 @@ int gemv_quantize_q4(const float* W, uint8_t* q, uint16_t* scale, float* row_sse
     if (int rc = cu_count(&cus); rc != GEMV_OK)
         return rc;
     (void)cus;
-    if (N == 0 || !aligned(W, 16) || !aligned(q, 2))
-        return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<7>), (M + 3) / 4, 256, W, q,
-                      scale, row_sse, M, N, stream);
+    const int grid4 = (int)(((int64_t)M + 3) / 4);
+    if (N == 0 || !aligned(W, 16) || !aligned(q, 2) || M > (1 << 30))   // as for INT8
+        return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<7>), grid4, 256, W, q, scale,
+                      row_sse, M, N, stream);
     // one wave per row, 4 waves per workgroup, 4 units in flight per wave
     const void* fn = row_sse != nullptr ? reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, true>)
                                         : reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, false>);
-    return launch(fn, (M + 3) / 4, 256, W, q, scale, row_sse, M, N, stream);
+    return launch(fn, grid4, 256, W, q, scale, row_sse, M, N, stream);
 }
 
 }  // extern "C"

@@ -309,7 +309,7 @@ quantize_elementwise_kernel(const float* __restrict__ W, uint8_t* __restrict__ q
                             float* __restrict__ row_sse, int M, int N)
 {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M)
         return;   // whole wave leaves together
     const float* w = W + (int64_t)row * N;

@@ -72,9 +72,12 @@ extern "C" int gemv_softmax_f16(const uint16_t* x, uint16_t* y, int M, int N, hi
         return rc;
     void* args[] = {(void*)&x, (void*)&y, (void*)&M, (void*)&N};
     hipError_t err;
-    if (N % 8 != 0 || !aligned16(x) || !aligned16(y)) {
-        err = hipLaunchKernel(reinterpret_cast<const void*>(&softmax_f16_elementwise), dim3((M + 3) / 4), dim3(256),
-                              args, 0, stream);
+    // more than 2^30 rows: the row-per-workgroup kernel's int row cursor
+    // could pass INT_MAX; the element-wise kernel indexes rows in 64 bits
+    if (N % 8 != 0 || !aligned16(x) || !aligned16(y) || M > (1 << 30)) {
+        const unsigned grid4 = (unsigned)(((int64_t)M + 3) / 4);
+        err = hipLaunchKernel(reinterpret_cast<const void*>(&softmax_f16_elementwise), dim3(grid4), dim3(256), args,
+                              0, stream);
     } else {
         int waves = 4, upw = 4;
         geometry((N / 8 + 63) / 64, &waves, &upw);

@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(256)
 softmax_f16_elementwise(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int N)
 {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M)
         return;   // whole wave leaves together
     const _Float16* src = reinterpret_cast<const _Float16*>(x) + (int64_t)row * N;

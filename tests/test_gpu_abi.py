@@ -146,6 +146,11 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("q4", 14336, 1024)["variant"] == 4
     assert binding.describe_launch("q8", 14336, 528)["variant"] == 1
     assert binding.describe_launch("q4", 14336, 1152)["variant"] == 1
+    # more than 2^30 rows: the row-walking kernels' int cursors could wrap,
+    # so the element-wise kernel (64-bit row indices) takes the call
+    for kind in ("f16", "q8", "q4"):
+        assert binding.describe_launch(kind, (1 << 30) + 1, 128)["variant"] == 3
+        assert binding.describe_launch(kind, 1 << 30, 128)["variant"] != 3
     # FP16 A with FP32 x: x staged in LDS for long rows or many rows, read
     # with each unit otherwise, and never staged beyond the LDS budget
     assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 1
