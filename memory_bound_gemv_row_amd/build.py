@@ -30,6 +30,7 @@ HIPCC_FLAGS = [
     "-shared",
     "-Wall",
     "-Wextra",
+    "-Werror",          # host and device warnings fail the build
     # no packed FP32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
