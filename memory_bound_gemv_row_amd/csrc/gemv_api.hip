@@ -94,14 +94,19 @@ struct Plan {
 //     row per wave, or two for very long rows; 8 units in flight when rows
 //     have at least 8 units; rows of 1-3 units put ceil(4 / P) rows on each
 //     wave so that 4 units are in flight without padding.
-//   INT8: rows of 8 units or more: 8 waves, 4 in flight, A first, a row per
-//     wave; rows of 1-2 units: 8 waves, 2 in flight, split staging (staging
-//     loads, A prologue, LDS writes), at most 3 workgroups per CU; other
-//     short rows: 8 waves, x first, a row per wave when M <= 8 x CUs, else
-//     4 waves, split staging, at most 3 workgroups per CU.
-//   INT4: rows under 4 units: 8 waves, 2 in flight, split staging; longer
-//     rows: 4 waves, 4 in flight, x staged before A; at most 3 workgroups
-//     per CU.
+//   INT8: few rows (M <= 16 x CUs for rows of 1-2 units, M <= 8 x CUs for
+//     rows up to 16 units): x read with each unit, 8 waves, 2 (short rows)
+//     or 4 in flight -- the staging and its barrier would dominate such
+//     launches.  Otherwise x is staged: rows of 8 units or more: 8 waves, 4
+//     in flight, A first, a row per wave; rows of 1-2 units: 8 waves, 2 in
+//     flight, split staging (staging loads, A prologue, LDS writes), at most
+//     3 workgroups per CU; other short rows: 8 waves, x first, a row per
+//     wave when M <= 8 x CUs, else 4 waves, split staging, at most 3
+//     workgroups per CU.
+//   INT4: few rows of 1 unit (M <= 8 x CUs) or 2 units (M <= 16 x CUs): x
+//     read with each unit, 8 waves, 2 in flight.  Otherwise staged: rows
+//     under 4 units: 8 waves, 2 in flight, split staging; longer rows: 4
+//     waves, 4 in flight, x staged before A; at most 3 workgroups per CU.
 //   INT8/INT4 rows of at most 32 chunks (half a wave load): the packed
 //     kernel, 64 / L rows per wave load, 8 waves; with up to 16 row groups
 //     per CU one group per wave, up to 32 two (both in flight), beyond that
@@ -196,7 +201,18 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.variant = 1;
         p.D = 4;
         p.rows = 1;
-        if (P >= 8) {
+        if (P <= 2 && M <= 16 * cus) {
+            // few short rows: x read with each unit (no staging, no
+            // barrier), 8 waves, 2 in flight
+            p.variant = 2;
+            p.waves = 8;
+            p.D = 2;
+        } else if (P <= 16 && M <= 8 * cus) {
+            // few rows (one GPU's share of a row-split matrix): x read with
+            // each unit, 8 waves, 4 in flight
+            p.variant = 2;
+            p.waves = 8;
+        } else if (P >= 8) {
             // long rows: 8 waves, A first, one row per wave
             p.waves = 8;
         } else if (P <= 2) {
@@ -218,6 +234,13 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.stg = 2;
             p.cap = 3;
         }
+    } else if ((P == 1 && M <= 8 * cus) || (P == 2 && M <= 16 * cus)) {
+        // INT4, few rows of one or two units: x read with each unit, 8 waves,
+        // 2 in flight
+        p.variant = 2;
+        p.waves = 8;
+        p.D = 2;
+        p.rows = 1;
     } else {
         // short INT4 rows: 8 waves, 2 units in flight, split staging;
         // longer rows: 4 waves, 4 units, x staged before A
@@ -272,7 +295,7 @@ const void* select_stream(const Plan& p)
 }
 
 // Variant 1 stages x in LDS, variant 2 reads it with each unit; FP32 and
-// FP16 always take variant 2, INT8 and INT4 variant 1.
+// FP16 always take variant 2.
 template <int F>
 const void* select_kernel(const Plan& p)
 {
@@ -282,10 +305,10 @@ const void* select_kernel(const Plan& p)
         if (p.variant == 4)
             return select_packed<F>(p);
     }
-    if constexpr (F == kF16X32)
-        return p.variant == 2 ? select_stream<F, true>(p) : select_stream<F, false>(p);
+    if constexpr (F == kF32 || F == kF16 || F == kF16H)
+        return select_stream<F, true>(p);
     else
-        return select_stream<F, F == kF32 || F == kF16 || F == kF16H>(p);
+        return p.variant == 2 ? select_stream<F, true>(p) : select_stream<F, false>(p);
 }
 
 const void* kernel_for(int kind, const Plan& p)

@@ -218,6 +218,18 @@ __device__ __forceinline__ float q8_sub_chunk(u32x4 a, u32x4 x0, u32x4 x1, float
     return acc;
 }
 
+// acc + the sum of the 16 binary16 x values of two granules (v_dot2_f32_f16
+// against (1, 1): FP32 accumulation of exact binary16 values).
+__device__ __forceinline__ float x_sum_chunk(u32x4 x0, u32x4 x1, float acc)
+{
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const unsigned xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        acc = __builtin_amdgcn_fdot2(as_h2(xs[k]), ones, acc, false);
+    return acc;
+}
+
 // Reorder one 8-column block of binary16 x from (x0..x7) to
 // (x0,x4), (x1,x5), (x2,x6), (x3,x7), the pairing q4_word expects.
 __device__ __forceinline__ u32x4 q4_pair_x(u32x4 v)
@@ -345,18 +357,19 @@ __device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<kQ8>::k
 // chunk per lane, 1 KiB per wave).  Loads run D units ahead of the
 // arithmetic in straight-line code, so the wait before each unit only needs
 // the oldest of D outstanding loads.  The first D loads are issued at
-// kernel start (INT4: right after x is staged).  A ragged last pass
-// (fewer than 64 chunks) contributes exactly zero in the lanes past the row
-// end: with global loads (unquantised A) those lanes load chunk 0 and zero it
-// before use; with buffer loads (INT8/INT4) the row-sized resource returns
-// zeros and meets zero-padded x.  The unit count is padded to
-// a multiple of D; padded units re-read the wave's last row and are never
-// stored.
+// kernel start (INT4: right after x is staged).  In a ragged last pass
+// (fewer than 64 chunks) the lanes past the row end contribute nothing,
+// whatever A or x hold (no 0 * inf = NaN from them): FP32/FP16 load chunk 0
+// with plain global loads and discard its products; the other formats read A
+// through a buffer resource of exactly one row's bytes, which returns zeros
+// there, against zero x (zero-padded in LDS, or read through a resource of
+// exactly x's bytes).  The unit count is padded to a multiple of D; padded
+// units re-read the wave's last row and are never stored.
 //
-//   XG  (unquantised A only) x granules are loaded from global memory with
-//       each unit instead of being staged in LDS (no staging, no barrier).
-//       INT8 and INT4 always stage x: INT8 also needs the sum of x for its
-//       offset-code decode, and INT4 reads four granules per unit.
+//   XG  x granules are loaded with each unit (through L1/L2) instead of
+//       being staged in LDS: no staging and no barrier, at the cost of
+//       G x loads per A load.  INT8 then sums x per lane as it goes, for
+//       the offset-code decode's row correction.
 template <int F, bool XG>
 __host__ __device__ constexpr int stream_lds_words(int nchunks)
 {
@@ -392,7 +405,6 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
     using T = Traits<F>;
-    static_assert(!XG || (F != kQ8 && F != kQ4), "INT8 and INT4 stage x in LDS");
     static_assert(WAVES <= 16, "the INT8 sum of x keeps one partial per wave");
     constexpr int kAux = NT ? 2 : 0;   // buffer-load cache policy: non-temporal
     constexpr int NT_ = WAVES * 64;
@@ -415,32 +427,39 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     float* lds_f = reinterpret_cast<float*>(lds_x + nxg_pad);
 
     // A unit's loads: the row's resource (wave-uniform), the pass offset
-    // (wave-uniform) and the lane's fixed offset.
+    // (wave-uniform) and the lane's fixed offset.  The whole offset goes in
+    // the VGPR operand, which is what the range check covers (the SGPR
+    // offset stays 0), so lanes past the row end read zeros.
     const int lane_off = lane * 16;
     constexpr int XGR = XG ? G : 1;   // x granules per unit held in registers
+    const auto xrsrc = make_rsrc(x, (uint32_t)nxg * 16);   // XG: zeros past x's end
+    // FP32/FP16 read A and x with plain global loads (measured faster for
+    // them than buffer loads); the others use buffer loads throughout
+    constexpr bool kGlobal = XG && (F == kF32 || F == kF16 || F == kF16H);
     u32x4 buf[D];
     u32x4 xbuf[XG ? D : 1][XGR];
     uint16_t sbuf[D];
     int l_row = wave_id, l_pass = 0;
     auto issue = [&](int d) {
         const int row = l_row <= last_row ? l_row : last_row;
-        const int c = l_pass * 64 + lane;
-        if constexpr (XG) {
-            // FP32/FP16: plain global loads; a lane past the row end loads
-            // chunk 0 of the row, which consume() replaces by zero.
+        if constexpr (kGlobal) {
+            // a lane past the row end loads chunk 0 of A and of x and
+            // discards its products (see consume)
+            const int c = l_pass * 64 + lane;
             const int cc = c < nchunks ? c : 0;
             buf[d] = load16<NT>(reinterpret_cast<const u32x4*>(A + (int64_t)row * row_bytes) + cc);
-#pragma unroll
-            for (int k = 0; k < XGR; ++k)
-                xbuf[d][k] = xg[cc * XGR + k];
+            xbuf[d][0] = xg[cc];
         } else {
-            // INT8/INT4: buffer loads through a resource of exactly the row's
-            // bytes.  The whole offset goes in the VGPR operand, which is what
-            // the range check covers (the SGPR offset stays 0), so lanes past
-            // the row end read zeros.
             const int voff = lane_off + l_pass * 1024;
             const auto rsrc = make_rsrc(A + (int64_t)row * row_bytes, row_bytes);
             buf[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, kAux));
+            if constexpr (XG) {
+                // granules c*G .. c*G+G-1 of x for chunk c = pass*64 + lane
+#pragma unroll
+                for (int k = 0; k < XGR; ++k)
+                    xbuf[d][k] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, voff * XGR + k * 16, 0, 0));
+            }
         }
         if constexpr (F == kQ4) {
             const auto srsrc = make_rsrc(scale + (int64_t)row * groups, (uint32_t)groups * 2);
@@ -527,11 +546,12 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     }
 
     float acc = 0.0f;
+    float xs = 0.0f;                                   // INT8 with XG: this lane's sum of x
     f16x2 acch = {(_Float16)0.0f, (_Float16)0.0f};   // FP16 accumulation only
     int c_row = wave_id, c_pass = 0;
     // One unit of arithmetic: a = the unit's 16 bytes of A per lane, xv = its
     // x granules in staged layout (INT4: pair-reordered).
-    auto compute = [&](u32x4 a, const u32x4 (&xv)[G], uint16_t sraw) {
+    auto accumulate = [&](u32x4 a, const u32x4 (&xv)[G], uint16_t sraw) {
         if constexpr (F == kF32) {
             acc = chunk_f32(a, xv[0], acc);
         } else if constexpr (F == kF16) {
@@ -542,16 +562,25 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             acch = chunk_f16h(a, xv[0], acch);
         } else if constexpr (F == kQ8) {
             acc = q8_sub_chunk(a, xv[0], xv[G - 1], acc);
+            if constexpr (XG)
+                xs = x_sum_chunk(xv[0], xv[G - 1], xs);
         } else {
             const u32x4 xp[4] = {xv[0], xv[1 % G], xv[2 % G], xv[3 % G]};
             acc = chunk_q4(a, xp, half_bits_to_float(sraw), acc);
         }
+    };
+    // Count the unit; at a row's last unit reduce and store.
+    auto finish_unit = [&](uint16_t sraw) {
         if (++c_pass == P) {
             if constexpr (F == kF16H) {
                 acc = (float)acch.x + (float)acch.y;
                 acch = f16x2{(_Float16)0.0f, (_Float16)0.0f};
             }
             float t = wave_sum(acc);
+            if constexpr (F == kQ8 && XG) {
+                xsum = wave_sum(xs);
+                xs = 0.0f;
+            }
             if (lane == 0 && c_row < M) {
                 if constexpr (F == kQ8) {
                     t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);   // remove the offset
@@ -566,11 +595,9 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     };
     auto consume = [&](int d) {
         const int cc = c_pass * 64 + lane;       // < P * 64: staged (possibly zero) x
-        u32x4 a = buf[d];
+        const u32x4 a = buf[d];
         u32x4 xv[G];
         if constexpr (XG) {
-            if (cc >= nchunks)                   // past the row end: chunk 0 was loaded
-                a = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int k = 0; k < G; ++k)
                 xv[k] = (F == kQ4) ? q4_pair_x(xbuf[d][k % XGR]) : xbuf[d][k % XGR];
@@ -579,7 +606,20 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             for (int k = 0; k < G; ++k)
                 xv[k] = lds_x[staged_index<F>(cc, k, P * 64)];
         }
-        compute(a, xv, sbuf[d]);
+        if constexpr (kGlobal) {
+            // past the row end: keep the sums as they were (one select,
+            // cheaper than zeroing A or x)
+            const float acc0 = acc;
+            const f16x2 acch0 = acch;
+            accumulate(a, xv, sbuf[d]);
+            if (cc >= nchunks) {
+                acc = acc0;
+                acch = acch0;
+            }
+        } else {
+            accumulate(a, xv, sbuf[d]);
+        }
+        finish_unit(sbuf[d]);
     };
 
     for (int k0 = D; k0 < units_pad; k0 += D) {

@@ -86,6 +86,20 @@ def test_waves_walk_several_rows(gpu, oracle_mod, kind, N):
     _check(oracle_mod, kind, ops, f"{kind} multi-row M={M} N={N} {info}")
 
 
+@pytest.mark.parametrize("kind,N", [("q8", 1024), ("q8", 2048), ("q8", 4096), ("q8", 8192 + 16),
+                                    ("q4", 2048), ("q4", 4096)])
+def test_quantised_x_read_per_unit_and_staged(gpu, oracle_mod, kind, N):
+    # INT8/INT4 read x with each unit for few rows and stage it in LDS for
+    # many: both plans at the same row length, each with a ragged last
+    # workgroup
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for M, variant in ((8 * cus - 5, 2), (16 * cus + 5, 1)):
+        info = binding.describe_launch(kind, M, N)
+        assert info["variant"] == variant, (M, info)
+        ops = inputs.make(kind, M, N, seed=M + N)
+        _check(oracle_mod, kind, ops, f"{kind} M={M} N={N} {info}")
+
+
 @pytest.mark.parametrize("kind,N", [("q8", 16), ("q8", 48), ("q8", 272), ("q8", 512),
                                     ("q4", 128), ("q4", 384), ("q4", 640), ("q4", 1024)])
 def test_packed_short_rows_many_groups(gpu, oracle_mod, kind, N):
@@ -315,6 +329,14 @@ def test_special_values_follow_ieee(gpu, oracle_mod, kind):
     A2[A2 == 0] = 0.5
     A2[6, 400] = 0.0                          # 0 * inf = NaN; other rows +-inf
     cases.append(("x special", {"A": A2.astype(adt), "x": x2.astype(xdt)}, []))
+    # a ragged last pass (N = 1000): the lanes past the row end must add
+    # nothing, not 0 * x[0] = NaN when x[0] is infinite
+    Nr = 1000
+    A3 = rng.uniform(0.25, 1, (M, Nr))
+    A3[1::2, 0] *= -1
+    x3 = rng.uniform(-1, 1, Nr)
+    x3[0] = np.inf
+    cases.append(("ragged, x[0] = inf", {"A": A3.astype(adt), "x": x3.astype(xdt)}, []))
     for label, ops, finite in cases:
         say(f"[special values] {kind} {label}")
         y = run_gpu(kind, ops)
