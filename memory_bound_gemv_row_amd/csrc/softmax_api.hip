@@ -33,26 +33,37 @@ int cu_count(int* out)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Waves per row and units held per wave, so that a row of P units stays in
-// registers up to 256 units (131072 columns) with at most 64 VGPRs of data.
-void geometry(int P, int* waves, int* upw)
+// Geometry for rows of P units: waves per row and units held per wave, so
+// that a row stays in registers up to 256 units (131072 columns) with at
+// most 64 VGPRs of data; workgroups per CU; and whether a workgroup loads its
+// next row while it stores the current one.  The prefetch and the deeper
+// grids for 4-wave rows were measured (graph-timed, rotating buffers):
+// 8192 x 8192 47.4 -> 46.3 us, 4096 x 32768 98.2 -> 94.0, 16384 x 4096
+// 61.7 -> 57.7; with 16 units per wave (rows over 64 units) the prefetch
+// was slower (2048 x 65536 98.9 -> 109.4) and stays off.
+struct Geometry {
+    int waves, upw, per_cu;
+    bool prefetch;
+};
+
+Geometry geometry(int P)
 {
-    if (P <= 16) { *waves = 4; *upw = 4; }
-    else if (P <= 32) { *waves = 4; *upw = 8; }
-    else if (P <= 64) { *waves = 8; *upw = 8; }
-    else if (P <= 128) { *waves = 8; *upw = 16; }
-    else { *waves = 16; *upw = 16; }
+    if (P <= 16) return {4, 4, 16, true};
+    if (P <= 32) return {4, 8, 16, true};
+    if (P <= 64) return {8, 8, 3, true};
+    if (P <= 128) return {8, 16, kWavesPerCu / 8, false};
+    return {16, 16, kWavesPerCu / 16, false};
 }
 
-const void* kernel_for(int waves, int upw)
+const void* kernel_for(const Geometry& g)
 {
-    if (waves == 4)
-        return upw == 4 ? reinterpret_cast<const void*>(&softmax_f16_kernel<4, 4>)
-                        : reinterpret_cast<const void*>(&softmax_f16_kernel<4, 8>);
-    if (waves == 8)
-        return upw == 8 ? reinterpret_cast<const void*>(&softmax_f16_kernel<8, 8>)
-                        : reinterpret_cast<const void*>(&softmax_f16_kernel<8, 16>);
-    return reinterpret_cast<const void*>(&softmax_f16_kernel<16, 16>);
+    if (g.waves == 4)
+        return g.upw == 4 ? reinterpret_cast<const void*>(&softmax_f16_kernel<4, 4, true>)
+                          : reinterpret_cast<const void*>(&softmax_f16_kernel<4, 8, true>);
+    if (g.waves == 8)
+        return g.upw == 8 ? reinterpret_cast<const void*>(&softmax_f16_kernel<8, 8, true>)
+                          : reinterpret_cast<const void*>(&softmax_f16_kernel<8, 16, false>);
+    return reinterpret_cast<const void*>(&softmax_f16_kernel<16, 16, false>);
 }
 
 }  // namespace
@@ -79,11 +90,9 @@ extern "C" int gemv_softmax_f16(const uint16_t* x, uint16_t* y, int M, int N, hi
         err = hipLaunchKernel(reinterpret_cast<const void*>(&softmax_f16_elementwise), dim3(grid4), dim3(256), args,
                               0, stream);
     } else {
-        int waves = 4, upw = 4;
-        geometry((N / 8 + 63) / 64, &waves, &upw);
-        const int per_cu = kWavesPerCu / waves;
-        const int grid = M < cus * per_cu ? M : cus * per_cu;
-        err = hipLaunchKernel(kernel_for(waves, upw), dim3(grid), dim3(waves * 64), args, 0, stream);
+        const Geometry g = geometry((N / 8 + 63) / 64);
+        const int grid = M < cus * g.per_cu ? M : cus * g.per_cu;
+        err = hipLaunchKernel(kernel_for(g), dim3(grid), dim3(g.waves * 64), args, 0, stream);
     }
     return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
 }

@@ -129,8 +129,11 @@ __device__ __forceinline__ u32x4 normalise8(u32x4 v, float m, float l2d)
 
 // Preconditions (host): N % 8 == 0, N >= 8, x and y 16-byte aligned, M >= 1.
 // One workgroup per row (grid-stride over rows); unit u of a row (64 chunks)
-// belongs to wave u % W.
-template <int W, int UPW>
+// belongs to wave u % W.  With PF, a workgroup whose row fits its registers
+// loads its next row's units while it normalises and stores the current one
+// (each register is reloaded right after its unit is stored), so the loads
+// of the next row overlap the stores of this one.
+template <int W, int UPW, bool PF>
 __global__ void __launch_bounds__(W * 64)
 softmax_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int N)
 {
@@ -142,22 +145,24 @@ softmax_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int
     const int P = (nchunks + 63) >> 6;
     constexpr int kSeg = W * UPW;
     const bool resident = P <= kSeg;
+    u32x4 buf[UPW];
+    auto load_unit = [&](const u32x4* src, int seg, int k) {
+        const int c = (seg + k * W + wave) * 64 + lane;
+        buf[k] = c < nchunks ? __builtin_nontemporal_load(src + c)
+                             : u32x4{kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair};
+    };
+    bool preloaded = false;   // this row's units already in buf (PF)
 
     for (int row = blockIdx.x; row < M; row += gridDim.x) {
         const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)row * N);
         u32x4* dst = reinterpret_cast<u32x4*>(y + (int64_t)row * N);
-        u32x4 buf[UPW];
-        auto load_seg = [&](int seg) {
-#pragma unroll
-            for (int k = 0; k < UPW; ++k) {
-                const int c = (seg + k * W + wave) * 64 + lane;
-                buf[k] = c < nchunks ? __builtin_nontemporal_load(src + c)
-                                     : u32x4{kNegInfPair, kNegInfPair, kNegInfPair, kNegInfPair};
-            }
-        };
         float m = -__builtin_inff(), d = 0.0f;
         for (int seg = 0; seg < P; seg += kSeg) {
-            load_seg(seg);
+            if (!preloaded) {
+#pragma unroll
+                for (int k = 0; k < UPW; ++k)
+                    load_unit(src, seg, k);
+            }
 #pragma unroll
             for (int k = 0; k < UPW; ++k)
                 sweep8(buf[k], m, d);
@@ -174,16 +179,25 @@ softmax_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int
         for (int w = 1; w < W; ++w)
             merge(m, d, red_m[w], red_d[w]);
         const float l2d = log2_hw(d);
+        const int next = row + gridDim.x;
+        const bool pf = PF && resident && next < M;
+        const u32x4* nsrc = reinterpret_cast<const u32x4*>(x + (int64_t)(pf ? next : row) * N);
         for (int seg = 0; seg < P; seg += kSeg) {
-            if (!resident)
-                load_seg(seg);
+            if (!resident) {
+#pragma unroll
+                for (int k = 0; k < UPW; ++k)
+                    load_unit(src, seg, k);
+            }
 #pragma unroll
             for (int k = 0; k < UPW; ++k) {
                 const int c = (seg + k * W + wave) * 64 + lane;
                 if (c < nchunks)
                     __builtin_nontemporal_store(normalise8(buf[k], m, l2d), dst + c);
+                if (pf)
+                    load_unit(nsrc, 0, k);
             }
         }
+        preloaded = pf;
         __syncthreads();   // the next row rewrites red_m / red_d
     }
 }

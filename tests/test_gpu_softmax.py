@@ -49,6 +49,22 @@ def test_shapes_and_tails(gpu, oracle_mod):
             _check(oracle_mod, x, f"M={M} N={N}")
 
 
+@pytest.mark.parametrize("N", [2056, 8200, 24584])
+def test_workgroups_walk_several_rows(gpu, oracle_mod, N):
+    # more rows than workgroups, so each workgroup loads its next row while
+    # it stores the current one (ragged last units padded with -inf); some
+    # rows hold special values, so a prefetched row may be all -inf or NaN
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M = 16 * cus * 2 + 3 if N <= 16384 else 3 * cus * 3 + 5
+    rng = np.random.default_rng(N)
+    x = (rng.standard_normal((M, N)) * 3).astype(np.float16)
+    x[5] = -np.inf
+    x[6, 100] = np.nan
+    x[7, :N // 2] = -np.inf
+    y, _ = _check(oracle_mod, x, f"M={M} N={N} several rows per workgroup")
+    assert np.all(np.isnan(y[5])) and np.all(np.isnan(y[6])) and np.all(y[7, :N // 2] == 0)
+
+
 def test_special_values(gpu, oracle_mod):
     N = 1024
     x = np.zeros((6, N), np.float16)
