@@ -79,12 +79,31 @@ __device__ __forceinline__ float absmax4(u32x4 v)
     return fmaxf(fmaxf(fabsf(as_f(v.x)), fabsf(as_f(v.y))), fmaxf(fabsf(as_f(v.z)), fabsf(as_f(v.w))));
 }
 
-// binary16 scale of a row or group: amax / qmax (correctly rounded binary32
-// division), rounded to nearest even binary16 by v_cvt_f16_f32 (binary16
-// subnormals kept), infinity clamped to 65504.
-__device__ __forceinline__ uint16_t scale_bits(float amax, float qmax)
+// amax / qmax correctly rounded in binary32, for qmax 7 or 127 and amax >= 0,
+// in three instructions instead of a full division: with r = RN(1/qmax),
+// q = RN(amax r), the remainder e = amax - q qmax is exact in one FMA, and
+// RN(q + e r) is the correctly rounded quotient for every finite amax >= 0
+// (subnormals included) -- checked exhaustively for both constants against
+// IEEE division.  An infinite amax gives e = NaN; then q (infinite) is the
+// quotient; a NaN amax stays NaN.
+template <int QMAX>
+__device__ __forceinline__ float div_by_qmax(float amax)
 {
-    const float s = amax / qmax;
+    constexpr float kQ = (float)QMAX;
+    constexpr float kR = 1.0f / kQ;
+    const float q = amax * kR;
+    const float e = __builtin_fmaf(-q, kQ, amax);
+    const float y = __builtin_fmaf(e, kR, q);
+    return y == y ? y : q;
+}
+
+// binary16 scale of a row or group: amax / qmax (correctly rounded binary32
+// quotient), rounded to nearest even binary16 by v_cvt_f16_f32 (binary16
+// subnormals kept), infinity clamped to 65504.
+template <int QMAX>
+__device__ __forceinline__ uint16_t scale_bits(float amax)
+{
+    const float s = div_by_qmax<QMAX>(amax);
     uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)s);
     if (b == 0x7C00u)
         b = 0x7BFFu;
@@ -94,30 +113,31 @@ __device__ __forceinline__ uint16_t scale_bits(float amax, float qmax)
 __device__ __forceinline__ float half_to_float(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 // Code of one weight: the binary32 quotient w / sf rounded half to even
-// (v_rndne_f32), clipped to [-QMAX, QMAX].  inv = 1 / sf, correctly rounded
+// (v_rndne_f32), clipped to [-QMAX, QMAX].  inv = 1 / sf from v_rcp_f32
 // (once per row or group), or 0 when sf == 0.
 //
 // A correctly rounded division costs about ten VALU instructions, more than
 // the memory stream leaves per weight, so the quotient is first taken as
-// t = w * inv.  t is within 2.5 ulp of the rounded quotient (two roundings
-// of relative size 2^-24 each, plus the quotient's own half ulp), i.e.
-// within 2.5 * 2^-17 < 2^-15 for |t| < 128.  Unless t lies within 2^-15 of
-// a half-integer, every value that close rounds to the same integer as the
-// correctly rounded quotient does, so the fast result is exact; the rare
-// weights near a half-integer take the correctly rounded division.  Values
-// with |t| >= 128 clip to QMAX either way.
+// t = w * inv.  With inv within 2 ulp of 1 / sf (v_rcp_f32 is specified to
+// 1 ulp, and measured within 0.82 ulp on every binary16 value), t differs from w / sf by at most 2^-22 + 2^-24 relative, and the
+// correctly rounded quotient q from w / sf by 2^-24, so |t - q| is below
+// 1.5 * 2^-22 * 128 < 2^-13 for |t| < 128.  Unless t lies within 2^-13 of a
+// half-integer, every value that close rounds to the same integer as q
+// does, so the fast result is exact; the rare weights near a half-integer
+// take the correctly rounded division.  Values with |t| >= 128 clip to QMAX
+// either way.
 template <int QMAX>
 __device__ __forceinline__ float code_of(float w, float sf, float inv)
 {
     float t = w * inv;
     const float frac = t - __builtin_floorf(t);
-    if (__builtin_expect(__builtin_fabsf(frac - 0.5f) < 0x1p-15f, 0) && sf != 0.0f)
+    if (__builtin_expect(__builtin_fabsf(frac - 0.5f) < 0x1p-13f, 0) && sf != 0.0f)
         t = w / sf;
     const float r = __builtin_rintf(t);
     return fminf(fmaxf(r, -(float)QMAX), (float)QMAX);
 }
 
-__device__ __forceinline__ float inverse_of(float sf) { return sf != 0.0f ? 1.0f / sf : 0.0f; }
+__device__ __forceinline__ float inverse_of(float sf) { return sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f; }
 
 // (q * sf - w)^2: q * sf is exact (at most 8 + 11 significant bits), so the
 // FMA rounds only the difference.
@@ -172,7 +192,7 @@ quantize_q8_kernel(const float* __restrict__ W, int8_t* __restrict__ q, uint16_t
 #pragma unroll
         for (int w = 1; w < WAVES; ++w)
             amax = fmaxf(amax, red_max[w]);
-        const uint16_t sb = scale_bits(amax, 127.0f);
+        const uint16_t sb = scale_bits<127>(amax);
         const float sf = half_to_float(sb);
         const float inv = inverse_of(sf);
         if (threadIdx.x == 0)
@@ -261,7 +281,7 @@ quantize_q4_kernel(const float* __restrict__ W, uint8_t* __restrict__ q, uint16_
         const int c = c_pass * 64 + lane;
         const bool live = c_row < M && c < nchunks;   // padded units and lanes past the row store nothing
         const float amax = half_wave_max(absmax4(v));
-        const uint16_t sb = scale_bits(amax, 7.0f);
+        const uint16_t sb = scale_bits<7>(amax);
         const float sf = half_to_float(sb);
         const float inv = inverse_of(sf);
         const float w0 = as_f(v.x), w1 = as_f(v.y), w2 = as_f(v.z), w3 = as_f(v.w);
@@ -319,7 +339,7 @@ quantize_elementwise_kernel(const float* __restrict__ W, uint8_t* __restrict__ q
         for (int64_t j = lane; j < N; j += 64)
             amax = fmaxf(amax, fabsf(w[j]));
         amax = wave_max(amax);
-        const uint16_t sb = scale_bits(amax, 127.0f);
+        const uint16_t sb = scale_bits<127>(amax);
         const float sf = half_to_float(sb);
         const float inv = inverse_of(sf);
         if (lane == 0)
@@ -338,7 +358,7 @@ quantize_elementwise_kernel(const float* __restrict__ W, uint8_t* __restrict__ q
         for (int g = 0; g < groups; ++g) {
             const float a = w[g * 128 + 2 * lane], b = w[g * 128 + 2 * lane + 1];
             const float amax = wave_max(fmaxf(fabsf(a), fabsf(b)));
-            const uint16_t sb = scale_bits(amax, 7.0f);
+            const uint16_t sb = scale_bits<7>(amax);
             const float sf = half_to_float(sb);
             const float inv = inverse_of(sf);
             if (lane == 0)
