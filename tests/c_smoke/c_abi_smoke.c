@@ -3,7 +3,7 @@
  * the HIP runtime's C API for device memory, the library through
  * include/gemv.h, and the CPU oracle library as the reference.  Runs each
  * GEMV format, the quantiser and the softmax once on a small seeded case
- * and checks the results; exits 0 on success, 1 on a mismatch, 2 on a setup
+ * and checks the results (FP16 weights with an FP32 x included); exits 0 on success, 1 on a mismatch, 2 on a setup
  * error.  Built by __graft_entry__.build(); run by tests/test_gpu_c_smoke.py.
  */
 #include <math.h>
@@ -21,9 +21,11 @@
 /* oracle entry points (oracle/gemv_oracle.c, quant_oracle.c, softmax_oracle.c) */
 int oracle_gemv_f32(const float* A, const float* x, double* y, int64_t M, int64_t N);
 int oracle_gemv_f16(const uint16_t* A, const uint16_t* x, double* y, int64_t M, int64_t N);
+int oracle_gemv_f16x32(const uint16_t* A, const float* x, double* y, int64_t M, int64_t N);
 int oracle_gemv_q8(const int8_t* A, const uint16_t* s, const uint16_t* x, double* y, int64_t M, int64_t N);
 int oracle_gemv_q4(const uint8_t* A, const uint16_t* s, const uint16_t* x, double* y, int64_t M, int64_t N);
 int oracle_quantize_q8(const float* W, int8_t* q, uint16_t* s, double* e, int64_t M, int64_t N);
+int oracle_quantize_q4(const float* W, uint8_t* q, uint16_t* s, double* e, int64_t M, int64_t N);
 int oracle_softmax_f16(const uint16_t* x, double* y, int64_t M, int64_t N);
 uint16_t oracle_double_to_half(double v);
 double oracle_half_to_double(uint16_t h);
@@ -119,6 +121,11 @@ int main(void)
     oracle_gemv_f16(A16, x16, ref, M, N);
     ok &= check("gemv_f16", rc, floored_rel(y, ref, M), 2e-3);
 
+    rc = gemv_f16x32((const uint16_t*)dA16, (const float*)dx32, dy, M, N, 0);
+    hipMemcpy(y, dy, sizeof y, hipMemcpyDeviceToHost);
+    oracle_gemv_f16x32(A16, x32, ref, M, N);
+    ok &= check("gemv_f16x32", rc, floored_rel(y, ref, M), 1e-4);
+
     rc = gemv_q8((const int8_t*)dA8, (const uint16_t*)ds8, (const uint16_t*)dx16, dy, M, N, 0);
     hipMemcpy(y, dy, sizeof y, hipMemcpyDeviceToHost);
     oracle_gemv_q8(A8, s8, x16, ref, M, N);
@@ -143,6 +150,26 @@ int main(void)
         oracle_quantize_q8(W, oq, os, NULL, M, N);
         const int same = memcmp(q, oq, sizeof q) == 0 && memcmp(s, os, sizeof s) == 0;
         ok &= check("quantize_q8", rc, same ? 0.0 : 1.0, 0.0);
+        hipFree(dW);
+        hipFree(dq);
+        hipFree(ds);
+    }
+
+    /* INT4 quantiser: codes and group scales bit for bit */
+    {
+        static uint8_t q[M * N / 2], oq[M * N / 2];
+        static uint16_t s[M * (N / 128)], os[M * (N / 128)];
+        void* dW = dev_copy(W, sizeof W);
+        void *dq = NULL, *ds = NULL;
+        hipMalloc(&dq, sizeof q);
+        hipMalloc(&ds, sizeof s);
+        rc = gemv_quantize_q4((const float*)dW, (uint8_t*)dq, (uint16_t*)ds, NULL, M, N, 0);
+        hipMemcpy(q, dq, sizeof q, hipMemcpyDeviceToHost);
+        hipMemcpy(s, ds, sizeof s, hipMemcpyDeviceToHost);
+        memset(oq, 0, sizeof oq);
+        oracle_quantize_q4(W, oq, os, NULL, M, N);
+        const int same = memcmp(q, oq, sizeof q) == 0 && memcmp(s, os, sizeof s) == 0;
+        ok &= check("quantize_q4", rc, same ? 0.0 : 1.0, 0.0);
         hipFree(dW);
         hipFree(dq);
         hipFree(ds);
