@@ -162,7 +162,7 @@ typedef struct gemv_launch_info {
     int rows_per_wave;
     int units_in_flight;
     int lds_bytes;
-    int stage_order;   /* variants 1, 4: 0 A first, 1 x first, 2 x loads / A / x writes; else -1 */
+    int stage_order;   /* variant 1: 0 A first, 1 x first, 2 x loads / A / x writes; else -1 */
 } gemv_launch_info;
 
 int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info);

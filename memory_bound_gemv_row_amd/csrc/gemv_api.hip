@@ -70,11 +70,6 @@ constexpr int kPackedMaxChunks = 32;
 
 int packed_rows_per_load(int nchunks) { return 64 / packed_lanes<kQ8>(nchunks); }
 
-int packed_lds(int kind, int nchunks)
-{
-    return 4 * (kind == kQ8 ? packed_lds_words<kQ8>(nchunks) : packed_lds_words<kQ4>(nchunks));
-}
-
 struct Plan {
     int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise,
                    // 4 packed short rows (INT8/INT4)
@@ -149,8 +144,8 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.waves = 8;
         p.D = per_cu <= 16 ? 1 : 2;
         p.rows = per_cu <= 32 ? p.D : 4;
-        p.stg = 1;
-        p.lds = packed_lds(kind, nchunks);
+        p.stg = -1;   // x goes straight to registers
+        p.lds = 0;
         p.block = p.waves * 64;
         const int64_t waves_needed = (groups + p.rows - 1) / p.rows;
         p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
@@ -481,7 +476,7 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
     }
     info->units_in_flight = p.D;
     info->lds_bytes = p.lds;
-    info->stage_order = (p.variant == 1 || p.variant == 4) ? p.stg : -1;
+    info->stage_order = p.variant == 1 ? p.stg : -1;
     return GEMV_OK;
 }
 

@@ -638,13 +638,14 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 // Rows shorter than half a wave load (at most 32 chunks): a wave load takes
 // R = 64 / L rows at once, L = the power of two >= the chunk count, and
 // lane l works on chunk l % L of row g * R + l / L of row group g.  A lane's
-// chunk, and so its x, is the same in every group: x is staged once and kept
-// in registers.  Each group's partial sums meet in a segmented butterfly of
-// L lanes.  Groups stream D ahead as in gemv_stream.
+// chunk, and so its x, is the same in every group: each wave loads its
+// lanes' x granules once, straight into registers (no LDS, no barrier).
+// Each group's partial sums meet in a segmented butterfly of L lanes.
+// Groups stream D ahead as in gemv_stream.
 //
 // Preconditions (checked by the host): F is kQ8 or kQ4, 1 <= N / kElems <= 32,
 // A and x 16-byte aligned, 1 <= M <= 2^30 (row and group indices stay in
-// int), and 4 * packed_lds_words<F>(N / kElems) bytes of dynamic LDS.
+// int).  No dynamic LDS.
 template <int F>
 __host__ __device__ constexpr int packed_lanes(int nchunks)
 {
@@ -652,12 +653,6 @@ __host__ __device__ constexpr int packed_lanes(int nchunks)
     while (L < nchunks)
         L <<= 1;
     return L;
-}
-
-template <int F>
-__host__ __device__ constexpr int packed_lds_words(int nchunks)
-{
-    return packed_lanes<F>(nchunks) * Traits<F>::kXGran * 4 + (F == kQ8 ? 16 : 0);
 }
 
 // Sum over aligned groups of L lanes (L a power of two, at most 32); the
@@ -685,8 +680,6 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     static_assert(F == kQ8 || F == kQ4, "packed short rows: INT8/INT4 only");
     using T = Traits<F>;
     constexpr int G = T::kXGran;
-    constexpr int NT_ = WAVES * 64;
-    extern __shared__ u32x4 lds_x[];
     const int lane = threadIdx.x & 63;
     const int nchunks = N / T::kElems;
     const int L = packed_lanes<F>(nchunks);
@@ -701,26 +694,17 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     const int mine = wave_id < groups ? (groups - 1 - wave_id) / nwaves + 1 : 0;
     const int mine_pad = (mine + D - 1) / D * D;
     const int last = wave_id + (mine - 1) * nwaves;
-    const u32x4* xg = reinterpret_cast<const u32x4*>(x);
-    float* lds_f = reinterpret_cast<float*>(lds_x + L * G);
-
-    float xsum = 0.0f;   // INT8: sum of x over the row
-    if constexpr (F == kQ8)
-        stage_x_sums<WAVES>(xg, lds_x, lds_f, nchunks, L);
-    else
-        stage_x<F, NT_>(xg, lds_x, nchunks * G, L * G);
-    __syncthreads();
-    if constexpr (F == kQ8) {
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w)
-            xsum += lds_f[w];
-    }
     if (mine == 0)
         return;
+    // x: this lane's chunk, G granules, straight into registers through a
+    // resource of exactly x's bytes (zeros for lanes past the row end); no
+    // LDS and no barrier.  INT8 sums x over each row segment of L lanes
+    // (every segment holds all of x).
+    const auto xrsrc = make_rsrc(x, (uint32_t)nchunks * G * 16);
     u32x4 xv[G];
 #pragma unroll
     for (int k = 0; k < G; ++k)
-        xv[k] = lds_x[c * G + k];
+        xv[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, (c * G + k) * 16, 0, 0));
 
     // One resource per row group (wave-uniform, so the loads need no
     // per-lane descriptors) covering the group's rows below M; a lane's
@@ -747,6 +731,15 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 #pragma unroll
     for (int d = 0; d < D; ++d)
         issue(d);
+    // x arrives before the first A loads (older in the load counter)
+    float xsum = 0.0f;   // INT8: sum of x over the row
+    if constexpr (F == kQ8)
+        xsum = segment_sum(x_sum_chunk(xv[0], xv[G - 1], 0.0f), L);
+    if constexpr (F == kQ4) {
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            xv[k] = q4_pair_x(xv[k]);
+    }
 
     int c_g = wave_id;
     auto consume = [&](int d) {
