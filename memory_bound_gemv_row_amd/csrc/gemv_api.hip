@@ -95,9 +95,8 @@ struct Plan {
 //     launches.  Otherwise x is staged: rows of 8 units or more: 8 waves, 4
 //     in flight, A first, a row per wave; rows of 1-2 units: 8 waves, 2 in
 //     flight, split staging (staging loads, A prologue, LDS writes), at most
-//     3 workgroups per CU; other short rows: 8 waves, x first, a row per
-//     wave when M <= 8 x CUs, else 4 waves, split staging, at most 3
-//     workgroups per CU.
+//     3 workgroups per CU; rows of 3-7 units: 4 waves, split staging, at
+//     most 3 workgroups per CU.
 //   INT4: few rows of 1 unit (M <= 8 x CUs) or 2 units (M <= 16 x CUs): x
 //     read with each unit, 8 waves, 2 in flight.  Otherwise staged: rows
 //     under 4 units: 8 waves, 2 in flight, split staging; longer rows: 4
@@ -217,14 +216,9 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.D = 2;
             p.stg = 2;
             p.cap = 3;
-        } else if (M <= 8 * cus) {
-            // few rows (one GPU's share of a row-split matrix): a row per
-            // wave, x staged first
-            p.waves = 8;
-            p.stg = 1;
         } else {
-            // short rows, many of them: 4 waves, split staging, at most 3
-            // workgroups per CU
+            // rows of 3-7 units, many of them: 4 waves, split staging, at
+            // most 3 workgroups per CU
             p.waves = 4;
             p.stg = 2;
             p.cap = 3;

@@ -44,7 +44,7 @@ _MS = [1, 2, 3, 4, 5, 7, 9, 16, 17, 33, 65, 257]
 _NS = {
     # multiples of the chunk width (bandwidth path) and ragged ones (element-wise)
     "f32": [1, 3, 4, 8, 60, 64, 252, 256, 260, 1020, 1024, 2052, 4100, 9000, 17000],
-    "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 8200, 14336, 20000],
+    "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 2056, 3584, 4648, 8200, 14336, 20000],
     # 16..512 (1-32 chunks) take the packed short-row kernel, 528 is the
     # first streaming width
     "q8": [1, 15, 16, 32, 48, 272, 512, 528, 1008, 1024, 1040, 5000, 8192, 9232, 20000],
