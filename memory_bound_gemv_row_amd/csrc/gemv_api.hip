@@ -72,7 +72,7 @@ int packed_rows_per_load(int nchunks) { return 64 / packed_lanes<kQ8>(nchunks); 
 
 struct Plan {
     int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise,
-                   // 4 packed short rows (INT8/INT4)
+                   // 4 packed short rows (INT8/INT4), 5 x in registers (INT8/INT4)
     int grid;
     int block;
     int waves;     // per workgroup
@@ -81,6 +81,7 @@ struct Plan {
     int lds;
     int stg;       // order of A prologue and x staging (default_stage_order)
     int cap;       // at most cap workgroups per CU (0: no cap)
+    int xk;        // variant 5: units per row (K)
 };
 
 // Geometry for one call, chosen from sweeps on MI355X.  A row of nchunks
@@ -89,18 +90,22 @@ struct Plan {
 //     row per wave, or two for very long rows; 8 units in flight when rows
 //     have at least 8 units; rows of 1-3 units put ceil(4 / P) rows on each
 //     wave so that 4 units are in flight without padding.
-//   INT8: few rows (M <= 16 x CUs for rows of 1-2 units, M <= 8 x CUs for
-//     rows up to 16 units): x read with each unit, 8 waves, 2 (short rows)
-//     or 4 in flight -- the staging and its barrier would dominate such
-//     launches.  Otherwise x is staged: rows of 8 units or more: 8 waves, 4
-//     in flight, A first, a row per wave; rows of 1-2 units: 8 waves, 2 in
-//     flight, split staging (staging loads, A prologue, LDS writes), at most
-//     3 workgroups per CU; rows of 3-7 units: 4 waves, split staging, at
-//     most 3 workgroups per CU.
-//   INT4: few rows of 1 unit (M <= 8 x CUs) or 2 units (M <= 16 x CUs): x
-//     read with each unit, 8 waves, 2 in flight.  Otherwise staged: rows
-//     under 4 units: 8 waves, 2 in flight, split staging; longer rows: 4
-//     waves, 4 in flight, x staged before A; at most 3 workgroups per CU.
+//   INT8/INT4 rows of one unit (33-64 chunks), and INT4 rows of two units
+//     when M <= 16 x CUs: x in registers (gemv_xreg), no staging: 4 waves,
+//     one unit in flight up to 32 rows per CU; beyond, 8 waves, 2 in
+//     flight, at most 3 workgroups per CU; two-unit rows: 4 waves, 2 in
+//     flight.
+//   INT8, other rows: few rows (M <= 16 x CUs for rows of 2 units, M <= 8 x
+//     CUs for rows up to 16 units): x read with each unit, 8 waves, 2 (two-
+//     unit rows) or 4 in flight -- the staging and its barrier would
+//     dominate such launches.  Otherwise x is staged: rows of 8 units or
+//     more: 8 waves, 4 in flight, A first, a row per wave; rows of 2 units:
+//     8 waves, 2 in flight, split staging (staging loads, A prologue, LDS
+//     writes), at most 3 workgroups per CU; rows of 3-7 units: 4 waves,
+//     split staging, at most 3 workgroups per CU.
+//   INT4, other rows, x staged: rows under 4 units: 8 waves, 2 in flight,
+//     split staging; longer rows: 4 waves, 4 in flight, x staged before A;
+//     at most 3 workgroups per CU.
 //   INT8/INT4 rows of at most 32 chunks (half a wave load): the packed
 //     kernel, 64 / L rows per wave load, 8 waves; with up to 16 row groups
 //     per CU one group per wave, up to 32 two (both in flight), beyond that
@@ -150,7 +155,23 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
         return p;
     }
-    if (kind == kF32 || kind == kF16 || kind == kF16H) {
+    if ((kind == kQ8 || kind == kQ4) && (P == 1 || (kind == kQ4 && P == 2 && M <= 16 * cus))) {
+        // rows of one unit (and few INT4 rows of two): x in registers
+        p.variant = 5;
+        p.xk = P;
+        p.rows = 1;
+        if (P == 2) {
+            p.waves = 4;
+            p.D = 2;
+        } else if (M <= 32 * cus) {
+            p.waves = 4;
+            p.D = 1;
+        } else {
+            p.waves = 8;
+            p.D = 2;
+            p.cap = 3;
+        }
+    } else if (kind == kF32 || kind == kF16 || kind == kF16H) {
         p.variant = 2;
         if (P >= 24) {            // very long rows: two per wave, fewer in flight each
             p.waves = 4;
@@ -195,8 +216,8 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.variant = 1;
         p.D = 4;
         p.rows = 1;
-        if (P <= 2 && M <= 16 * cus) {
-            // few short rows: x read with each unit (no staging, no
+        if (P == 2 && M <= 16 * cus) {
+            // few rows of two units: x read with each unit (no staging, no
             // barrier), 8 waves, 2 in flight
             p.variant = 2;
             p.waves = 8;
@@ -210,8 +231,8 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             // long rows: 8 waves, A first, one row per wave
             p.waves = 8;
         } else if (P <= 2) {
-            // rows of at most 2 units: 8 waves, 2 in flight, split staging,
-            // at most 3 workgroups per CU (waves walk several rows)
+            // rows of 2 units: 8 waves, 2 in flight, split staging, at most
+            // 3 workgroups per CU (waves walk several rows)
             p.waves = 8;
             p.D = 2;
             p.stg = 2;
@@ -223,13 +244,6 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.stg = 2;
             p.cap = 3;
         }
-    } else if ((P == 1 && M <= 8 * cus) || (P == 2 && M <= 16 * cus)) {
-        // INT4, few rows of one or two units: x read with each unit, 8 waves,
-        // 2 in flight
-        p.variant = 2;
-        p.waves = 8;
-        p.D = 2;
-        p.rows = 1;
     } else {
         // short INT4 rows: 8 waves, 2 units in flight, split staging;
         // longer rows: 4 waves, 4 units, x staged before A
@@ -255,6 +269,15 @@ const void* select_packed(const Plan& p)
 {
     return p.D == 1 ? reinterpret_cast<const void*>(&gemv_packed<F, 8, 1>)
                     : reinterpret_cast<const void*>(&gemv_packed<F, 8, 2>);
+}
+
+template <int F>
+const void* select_xreg(const Plan& p)
+{
+    if (p.xk == 2)
+        return reinterpret_cast<const void*>(&gemv_xreg<F, 4, 2, 2>);
+    return p.D == 1 ? reinterpret_cast<const void*>(&gemv_xreg<F, 4, 1, 1>)
+                    : reinterpret_cast<const void*>(&gemv_xreg<F, 8, 2, 1>);
 }
 
 template <int F, int W, int D, bool XG, int STG>
@@ -293,6 +316,8 @@ const void* select_kernel(const Plan& p)
     if constexpr (F == kQ8 || F == kQ4) {
         if (p.variant == 4)
             return select_packed<F>(p);
+        if (p.variant == 5)
+            return select_xreg<F>(p);
     }
     if constexpr (F == kF32 || F == kF16 || F == kF16H)
         return select_stream<F, true>(p);

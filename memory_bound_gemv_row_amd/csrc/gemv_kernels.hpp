@@ -634,6 +634,121 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         consume(d);
 }
 
+// ---------------------------------------------------------------- x in registers (INT8/INT4, rows of K units)
+// For rows of exactly K units (K = 1, 2 or 4), lane l's chunks are l, l + 64,
+// ... in every row, so each wave loads its lanes' x granules for all K passes
+// once, straight into registers (through a resource of x's bytes: zeros past
+// the row end), and streams its rows like gemv_stream with no LDS staging
+// and no barrier.  With D a multiple of K, load slot d always holds pass
+// d % K, so the pass of every unit, and the row end, are known at compile
+// time.
+//
+// Preconditions (checked by the host): F is kQ8 or kQ4, ceil(N / kElems / 64)
+// == K, D % K == 0, A and x 16-byte aligned, 1 <= M <= 2^30.  No dynamic LDS.
+template <int F, int WAVES, int D, int K>
+__global__ void __launch_bounds__(WAVES * 64)
+gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
+          const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
+{
+    static_assert(F == kQ8 || F == kQ4, "x in registers: INT8/INT4 only");
+    static_assert(D % K == 0, "load slots must map to fixed passes");
+    using T = Traits<F>;
+    constexpr int G = T::kXGran;
+    const int lane = threadIdx.x & 63;
+    const int nchunks = N / T::kElems;
+    const uint32_t row_bytes = (uint32_t)nchunks * 16;
+    const int groups = N / 128;                 // INT4 scales per row
+    const int wave_id = blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nwaves = gridDim.x * WAVES;
+    const int my_rows = wave_id < M ? (M - 1 - wave_id) / nwaves + 1 : 0;
+    if (my_rows == 0)
+        return;
+    const int units = my_rows * K;
+    const int units_pad = (units + D - 1) / D * D;
+    const int last_row = wave_id + (my_rows - 1) * nwaves;
+    constexpr int kAux = 2;                     // A: non-temporal
+
+    const auto xrsrc = make_rsrc(x, (uint32_t)nchunks * G * 16);
+    u32x4 xr[K][G];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            xr[k][g] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, ((k * 64 + lane) * G + g) * 16, 0, 0));
+
+    u32x4 buf[D];
+    uint16_t sbuf[D];
+    int l_row = wave_id;
+    auto issue = [&](int d) {
+        const int pass = d % K;
+        const int row = l_row <= last_row ? l_row : last_row;
+        const auto rsrc = make_rsrc(A + (int64_t)row * row_bytes, row_bytes);
+        buf[d] = __builtin_bit_cast(u32x4,
+                                    __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane * 16 + pass * 1024, 0, kAux));
+        if constexpr (F == kQ4) {
+            const auto srsrc = make_rsrc(scale + (int64_t)row * groups, (uint32_t)groups * 2);
+            sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (lane >> 2) * 2 + pass * 32, 0, 0);
+        } else {
+            sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(scale + row, 2), 0, 0, 0);
+        }
+        if (pass == K - 1)
+            l_row += nwaves;
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        issue(d);
+
+    // x is older than every A load in the counter: ready before the first unit
+    float xsum = 0.0f;   // INT8: sum of x over the row
+    if constexpr (F == kQ8) {
+        float xs = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            xs = x_sum_chunk(xr[k][0], xr[k][G - 1], xs);
+        xsum = wave_sum(xs);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                xr[k][g] = q4_pair_x(xr[k][g]);
+    }
+
+    float acc = 0.0f;
+    int c_row = wave_id;
+    auto consume = [&](int d) {
+        const int pass = d % K;
+        if constexpr (F == kQ8) {
+            acc = q8_sub_chunk(buf[d], xr[pass][0], xr[pass][G - 1], acc);
+        } else {
+            acc = chunk_q4(buf[d], xr[pass], half_bits_to_float(sbuf[d]), acc);
+        }
+        if (pass == K - 1) {
+            float t = wave_sum(acc);
+            if (lane == 0 && c_row < M) {
+                if constexpr (F == kQ8) {
+                    t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);   // remove the offset
+                    t *= half_bits_to_float(sbuf[d]);
+                }
+                y[c_row] = t;
+            }
+            acc = 0.0f;
+            c_row += nwaves;
+        }
+    };
+    for (int k0 = D; k0 < units_pad; k0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            consume(d);
+            issue(d);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        consume(d);
+}
+
 // ---------------------------------------------------------------- packed short rows (INT8/INT4)
 // Rows shorter than half a wave load (at most 32 chunks): a wave load takes
 // R = 64 / L rows at once, L = the power of two >= the chunk count, and

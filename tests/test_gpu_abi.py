@@ -144,8 +144,11 @@ def test_describe_launch_fills_all_cus(gpu):
     # INT8/INT4 rows of at most 32 chunks: the packed short-row kernel
     assert binding.describe_launch("q8", 14336, 512)["variant"] == 4
     assert binding.describe_launch("q4", 14336, 1024)["variant"] == 4
-    assert binding.describe_launch("q8", 14336, 528)["variant"] == 1
-    assert binding.describe_launch("q4", 14336, 1152)["variant"] == 1
+    # one-unit rows just past that: x in registers; two-unit rows: staged
+    assert binding.describe_launch("q8", 14336, 528)["variant"] == 5
+    assert binding.describe_launch("q4", 14336, 1152)["variant"] == 5
+    assert binding.describe_launch("q8", 14336, 1040)["variant"] == 1
+    assert binding.describe_launch("q4", 14336, 2176)["variant"] == 1
     # more than 2^30 rows: the row-walking kernels' int cursors could wrap,
     # so the element-wise kernel (64-bit row indices) takes the call
     for kind in ("f16", "q8", "q4"):

@@ -86,14 +86,17 @@ def test_waves_walk_several_rows(gpu, oracle_mod, kind, N):
     _check(oracle_mod, kind, ops, f"{kind} multi-row M={M} N={N} {info}")
 
 
-@pytest.mark.parametrize("kind,N", [("q8", 1024), ("q8", 2048), ("q8", 4096), ("q8", 8192 + 16),
-                                    ("q4", 2048), ("q4", 4096)])
-def test_quantised_x_read_per_unit_and_staged(gpu, oracle_mod, kind, N):
-    # INT8/INT4 read x with each unit for few rows and stage it in LDS for
-    # many: both plans at the same row length, each with a ragged last
-    # workgroup
+@pytest.mark.parametrize("kind,N,small,large", [("q8", 1024, 5, 5), ("q8", 1008, 5, 5), ("q8", 2048, 2, 1),
+                                                ("q8", 4096, 2, 1), ("q8", 8192 + 16, 2, 1),
+                                                ("q4", 2048, 5, 5), ("q4", 4096, 5, 1), ("q4", 2176, 5, 1)])
+def test_quantised_x_paths_by_rows(gpu, oracle_mod, kind, N, small, large):
+    # INT8/INT4 take x in registers (variant 5: rows of one unit, and few
+    # INT4 rows of two), read with each unit (2) for few longer rows, and
+    # staged in LDS (1) for many: each plan at the same row length, with a
+    # ragged last workgroup (and, for many one-unit rows, waves walking
+    # several rows two loads deep)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for M, variant in ((8 * cus - 5, 2), (16 * cus + 5, 1)):
+    for M, variant in ((8 * cus - 5, small), (16 * cus + 5, large), (40 * cus + 7, large)):
         info = binding.describe_launch(kind, M, N)
         assert info["variant"] == variant, (M, info)
         ops = inputs.make(kind, M, N, seed=M + N)
