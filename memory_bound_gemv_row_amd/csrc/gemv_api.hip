@@ -72,7 +72,7 @@ int packed_rows_per_load(int nchunks) { return 64 / packed_lanes<kQ8>(nchunks); 
 
 struct Plan {
     int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise,
-                   // 4 packed short rows (INT8/INT4), 5 x in registers (INT8/INT4)
+                   // 4 packed short rows (INT8/INT4), 5 x in registers
     int grid;
     int block;
     int waves;     // per workgroup
@@ -86,15 +86,17 @@ struct Plan {
 
 // Geometry for one call, chosen from sweeps on MI355X.  A row of nchunks
 // 16-byte chunks is P = ceil(nchunks / 64) units (one 1-KiB wave load each).
-//   FP32/FP16 (either accumulation): x read with each unit (no staging); one
+//   FP32/FP16 (either accumulation), other rows: x read with each unit; one
 //     row per wave, or two for very long rows; 8 units in flight when rows
 //     have at least 8 units; rows of 1-3 units put ceil(4 / P) rows on each
 //     wave so that 4 units are in flight without padding.
-//   INT8/INT4 rows of one unit (33-64 chunks), and INT4 rows of two units
-//     when M <= 16 x CUs: x in registers (gemv_xreg), no staging: 4 waves,
-//     one unit in flight up to 32 rows per CU; beyond, 8 waves, 2 in
-//     flight, at most 3 workgroups per CU; two-unit rows: 4 waves, 2 in
-//     flight.
+//   Rows of one unit (any format; FP32/FP16 only up to 32 rows per CU) and
+//     of two units (FP32/FP16; INT4 up to 16 rows per CU; FP16 with FP32 x
+//     beyond that): x in registers (gemv_xreg), no staging: one-unit rows
+//     4 waves (8 for FP32/FP16), one unit in flight up to 32 rows per CU,
+//     beyond that 8 waves, 2 in flight, at most 3 workgroups per CU;
+//     two-unit rows 4 waves, 2 in flight (FP16 with FP32 x: at most 6
+//     workgroups per CU).
 //   INT8, other rows: few rows (M <= 16 x CUs for rows of 2 units, M <= 8 x
 //     CUs for rows up to 16 units): x read with each unit, 8 waves, 2 (two-
 //     unit rows) or 4 in flight -- the staging and its barrier would
@@ -155,23 +157,29 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
         return p;
     }
-    if ((kind == kQ8 || kind == kQ4) && (P == 1 || (kind == kQ4 && P == 2 && M <= 16 * cus))) {
-        // rows of one unit (and few INT4 rows of two): x in registers
+    const bool fp = kind == kF32 || kind == kF16 || kind == kF16H;
+    if (P == 1 && (!fp || M <= 32 * cus)) {
+        // rows of one unit: x in registers
         p.variant = 5;
-        p.xk = P;
+        p.xk = 1;
         p.rows = 1;
-        if (P == 2) {
-            p.waves = 4;
-            p.D = 2;
-        } else if (M <= 32 * cus) {
-            p.waves = 4;
+        if (M <= 32 * cus) {
+            p.waves = fp ? 8 : 4;
             p.D = 1;
         } else {
             p.waves = 8;
             p.D = 2;
             p.cap = 3;
         }
-    } else if (kind == kF32 || kind == kF16 || kind == kF16H) {
+    } else if (P == 2 && (fp || (kind == kQ4 && M <= 16 * cus) || (kind == kF16X32 && M > 16 * cus))) {
+        // rows of two units: x in registers
+        p.variant = 5;
+        p.xk = 2;
+        p.rows = 1;
+        p.waves = 4;
+        p.D = 2;
+        p.cap = kind == kF16X32 ? 6 : 0;
+    } else if (fp) {
         p.variant = 2;
         if (P >= 24) {            // very long rows: two per wave, fewer in flight each
             p.waves = 4;
@@ -276,8 +284,10 @@ const void* select_xreg(const Plan& p)
 {
     if (p.xk == 2)
         return reinterpret_cast<const void*>(&gemv_xreg<F, 4, 2, 2>);
-    return p.D == 1 ? reinterpret_cast<const void*>(&gemv_xreg<F, 4, 1, 1>)
-                    : reinterpret_cast<const void*>(&gemv_xreg<F, 8, 2, 1>);
+    if (p.D == 2)
+        return reinterpret_cast<const void*>(&gemv_xreg<F, 8, 2, 1>);
+    return p.waves == 8 ? reinterpret_cast<const void*>(&gemv_xreg<F, 8, 1, 1>)
+                        : reinterpret_cast<const void*>(&gemv_xreg<F, 4, 1, 1>);
 }
 
 template <int F, int W, int D, bool XG, int STG>
@@ -313,11 +323,11 @@ const void* select_kernel(const Plan& p)
 {
     if (p.variant == 3)
         return reinterpret_cast<const void*>(&gemv_elementwise<F>);
+    if (p.variant == 5)
+        return select_xreg<F>(p);
     if constexpr (F == kQ8 || F == kQ4) {
         if (p.variant == 4)
             return select_packed<F>(p);
-        if (p.variant == 5)
-            return select_xreg<F>(p);
     }
     if constexpr (F == kF32 || F == kF16 || F == kF16H)
         return select_stream<F, true>(p);

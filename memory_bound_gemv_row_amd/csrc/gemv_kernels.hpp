@@ -634,7 +634,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         consume(d);
 }
 
-// ---------------------------------------------------------------- x in registers (INT8/INT4, rows of K units)
+// ---------------------------------------------------------------- x in registers (rows of K units)
 // For rows of exactly K units (K = 1, 2 or 4), lane l's chunks are l, l + 64,
 // ... in every row, so each wave loads its lanes' x granules for all K passes
 // once, straight into registers (through a resource of x's bytes: zeros past
@@ -643,14 +643,13 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 // d % K, so the pass of every unit, and the row end, are known at compile
 // time.
 //
-// Preconditions (checked by the host): F is kQ8 or kQ4, ceil(N / kElems / 64)
-// == K, D % K == 0, A and x 16-byte aligned, 1 <= M <= 2^30.  No dynamic LDS.
+// Preconditions (checked by the host): ceil(N / kElems / 64) == K,
+// D % K == 0, A and x 16-byte aligned, 1 <= M <= 2^30.  No dynamic LDS.
 template <int F, int WAVES, int D, int K>
 __global__ void __launch_bounds__(WAVES * 64)
 gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
           const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
-    static_assert(F == kQ8 || F == kQ4, "x in registers: INT8/INT4 only");
     static_assert(D % K == 0, "load slots must map to fixed passes");
     using T = Traits<F>;
     constexpr int G = T::kXGran;
@@ -689,7 +688,7 @@ gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         if constexpr (F == kQ4) {
             const auto srsrc = make_rsrc(scale + (int64_t)row * groups, (uint32_t)groups * 2);
             sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (lane >> 2) * 2 + pass * 32, 0, 0);
-        } else {
+        } else if constexpr (F == kQ8) {
             sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(scale + row, 2), 0, 0, 0);
         }
         if (pass == K - 1)
@@ -707,7 +706,7 @@ gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         for (int k = 0; k < K; ++k)
             xs = x_sum_chunk(xr[k][0], xr[k][G - 1], xs);
         xsum = wave_sum(xs);
-    } else {
+    } else if constexpr (F == kQ4) {
 #pragma unroll
         for (int k = 0; k < K; ++k)
 #pragma unroll
@@ -716,15 +715,28 @@ gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     }
 
     float acc = 0.0f;
+    f16x2 acch = {(_Float16)0.0f, (_Float16)0.0f};   // FP16 accumulation only
     int c_row = wave_id;
     auto consume = [&](int d) {
         const int pass = d % K;
-        if constexpr (F == kQ8) {
+        if constexpr (F == kF32) {
+            acc = chunk_f32(buf[d], xr[pass][0], acc);
+        } else if constexpr (F == kF16) {
+            acc = chunk_f16(buf[d], xr[pass][0], acc);
+        } else if constexpr (F == kF16X32) {
+            acc = chunk_f16x32(buf[d], xr[pass][0], xr[pass][G - 1], acc);
+        } else if constexpr (F == kF16H) {
+            acch = chunk_f16h(buf[d], xr[pass][0], acch);
+        } else if constexpr (F == kQ8) {
             acc = q8_sub_chunk(buf[d], xr[pass][0], xr[pass][G - 1], acc);
         } else {
             acc = chunk_q4(buf[d], xr[pass], half_bits_to_float(sbuf[d]), acc);
         }
         if (pass == K - 1) {
+            if constexpr (F == kF16H) {
+                acc = (float)acch.x + (float)acch.y;
+                acch = f16x2{(_Float16)0.0f, (_Float16)0.0f};
+            }
             float t = wave_sum(acc);
             if (lane == 0 && c_row < M) {
                 if constexpr (F == kQ8) {

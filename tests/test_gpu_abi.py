@@ -149,6 +149,12 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("q4", 14336, 1152)["variant"] == 5
     assert binding.describe_launch("q8", 14336, 1040)["variant"] == 1
     assert binding.describe_launch("q4", 14336, 2176)["variant"] == 1
+    # FP rows of one unit (up to 32 rows per CU) and of two units: x in registers
+    assert binding.describe_launch("f16", 4096, 512)["variant"] == 5
+    assert binding.describe_launch("f16", 14336, 1024)["variant"] == 5
+    assert binding.describe_launch("f32", 14336, 256)["variant"] == 2
+    assert binding.describe_launch("f16x32", 14336, 512)["variant"] == 5
+    assert binding.describe_launch("f16x32", 4096, 1024)["variant"] == 2
     # more than 2^30 rows: the row-walking kernels' int cursors could wrap,
     # so the element-wise kernel (64-bit row indices) takes the call
     for kind in ("f16", "q8", "q4"):

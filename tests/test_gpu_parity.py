@@ -103,6 +103,18 @@ def test_quantised_x_paths_by_rows(gpu, oracle_mod, kind, N, small, large):
         _check(oracle_mod, kind, ops, f"{kind} M={M} N={N} {info}")
 
 
+@pytest.mark.parametrize("kind,M,N", [("f32", 8000, 252), ("f32", 9000, 260), ("f16", 14336, 1000),
+                                      ("f16x32", 14336, 512), ("f16x32", 14336, 1016), ("f16_acc16", 6000, 1024),
+                                      ("q8", 14336, 1008), ("q4", 14336, 2048)])
+def test_x_in_registers_many_rows(gpu, oracle_mod, kind, M, N):
+    # rows of one or two wave loads with x held in registers, enough rows
+    # for capped grids (waves walking several rows) and ragged last passes
+    info = binding.describe_launch(kind, M, N)
+    assert info["variant"] == 5, info
+    ops = inputs.make(kind, M, N, seed=M ^ N)
+    _check(oracle_mod, kind, ops, f"{kind} x-in-registers M={M} N={N} {info}")
+
+
 @pytest.mark.parametrize("kind,N", [("q8", 16), ("q8", 48), ("q8", 272), ("q8", 512),
                                     ("q4", 128), ("q4", 384), ("q4", 640), ("q4", 1024)])
 def test_packed_short_rows_many_groups(gpu, oracle_mod, kind, N):
