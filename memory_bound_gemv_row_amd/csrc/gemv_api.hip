@@ -88,15 +88,19 @@ struct Plan {
 // 16-byte chunks is P = ceil(nchunks / 64) units (one 1-KiB wave load each).
 //   FP32/FP16 (either accumulation), other rows: x read with each unit; one
 //     row per wave, or two for very long rows; 8 units in flight when rows
-//     have at least 8 units; rows of 1-3 units put ceil(4 / P) rows on each
-//     wave so that 4 units are in flight without padding.
-//   Rows of one unit (any format; FP32/FP16 only up to 32 rows per CU) and
-//     of two units (FP32/FP16; INT4 up to 16 rows per CU; FP16 with FP32 x
-//     beyond that): x in registers (gemv_xreg), no staging: one-unit rows
-//     4 waves (8 for FP32/FP16), one unit in flight up to 32 rows per CU,
-//     beyond that 8 waves, 2 in flight, at most 3 workgroups per CU;
+//     have at least 8 units; one-unit rows (beyond 32 rows per CU) put 4
+//     rows on each wave so that 4 units are in flight without padding.
+//   Rows of one unit (any format; FP32/FP16 only up to 32 rows per CU), of
+//     two units (FP32/FP16; INT4 up to 16 rows per CU; FP16 with FP32 x
+//     beyond that) and of three: x in registers (gemv_xreg), no staging.
+//     One-unit rows: 4 waves (8 for FP32/FP16), one unit in flight up to 32
+//     rows per CU, beyond that 8 waves, 2 in flight, at most 3 workgroups
+//     per CU;
 //     two-unit rows 4 waves, 2 in flight (FP16 with FP32 x: at most 6
-//     workgroups per CU).
+//     workgroups per CU).  Rows of three units (FP32/FP16, FP16 with FP32 x;
+//     INT4 up to 8 rows per CU): 3 in flight, 8 waves (FP32/FP16 beyond 32
+//     rows per CU: 4; FP16 with FP32 x: 4 up to 16 rows per CU, beyond
+//     that 8 with at most 3 workgroups per CU).
 //   INT8, other rows: few rows (M <= 16 x CUs for rows of 2 units, M <= 8 x
 //     CUs for rows up to 16 units): x read with each unit, 8 waves, 2 (two-
 //     unit rows) or 4 in flight -- the staging and its barrier would
@@ -179,6 +183,20 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.waves = 4;
         p.D = 2;
         p.cap = kind == kF16X32 ? 6 : 0;
+    } else if (P == 3 && (fp || kind == kF16X32 || (kind == kQ4 && M <= 8 * cus))) {
+        // rows of three units: x in registers
+        p.variant = 5;
+        p.xk = 3;
+        p.rows = 1;
+        p.D = 3;
+        if (fp) {
+            p.waves = M <= 32 * cus ? 8 : 4;
+        } else if (kind == kF16X32 && M > 16 * cus) {
+            p.waves = 8;
+            p.cap = 3;
+        } else {
+            p.waves = kind == kF16X32 ? 4 : 8;
+        }
     } else if (fp) {
         p.variant = 2;
         if (P >= 24) {            // very long rows: two per wave, fewer in flight each
@@ -282,6 +300,9 @@ const void* select_packed(const Plan& p)
 template <int F>
 const void* select_xreg(const Plan& p)
 {
+    if (p.xk == 3)
+        return p.waves == 8 ? reinterpret_cast<const void*>(&gemv_xreg<F, 8, 3, 3>)
+                            : reinterpret_cast<const void*>(&gemv_xreg<F, 4, 3, 3>);
     if (p.xk == 2)
         return reinterpret_cast<const void*>(&gemv_xreg<F, 4, 2, 2>);
     if (p.D == 2)

@@ -635,7 +635,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 }
 
 // ---------------------------------------------------------------- x in registers (rows of K units)
-// For rows of exactly K units (K = 1, 2 or 4), lane l's chunks are l, l + 64,
+// For rows of exactly K units (K = 1, 2 or 3), lane l's chunks are l, l + 64,
 // ... in every row, so each wave loads its lanes' x granules for all K passes
 // once, straight into registers (through a resource of x's bytes: zeros past
 // the row end), and streams its rows like gemv_stream with no LDS staging

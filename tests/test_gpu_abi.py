@@ -155,6 +155,8 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("f32", 14336, 256)["variant"] == 2
     assert binding.describe_launch("f16x32", 14336, 512)["variant"] == 5
     assert binding.describe_launch("f16x32", 4096, 1024)["variant"] == 2
+    assert binding.describe_launch("f16", 14336, 1536)["variant"] == 5
+    assert binding.describe_launch("q8", 4096, 3072)["variant"] == 1   # INT8 three-unit rows stay staged
     # more than 2^30 rows: the row-walking kernels' int cursors could wrap,
     # so the element-wise kernel (64-bit row indices) takes the call
     for kind in ("f16", "q8", "q4"):

@@ -44,7 +44,7 @@ _MS = [1, 2, 3, 4, 5, 7, 9, 16, 17, 33, 65, 257]
 _NS = {
     # multiples of the chunk width (bandwidth path) and ragged ones (element-wise)
     "f32": [1, 3, 4, 8, 60, 64, 252, 256, 260, 1020, 1024, 2052, 4100, 9000, 17000],
-    "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 2056, 3584, 4648, 8200, 14336, 20000],
+    "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 1528, 1536, 2056, 3584, 4648, 8200, 14336, 20000],
     # 16..512 (1-32 chunks) take the packed short-row kernel, 528 is the
     # first streaming width
     "q8": [1, 15, 16, 32, 48, 272, 512, 528, 1008, 1024, 1040, 5000, 8192, 9232, 20000],
@@ -105,7 +105,8 @@ def test_quantised_x_paths_by_rows(gpu, oracle_mod, kind, N, small, large):
 
 @pytest.mark.parametrize("kind,M,N", [("f32", 8000, 252), ("f32", 9000, 260), ("f16", 14336, 1000),
                                       ("f16x32", 14336, 512), ("f16x32", 14336, 1016), ("f16_acc16", 6000, 1024),
-                                      ("q8", 14336, 1008), ("q4", 14336, 2048)])
+                                      ("q8", 14336, 1008), ("q4", 14336, 2048), ("f16", 14336, 1528),
+                                      ("f32", 4096, 768), ("f16x32", 14336, 1536), ("q4", 2000, 6144)])
 def test_x_in_registers_many_rows(gpu, oracle_mod, kind, M, N):
     # rows of one or two wave loads with x held in registers, enough rows
     # for capped grids (waves walking several rows) and ragged last passes
