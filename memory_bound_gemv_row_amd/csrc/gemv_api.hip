@@ -94,8 +94,8 @@ struct Plan {
 //     two units (FP32/FP16; INT4 up to 16 rows per CU; FP16 with FP32 x
 //     beyond that) and of three: x in registers (gemv_xreg), no staging.
 //     One-unit rows: 4 waves (8 for FP32/FP16), one unit in flight up to 32
-//     rows per CU, beyond that 8 waves, 2 in flight, at most 3 workgroups
-//     per CU;
+//     rows per CU; up to 64, 4 waves with two rows each, both in flight;
+//     beyond that 8 waves, 2 in flight, at most 3 workgroups per CU;
 //     two-unit rows 4 waves, 2 in flight (FP16 with FP32 x: at most 6
 //     workgroups per CU).  Rows of three units (FP32/FP16, FP16 with FP32 x;
 //     INT4 up to 8 rows per CU): 3 in flight, 8 waves (FP32/FP16 beyond 32
@@ -170,6 +170,10 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         if (M <= 32 * cus) {
             p.waves = fp ? 8 : 4;
             p.D = 1;
+        } else if (M <= 64 * cus) {
+            p.waves = 4;
+            p.D = 2;
+            p.rows = 2;
         } else {
             p.waves = 8;
             p.D = 2;
@@ -306,7 +310,8 @@ const void* select_xreg(const Plan& p)
     if (p.xk == 2)
         return reinterpret_cast<const void*>(&gemv_xreg<F, 4, 2, 2>);
     if (p.D == 2)
-        return reinterpret_cast<const void*>(&gemv_xreg<F, 8, 2, 1>);
+        return p.waves == 8 ? reinterpret_cast<const void*>(&gemv_xreg<F, 8, 2, 1>)
+                            : reinterpret_cast<const void*>(&gemv_xreg<F, 4, 2, 1>);
     return p.waves == 8 ? reinterpret_cast<const void*>(&gemv_xreg<F, 8, 1, 1>)
                         : reinterpret_cast<const void*>(&gemv_xreg<F, 4, 1, 1>);
 }

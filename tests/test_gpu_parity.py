@@ -73,7 +73,7 @@ def test_many_passes_and_row_groups(gpu, oracle_mod, kind, N):
     _check(oracle_mod, kind, ops, f"{kind} tiles N={N}")
 
 
-@pytest.mark.parametrize("kind,N", [("q8", 1024), ("q8", 4096 + 16), ("q4", 2048 + 128), ("q4", 14336),
+@pytest.mark.parametrize("kind,N", [("q8", 2048), ("q8", 4096 + 16), ("q4", 2048 + 128), ("q4", 14336),
                                     ("f16x32", 1024), ("f16x32", 8192 + 8)])
 def test_waves_walk_several_rows(gpu, oracle_mod, kind, N):
     # grids capped per CU: each wave walks two or three rows, the last ones
