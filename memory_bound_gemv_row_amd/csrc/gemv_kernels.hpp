@@ -5,16 +5,19 @@
 //   refresher").
 //
 // Design (wave64, one pass of HBM over A):
-//   * A wave owns R rows at a time ("Making GEMV Fast", section "What access
+//   * A wave owns whole rows ("Making GEMV Fast", section "What access
 //     pattern do we actually want?": give a row to a warp, not a thread).
 //     Lane l reads the 16-byte chunks l, l+64, l+128, ... of each row, so one
 //     wave-wide load instruction moves 1 KiB of contiguous bytes: the
 //     coalesced mapping "column = lane + width * pass" at 16-byte
-//     granularity ("membound", stage 3: 128-bit loads).
-//   * U chunks per lane and row are issued before any is consumed, so each
-//     wave keeps U*R KiB of A in flight.
-//   * x is staged once per workgroup in LDS ("membound", stage 2 stages x in
-//     shared memory), or, when it does not fit, read through the caches.
+//     granularity ("membound", stage 3: 128-bit loads).  Rows shorter than
+//     half a wave load share wave loads (gemv_packed).
+//   * D such 1-KiB units are issued before any is consumed, so each wave
+//     keeps D KiB of A in flight.
+//   * x reaches the lanes one of three ways, by shape: staged once per
+//     workgroup in LDS ("membound", stage 2 stages x in shared memory), read
+//     through the caches with each unit, or, for rows of one to three wave
+//     loads (and packed short rows), loaded once per wave into registers.
 //   * Accumulation is FP32 in registers.  FP16 operands enter through
 //     v_dot2_f32_f16; INT8/INT4 codes are unpacked in registers to exact
 //     binary16 values (INT8 as offset subnormals, INT4 as exponent-biased
