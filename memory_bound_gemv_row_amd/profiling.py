@@ -19,6 +19,7 @@ from __future__ import annotations
 import csv
 import hashlib
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -32,13 +33,25 @@ PROBE_READ_BYTES = 1 << 30
 PROBE_COPY_BYTES = 256 << 20
 
 
+_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (string and
+    character literals kept), so that editing a comment does not change
+    the hash below."""
+    kept = _TOKENS.sub(lambda m: " " if m.group(0).startswith("/") else m.group(0), text)
+    return " ".join(kept.split())
+
+
 def kernel_source_hash(op: str = "gemv") -> str:
-    """Hash of the sources of one operation's kernels (the GEMV by default):
-    a traffic summary is valid only for the sources it was taken on."""
+    """Hash of the code (comments aside) of one operation's kernel sources
+    (the GEMV by default): a traffic summary is valid only for the code it
+    was taken on."""
     h = hashlib.sha256()
     for rel in OP_SOURCES[op]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -58,3 +58,12 @@ def test_committed_summaries_parse():
         if f.endswith("_traffic.txt"):
             got = profiling.read_traffic(os.path.join(root, f))
             assert got is not None and got[0] > 0, f
+
+
+def test_source_hash_ignores_comments_not_code():
+    src = 'int f(int a) { // add one\n  return a + 1; /* done */ }\nconst char* s = "a // b";\n'
+    same = 'int f(int a) {\n  // a different comment\n  return a + 1; }\nconst char* s = "a // b";\n'
+    other = 'int f(int a) { return a + 2; }\nconst char* s = "a // b";\n'
+    assert profiling.code_only(src) == profiling.code_only(same)
+    assert profiling.code_only(src) != profiling.code_only(other)
+    assert '"a // b"' in profiling.code_only(src)   # string literals are code
