@@ -40,9 +40,13 @@ def _compare(oracle, kind, W, label):
     if not np.array_equal(q, oq):
         bad = np.argwhere(q != oq)[:5]
         raise AssertionError((label, "codes differ at", bad.tolist()))
-    denom = np.maximum(oe, 1e-30)
-    rel = np.max(np.abs(e.astype(np.float64) - oe) / denom) if oe.size else 0.0
-    assert rel <= _sse_tol(W.shape[1]) or np.all(np.abs(e - oe) <= 1e-30), (label, rel)
+    # an infinite weight makes its row's squared error infinite on both sides
+    assert np.array_equal(np.isinf(e), np.isinf(oe)), (label, "infinite errors")
+    fin = np.isfinite(oe)
+    e_f, oe_f = e[fin], oe[fin]
+    denom = np.maximum(oe_f, 1e-30)
+    rel = np.max(np.abs(e_f.astype(np.float64) - oe_f) / denom) if oe_f.size else 0.0
+    assert rel <= _sse_tol(W.shape[1]) or np.all(np.abs(e_f - oe_f) <= 1e-30), (label, rel)
     return q, s, e, oe
 
 
@@ -115,13 +119,16 @@ def test_near_ties_match_the_correctly_rounded_division(gpu, oracle_mod, kind):
 
 @pytest.mark.parametrize("kind", ["q8", "q4"])
 def test_degenerate_rows(gpu, oracle_mod, kind):
-    M, N = 6, 512
+    M, N = 8, 512
     W = np.zeros((M, N), np.float32)
     W[1] = 1.0e7                                   # scale saturates at 65504, codes clip
     W[2, :] = np.linspace(-1e-4, 1e-4, N)          # binary16-subnormal scales
     W[3, 5] = 1.0e-9                               # scale rounds to zero
     W[4] = inputs.make_weights(1, N, seed=1)[0]
     W[5] = -W[4]
+    W[6] = np.float32(3e-39) * np.sign(W[4])       # binary32-subnormal maximum
+    W[7] = W[4]
+    W[7, 200] = np.inf                             # infinite maximum: scale 65504, codes clip
     _compare(oracle_mod, kind, W, f"{kind} degenerate")
 
 
