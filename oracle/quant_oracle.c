@@ -121,6 +121,8 @@ static int code_of(float w, float sf, float qmax)
     if (sf == 0.0f)
         return 0;
     const float t = w / sf;           /* one binary32 division */
+    if (isnan(t))
+        return 0;                     /* a NaN weight has no code under the rule; 0 keeps this defined */
     double r = (t < 0.0f) ? -round_half_even(-(double)t) : round_half_even((double)t);
     if (r > qmax)
         r = qmax;
