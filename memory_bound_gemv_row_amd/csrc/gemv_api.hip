@@ -134,8 +134,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
     // M in int: more than 2^30 rows also take the element-wise kernel.
     const bool huge_row = (int64_t)(N / epc) * 16 >= ((int64_t)1 << 31);
     const bool huge_m = M > (1 << 30);
-    if (!aligned || N == 0 || N % epc != 0 || huge_row || huge_m ||
-        ((kind == kQ8 || kind == kQ4) && lds_bytes(kind, N / epc) > kMaxLdsBytes)) {
+    if (!aligned || N == 0 || N % epc != 0 || huge_row || huge_m) {
         p.variant = 3;
         p.block = 256;
         p.waves = 4;
@@ -246,7 +245,11 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.variant = 1;
         p.D = 4;
         p.rows = 1;
-        if (P == 2 && M <= 16 * cus) {
+        if (lds_bytes(kind, nchunks) > kMaxLdsBytes) {
+            // staged x would pass the LDS budget: x read with each unit
+            p.variant = 2;
+            p.waves = 8;
+        } else if (P == 2 && M <= 16 * cus) {
             // few rows of two units: x read with each unit (no staging, no
             // barrier), 8 waves, 2 in flight
             p.variant = 2;
@@ -274,6 +277,13 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.stg = 2;
             p.cap = 3;
         }
+    } else if (lds_bytes(kind, nchunks) > kMaxLdsBytes) {
+        // INT4 rows whose staged x would pass the LDS budget: x read with
+        // each unit, 4 waves, 4 in flight
+        p.variant = 2;
+        p.waves = 4;
+        p.D = 4;
+        p.rows = 1;
     } else {
         // short INT4 rows: 8 waves, 2 units in flight, split staging;
         // longer rows: 4 waves, 4 units, x staged before A

@@ -141,6 +141,11 @@ def test_describe_launch_fills_all_cus(gpu):
         info = binding.describe_launch(kind, M, N)
         assert info["grid"] >= cus, (kind, M, N, info, cus)
     assert binding.describe_launch("f16", 8, 1001)["variant"] == 3
+    # INT8/INT4 rows whose staged x would pass the 64 KiB LDS budget read x
+    # with each unit
+    assert binding.describe_launch("q8", 1024, 32768)["variant"] == 2
+    assert binding.describe_launch("q4", 1024, 33280)["variant"] == 2
+    assert binding.describe_launch("q8", 4096, 31744)["variant"] == 1
     # INT8/INT4 rows of at most 32 chunks: the packed short-row kernel
     assert binding.describe_launch("q8", 14336, 512)["variant"] == 4
     assert binding.describe_launch("q4", 14336, 1024)["variant"] == 4
