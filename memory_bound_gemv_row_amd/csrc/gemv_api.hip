@@ -16,27 +16,35 @@
 namespace gemv {
 namespace {
 
-constexpr int kMaxLdsBytes = 64 * 1024;    // x staged in LDS up to this size
-constexpr bool kNT = true;                 // stream A with non-temporal loads
+constexpr int kLdsBytes = 64 * 1024;   // x staged in LDS up to this size
+constexpr bool kNT = true;             // stream A with non-temporal loads
 constexpr int kMaxDevices = 64;
 
-std::mutex g_cu_mutex;
-int g_cu_count[kMaxDevices] = {0};
+// What the plans need to know of a device.
+struct Device {
+    int cus;       // compute units
+    int lds_max;   // bytes of LDS one workgroup may hold
+};
 
-// Compute-unit count of the current device, cached per device.
-int current_cu_count(int* out)
+std::mutex g_dev_mutex;
+Device g_dev[kMaxDevices] = {};
+
+// Properties of the current device, cached per device.
+int current_device(Device* out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return GEMV_E_DEVICE;
-    std::lock_guard<std::mutex> lock(g_cu_mutex);
-    if (g_cu_count[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_dev[dev].cus == 0) {
+        int n = 0, lds = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0 ||
+            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            lds <= 0)
             return GEMV_E_DEVICE;
-        g_cu_count[dev] = n;
+        g_dev[dev] = {n, lds};
     }
-    *out = g_cu_count[dev];
+    *out = g_dev[dev];
     return GEMV_OK;
 }
 
@@ -109,9 +117,18 @@ struct Plan {
 //     8 waves, 2 in flight, split staging (staging loads, A prologue, LDS
 //     writes), at most 3 workgroups per CU; rows of 3-7 units: 4 waves,
 //     split staging, at most 3 workgroups per CU.
+//     Staged x past 64 KiB (rows of 32 units and more): with two workgroups
+//     per CU fitting the device's LDS and over 4 x CUs rows, 4 waves, split
+//     staging, at most 2 workgroups per CU; otherwise 8 waves, x staged
+//     before A, one workgroup per CU -- but x read with each unit (4 waves
+//     of two rows, 8 in flight) where only one workgroup fits and M <= 8 x
+//     CUs, or where the staged x would not fit at all.
 //   INT4, other rows, x staged: rows under 4 units: 8 waves, 2 in flight,
 //     split staging; longer rows: 4 waves, 4 in flight, x staged before A;
-//     at most 3 workgroups per CU.
+//     at most 3 workgroups per CU.  Staged x past 64 KiB (rows over 16
+//     units): 8 waves, 4 in flight, x staged before A, one workgroup per
+//     CU; x read with each unit (4 waves, 4 in flight) instead for M <= 4 x
+//     CUs, or where the staged x would not fit the device's LDS.
 //   INT8/INT4 rows of at most 32 chunks (half a wave load): the packed
 //     kernel, 64 / L rows per wave load, 8 waves; with up to 16 row groups
 //     per CU one group per wave, up to 32 two (both in flight), beyond that
@@ -120,12 +137,13 @@ struct Plan {
 //     every unit costs more cache bandwidth than staging it, once the staging
 //     (4N bytes per workgroup) is spread over enough rows: staged for rows of
 //     at least 12 units, or for 8192 rows and more; read with each unit
-//     otherwise, and whenever the staged x would exceed the LDS budget.
+//     otherwise, and whenever the staged x would pass 64 KiB.
 // With a cap the grid stays below the row count and waves walk several
 // rows; otherwise every launch gives each CU work once M >= CUs.
-Plan make_plan(int kind, int M, int N, bool aligned, int cus)
+Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
 {
     Plan p{};
+    const int cus = dev.cus;
     const int epc = elems_per_chunk(kind);
     // The streaming kernel addresses a row through a 32-bit byte count (the
     // INT8/INT4 buffer resource's range, the row stride): rows of 2 GiB or
@@ -218,7 +236,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.rows = (4 + P - 1) / P;
         }
     } else if (kind == kF16X32) {
-        const bool fits = lds_bytes(kind, nchunks) <= kMaxLdsBytes;
+        const bool fits = lds_bytes(kind, nchunks) <= kLdsBytes;
         p.rows = 1;
         if (fits && P >= 24) {
             p.variant = 1;
@@ -245,10 +263,24 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
         p.variant = 1;
         p.D = 4;
         p.rows = 1;
-        if (lds_bytes(kind, nchunks) > kMaxLdsBytes) {
-            // staged x would pass the LDS budget: x read with each unit
+        const int lds = lds_bytes(kind, nchunks);
+        if (lds > dev.lds_max || (lds > kLdsBytes && 2 * lds > dev.lds_max && M <= 8 * cus)) {
+            // staged x would not fit a workgroup, or only one workgroup
+            // per CU and few rows to spread its staging over: x read with
+            // each unit, 4 waves of two rows each, 8 units in flight
             p.variant = 2;
-            p.waves = 8;
+            p.waves = 4;
+            p.D = 8;
+            p.rows = 2;
+        } else if (lds > kLdsBytes) {
+            // long rows, staged x past the usual budget: 4 waves, split
+            // staging, at most 2 workgroups per CU when two fit and the
+            // rows are many; else 8 waves, x staged before A, one
+            // workgroup per CU
+            const bool two = 2 * lds <= dev.lds_max && M > 4 * cus;
+            p.waves = two ? 4 : 8;
+            p.stg = two ? 2 : 1;
+            p.cap = two ? 2 : 1;
         } else if (P == 2 && M <= 16 * cus) {
             // few rows of two units: x read with each unit (no staging, no
             // barrier), 8 waves, 2 in flight
@@ -277,13 +309,23 @@ Plan make_plan(int kind, int M, int N, bool aligned, int cus)
             p.stg = 2;
             p.cap = 3;
         }
-    } else if (lds_bytes(kind, nchunks) > kMaxLdsBytes) {
-        // INT4 rows whose staged x would pass the LDS budget: x read with
-        // each unit, 4 waves, 4 in flight
+    } else if (const int lds = lds_bytes(kind, nchunks);
+               lds > dev.lds_max || (lds > kLdsBytes && M <= 4 * cus)) {
+        // INT4 rows whose staged x would not fit a workgroup, or long rows
+        // and few of them: x read with each unit, 4 waves, 4 in flight
         p.variant = 2;
         p.waves = 4;
         p.D = 4;
         p.rows = 1;
+    } else if (lds > kLdsBytes) {
+        // long INT4 rows, staged x past the usual budget: 8 waves, 4 in
+        // flight, x staged before A, one workgroup per CU
+        p.variant = 1;
+        p.waves = 8;
+        p.D = 4;
+        p.rows = 1;
+        p.stg = 1;
+        p.cap = 1;
     } else {
         // short INT4 rows: 8 waves, 2 units in flight, split staging;
         // longer rows: 4 waves, 4 units, x staged before A
@@ -400,11 +442,11 @@ int launch(int kind, const void* A, const uint16_t* scale, const void* x, float*
         return GEMV_E_INVAL;
     if ((kind == kQ8 || kind == kQ4) && N > 0 && scale == nullptr)
         return GEMV_E_INVAL;
-    int cus = 0;
-    if (int rc = current_cu_count(&cus); rc != GEMV_OK)
+    Device dev{};
+    if (int rc = current_device(&dev); rc != GEMV_OK)
         return rc;
     const bool aligned = aligned16(A) && aligned16(x);
-    const Plan p = make_plan(kind, M, N, aligned, cus);
+    const Plan p = make_plan(kind, M, N, aligned, dev);
     const uint8_t* a8 = static_cast<const uint8_t*>(A);
     const uint8_t* x8 = static_cast<const uint8_t*>(x);
     void* args[] = {(void*)&a8, (void*)&scale, (void*)&x8, (void*)&y, (void*)&M, (void*)&N};
@@ -419,9 +461,10 @@ constexpr int kProbeWgPerCu = 8;
 
 int probe_grid(int64_t n16, int* grid)
 {
-    int cus = 0;
-    if (int rc = current_cu_count(&cus); rc != GEMV_OK)
+    Device dev{};
+    if (int rc = current_device(&dev); rc != GEMV_OK)
         return rc;
+    const int cus = dev.cus;
     const int64_t per_wg = 256 * kProbeU;
     const int64_t need = (n16 + per_wg - 1) / per_wg;
     const int64_t cap = (int64_t)cus * kProbeWgPerCu;
@@ -523,10 +566,10 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
         return GEMV_E_INVAL;
     if (kind == gemv::kQ4 && N % 128 != 0)
         return GEMV_E_UNSUPPORTED;
-    int cus = 0;
-    if (int rc = gemv::current_cu_count(&cus); rc != GEMV_OK)
+    gemv::Device dev{};
+    if (int rc = gemv::current_device(&dev); rc != GEMV_OK)
         return rc;
-    const gemv::Plan p = gemv::make_plan(kind, M, N, aligned != 0, cus);
+    const gemv::Plan p = gemv::make_plan(kind, M, N, aligned != 0, dev);
     info->variant = p.variant;
     info->grid = p.grid;
     info->block = p.block;

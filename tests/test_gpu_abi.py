@@ -141,11 +141,20 @@ def test_describe_launch_fills_all_cus(gpu):
         info = binding.describe_launch(kind, M, N)
         assert info["grid"] >= cus, (kind, M, N, info, cus)
     assert binding.describe_launch("f16", 8, 1001)["variant"] == 3
-    # INT8/INT4 rows whose staged x would pass the 64 KiB LDS budget read x
-    # with each unit
-    assert binding.describe_launch("q8", 1024, 32768)["variant"] == 2
-    assert binding.describe_launch("q4", 1024, 33280)["variant"] == 2
+    # INT8/INT4 rows whose staged x passes 64 KiB: staged while it fits a
+    # workgroup's LDS and the rows are many, else x read with each unit
+    lds_max = props.shared_memory_per_block
     assert binding.describe_launch("q8", 4096, 31744)["variant"] == 1
+    assert binding.describe_launch("q8", 4096, 32768)["variant"] == 1
+    assert binding.describe_launch("q4", 4096, 34816)["variant"] == 1
+    assert binding.describe_launch("q4", 1024, 33280)["variant"] == 2
+    q8_beyond = (lds_max - 64) // 2048 * 1024 + 1024     # one unit past what fits
+    q4_beyond = lds_max // 4096 * 2048 + 2048
+    assert binding.describe_launch("q8", 4096, q8_beyond)["variant"] == 2
+    assert binding.describe_launch("q4", 4096, q4_beyond)["variant"] == 2
+    for kind, M, N in (("q8", 4096, 32768), ("q4", 4096, 34816), ("q8", 1024, 32768)):
+        info = binding.describe_launch(kind, M, N)
+        assert info["variant"] == 2 or info["lds_bytes"] <= lds_max, (kind, M, N, info)
     # INT8/INT4 rows of at most 32 chunks: the packed short-row kernel
     assert binding.describe_launch("q8", 14336, 512)["variant"] == 4
     assert binding.describe_launch("q4", 14336, 1024)["variant"] == 4

@@ -105,6 +105,33 @@ def test_quantised_x_paths_by_rows(gpu, oracle_mod, kind, N, small, large):
         _check(oracle_mod, kind, ops, f"{kind} M={M} N={N} {info}")
 
 
+# (kind, M, N, variant, stage order) on a device of 256 CUs whose workgroups
+# may hold 160 KiB of LDS; rows end in a ragged last pass
+_LONG_INT_ROWS = [
+    ("q8", 1024, 32848, 1, 1),    # 66 KiB of staged x, few rows: one workgroup per CU
+    ("q8", 3000, 32848, 1, 2),    # two workgroups per CU, waves walk two rows
+    ("q8", 3000, 49168, 1, 1),    # 98 KiB: one workgroup per CU, waves walk two rows
+    ("q8", 1500, 49168, 2, -1),   # one workgroup per CU and few rows: x per unit
+    ("q8", 300, 81936, 2, -1),    # staged x would not fit a workgroup
+    ("q4", 3000, 34944, 1, 1),    # 72 KiB: one workgroup per CU
+    ("q4", 1000, 34944, 2, -1),   # few rows: x per unit
+    ("q4", 300, 82048, 2, -1),    # staged x would not fit a workgroup
+]
+
+
+@pytest.mark.parametrize("kind,M,N,variant,stg", _LONG_INT_ROWS)
+def test_long_quantised_rows(gpu, oracle_mod, kind, M, N, variant, stg):
+    # INT8/INT4 rows whose staged x passes 64 KiB: staged up to what one
+    # workgroup may hold (one or two workgroups per CU), x read with each
+    # unit for few rows or beyond that
+    props = torch.cuda.get_device_properties(0)
+    info = binding.describe_launch(kind, M, N)
+    if props.multi_processor_count == 256 and props.shared_memory_per_block == 160 * 1024:
+        assert (info["variant"], info["stage_order"]) == (variant, stg), info
+    ops = inputs.make(kind, M, N, seed=M + 7 * N)
+    _check(oracle_mod, kind, ops, f"{kind} long rows M={M} N={N} {info}")
+
+
 @pytest.mark.parametrize("kind,M,N", [("f32", 8000, 252), ("f32", 9000, 260), ("f16", 14336, 1000),
                                       ("f16x32", 14336, 512), ("f16x32", 14336, 1016), ("f16_acc16", 6000, 1024),
                                       ("q8", 14336, 1008), ("q4", 14336, 2048), ("f16", 14336, 1528),
