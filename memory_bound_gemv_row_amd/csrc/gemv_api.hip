@@ -110,9 +110,10 @@ struct Plan {
 //     rows per CU: 4; FP16 with FP32 x: 4 up to 16 rows per CU, beyond
 //     that 8 with at most 3 workgroups per CU).
 //   INT8, other rows: few rows (M <= 16 x CUs for rows of 2 units, M <= 8 x
-//     CUs for rows up to 16 units): x read with each unit, 8 waves, 2 (two-
-//     unit rows) or 4 in flight -- the staging and its barrier would
-//     dominate such launches.  Otherwise x is staged: rows of 8 units or
+//     CUs for rows up to 16 units, save rows of 8 units or more with M <= 4
+//     x CUs, which stage x as below with 8 waves, x before A, one workgroup
+//     per CU): x read with each unit, 8 waves, 2 (two-unit rows) or 4 in
+//     flight -- the staging and its barrier would dominate such launches.  Otherwise x is staged: rows of 8 units or
 //     more: 8 waves, 4 in flight, A first, a row per wave; rows of 2 units:
 //     8 waves, 2 in flight, split staging (staging loads, A prologue, LDS
 //     writes), at most 3 workgroups per CU; rows of 3-7 units: 4 waves,
@@ -127,8 +128,9 @@ struct Plan {
 //     split staging; longer rows: 4 waves, 4 in flight, x staged before A;
 //     at most 3 workgroups per CU.  Staged x past 64 KiB (rows over 16
 //     units): 8 waves, 4 in flight, x staged before A, one workgroup per
-//     CU; x read with each unit (4 waves, 4 in flight) instead for M <= 4 x
-//     CUs, or where the staged x would not fit the device's LDS.
+//     CU.  x read with each unit (4 waves, 4 in flight) instead for M <= 4
+//     x CUs (any row length), or where the staged x would not fit the
+//     device's LDS.
 //   INT8/INT4 rows of at most 32 chunks (half a wave load): the packed
 //     kernel, 64 / L rows per wave load, 8 waves; with up to 16 row groups
 //     per CU one group per wave, up to 32 two (both in flight), beyond that
@@ -137,7 +139,9 @@ struct Plan {
 //     every unit costs more cache bandwidth than staging it, once the staging
 //     (4N bytes per workgroup) is spread over enough rows: staged for rows of
 //     at least 12 units, or for 8192 rows and more; read with each unit
-//     otherwise, and whenever the staged x would pass 64 KiB.
+//     otherwise.  Rows whose staged x passes 64 KiB stage it up to the
+//     device's LDS per workgroup (8 waves, 4 in flight, x before A, one
+//     workgroup per CU), reading x with each unit beyond that.
 // With a cap the grid stays below the row count and waves walk several
 // rows; otherwise every launch gives each CU work once M >= CUs.
 Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
@@ -253,6 +257,14 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.waves = 4;
             p.D = 8;
             p.cap = 4;
+        } else if (lds_bytes(kind, nchunks) <= dev.lds_max && P > 32) {
+            // staged x past 64 KiB: 8 waves, 4 in flight, x staged before
+            // A, one workgroup per CU
+            p.variant = 1;
+            p.waves = 8;
+            p.D = 4;
+            p.stg = 1;
+            p.cap = 1;
         } else {
             p.variant = 2;
             p.waves = 4;
@@ -287,6 +299,12 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.variant = 2;
             p.waves = 8;
             p.D = 2;
+        } else if (P >= 8 && M <= 4 * cus) {
+            // rows of 8-32 units, at most 4 per CU: 8 waves, x staged before
+            // A, one workgroup per CU
+            p.waves = 8;
+            p.stg = 1;
+            p.cap = 1;
         } else if (P <= 16 && M <= 8 * cus) {
             // few rows (one GPU's share of a row-split matrix): x read with
             // each unit, 8 waves, 4 in flight
@@ -309,10 +327,10 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.stg = 2;
             p.cap = 3;
         }
-    } else if (const int lds = lds_bytes(kind, nchunks);
-               lds > dev.lds_max || (lds > kLdsBytes && M <= 4 * cus)) {
-        // INT4 rows whose staged x would not fit a workgroup, or long rows
-        // and few of them: x read with each unit, 4 waves, 4 in flight
+    } else if (const int lds = lds_bytes(kind, nchunks); lds > dev.lds_max || M <= 4 * cus) {
+        // INT4 rows whose staged x would not fit a workgroup, or at most 4
+        // rows per CU (of 4 units or more: shorter ones took x in
+        // registers): x read with each unit, 4 waves, 4 in flight
         p.variant = 2;
         p.waves = 4;
         p.D = 4;

@@ -177,11 +177,20 @@ def test_describe_launch_fills_all_cus(gpu):
         assert binding.describe_launch(kind, (1 << 30) + 1, 128)["variant"] == 3
         assert binding.describe_launch(kind, 1 << 30, 128)["variant"] != 3
     # FP16 A with FP32 x: x staged in LDS for long rows or many rows, read
-    # with each unit otherwise, and never staged beyond the LDS budget
+    # with each unit otherwise, and never staged beyond what a workgroup may
+    # hold
     assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 1
     assert binding.describe_launch("f16x32", 14336, 4096)["variant"] == 1
     assert binding.describe_launch("f16x32", 4096, 4096)["variant"] == 2
-    assert binding.describe_launch("f16x32", 64, 32768)["variant"] == 2
+    info = binding.describe_launch("f16x32", 64, 32768)
+    assert info["variant"] == 1 and info["lds_bytes"] == 4 * 32768 <= lds_max, info
+    assert binding.describe_launch("f16x32", 64, lds_max // 4 + 512)["variant"] == 2
+    # few long INT8 rows stage x (one workgroup per CU); few INT4 rows of
+    # four units or more read x with each unit
+    assert binding.describe_launch("q8", 4 * cus, 8192)["stage_order"] == 1
+    assert binding.describe_launch("q8", 4 * cus + 1, 8192)["variant"] == 2
+    assert binding.describe_launch("q4", 4 * cus, 8192)["variant"] == 2
+    assert binding.describe_launch("q4", 4 * cus + 1, 8192)["variant"] == 1
 
 
 def test_probe_copy_and_read(gpu):

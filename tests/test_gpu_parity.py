@@ -116,14 +116,18 @@ _LONG_INT_ROWS = [
     ("q4", 3000, 34944, 1, 1),    # 72 KiB: one workgroup per CU
     ("q4", 1000, 34944, 2, -1),   # few rows: x per unit
     ("q4", 300, 82048, 2, -1),    # staged x would not fit a workgroup
+    ("q8", 1000, 16400, 1, 1),    # rows of 17 units, few of them: staged, one workgroup per CU
+    ("q4", 1000, 8320, 2, -1),    # few INT4 rows of 5 units: x per unit
+    ("f16x32", 700, 24584, 1, 1),  # 96 KiB of FP32 x: staged, one workgroup per CU
+    ("f16x32", 300, 40968, 2, -1),  # FP32 x would not fit a workgroup
 ]
 
 
 @pytest.mark.parametrize("kind,M,N,variant,stg", _LONG_INT_ROWS)
 def test_long_quantised_rows(gpu, oracle_mod, kind, M, N, variant, stg):
-    # INT8/INT4 rows whose staged x passes 64 KiB: staged up to what one
-    # workgroup may hold (one or two workgroups per CU), x read with each
-    # unit for few rows or beyond that
+    # rows whose staged x passes 64 KiB (and few long INT rows): staged up
+    # to what one workgroup may hold (one or two workgroups per CU), x read
+    # with each unit for few rows or beyond that
     props = torch.cuda.get_device_properties(0)
     info = binding.describe_launch(kind, M, N)
     if props.multi_processor_count == 256 and props.shared_memory_per_block == 160 * 1024:
