@@ -38,7 +38,10 @@
  *              enqueued.  Faults during execution surface at the caller's
  *              next synchronisation, as for any HIP kernel.
  *   Threads    Entry points are thread-safe and may be called concurrently on
- *              different streams.
+ *              different streams.  The only state the library keeps is each
+ *              device's compute-unit count and LDS per workgroup, read on its
+ *              first call on that device (under a lock) and kept until the
+ *              process ends; the launch geometry is chosen from them.
  */
 #ifndef MBGR_GEMV_H
 #define MBGR_GEMV_H

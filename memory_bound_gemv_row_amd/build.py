@@ -18,7 +18,8 @@ SRC_DIR = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemv_amd.so")
 SOURCES = [os.path.join(SRC_DIR, f) for f in ("gemv_api.hip", "quant_api.hip", "softmax_api.hip")]
-DEPENDS = SOURCES + [os.path.join(SRC_DIR, f) for f in ("gemv_kernels.hpp", "quant_kernels.hpp", "softmax_kernels.hpp")] \
+DEPENDS = SOURCES + [os.path.join(SRC_DIR, f) for f in ("gemv_kernels.hpp", "quant_kernels.hpp", "softmax_kernels.hpp",
+                                                    "device_info.hpp")] \
     + [os.path.join(INCLUDE, f) for f in ("gemv.h", "gemv_quant.h", "gemv_softmax.h")]
 ARCH = "gfx950"
 

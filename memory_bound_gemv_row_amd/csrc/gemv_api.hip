@@ -7,46 +7,17 @@
 // grid is sized from the row count and the device's compute-unit count, and
 // a launch failure is returned as a status instead of ending the process.
 #include "gemv.h"
+#include "device_info.hpp"
 #include "gemv_kernels.hpp"
 
 #include <hip/hip_runtime.h>
-
-#include <mutex>
 
 namespace gemv {
 namespace {
 
 constexpr int kLdsBytes = 64 * 1024;   // x staged in LDS up to this size
 constexpr bool kNT = true;             // stream A with non-temporal loads
-constexpr int kMaxDevices = 64;
-
-// What the plans need to know of a device.
-struct Device {
-    int cus;       // compute units
-    int lds_max;   // bytes of LDS one workgroup may hold
-};
-
-std::mutex g_dev_mutex;
-Device g_dev[kMaxDevices] = {};
-
-// Properties of the current device, cached per device.
-int current_device(Device* out)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return GEMV_E_DEVICE;
-    std::lock_guard<std::mutex> lock(g_dev_mutex);
-    if (g_dev[dev].cus == 0) {
-        int n = 0, lds = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0 ||
-            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-            lds <= 0)
-            return GEMV_E_DEVICE;
-        g_dev[dev] = {n, lds};
-    }
-    *out = g_dev[dev];
-    return GEMV_OK;
-}
+using gemv_device::Device;
 
 int elems_per_chunk(int kind)
 {
@@ -461,7 +432,7 @@ int launch(int kind, const void* A, const uint16_t* scale, const void* x, float*
     if ((kind == kQ8 || kind == kQ4) && N > 0 && scale == nullptr)
         return GEMV_E_INVAL;
     Device dev{};
-    if (int rc = current_device(&dev); rc != GEMV_OK)
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
         return rc;
     const bool aligned = aligned16(A) && aligned16(x);
     const Plan p = make_plan(kind, M, N, aligned, dev);
@@ -480,7 +451,7 @@ constexpr int kProbeWgPerCu = 8;
 int probe_grid(int64_t n16, int* grid)
 {
     Device dev{};
-    if (int rc = current_device(&dev); rc != GEMV_OK)
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
         return rc;
     const int cus = dev.cus;
     const int64_t per_wg = 256 * kProbeU;
@@ -585,7 +556,7 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
     if (kind == gemv::kQ4 && N % 128 != 0)
         return GEMV_E_UNSUPPORTED;
     gemv::Device dev{};
-    if (int rc = gemv::current_device(&dev); rc != GEMV_OK)
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
         return rc;
     const gemv::Plan p = gemv::make_plan(kind, M, N, aligned != 0, dev);
     info->variant = p.variant;

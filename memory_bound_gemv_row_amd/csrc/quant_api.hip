@@ -1,32 +1,21 @@
 // quant_api.hip -- C ABI of the weight quantiser (declared in
 // include/gemv_quant.h): validation, geometry and launch.
 #include "gemv_quant.h"
+#include "device_info.hpp"
 #include "quant_kernels.hpp"
 
 #include <hip/hip_runtime.h>
 
-#include <mutex>
-
 namespace gquant {
 namespace {
 
-constexpr int kMaxDevices = 64;
-std::mutex g_mutex;
-int g_cus[kMaxDevices] = {0};
-
+// compute units of the current device
 int cu_count(int* out)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return GEMV_E_DEVICE;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    if (g_cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return GEMV_E_DEVICE;
-        g_cus[dev] = n;
-    }
-    *out = g_cus[dev];
+    gemv_device::Device dev{};
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
+        return rc;
+    *out = dev.cus;
     return GEMV_OK;
 }
 
@@ -96,10 +85,11 @@ int gemv_quantize_q4(const float* W, uint8_t* q, uint16_t* scale, float* row_sse
         return GEMV_E_UNSUPPORTED;
     if (M == 0)
         return GEMV_OK;
-    int cus = 0;
-    if (int rc = cu_count(&cus); rc != GEMV_OK)
+    // the grid is one wave per row and needs no CU count, but a call
+    // without a usable device fails here like the others
+    gemv_device::Device dev{};
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
         return rc;
-    (void)cus;
     const int grid4 = (int)(((int64_t)M + 3) / 4);
     if (N == 0 || !aligned(W, 16) || !aligned(q, 2) || M > (1 << 30))   // as for INT8
         return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<7>), grid4, 256, W, q, scale,

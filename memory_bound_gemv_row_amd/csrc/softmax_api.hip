@@ -1,33 +1,23 @@
 // softmax_api.hip -- C ABI of the row softmax (declared in
 // include/gemv_softmax.h): validation, geometry and launch.
 #include "gemv_softmax.h"
+#include "device_info.hpp"
 #include "softmax_kernels.hpp"
 
 #include <hip/hip_runtime.h>
 
-#include <mutex>
-
 namespace gsoftmax {
 namespace {
 
-constexpr int kMaxDevices = 64;
 constexpr int kWavesPerCu = 32;   // resident waves a CU can hold
-std::mutex g_mutex;
-int g_cus[kMaxDevices] = {0};
 
+// compute units of the current device
 int cu_count(int* out)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return GEMV_E_DEVICE;
-    std::lock_guard<std::mutex> lock(g_mutex);
-    if (g_cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return GEMV_E_DEVICE;
-        g_cus[dev] = n;
-    }
-    *out = g_cus[dev];
+    gemv_device::Device dev{};
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
+        return rc;
+    *out = dev.cus;
     return GEMV_OK;
 }
 

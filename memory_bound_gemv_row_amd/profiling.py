@@ -23,11 +23,13 @@ import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ("memory_bound_gemv_row_amd/csrc/gemv_kernels.hpp", "memory_bound_gemv_row_amd/csrc/gemv_api.hip")
+_CSRC = "memory_bound_gemv_row_amd/csrc/"
+# the device properties the plans read are part of every operation's code
+KERNEL_SOURCES = (_CSRC + "gemv_kernels.hpp", _CSRC + "gemv_api.hip", _CSRC + "device_info.hpp")
 OP_SOURCES = {
     "gemv": KERNEL_SOURCES,
-    "quant": ("memory_bound_gemv_row_amd/csrc/quant_kernels.hpp", "memory_bound_gemv_row_amd/csrc/quant_api.hip"),
-    "softmax": ("memory_bound_gemv_row_amd/csrc/softmax_kernels.hpp", "memory_bound_gemv_row_amd/csrc/softmax_api.hip"),
+    "quant": (_CSRC + "quant_kernels.hpp", _CSRC + "quant_api.hip", _CSRC + "device_info.hpp"),
+    "softmax": (_CSRC + "softmax_kernels.hpp", _CSRC + "softmax_api.hip", _CSRC + "device_info.hpp"),
 }
 PROBE_READ_BYTES = 1 << 30
 PROBE_COPY_BYTES = 256 << 20

@@ -107,7 +107,7 @@ def test_quantised_x_paths_by_rows(gpu, oracle_mod, kind, N, small, large):
 
 # (kind, M, N, variant, stage order) on a device of 256 CUs whose workgroups
 # may hold 160 KiB of LDS; rows end in a ragged last pass
-_LONG_INT_ROWS = [
+_LONG_ROWS = [
     ("q8", 1024, 32848, 1, 1),    # 66 KiB of staged x, few rows: one workgroup per CU
     ("q8", 3000, 32848, 1, 2),    # two workgroups per CU, waves walk two rows
     ("q8", 3000, 49168, 1, 1),    # 98 KiB: one workgroup per CU, waves walk two rows
@@ -120,11 +120,14 @@ _LONG_INT_ROWS = [
     ("q4", 1000, 8320, 2, -1),    # few INT4 rows of 5 units: x per unit
     ("f16x32", 700, 24584, 1, 1),  # 96 KiB of FP32 x: staged, one workgroup per CU
     ("f16x32", 300, 40968, 2, -1),  # FP32 x would not fit a workgroup
+    ("q4", 3000, 81920, 1, 1),    # staged x of exactly 160 KiB
+    ("q8", 3000, 80848, 1, 1),    # 158 KiB, ragged last pass
+    ("f16x32", 700, 40960, 1, 1),  # 160 KiB of FP32 x
 ]
 
 
-@pytest.mark.parametrize("kind,M,N,variant,stg", _LONG_INT_ROWS)
-def test_long_quantised_rows(gpu, oracle_mod, kind, M, N, variant, stg):
+@pytest.mark.parametrize("kind,M,N,variant,stg", _LONG_ROWS)
+def test_long_rows_staged_or_per_unit(gpu, oracle_mod, kind, M, N, variant, stg):
     # rows whose staged x passes 64 KiB (and few long INT rows): staged up
     # to what one workgroup may hold (one or two workgroups per CU), x read
     # with each unit for few rows or beyond that
