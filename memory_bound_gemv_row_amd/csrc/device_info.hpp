@@ -1,7 +1,8 @@
-// device_info.hpp -- the properties of the current HIP device that the
-// launch plans read (compute units, LDS one workgroup may hold), looked up
-// once per device and kept for the life of the process.  Shared by the
-// GEMV, quantiser and softmax entry points.
+// device_info.hpp -- what every launch of the library reads about the
+// device: the properties of the current HIP device that the launch plans
+// use (compute units, LDS one workgroup may hold), looked up once per
+// device and kept for the life of the process, and the bound on a launch's
+// work-items.  Shared by the GEMV, quantiser and softmax entry points.
 #pragma once
 
 #include "gemv.h"
@@ -9,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <stdint.h>
 
 namespace gemv_device {
 
@@ -18,6 +20,17 @@ struct Device {
 };
 
 constexpr int kMaxDevices = 64;
+
+// A dispatch counts its work-items in 32 bits, so every launch keeps
+// grid x block at or below 2^30; the kernels walk whatever rows (or row
+// groups) lie beyond their grid.
+constexpr int64_t kMaxWorkItems = int64_t(1) << 30;
+
+inline int capped_grid(int64_t grid, int block)
+{
+    const int64_t cap = kMaxWorkItems / block;
+    return (int)(grid < cap ? grid : cap);
+}
 
 // Properties of the current device; GEMV_E_DEVICE when there is none or its
 // attributes cannot be read.  Thread-safe; one cache for the whole library

@@ -131,7 +131,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.variant = 3;
         p.block = 256;
         p.waves = 4;
-        p.grid = (int)(((int64_t)M + 3) / 4);
+        p.grid = gemv_device::capped_grid(((int64_t)M + 3) / 4, p.block);
         p.rows = 1;
         p.D = 1;
         return p;
@@ -150,7 +150,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.lds = 0;
         p.block = p.waves * 64;
         const int64_t waves_needed = (groups + p.rows - 1) / p.rows;
-        p.grid = (int)((waves_needed + p.waves - 1) / p.waves);
+        p.grid = gemv_device::capped_grid((waves_needed + p.waves - 1) / p.waves, p.block);
         return p;
     }
     const bool fp = kind == kF32 || kind == kF16 || kind == kF16H;
@@ -331,7 +331,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
     int64_t grid = (waves_needed + p.waves - 1) / p.waves;
     if (p.cap > 0 && grid > (int64_t)p.cap * cus)
         grid = (int64_t)p.cap * cus;
-    p.grid = (int)grid;
+    p.grid = gemv_device::capped_grid(grid, p.block);
     return p;
 }
 

@@ -905,66 +905,67 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 // ---------------------------------------------------------------- element-wise kernel
 // Any N >= 0 and any alignment: one wave per row, lane l takes columns
 // l, l+64, ... with scalar loads (INT4: bytes l, l+64, ..., two columns
-// each).  Four waves per workgroup.
+// each).  Four waves per workgroup; waves walk rows 4 x gridDim.x apart.
 template <int F>
 __global__ void __launch_bounds__(256)
 gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
                  const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M)
-        return;   // whole wave leaves together
-    float acc = 0.0f;
-    if constexpr (F == kF32) {
-        const float* a = reinterpret_cast<const float*>(A) + (int64_t)row * N;
-        const float* xf = reinterpret_cast<const float*>(x);
-        for (int64_t j = lane; j < N; j += 64)
-            acc = __builtin_fmaf(a[j], xf[j], acc);
-    } else if constexpr (F == kF16) {
-        const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
-        const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
-        for (int64_t j = lane; j < N; j += 64)
-            acc = __builtin_fmaf(half_bits_to_float(a[j]), half_bits_to_float(xh[j]), acc);
-    } else if constexpr (F == kF16X32) {
-        const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
-        const float* xf = reinterpret_cast<const float*>(x);
-        for (int64_t j = lane; j < N; j += 64)
-            acc = __builtin_fmaf(half_bits_to_float(a[j]), xf[j], acc);
-    } else if constexpr (F == kF16H) {
-        // one binary16 running sum per lane (ceil(N/64) terms)
-        const _Float16* a = reinterpret_cast<const _Float16*>(A) + (int64_t)row * N;
-        const _Float16* xh = reinterpret_cast<const _Float16*>(x);
-        _Float16 h = (_Float16)0.0f;
-        for (int64_t j = lane; j < N; j += 64)
-            h = __builtin_fmaf16(a[j], xh[j], h);
-        acc = (float)h;
-    } else if constexpr (F == kQ8) {
-        const int8_t* a = reinterpret_cast<const int8_t*>(A) + (int64_t)row * N;
-        const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
-        for (int64_t j = lane; j < N; j += 64)
-            acc = __builtin_fmaf((float)a[j], half_bits_to_float(xh[j]), acc);
-    } else {
-        const int half_n = N / 2;
-        const uint8_t* a = A + (int64_t)row * half_n;
-        const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
-        const uint16_t* srow = scale + (int64_t)row * (N / 128);
-        for (int b = lane; b < half_n; b += 64) {
-            const unsigned byte = a[b];
-            const int q0 = (int)(byte & 0xFu) - (int)((byte & 0x8u) << 1);
-            const int q1 = (int)(byte >> 4) - (int)((byte & 0x80u) >> 3);
-            const float s = half_bits_to_float(srow[(2 * b) >> 7]);
-            acc = __builtin_fmaf((float)q0 * s, half_bits_to_float(xh[2 * b]), acc);
-            acc = __builtin_fmaf((float)q1 * s, half_bits_to_float(xh[2 * b + 1]), acc);
+    // rows walked grid-stride (wave-uniform), so any grid covers them
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < M; row += stride) {
+        float acc = 0.0f;
+        if constexpr (F == kF32) {
+            const float* a = reinterpret_cast<const float*>(A) + (int64_t)row * N;
+            const float* xf = reinterpret_cast<const float*>(x);
+            for (int64_t j = lane; j < N; j += 64)
+                acc = __builtin_fmaf(a[j], xf[j], acc);
+        } else if constexpr (F == kF16) {
+            const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
+            const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+            for (int64_t j = lane; j < N; j += 64)
+                acc = __builtin_fmaf(half_bits_to_float(a[j]), half_bits_to_float(xh[j]), acc);
+        } else if constexpr (F == kF16X32) {
+            const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
+            const float* xf = reinterpret_cast<const float*>(x);
+            for (int64_t j = lane; j < N; j += 64)
+                acc = __builtin_fmaf(half_bits_to_float(a[j]), xf[j], acc);
+        } else if constexpr (F == kF16H) {
+            // one binary16 running sum per lane (ceil(N/64) terms)
+            const _Float16* a = reinterpret_cast<const _Float16*>(A) + (int64_t)row * N;
+            const _Float16* xh = reinterpret_cast<const _Float16*>(x);
+            _Float16 h = (_Float16)0.0f;
+            for (int64_t j = lane; j < N; j += 64)
+                h = __builtin_fmaf16(a[j], xh[j], h);
+            acc = (float)h;
+        } else if constexpr (F == kQ8) {
+            const int8_t* a = reinterpret_cast<const int8_t*>(A) + (int64_t)row * N;
+            const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+            for (int64_t j = lane; j < N; j += 64)
+                acc = __builtin_fmaf((float)a[j], half_bits_to_float(xh[j]), acc);
+        } else {
+            const int half_n = N / 2;
+            const uint8_t* a = A + (int64_t)row * half_n;
+            const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+            const uint16_t* srow = scale + (int64_t)row * (N / 128);
+            for (int b = lane; b < half_n; b += 64) {
+                const unsigned byte = a[b];
+                const int q0 = (int)(byte & 0xFu) - (int)((byte & 0x8u) << 1);
+                const int q1 = (int)(byte >> 4) - (int)((byte & 0x80u) >> 3);
+                const float s = half_bits_to_float(srow[(2 * b) >> 7]);
+                acc = __builtin_fmaf((float)q0 * s, half_bits_to_float(xh[2 * b]), acc);
+                acc = __builtin_fmaf((float)q1 * s, half_bits_to_float(xh[2 * b + 1]), acc);
+            }
         }
-    }
-    float t = wave_sum(acc);
-    if (lane == 0) {
-        // N == 0 is the empty sum: y = 0 whatever the scale (which is not read)
-        if constexpr (F == kQ8)
-            if (N > 0)
-                t *= half_bits_to_float(scale[row]);
-        y[row] = t;
+        float t = wave_sum(acc);
+        if (lane == 0) {
+            // N == 0 is the empty sum: y = 0 whatever the scale (which is not read)
+            if constexpr (F == kQ8)
+                if (N > 0)
+                    t *= half_bits_to_float(scale[row]);
+            y[row] = t;
+        }
     }
 }
 

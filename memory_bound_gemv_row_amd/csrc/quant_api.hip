@@ -36,6 +36,19 @@ const void* q8_kernel(int P)
                    : reinterpret_cast<const void*>(&quantize_q8_kernel<4, 16, SSE>);
 }
 
+template <bool SSE>
+const void* row_kernel_q4_sse(int waves)
+{
+    return waves == 4 ? reinterpret_cast<const void*>(&quantize_q4_rows_kernel<4, 4, SSE>)
+         : waves == 8 ? reinterpret_cast<const void*>(&quantize_q4_rows_kernel<8, 4, SSE>)
+                      : reinterpret_cast<const void*>(&quantize_q4_rows_kernel<16, 4, SSE>);
+}
+
+const void* row_kernel_q4(int waves, bool sse)
+{
+    return sse ? row_kernel_q4_sse<true>(waves) : row_kernel_q4_sse<false>(waves);
+}
+
 int check(const float* W, const void* q, const uint16_t* scale, int M, int N)
 {
     if (M < 0 || N < 0)
@@ -63,7 +76,7 @@ int gemv_quantize_q8(const float* W, int8_t* q, uint16_t* scale, float* row_sse,
         return rc;
     // more than 2^30 rows: the row-walking kernels' int row cursors could
     // pass INT_MAX; the element-wise kernel indexes rows in 64 bits
-    const int grid4 = (int)(((int64_t)M + 3) / 4);
+    const int grid4 = gemv_device::capped_grid(((int64_t)M + 3) / 4, 256);
     if (N == 0 || N % 4 != 0 || !aligned(W, 16) || !aligned(q, 4) || M > (1 << 30))
         return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<127>), grid4, 256, W, q, scale,
                       row_sse, M, N, stream);
@@ -85,19 +98,27 @@ int gemv_quantize_q4(const float* W, uint8_t* q, uint16_t* scale, float* row_sse
         return GEMV_E_UNSUPPORTED;
     if (M == 0)
         return GEMV_OK;
-    // the grid is one wave per row and needs no CU count, but a call
-    // without a usable device fails here like the others
+    // the grids need no CU count, but a call without a usable device fails
+    // here like the others
     gemv_device::Device dev{};
     if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
         return rc;
-    const int grid4 = (int)(((int64_t)M + 3) / 4);
+    const int grid4 = gemv_device::capped_grid(((int64_t)M + 3) / 4, 256);
     if (N == 0 || !aligned(W, 16) || !aligned(q, 2) || M > (1 << 30))   // as for INT8
         return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<7>), grid4, 256, W, q, scale,
                       row_sse, M, N, stream);
-    // one wave per row, 4 waves per workgroup, 4 units in flight per wave
-    const void* fn = row_sse != nullptr ? reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, true>)
-                                        : reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, false>);
-    return launch(fn, grid4, 256, W, q, scale, row_sse, M, N, stream);
+    const int P = (N / 4 + 63) / 64;
+    if (P < 16) {
+        // one wave per row, 4 waves per workgroup, 4 units in flight per wave
+        const void* fn = row_sse != nullptr ? reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, true>)
+                                            : reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, false>);
+        return launch(fn, grid4, 256, W, q, scale, row_sse, M, N, stream);
+    }
+    // a workgroup per row, 4 units in flight per wave, 4 to 16 waves so that
+    // each takes about 4 to 8 of the row's units
+    const int waves = P < 48 ? 4 : (P < 128 ? 8 : 16);
+    return launch(row_kernel_q4(waves, row_sse != nullptr), gemv_device::capped_grid(M, waves * 64), waves * 64, W, q,
+                  scale, row_sse, M, N, stream);
 }
 
 }  // extern "C"

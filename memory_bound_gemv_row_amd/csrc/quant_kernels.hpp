@@ -20,7 +20,10 @@
 //   * INT4 (a scale per 128 columns): a group is 32 lanes' 16-byte chunks,
 //     so one wave load holds two whole groups; the group maximum is a
 //     32-lane butterfly and every unit is quantised as soon as it arrives.
-//     Waves stream their rows with loads D units ahead, like the GEMV.
+//     Short rows: each wave streams whole rows with loads D units ahead,
+//     like the GEMV.  Rows of 16 units and more: a workgroup per row, its
+//     waves taking every WAVES-th unit (no group spans two waves, so they
+//     share nothing but the row's squared error, summed through LDS).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -234,6 +237,36 @@ quantize_q8_kernel(const float* __restrict__ W, int8_t* __restrict__ q, uint16_t
 }
 
 // ---------------------------------------------------------------- INT4
+// One INT4 unit of row `row`: lane `lane` holds chunk c (columns 4c..4c+3)
+// of unit `unit` in v; lanes 0-31 hold the unit's first group, 32-63 its
+// second.  Every lane takes part in the group maxima; only `live` lanes
+// store codes (bytes 2c and 2c+1, the even column in the low nibble) and,
+// lanes 0 and 32, the group scales.  Returns the lane's squared error (0
+// unless SSE and live).
+template <bool SSE>
+__device__ __forceinline__ float q4_unit(const u32x4 v, int lane, int c, bool live, int row, int unit, int N,
+                                         uint8_t* __restrict__ q, uint16_t* __restrict__ scale)
+{
+    const float amax = half_wave_max(absmax4(v));
+    const uint16_t sb = scale_bits<7>(amax);
+    const float sf = half_to_float(sb);
+    const float inv = inverse_of(sf);
+    const float w0 = as_f(v.x), w1 = as_f(v.y), w2 = as_f(v.z), w3 = as_f(v.w);
+    const float c0 = code_of<7>(w0, sf, inv), c1 = code_of<7>(w1, sf, inv);
+    const float c2 = code_of<7>(w2, sf, inv), c3 = code_of<7>(w3, sf, inv);
+    float e = 0.0f;
+    if (live) {
+        if constexpr (SSE)
+            e = sq_err(c0, sf, w0) + sq_err(c1, sf, w1) + sq_err(c2, sf, w2) + sq_err(c3, sf, w3);
+        const uint32_t packed = ((uint32_t)(int)c0 & 0xFu) | (((uint32_t)(int)c1 & 0xFu) << 4) |
+                                (((uint32_t)(int)c2 & 0xFu) << 8) | (((uint32_t)(int)c3 & 0xFu) << 12);
+        reinterpret_cast<uint16_t*>(q + (int64_t)row * (N >> 1))[c] = (uint16_t)packed;
+        if ((lane & 31) == 0)
+            scale[(int64_t)row * (N >> 7) + unit * 2 + (lane >> 5)] = sb;
+    }
+    return e;
+}
+
 // Preconditions (host): N % 128 == 0, W 16-byte aligned, q 2-byte aligned,
 // M >= 1.  Each wave owns rows wave_id, wave_id + nwaves, ... and walks
 // their units (one 1-KiB wave load = two 128-column groups; a ragged last
@@ -248,7 +281,6 @@ quantize_q4_kernel(const float* __restrict__ W, uint8_t* __restrict__ q, uint16_
     const int lane = threadIdx.x & 63;
     const int nchunks = N >> 2;
     const int P = (nchunks + 63) >> 6;
-    const int groups = N >> 7;
     const int wave_id = blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nwaves = gridDim.x * WAVES;
     const int my_rows = wave_id < M ? (M - 1 - wave_id) / nwaves + 1 : 0;
@@ -277,26 +309,11 @@ quantize_q4_kernel(const float* __restrict__ W, uint8_t* __restrict__ q, uint16_
     float sse = 0.0f;
     int c_row = wave_id, c_pass = 0;
     auto consume = [&](int d) {
-        const u32x4 v = buf[d];
+        // padded units and lanes past the row store nothing
         const int c = c_pass * 64 + lane;
-        const bool live = c_row < M && c < nchunks;   // padded units and lanes past the row store nothing
-        const float amax = half_wave_max(absmax4(v));
-        const uint16_t sb = scale_bits<7>(amax);
-        const float sf = half_to_float(sb);
-        const float inv = inverse_of(sf);
-        const float w0 = as_f(v.x), w1 = as_f(v.y), w2 = as_f(v.z), w3 = as_f(v.w);
-        const float c0 = code_of<7>(w0, sf, inv), c1 = code_of<7>(w1, sf, inv);
-        const float c2 = code_of<7>(w2, sf, inv), c3 = code_of<7>(w3, sf, inv);
-        if (live) {
-            if constexpr (SSE)
-                sse += sq_err(c0, sf, w0) + sq_err(c1, sf, w1) + sq_err(c2, sf, w2) + sq_err(c3, sf, w3);
-            // columns 4c..4c+3 -> bytes 2c (low nibble: even column) and 2c+1
-            const uint32_t packed = ((uint32_t)(int)c0 & 0xFu) | (((uint32_t)(int)c1 & 0xFu) << 4) |
-                                    (((uint32_t)(int)c2 & 0xFu) << 8) | (((uint32_t)(int)c3 & 0xFu) << 12);
-            reinterpret_cast<uint16_t*>(q + (int64_t)c_row * (N >> 1))[c] = (uint16_t)packed;
-            if ((lane & 31) == 0)
-                scale[(int64_t)c_row * groups + c_pass * 2 + (lane >> 5)] = sb;
-        }
+        const float e = q4_unit<SSE>(buf[d], lane, c, c_row < M && c < nchunks, c_row, c_pass, N, q, scale);
+        if constexpr (SSE)
+            sse += e;
         if (++c_pass == P) {
             if constexpr (SSE) {
                 const float t = wave_sum(sse);
@@ -320,57 +337,117 @@ quantize_q4_kernel(const float* __restrict__ W, uint8_t* __restrict__ q, uint16_
         consume(d);
 }
 
+// Rows of many units: workgroup g quantises rows g, g + gridDim.x, ...;
+// wave w takes the row's units w, w + WAVES, ... with loads D units ahead
+// (within the row).  With SSE the waves' partial sums meet in LDS and one
+// lane adds them in wave order, so the result does not depend on timing.
+// Same preconditions as quantize_q4_kernel.
+template <int WAVES, int D, bool SSE>
+__global__ void __launch_bounds__(WAVES * 64)
+quantize_q4_rows_kernel(const float* __restrict__ W, uint8_t* __restrict__ q, uint16_t* __restrict__ scale,
+                        float* __restrict__ row_sse, int M, int N)
+{
+    __shared__ float red[WAVES];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nchunks = N >> 2;
+    const int P = (nchunks + 63) >> 6;
+    const int k = P > wave ? (P - 1 - wave) / WAVES + 1 : 0;   // this wave's units in every row
+    for (int row = blockIdx.x; row < M; row += gridDim.x) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(W + (int64_t)row * N);
+        auto load = [&](int j) {   // this wave's j-th unit of the row
+            const int c = (wave + j * WAVES) * 64 + lane;
+            return c < nchunks ? __builtin_nontemporal_load(src + c) : u32x4{0u, 0u, 0u, 0u};
+        };
+        u32x4 buf[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (d < k)
+                buf[d] = load(d);
+        float sse = 0.0f;
+        for (int j0 = 0; j0 < k; j0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int j = j0 + d;
+                if (j < k) {   // wave-uniform
+                    const int u = wave + j * WAVES;
+                    const int c = u * 64 + lane;
+                    const float e = q4_unit<SSE>(buf[d], lane, c, c < nchunks, row, u, N, q, scale);
+                    if constexpr (SSE)
+                        sse += e;
+                    if (j + D < k)
+                        buf[d] = load(j + D);
+                }
+            }
+        }
+        if constexpr (SSE) {
+            const float t = wave_sum(sse);
+            if (lane == 0)
+                red[wave] = t;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                float r = 0.0f;
+                for (int w = 0; w < WAVES; ++w)
+                    r += red[w];
+                row_sse[row] = r;
+            }
+            __syncthreads();   // red is reused by the next row
+        }
+    }
+}
+
 // ---------------------------------------------------------------- element-wise
 // Any alignment and (INT8) any N: one wave per row, two passes with scalar
-// loads (maximum, then codes).  INT4 still needs N % 128 == 0.
+// loads (maximum, then codes).  INT4 still needs N % 128 == 0.  Waves walk
+// rows 4 x gridDim.x apart, so any grid covers them.
 template <int QMAX>
 __global__ void __launch_bounds__(256)
 quantize_elementwise_kernel(const float* __restrict__ W, uint8_t* __restrict__ q, uint16_t* __restrict__ scale,
                             float* __restrict__ row_sse, int M, int N)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M)
-        return;   // whole wave leaves together
-    const float* w = W + (int64_t)row * N;
-    float sse = 0.0f;
-    if constexpr (QMAX == 127) {
-        float amax = 0.0f;
-        for (int64_t j = lane; j < N; j += 64)
-            amax = fmaxf(amax, fabsf(w[j]));
-        amax = wave_max(amax);
-        const uint16_t sb = scale_bits<127>(amax);
-        const float sf = half_to_float(sb);
-        const float inv = inverse_of(sf);
-        if (lane == 0)
-            scale[row] = sb;
-        int8_t* dst = reinterpret_cast<int8_t*>(q) + (int64_t)row * N;
-        for (int64_t j = lane; j < N; j += 64) {
-            const float c = code_of<127>(w[j], sf, inv);
-            dst[j] = (int8_t)(int)c;
-            sse += sq_err(c, sf, w[j]);
-        }
-    } else {
-        // lane l handles byte pairs: columns 2b, 2b+1 for b = l, l+64, ...;
-        // a group of 128 columns is 64 bytes, i.e. exactly one pass
-        const int groups = N >> 7;
-        uint8_t* dst = q + (int64_t)row * (N >> 1);
-        for (int g = 0; g < groups; ++g) {
-            const float a = w[g * 128 + 2 * lane], b = w[g * 128 + 2 * lane + 1];
-            const float amax = wave_max(fmaxf(fabsf(a), fabsf(b)));
-            const uint16_t sb = scale_bits<7>(amax);
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < M; row += stride) {   // wave-uniform
+        const float* w = W + (int64_t)row * N;
+        float sse = 0.0f;
+        if constexpr (QMAX == 127) {
+            float amax = 0.0f;
+            for (int64_t j = lane; j < N; j += 64)
+                amax = fmaxf(amax, fabsf(w[j]));
+            amax = wave_max(amax);
+            const uint16_t sb = scale_bits<127>(amax);
             const float sf = half_to_float(sb);
             const float inv = inverse_of(sf);
             if (lane == 0)
-                scale[(int64_t)row * groups + g] = sb;
-            const float ca = code_of<7>(a, sf, inv), cb = code_of<7>(b, sf, inv);
-            dst[g * 64 + lane] = (uint8_t)(((uint32_t)(int)ca & 0xFu) | (((uint32_t)(int)cb & 0xFu) << 4));
-            sse += sq_err(ca, sf, a) + sq_err(cb, sf, b);
+                scale[row] = sb;
+            int8_t* dst = reinterpret_cast<int8_t*>(q) + (int64_t)row * N;
+            for (int64_t j = lane; j < N; j += 64) {
+                const float c = code_of<127>(w[j], sf, inv);
+                dst[j] = (int8_t)(int)c;
+                sse += sq_err(c, sf, w[j]);
+            }
+        } else {
+            // lane l handles byte pairs: columns 2b, 2b+1 for b = l, l+64, ...;
+            // a group of 128 columns is 64 bytes, i.e. exactly one pass
+            const int groups = N >> 7;
+            uint8_t* dst = q + (int64_t)row * (N >> 1);
+            for (int g = 0; g < groups; ++g) {
+                const float a = w[g * 128 + 2 * lane], b = w[g * 128 + 2 * lane + 1];
+                const float amax = wave_max(fmaxf(fabsf(a), fabsf(b)));
+                const uint16_t sb = scale_bits<7>(amax);
+                const float sf = half_to_float(sb);
+                const float inv = inverse_of(sf);
+                if (lane == 0)
+                    scale[(int64_t)row * groups + g] = sb;
+                const float ca = code_of<7>(a, sf, inv), cb = code_of<7>(b, sf, inv);
+                dst[g * 64 + lane] = (uint8_t)(((uint32_t)(int)ca & 0xFu) | (((uint32_t)(int)cb & 0xFu) << 4));
+                sse += sq_err(ca, sf, a) + sq_err(cb, sf, b);
+            }
         }
+        const float t = wave_sum(sse);
+        if (lane == 0 && row_sse != nullptr)
+            row_sse[row] = t;
     }
-    const float t = wave_sum(sse);
-    if (lane == 0 && row_sse != nullptr)
-        row_sse[row] = t;
 }
 
 }  // namespace gquant

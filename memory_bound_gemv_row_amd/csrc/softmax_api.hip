@@ -76,7 +76,7 @@ extern "C" int gemv_softmax_f16(const uint16_t* x, uint16_t* y, int M, int N, hi
     // more than 2^30 rows: the row-per-workgroup kernel's int row cursor
     // could pass INT_MAX; the element-wise kernel indexes rows in 64 bits
     if (N % 8 != 0 || !aligned16(x) || !aligned16(y) || M > (1 << 30)) {
-        const unsigned grid4 = (unsigned)(((int64_t)M + 3) / 4);
+        const int grid4 = gemv_device::capped_grid(((int64_t)M + 3) / 4, 256);
         err = hipLaunchKernel(reinterpret_cast<const void*>(&softmax_f16_elementwise), dim3(grid4), dim3(256), args,
                               0, stream);
     } else {

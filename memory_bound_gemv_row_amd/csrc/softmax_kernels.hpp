@@ -203,23 +203,24 @@ softmax_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int
 }
 
 // Any N and alignment: one wave per row, three passes with scalar loads
-// (online max and normaliser, then outputs).
+// (online max and normaliser, then outputs).  Waves walk rows 4 x gridDim.x
+// apart (wave-uniform), so any grid covers them.
 __global__ void __launch_bounds__(256)
 softmax_f16_elementwise(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int M, int N)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M)
-        return;   // whole wave leaves together
-    const _Float16* src = reinterpret_cast<const _Float16*>(x) + (int64_t)row * N;
-    _Float16* dst = reinterpret_cast<_Float16*>(y) + (int64_t)row * N;
-    float m = -__builtin_inff(), d = 0.0f;
-    for (int64_t j = lane; j < N; j += 64)
-        merge(m, d, (float)src[j], 1.0f);
-    wave_merge(m, d);
-    const float l2d = log2_hw(d);
-    for (int64_t j = lane; j < N; j += 64)
-        dst[j] = (_Float16)exp2_hw(__builtin_fmaf((float)src[j] - m, kLog2e, -l2d));
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < M; row += stride) {
+        const _Float16* src = reinterpret_cast<const _Float16*>(x) + (int64_t)row * N;
+        _Float16* dst = reinterpret_cast<_Float16*>(y) + (int64_t)row * N;
+        float m = -__builtin_inff(), d = 0.0f;
+        for (int64_t j = lane; j < N; j += 64)
+            merge(m, d, (float)src[j], 1.0f);
+        wave_merge(m, d);
+        const float l2d = log2_hw(d);
+        for (int64_t j = lane; j < N; j += 64)
+            dst[j] = (_Float16)exp2_hw(__builtin_fmaf((float)src[j] - m, kLog2e, -l2d));
+    }
 }
 
 }  // namespace gsoftmax

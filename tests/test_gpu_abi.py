@@ -193,6 +193,18 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("q4", 4 * cus + 1, 8192)["variant"] == 1
 
 
+def test_launches_stay_within_the_dispatch_limit(gpu):
+    # a dispatch counts work-items in 32 bits: every plan keeps grid x block
+    # at or below 2^30, the waves walking any rows beyond
+    for kind in ("f32", "f16", "f16x32", "f16_acc16", "q8", "q4"):
+        for M in (1 << 22, 1 << 24, (1 << 26) + 7, 1 << 28, 1 << 30):
+            for N in (3, 8, 16, 128, 512, 1024, 4096, 65536):
+                if kind == "q4" and N % 128:
+                    continue
+                info = binding.describe_launch(kind, M, N)
+                assert 1 <= info["grid"] and info["grid"] * info["block"] <= 1 << 30, (kind, M, N, info)
+
+
 def test_probe_copy_and_read(gpu):
     n = 64 << 20
     src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")

@@ -440,6 +440,32 @@ def test_nan_propagates(gpu, oracle_mod):
 
 
 # ---------------------------------------------------------------- brute force over small shapes
+@pytest.mark.parametrize("M,N,variant", [((1 << 24) + (1 << 20) + 3, 3, 3), ((1 << 26) + 1000, 8, 2)])
+def test_grids_past_the_dispatch_limit(gpu, oracle_mod, M, N, variant):
+    # so many rows that one wave per row (element-wise path), or four rows
+    # per wave, would pass 2^30 work-items: the grid is capped and the waves
+    # walk the rest.  Integer-valued operands make every order exact, so the
+    # sampled rows (both ends, the first rows past the grid, random others)
+    # must match bit for bit.
+    info = binding.describe_launch("f16", M, N)
+    assert info["variant"] == variant, info
+    assert info["grid"] * info["block"] <= 1 << 30, info
+    assert info["rows_per_wave"] >= 2, info
+    rng = np.random.default_rng(M)
+    A = rng.integers(-3, 4, size=(M, N), dtype=np.int8).astype(np.float16)
+    x = rng.integers(-3, 4, size=N, dtype=np.int8).astype(np.float16)
+    say(f"[parity] f16 M={M} N={N} past the dispatch limit {info}")
+    y = binding.gemv_f16(dev(A), dev(x))
+    torch.cuda.synchronize()
+    first_walk = info["grid"] * info["block"] // 64   # waves take rows w, w + waves, ...
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M),
+                                     np.arange(first_walk - 32, min(first_walk + 32, M)),
+                                     rng.integers(0, M, 4096)]))
+    got = y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    want = oracle_mod.gemv_f16(np.ascontiguousarray(A[rows]), x)
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_brute_force_small_shapes(gpu, oracle_mod, kind):
     # every N in 1..300 (odd, below one wave's width, not a multiple of the

@@ -66,7 +66,9 @@ _NS = {
     # 16384 is the longest row held in registers, 16388 the first read twice;
     # N % 4 != 0 takes the element-wise path
     "q8": [1, 3, 4, 8, 252, 256, 260, 1000, 1024, 4100, 16384, 16388, 20000, 40000],
-    "q4": [128, 256, 384, 1024, 2176, 7296, 14336, 16384, 16512],
+    # up to 15 units a wave per row; from 16 (4096) a workgroup per row of
+    # 4, 8 (12416: 49 units) or 16 waves (32896: 129 units)
+    "q4": [128, 256, 384, 1024, 2176, 3968, 4096, 7296, 12416, 14336, 16384, 16512, 32896],
 }
 
 
@@ -97,13 +99,13 @@ def test_unaligned_weights_take_the_elementwise_path(gpu, oracle_mod, kind):
     assert np.array_equal(s.cpu().numpy().view(np.uint16).reshape(os_.shape), os_)
 
 
-@pytest.mark.parametrize("kind", ["q8", "q4"])
-def test_near_ties_match_the_correctly_rounded_division(gpu, oracle_mod, kind):
+@pytest.mark.parametrize("kind,N", [("q8", 1024), ("q4", 1024), ("q4", 4096)])
+def test_near_ties_match_the_correctly_rounded_division(gpu, oracle_mod, kind, N):
     # weights within a few ulp of (k + 1/2) * scale: the kernels' fast
     # multiply-by-inverse path must hand these to the exact division
     rng = np.random.default_rng(7)
     qmax = 127 if kind == "q8" else 7
-    M, N = 64, 1024
+    M = 64
     W = np.zeros((M, N), np.float32)
     for i in range(M):
         scale = np.float32(np.float16(rng.uniform(0.01, 2.0)))
@@ -114,12 +116,12 @@ def test_near_ties_match_the_correctly_rounded_division(gpu, oracle_mod, kind):
         W[i] = np.where(ulps == 0, w, W[i])
         # pin each row's or group's absmax so that the scale is exactly `scale`
         W[i, ::128] = np.float32(qmax * np.float64(scale))
-    _compare(oracle_mod, kind, W, f"{kind} near ties")
+    _compare(oracle_mod, kind, W, f"{kind} near ties N={N}")
 
 
-@pytest.mark.parametrize("kind", ["q8", "q4"])
-def test_degenerate_rows(gpu, oracle_mod, kind):
-    M, N = 8, 512
+@pytest.mark.parametrize("kind,N", [("q8", 512), ("q4", 512), ("q4", 4096)])
+def test_degenerate_rows(gpu, oracle_mod, kind, N):
+    M = 8
     W = np.zeros((M, N), np.float32)
     W[1] = 1.0e7                                   # scale saturates at 65504, codes clip
     W[2, :] = np.linspace(-1e-4, 1e-4, N)          # binary16-subnormal scales
@@ -129,16 +131,35 @@ def test_degenerate_rows(gpu, oracle_mod, kind):
     W[6] = np.float32(3e-39) * np.sign(W[4])       # binary32-subnormal maximum
     W[7] = W[4]
     W[7, 200] = np.inf                             # infinite maximum: scale 65504, codes clip
-    _compare(oracle_mod, kind, W, f"{kind} degenerate")
+    _compare(oracle_mod, kind, W, f"{kind} degenerate N={N}")
 
 
-@pytest.mark.parametrize("kind", ["q8", "q4"])
-def test_without_error_output(gpu, oracle_mod, kind):
-    W = inputs.make_weights(100, 2048, seed=5)
+@pytest.mark.parametrize("kind,N", [("q8", 2048), ("q4", 2048), ("q4", 4096), ("q4", 12416), ("q4", 32896)])
+def test_without_error_output(gpu, oracle_mod, kind, N):
+    W = inputs.make_weights(100, N, seed=5)
     q, s, e = _gpu_quant(kind, W, with_error=False)
     assert e is None
     oq, os_, _ = (oracle_mod.quantize_q8 if kind == "q8" else oracle_mod.quantize_q4)(W)
     assert np.array_equal(q, oq) and np.array_equal(s, os_)
+
+
+def test_elementwise_grid_past_the_dispatch_limit(gpu, oracle_mod):
+    # INT8 rows of 3 weights take the element-wise kernel, one wave per row:
+    # 2^24 + 5 rows would pass 2^30 work-items, so the grid is capped and the
+    # waves walk the rest; rows are independent, so sampled ones (both ends,
+    # the first walked rows, random others) are checked against the oracle
+    M, N = (1 << 24) + 5, 3
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((M, N)).astype(np.float32)
+    say(f"[quant] q8 M={M} N={N} past the dispatch limit")
+    q, s, e = _gpu_quant("q8", W)
+    nwaves = (1 << 30) // 64
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), np.arange(nwaves - 32, nwaves + 5),
+                                     rng.integers(0, M, 4096)]))
+    oq, os_, oe = oracle_mod.quantize_q8(np.ascontiguousarray(W[rows]))
+    assert np.array_equal(q.reshape(M, N)[rows], oq)
+    assert np.array_equal(s[rows], os_)
+    assert np.max(np.abs(e[rows].astype(np.float64) - oe) / np.maximum(oe, 1e-30)) <= _sse_tol(N)
 
 
 def test_status_codes(gpu):

@@ -106,3 +106,19 @@ def test_status_codes_and_determinism(gpu):
     b = binding.softmax_f16(x)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_elementwise_grid_past_the_dispatch_limit(gpu, oracle_mod):
+    # rows of 7 logits take the element-wise kernel, one wave per row:
+    # 2^24 + 5 rows would pass 2^30 work-items, so the grid is capped and the
+    # waves walk the rest; sampled rows (both ends, the first walked rows,
+    # random others) are checked against the oracle
+    M, N = (1 << 24) + 5, 7
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((M, N)) * 3).astype(np.float16)
+    say(f"[softmax] M={M} N={N} past the dispatch limit")
+    y = _run(x)
+    nwaves = (1 << 30) // 64
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), np.arange(nwaves - 32, nwaves + 5),
+                                     rng.integers(0, M, 4096)]))
+    assert softmax_error(y[rows], oracle_mod.softmax_f16(np.ascontiguousarray(x[rows]))) <= SOFTMAX_GATE
