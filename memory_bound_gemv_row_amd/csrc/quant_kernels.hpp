@@ -361,9 +361,8 @@ quantize_q4_rows_kernel(const float* __restrict__ W, uint8_t* __restrict__ q, ui
         };
         u32x4 buf[D];
 #pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (d < k)
-                buf[d] = load(d);
+        for (int d = 0; d < D; ++d)   // (a conditional load per d made the compiler wait for each in turn)
+            buf[d] = d < k ? load(d) : u32x4{0u, 0u, 0u, 0u};
         float sse = 0.0f;
         for (int j0 = 0; j0 < k; j0 += D) {
 #pragma unroll
