@@ -23,7 +23,9 @@
  *
  * Conventions: device pointers, caller-owned buffers, asynchronous on
  * `stream`, status codes from gemv.h (gemv_status), nothing allocated.
- * W must hold finite values (NaN or infinity give unspecified codes).
+ * An infinite weight gives its row (INT8) or group (INT4) the largest
+ * binary16 scale, 65504, and clipped codes; NaN weights are outside the rule
+ * and give unspecified codes (and a NaN row_sse).
  * row_sse, if not NULL, receives per row sum_j (q_ij * scale - w_ij)^2 in
  * FP32; RMSE = sqrt(sum_i row_sse[i] / (M * N)).  Results are deterministic.
  * The bandwidth path needs a 16-byte-aligned W (and, for INT8, N % 4 == 0
