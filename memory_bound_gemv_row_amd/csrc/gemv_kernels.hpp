@@ -905,7 +905,9 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 // ---------------------------------------------------------------- element-wise kernel
 // Any N >= 0 and any alignment: one wave per row, lane l takes columns
 // l, l+64, ... with scalar loads (INT4: bytes l, l+64, ..., two columns
-// each).  Four waves per workgroup; waves walk rows 4 x gridDim.x apart.
+// each), the loops unrolled so that several loads are in flight (the sums
+// keep their order).  Four waves per workgroup; waves walk rows
+// 4 x gridDim.x apart.
 template <int F>
 __global__ void __launch_bounds__(256)
 gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
@@ -919,16 +921,19 @@ gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sca
         if constexpr (F == kF32) {
             const float* a = reinterpret_cast<const float*>(A) + (int64_t)row * N;
             const float* xf = reinterpret_cast<const float*>(x);
+#pragma unroll 8
             for (int64_t j = lane; j < N; j += 64)
                 acc = __builtin_fmaf(a[j], xf[j], acc);
         } else if constexpr (F == kF16) {
             const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
             const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+#pragma unroll 8
             for (int64_t j = lane; j < N; j += 64)
                 acc = __builtin_fmaf(half_bits_to_float(a[j]), half_bits_to_float(xh[j]), acc);
         } else if constexpr (F == kF16X32) {
             const uint16_t* a = reinterpret_cast<const uint16_t*>(A) + (int64_t)row * N;
             const float* xf = reinterpret_cast<const float*>(x);
+#pragma unroll 8
             for (int64_t j = lane; j < N; j += 64)
                 acc = __builtin_fmaf(half_bits_to_float(a[j]), xf[j], acc);
         } else if constexpr (F == kF16H) {
@@ -936,12 +941,14 @@ gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sca
             const _Float16* a = reinterpret_cast<const _Float16*>(A) + (int64_t)row * N;
             const _Float16* xh = reinterpret_cast<const _Float16*>(x);
             _Float16 h = (_Float16)0.0f;
+#pragma unroll 8
             for (int64_t j = lane; j < N; j += 64)
                 h = __builtin_fmaf16(a[j], xh[j], h);
             acc = (float)h;
         } else if constexpr (F == kQ8) {
             const int8_t* a = reinterpret_cast<const int8_t*>(A) + (int64_t)row * N;
             const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+#pragma unroll 8
             for (int64_t j = lane; j < N; j += 64)
                 acc = __builtin_fmaf((float)a[j], half_bits_to_float(xh[j]), acc);
         } else {
@@ -949,6 +956,7 @@ gemv_elementwise(const uint8_t* __restrict__ A, const uint16_t* __restrict__ sca
             const uint8_t* a = A + (int64_t)row * half_n;
             const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
             const uint16_t* srow = scale + (int64_t)row * (N / 128);
+#pragma unroll 4
             for (int b = lane; b < half_n; b += 64) {
                 const unsigned byte = a[b];
                 const int q0 = (int)(byte & 0xFu) - (int)((byte & 0x8u) << 1);

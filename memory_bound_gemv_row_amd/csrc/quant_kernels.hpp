@@ -411,6 +411,7 @@ quantize_elementwise_kernel(const float* __restrict__ W, uint8_t* __restrict__ q
         float sse = 0.0f;
         if constexpr (QMAX == 127) {
             float amax = 0.0f;
+#pragma unroll 8
             for (int64_t j = lane; j < N; j += 64)
                 amax = fmaxf(amax, fabsf(w[j]));
             amax = wave_max(amax);
@@ -420,6 +421,7 @@ quantize_elementwise_kernel(const float* __restrict__ W, uint8_t* __restrict__ q
             if (lane == 0)
                 scale[row] = sb;
             int8_t* dst = reinterpret_cast<int8_t*>(q) + (int64_t)row * N;
+#pragma unroll 8
             for (int64_t j = lane; j < N; j += 64) {
                 const float c = code_of<127>(w[j], sf, inv);
                 dst[j] = (int8_t)(int)c;

@@ -214,10 +214,12 @@ softmax_f16_elementwise(const uint16_t* __restrict__ x, uint16_t* __restrict__ y
         const _Float16* src = reinterpret_cast<const _Float16*>(x) + (int64_t)row * N;
         _Float16* dst = reinterpret_cast<_Float16*>(y) + (int64_t)row * N;
         float m = -__builtin_inff(), d = 0.0f;
+#pragma unroll 8
         for (int64_t j = lane; j < N; j += 64)
             merge(m, d, (float)src[j], 1.0f);
         wave_merge(m, d);
         const float l2d = log2_hw(d);
+#pragma unroll 8
         for (int64_t j = lane; j < N; j += 64)
             dst[j] = (_Float16)exp2_hw(__builtin_fmaf((float)src[j] - m, kLog2e, -l2d));
     }

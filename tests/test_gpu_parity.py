@@ -466,6 +466,32 @@ def test_grids_past_the_dispatch_limit(gpu, oracle_mod, M, N, variant):
     assert np.array_equal(got, want)
 
 
+def test_rows_of_two_gibibytes(gpu, oracle_mod):
+    # FP16 rows of 2^30 + 8 columns (2 GiB + 16 bytes): past a 32-bit byte
+    # count, so the element-wise kernel with 64-bit offsets runs.  Sparse
+    # integer entries near both ends of each row and past the 2^31-byte mark
+    # of the second row make the sums exact and any offset slip visible.
+    M, N = 2, (1 << 30) + 8
+    info = binding.describe_launch("f16", M, N)
+    assert info["variant"] == 3, info
+    A = np.zeros((M, N), np.float16)
+    cols = [0, 1, (1 << 29) + 3, (1 << 30) - 1, (1 << 30) + 7]
+    for i in range(M):
+        for k, j in enumerate(cols):
+            A[i, j] = (i + 1) * (k + 1) * (-1) ** k
+    x = np.ones(N, np.float16)
+    x[cols[2]] = 2.0
+    say(f"[parity] f16 M={M} N={N} rows of 2 GiB {info}")
+    y = binding.gemv_f16(dev(A), dev(x))
+    torch.cuda.synchronize()
+    want = np.array([sum(float(A[i, j]) * float(x[j]) for j in cols) for i in range(M)])
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
+    # the oracle agrees on a column slice holding every nonzero term's
+    # neighbourhood (the full rows would take it minutes)
+    sl = np.r_[0:64, (1 << 29):(1 << 29) + 64, (1 << 30) - 64:N]
+    assert np.array_equal(oracle_mod.gemv_f16(np.ascontiguousarray(A[:, sl]), np.ascontiguousarray(x[sl])), want)
+
+
 @pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
 def test_brute_force_small_shapes(gpu, oracle_mod, kind):
     # every N in 1..300 (odd, below one wave's width, not a multiple of the
