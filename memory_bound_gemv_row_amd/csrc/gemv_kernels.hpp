@@ -289,37 +289,54 @@ __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds
     }
 }
 
+// Chunks c0, c0 + NT, ..., c0 + (R-1) NT of stage_x_sums: all loads first
+// (2R granules in flight), then the sums in chunk order.
+template <int NT, int R>
+__device__ __forceinline__ void stage_sums_round(const u32x4* __restrict__ xg, u32x4* lds, int c0, int nchunks,
+                                                 int nchunks_pad, float& part)
+{
+    constexpr int G = Traits<kQ8>::kXGran;
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    u32x4 v[R][G];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int c = c0 + r * NT;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            v[r][k] = c < nchunks ? xg[c * G + k] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int c = c0 + r * NT;
+        if (c >= nchunks_pad)
+            break;
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].x), ones, part, false);
+            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].y), ones, part, false);
+            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].z), ones, part, false);
+            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].w), ones, part, false);
+            lds[c * G + k] = v[r][k];
+        }
+    }
+}
+
 // Staging for the INT8 decode: thread t stages whole chunks t, t + NT, ...
 // and accumulates the sum of all x (one partial per wave in lds_f[wave]).
 // Sums use v_dot2_f32_f16 against (1, 1): FP32 accumulation of exact
-// binary16 values.
+// binary16 values; zero x (whole-pass padding) adds nothing.  Rows of more
+// chunks than threads load 4 chunks per thread at a time.
 template <int WAVES>
 __device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4* lds, float* lds_f, int nchunks,
                                              int nchunks_pad)
 {
     constexpr int NT = WAVES * 64;
-    constexpr int G = Traits<kQ8>::kXGran;
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     float part = 0.0f;
-    for (int c = threadIdx.x; c < nchunks_pad; c += NT) {
-        if (c >= nchunks) {          // whole-pass padding: zero x
-#pragma unroll
-            for (int k = 0; k < G; ++k)
-                lds[c * G + k] = u32x4{0u, 0u, 0u, 0u};
-            continue;
-        }
-        u32x4 v[G];
-#pragma unroll
-        for (int k = 0; k < G; ++k)
-            v[k] = xg[c * G + k];
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            part = __builtin_amdgcn_fdot2(as_h2(v[k].x), ones, part, false);
-            part = __builtin_amdgcn_fdot2(as_h2(v[k].y), ones, part, false);
-            part = __builtin_amdgcn_fdot2(as_h2(v[k].z), ones, part, false);
-            part = __builtin_amdgcn_fdot2(as_h2(v[k].w), ones, part, false);
-            lds[c * G + k] = v[k];
-        }
+    if (nchunks_pad <= NT) {
+        stage_sums_round<NT, 1>(xg, lds, threadIdx.x, nchunks, nchunks_pad, part);
+    } else {
+        for (int c0 = threadIdx.x; c0 < nchunks_pad; c0 += 4 * NT)
+            stage_sums_round<NT, 4>(xg, lds, c0, nchunks, nchunks_pad, part);
     }
     const float w = wave_sum(part);
     if ((threadIdx.x & 63) == 0)
