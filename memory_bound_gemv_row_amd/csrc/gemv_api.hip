@@ -256,7 +256,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.D = 8;
             p.rows = 2;
         } else if (lds > kLdsBytes) {
-            // long rows, staged x past the usual budget: 4 waves, split
+            // long rows, staged x past 64 KiB: 4 waves, split
             // staging, at most 2 workgroups per CU when two fit and the
             // rows are many; else 8 waves, x staged before A, one
             // workgroup per CU
@@ -307,7 +307,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.D = 4;
         p.rows = 1;
     } else if (lds > kLdsBytes) {
-        // long INT4 rows, staged x past the usual budget: 8 waves, 4 in
+        // long INT4 rows, staged x past 64 KiB: 8 waves, 4 in
         // flight, x staged before A, one workgroup per CU
         p.variant = 1;
         p.waves = 8;

@@ -47,10 +47,11 @@ _NS = {
     "f16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 1528, 1536, 2056, 3584, 4648, 8200, 14336, 20000],
     # 16..512 (1-32 chunks) take the packed short-row kernel, 528 is the
     # first streaming width
-    # 33024 (33 units) and INT4 33280 (17 units) would stage more x than the
-    # LDS budget allows and read it with each unit instead
+    # 33024 (33 units) stages 66 KiB of x, past 64 KiB: one workgroup per CU
+    # with so few rows; INT4 33280 (17 units, 68 KiB): few rows, x per unit
     "q8": [1, 15, 16, 32, 48, 272, 512, 528, 1008, 1024, 1040, 5000, 8192, 9232, 20000, 33024],
-    # 5632 | 6144 straddle the staged-x threshold, 16392 is just past the LDS budget
+    # 5632 | 6144 straddle the staged-x threshold; 16392 stages just over
+    # 64 KiB of FP32 x (one workgroup per CU)
     "f16x32": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 5632, 6144, 8200, 14336, 16384, 16392, 20000],
     "f16_acc16": [1, 7, 8, 16, 504, 512, 520, 1000, 1024, 4648, 8200, 14336, 20000],
     # up to 1024 (32 chunks) packed; 640 and 896 fill 20 and 28 of 32 lanes
