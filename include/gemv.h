@@ -173,6 +173,12 @@ typedef struct gemv_launch_info {
 
 int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info);
 
+/* The same report for a device with `cus` compute units whose workgroups may
+ * hold `lds_max` bytes of LDS (MI355X: 256 and 163840), without touching
+ * any device: for planning, and for testing the geometry rules on a host
+ * without a GPU.  GEMV_E_INVAL also for cus <= 0 or lds_max <= 0. */
+int gemv_describe_launch_for(int kind, int M, int N, int aligned, int cus, int lds_max, gemv_launch_info* info);
+
 #ifdef __cplusplus
 }
 #endif

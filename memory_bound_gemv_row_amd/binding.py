@@ -64,6 +64,8 @@ def load():
         lib.gemv_probe_copy.restype = i
         lib.gemv_describe_launch.argtypes = [i, i, i, i, ctypes.POINTER(LaunchInfo)]
         lib.gemv_describe_launch.restype = i
+        lib.gemv_describe_launch_for.argtypes = [i, i, i, i, i, i, ctypes.POINTER(LaunchInfo)]
+        lib.gemv_describe_launch_for.restype = i
         _lib = lib
         return lib
 
@@ -126,6 +128,15 @@ def probe_copy_ptr(src: int, dst: int, nbytes: int, stream: int = 0) -> int:
 def describe_launch(kind: str, M: int, N: int, aligned: bool = True) -> dict:
     info = LaunchInfo()
     _check(load().gemv_describe_launch(KIND[kind], M, N, int(aligned), ctypes.byref(info)), "gemv_describe_launch")
+    return {f: getattr(info, f) for f, _ in LaunchInfo._fields_}
+
+
+def describe_launch_for(kind: str, M: int, N: int, cus: int, lds_max: int, aligned: bool = True) -> dict:
+    """describe_launch for a device of `cus` CUs and `lds_max` bytes of LDS
+    per workgroup; touches no device."""
+    info = LaunchInfo()
+    _check(load().gemv_describe_launch_for(KIND[kind], M, N, int(aligned), cus, lds_max, ctypes.byref(info)),
+           "gemv_describe_launch_for")
     return {f: getattr(info, f) for f, _ in LaunchInfo._fields_}
 
 

@@ -549,23 +549,22 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
     return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
 }
 
-int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info)
+}  // extern "C"
+
+namespace gemv {
+namespace {
+
+// gemv_describe_launch's report for a device of `dev`'s properties.
+void fill_launch_info(int kind, int M, int N, bool aligned, const Device& dev, gemv_launch_info* info)
 {
-    if (info == nullptr || kind < 0 || kind > 5 || M < 0 || N < 0)
-        return GEMV_E_INVAL;
-    if (kind == gemv::kQ4 && N % 128 != 0)
-        return GEMV_E_UNSUPPORTED;
-    gemv::Device dev{};
-    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
-        return rc;
-    const gemv::Plan p = gemv::make_plan(kind, M, N, aligned != 0, dev);
+    const Plan p = make_plan(kind, M, N, aligned, dev);
     info->variant = p.variant;
     info->grid = p.grid;
     info->block = p.block;
     const int64_t waves = (int64_t)p.grid * p.waves;
     if (p.variant == 4) {
         // row groups of 64 / L rows, walked grid-stride by the waves
-        const int64_t R = gemv::packed_rows_per_load(N / gemv::elems_per_chunk(kind));
+        const int64_t R = packed_rows_per_load(N / elems_per_chunk(kind));
         const int64_t groups = ((int64_t)M + R - 1) / R;
         info->rows_per_wave = waves > 0 ? (int)((groups + waves - 1) / waves * R) : 0;
     } else {
@@ -574,6 +573,40 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
     info->units_in_flight = p.D;
     info->lds_bytes = p.lds;
     info->stage_order = p.variant == 1 ? p.stg : -1;
+}
+
+int check_describe(int kind, int M, int N, const gemv_launch_info* info)
+{
+    if (info == nullptr || kind < 0 || kind > 5 || M < 0 || N < 0)
+        return GEMV_E_INVAL;
+    if (kind == kQ4 && N % 128 != 0)
+        return GEMV_E_UNSUPPORTED;
+    return GEMV_OK;
+}
+
+}  // namespace
+}  // namespace gemv
+
+extern "C" {
+
+int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* info)
+{
+    if (int rc = gemv::check_describe(kind, M, N, info); rc != GEMV_OK)
+        return rc;
+    gemv::Device dev{};
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
+        return rc;
+    gemv::fill_launch_info(kind, M, N, aligned != 0, dev, info);
+    return GEMV_OK;
+}
+
+int gemv_describe_launch_for(int kind, int M, int N, int aligned, int cus, int lds_max, gemv_launch_info* info)
+{
+    if (int rc = gemv::check_describe(kind, M, N, info); rc != GEMV_OK)
+        return rc;
+    if (cus <= 0 || lds_max <= 0)
+        return GEMV_E_INVAL;
+    gemv::fill_launch_info(kind, M, N, aligned != 0, gemv::Device{cus, lds_max}, info);
     return GEMV_OK;
 }
 

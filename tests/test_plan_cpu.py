@@ -1,0 +1,144 @@
+"""Launch geometry rules, checked on the host through
+gemv_describe_launch_for (the library's planner for a device of given CU
+count and LDS per workgroup; no GPU needed)."""
+import itertools
+
+import pytest
+
+from memory_bound_gemv_row_amd import binding
+from memory_bound_gemv_row_amd.binding import GemvError
+
+MI355X = dict(cus=256, lds_max=160 * 1024)
+ELEMS_PER_CHUNK = {"f32": 4, "f16": 8, "f16_acc16": 8, "f16x32": 8, "q8": 16, "q4": 32}
+X_GRANULES = {"f32": 1, "f16": 1, "f16_acc16": 1, "f16x32": 2, "q8": 2, "q4": 4}   # 16-byte granules of x per chunk
+KINDS = list(ELEMS_PER_CHUNK)
+
+
+def plan(kind, M, N, cus=256, lds_max=160 * 1024, aligned=True):
+    return binding.describe_launch_for(kind, M, N, cus, lds_max, aligned)
+
+
+def staged_bytes(kind, N):
+    nchunks = N // ELEMS_PER_CHUNK[kind]
+    return (nchunks + 63) // 64 * 64 * X_GRANULES[kind] * 16 + (64 if kind == "q8" else 0)
+
+
+_MS = [1, 7, 64, 255, 1000, 1024, 1025, 2048, 4096, 8192, 14336, 40000, 300000, (1 << 24) + 3]
+_NS = [0, 3, 8, 16, 128, 256, 512, 1000, 1024, 1536, 2048, 4096, 8192, 14336, 16384, 20480, 32768, 34816, 49152,
+       65536, 81920, 98304]
+_DEVICES = [MI355X, dict(cus=304, lds_max=64 * 1024), dict(cus=80, lds_max=64 * 1024)]
+
+
+@pytest.mark.parametrize("dev", _DEVICES, ids=lambda d: f"{d['cus']}cu_{d['lds_max'] // 1024}k")
+@pytest.mark.parametrize("kind", KINDS)
+def test_every_plan_is_consistent(kind, dev):
+    for M, N in itertools.product(_MS, _NS):
+        if kind == "q4" and N % 128:
+            continue
+        p = plan(kind, M, N, **dev)
+        where = (kind, M, N, dev, p)
+        assert p["variant"] in (1, 2, 3, 4, 5), where
+        assert 1 <= p["grid"] and p["block"] in (256, 512), where
+        assert p["grid"] * p["block"] <= 1 << 30, where            # 32-bit work-item count
+        aligned_path = N > 0 and N % ELEMS_PER_CHUNK[kind] == 0
+        if not aligned_path:
+            assert p["variant"] == 3, where
+        if p["variant"] == 4:                                       # packed short rows
+            assert kind in ("q8", "q4") and N // ELEMS_PER_CHUNK[kind] <= 32, where
+        elif p["variant"] in (1, 2, 3, 5):
+            # every row has a wave: grid x waves x rows per wave covers M
+            assert p["grid"] * (p["block"] // 64) * p["rows_per_wave"] >= M, where
+        if p["variant"] == 1:
+            assert kind in ("q8", "q4", "f16x32"), where           # FP32/FP16 read x with each unit
+            assert p["lds_bytes"] == staged_bytes(kind, N) <= dev["lds_max"], where
+            assert p["stage_order"] in (0, 1, 2), where
+        else:
+            assert p["lds_bytes"] == 0 and p["stage_order"] == -1, where
+        if p["variant"] == 5:
+            assert 1 <= -(-(N // ELEMS_PER_CHUNK[kind]) // 64) <= 3, where   # rows of one to three units
+        assert 1 <= p["units_in_flight"] <= 8, where
+
+
+def test_unaligned_operands_take_the_elementwise_kernel():
+    for kind in KINDS:
+        assert plan(kind, 4096, 4096, aligned=False)["variant"] == 3
+
+
+def test_huge_shapes_take_the_elementwise_kernel():
+    for kind in ("f16", "q8", "q4"):
+        assert plan(kind, (1 << 30) + 1, 128)["variant"] == 3
+        assert plan(kind, 1 << 30, 128)["variant"] != 3
+    # rows of 2 GiB or more: 64-bit offsets
+    assert plan("f16", 2, 1 << 30)["variant"] == 3
+    assert plan("f16", 2, (1 << 30) - 8)["variant"] != 3
+    assert plan("f32", 2, 1 << 29)["variant"] == 3
+
+
+def test_headline_shapes_on_mi355x():
+    # FP16 and FP32 read x with each unit; INT8/INT4 stage it; all fill every CU
+    for kind, M, N, variant in (("f16", 8192, 8192, 2), ("f16", 4096, 14336, 2), ("f16", 14336, 4096, 2),
+                                ("f32", 8192, 8192, 2), ("q8", 8192, 8192, 1), ("q8", 14336, 4096, 1),
+                                ("q4", 4096, 14336, 1), ("q4", 14336, 4096, 1)):
+        p = plan(kind, M, N)
+        assert p["variant"] == variant and p["grid"] >= 256, (kind, M, N, p)
+
+
+def test_long_rows_stage_x_up_to_the_device_limit():
+    # INT8/INT4 and FP16-with-FP32-x rows whose staged x passes 64 KiB stage
+    # it while it fits a workgroup; a 64-KiB device reads x with each unit
+    for kind, M, N in (("q8", 4096, 32768), ("q4", 4096, 34816), ("q4", 2048, 81920), ("f16x32", 4096, 24576)):
+        assert staged_bytes(kind, N) > 64 * 1024
+        p = plan(kind, M, N)
+        assert p["variant"] == 1 and p["lds_bytes"] == staged_bytes(kind, N), (kind, M, N, p)
+        assert plan(kind, M, N, lds_max=64 * 1024)["variant"] == 2, (kind, M, N)
+    # one unit past what a workgroup may hold
+    assert plan("q8", 4096, 81920)["variant"] == 2
+    assert plan("q4", 4096, 83968)["variant"] == 2
+    assert plan("f16x32", 64, 40960 + 512)["variant"] == 2
+
+
+def test_few_rows_rules():
+    cus = 256
+    # few INT4 rows of four units or more: x per unit; one more row: staged
+    assert plan("q4", 4 * cus, 8192)["variant"] == 2
+    assert plan("q4", 4 * cus + 1, 8192)["variant"] == 1
+    # few long INT8 rows: staged, x before A, one workgroup per CU
+    p = plan("q8", 4 * cus, 8192)
+    assert (p["variant"], p["stage_order"], p["block"]) == (1, 1, 512) and p["grid"] <= cus
+    assert plan("q8", 4 * cus + 1, 8192)["variant"] == 2
+    # INT8 rows of 64 units with at most 8 rows per CU: x per unit, two rows a wave
+    p = plan("q8", 2048, 65536)
+    assert (p["variant"], p["units_in_flight"]) == (2, 8)
+
+
+def test_short_rows_rules():
+    # INT8/INT4 rows of at most 32 chunks: the packed kernel
+    assert plan("q8", 14336, 512)["variant"] == 4
+    assert plan("q4", 14336, 1024)["variant"] == 4
+    # one unit just past: x in registers
+    assert plan("q8", 14336, 528)["variant"] == 5
+    assert plan("q4", 14336, 1152)["variant"] == 5
+    # FP16 rows of one and two units: x in registers
+    assert plan("f16", 4096, 512)["variant"] == 5
+    assert plan("f16", 14336, 1024)["variant"] == 5
+
+
+def test_grid_cap_makes_waves_walk():
+    # more rows than 2^30 work-items allow at one row (or four) per wave
+    p = plan("f16", (1 << 24) + (1 << 20) + 3, 3)
+    assert p["variant"] == 3 and p["grid"] * p["block"] == 1 << 30 and p["rows_per_wave"] == 2
+    p = plan("f16", (1 << 26) + 1000, 8)
+    assert p["grid"] * p["block"] <= 1 << 30 and p["rows_per_wave"] >= 5
+
+
+def test_describe_launch_for_rejects_bad_arguments():
+    with pytest.raises(GemvError):
+        plan("q4", 16, 200)              # N % 128 != 0
+    with pytest.raises(GemvError):
+        plan("f16", -1, 16)
+    with pytest.raises(GemvError):
+        plan("f16", 16, 16, cus=0)
+    with pytest.raises(GemvError):
+        plan("f16", 16, 16, lds_max=0)
+    lib = binding.load()
+    assert lib.gemv_describe_launch_for(6, 16, 16, 1, 256, 163840, None) == 1
