@@ -205,6 +205,17 @@ def test_launches_stay_within_the_dispatch_limit(gpu):
                 assert 1 <= info["grid"] and info["grid"] * info["block"] <= 1 << 30, (kind, M, N, info)
 
 
+def test_describe_launch_for_matches_the_device(gpu):
+    # the device-free planner, given this device's CU count and LDS per
+    # workgroup, reports exactly the plan the library launches
+    props = torch.cuda.get_device_properties(0)
+    cus, lds_max = props.multi_processor_count, props.shared_memory_per_block
+    for kind in ("f32", "f16", "f16x32", "f16_acc16", "q8", "q4"):
+        for M in (1, 1000, 1792, 4096, 8192, 14336, 100000):
+            for N in (128, 512, 1024, 4096, 8192, 14336, 34816, 81920):
+                assert binding.describe_launch(kind, M, N) == binding.describe_launch_for(kind, M, N, cus, lds_max)
+
+
 def test_probe_copy_and_read(gpu):
     n = 64 << 20
     src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
