@@ -9,16 +9,6 @@
 namespace gquant {
 namespace {
 
-// compute units of the current device
-int cu_count(int* out)
-{
-    gemv_device::Device dev{};
-    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
-        return rc;
-    *out = dev.cus;
-    return GEMV_OK;
-}
-
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int launch(const void* fn, int grid, int block, const float* W, void* q, uint16_t* scale, float* row_sse, int M,
@@ -28,12 +18,19 @@ int launch(const void* fn, int grid, int block, const float* W, void* q, uint16_
     return hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream) == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
 }
 
+// INT8 kernel for rows of P units and its waves per workgroup: 4 waves of 4
+// units up to 16 units, 8 of 4 up to 32, 8 of 8 beyond (rows of more than 64
+// units are read twice).  Graph-timed A/B with a workgroup per row against
+// 4 waves and rows walked by 8 workgroups per CU: 16384x2048 34.0 -> 31.3 us,
+// 14336x4096 52.5 -> 48.2, 8192x6144 45.5 -> 43.6, 8192x8192 58.3 -> 56.3,
+// 4096x14336 57.9 -> 51.8, 4096x16384 65.6 -> 59.2, 2048x32768 101.9 -> 97.9.
 template <bool SSE>
-const void* q8_kernel(int P)
+const void* q8_kernel(int P, int* waves)
 {
+    *waves = P <= 16 ? 4 : 8;
     return P <= 16 ? reinterpret_cast<const void*>(&quantize_q8_kernel<4, 4, SSE>)
-         : P <= 32 ? reinterpret_cast<const void*>(&quantize_q8_kernel<4, 8, SSE>)
-                   : reinterpret_cast<const void*>(&quantize_q8_kernel<4, 16, SSE>);
+         : P <= 32 ? reinterpret_cast<const void*>(&quantize_q8_kernel<8, 4, SSE>)
+                   : reinterpret_cast<const void*>(&quantize_q8_kernel<8, 8, SSE>);
 }
 
 template <bool SSE>
@@ -71,8 +68,10 @@ int gemv_quantize_q8(const float* W, int8_t* q, uint16_t* scale, float* row_sse,
         return rc;
     if (M == 0)
         return GEMV_OK;
-    int cus = 0;
-    if (int rc = cu_count(&cus); rc != GEMV_OK)
+    // the grids need no CU count, but a call without a usable device fails
+    // here like the others
+    gemv_device::Device dev{};
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
         return rc;
     // more than 2^30 rows: the row-walking kernels' int row cursors could
     // pass INT_MAX; the element-wise kernel indexes rows in 64 bits
@@ -80,12 +79,12 @@ int gemv_quantize_q8(const float* W, int8_t* q, uint16_t* scale, float* row_sse,
     if (N == 0 || N % 4 != 0 || !aligned(W, 16) || !aligned(q, 4) || M > (1 << 30))
         return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<127>), grid4, 256, W, q, scale,
                       row_sse, M, N, stream);
-    // a workgroup of 4 waves per row; units per wave sized so that rows up
-    // to 64 units (N <= 16384) stay in registers
+    // a workgroup per row; units per wave sized so that rows up to 64 units
+    // (N <= 16384) stay in registers
     const int P = (N / 4 + 63) / 64;
-    const void* fn = row_sse != nullptr ? q8_kernel<true>(P) : q8_kernel<false>(P);
-    const int grid = M < cus * 8 ? M : cus * 8;
-    return launch(fn, grid, 256, W, q, scale, row_sse, M, N, stream);
+    int waves = 4;
+    const void* fn = row_sse != nullptr ? q8_kernel<true>(P, &waves) : q8_kernel<false>(P, &waves);
+    return launch(fn, gemv_device::capped_grid(M, waves * 64), waves * 64, W, q, scale, row_sse, M, N, stream);
 }
 
 int gemv_quantize_q4(const float* W, uint8_t* q, uint16_t* scale, float* row_sse, int M, int N,
