@@ -9,8 +9,6 @@
 namespace gsoftmax {
 namespace {
 
-constexpr int kWavesPerCu = 32;   // resident waves a CU can hold
-
 // compute units of the current device
 int cu_count(int* out)
 {
@@ -25,8 +23,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Geometry for rows of P units: waves per row and units held per wave, so
 // that a row stays in registers up to 256 units (131072 columns) with at
-// most 64 VGPRs of data; workgroups per CU; and whether a workgroup loads its
-// next row while it stores the current one.  The prefetch and the deeper
+// most 64 VGPRs of data; whether a workgroup loads its next row while it
+// stores the current one; and for those, workgroups per CU.  The prefetch and the deeper
 // grids for 4-wave rows were measured (graph-timed, rotating buffers):
 // 8192 x 8192 47.4 -> 46.3 us, 4096 x 32768 98.2 -> 94.0, 16384 x 4096
 // 61.7 -> 57.7; with 16 units per wave (rows over 64 units) the prefetch
@@ -41,8 +39,8 @@ Geometry geometry(int P)
     if (P <= 16) return {4, 4, 16, true};
     if (P <= 32) return {4, 8, 16, true};
     if (P <= 64) return {8, 8, 3, true};
-    if (P <= 128) return {8, 16, kWavesPerCu / 8, false};
-    return {16, 16, kWavesPerCu / 16, false};
+    if (P <= 128) return {8, 16, 0, false};   // a workgroup per row (per_cu unused)
+    return {16, 16, 0, false};
 }
 
 const void* kernel_for(const Geometry& g)
@@ -80,8 +78,12 @@ extern "C" int gemv_softmax_f16(const uint16_t* x, uint16_t* y, int M, int N, hi
         err = hipLaunchKernel(reinterpret_cast<const void*>(&softmax_f16_elementwise), dim3(grid4), dim3(256), args,
                               0, stream);
     } else {
+        // rows that reload the next row walk a grid of per_cu workgroups per
+        // CU; the others take a workgroup per row (2048 x 65536 99.5 ->
+        // 98.0 us, 1024 x 131072 107.3 -> 106.6 against walking)
         const Geometry g = geometry((N / 8 + 63) / 64);
-        const int grid = M < cus * g.per_cu ? M : cus * g.per_cu;
+        const int grid = !g.prefetch ? gemv_device::capped_grid(M, g.waves * 64)
+                                     : (M < cus * g.per_cu ? M : cus * g.per_cu);
         err = hipLaunchKernel(kernel_for(g), dim3(grid), dim3(g.waves * 64), args, 0, stream);
     }
     return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
