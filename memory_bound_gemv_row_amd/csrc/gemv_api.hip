@@ -15,7 +15,9 @@
 namespace gemv {
 namespace {
 
-constexpr int kLdsBytes = 64 * 1024;   // x staged in LDS up to this size
+// Staged x up to this size takes the plans tuned for ordinary rows; longer
+// rows have their own plans, up to the LDS one workgroup may hold.
+constexpr int kLdsBytes = 64 * 1024;
 constexpr bool kNT = true;             // stream A with non-temporal loads
 using gemv_device::Device;
 
