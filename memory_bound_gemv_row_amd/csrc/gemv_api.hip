@@ -86,11 +86,13 @@ struct Plan {
 //     CUs for rows up to 16 units, save rows of 8 units or more with M <= 4
 //     x CUs, which stage x as below with 8 waves, x before A, one workgroup
 //     per CU): x read with each unit, 8 waves, 2 (two-unit rows) or 4 in
-//     flight -- the staging and its barrier would dominate such launches.  Otherwise x is staged: rows of 8 units or
-//     more: 8 waves, 4 in flight, A first, a row per wave; rows of 2 units:
-//     8 waves, 2 in flight, split staging (staging loads, A prologue, LDS
-//     writes), at most 3 workgroups per CU; rows of 3-7 units: 4 waves,
-//     split staging, at most 3 workgroups per CU.
+//     flight -- the staging and its barrier would dominate such launches.
+//     Otherwise x is staged: rows of 8 units or more: 8 waves, 4 in flight,
+//     A first, a row per wave (rows of 8-16 units with 20-32 rows per CU:
+//     12 waves, at most 2 workgroups per CU); rows of 2 units: 8 waves, 2 in
+//     flight, split staging (staging loads, A prologue, LDS writes), at most
+//     3 workgroups per CU; rows of 3-7 units: 4 waves, split staging, at
+//     most 3 workgroups per CU.
 //     Staged x past 64 KiB (rows of 32 units and more): with two workgroups
 //     per CU fitting the device's LDS and over 4 x CUs rows, 4 waves, split
 //     staging, at most 2 workgroups per CU; otherwise 8 waves, x staged
@@ -283,6 +285,11 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             // each unit, 8 waves, 4 in flight
             p.variant = 2;
             p.waves = 8;
+        } else if (P >= 8 && P <= 16 && M >= 20 * cus && M <= 32 * cus) {
+            // rows of 8-16 units, 20-32 per CU: 12 waves, A first, at most 2
+            // workgroups per CU (half the staging of four 8-wave ones)
+            p.waves = 12;
+            p.cap = 2;
         } else if (P >= 8) {
             // long rows: 8 waves, A first, one row per wave
             p.waves = 8;
@@ -368,6 +375,10 @@ const void* stream_kernel()
 template <int F, bool XG, int STG>
 const void* select_stream_stg(const Plan& p)
 {
+    if constexpr (F == kQ8 && !XG && STG == 0) {
+        if (p.waves == 12)
+            return stream_kernel<F, 12, 4, XG, STG>();
+    }
     if (p.waves == 8)
         return p.D == 8 ? stream_kernel<F, 8, 8, XG, STG>()
                         : (p.D == 4 ? stream_kernel<F, 8, 4, XG, STG>() : stream_kernel<F, 8, 2, XG, STG>());

@@ -140,6 +140,20 @@ def test_long_rows_staged_or_per_unit(gpu, oracle_mod, kind, M, N, variant, stg)
     _check(oracle_mod, kind, ops, f"{kind} long rows M={M} N={N} {info}")
 
 
+@pytest.mark.parametrize("M,N", [(20 * 256 + 5, 8192 + 16), (32 * 256, 16384), (24 * 256 + 3, 12288)])
+def test_int8_twelve_wave_workgroups(gpu, oracle_mod, M, N):
+    # INT8 rows of 8-16 units, 20-32 rows per CU: 12-wave workgroups, at
+    # most 2 per CU, so that beyond 24 rows per CU some waves walk two rows
+    # (ragged last pass too)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    info = binding.describe_launch("q8", M, N)
+    if cus == 256:
+        assert (info["variant"], info["block"], info["stage_order"]) == (1, 768, 0), info
+        assert info["grid"] == min(-(-M // 12), 2 * cus), info
+    ops = inputs.make("q8", M, N, seed=M ^ N)
+    _check(oracle_mod, "q8", ops, f"q8 12-wave M={M} N={N} {info}")
+
+
 @pytest.mark.parametrize("kind,M,N", [("f32", 8000, 252), ("f32", 9000, 260), ("f16", 14336, 1000),
                                       ("f16x32", 14336, 512), ("f16x32", 14336, 1016), ("f16_acc16", 6000, 1024),
                                       ("q8", 14336, 1008), ("q4", 14336, 2048), ("f16", 14336, 1528),

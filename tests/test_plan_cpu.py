@@ -38,7 +38,7 @@ def test_every_plan_is_consistent(kind, dev):
         p = plan(kind, M, N, **dev)
         where = (kind, M, N, dev, p)
         assert p["variant"] in (1, 2, 3, 4, 5), where
-        assert 1 <= p["grid"] and p["block"] in (256, 512), where
+        assert 1 <= p["grid"] and p["block"] in (256, 512, 768), where
         assert p["grid"] * p["block"] <= 1 << 30, where            # 32-bit work-item count
         aligned_path = N > 0 and N % ELEMS_PER_CHUNK[kind] == 0
         if not aligned_path:
