@@ -68,9 +68,12 @@ struct Plan {
 // Geometry for one call, chosen from sweeps on MI355X.  A row of nchunks
 // 16-byte chunks is P = ceil(nchunks / 64) units (one 1-KiB wave load each).
 //   FP32/FP16 (either accumulation), other rows: x read with each unit; one
-//     row per wave, or two for very long rows; 8 units in flight when rows
-//     have at least 8 units; one-unit rows (beyond 32 rows per CU) put 4
-//     rows on each wave so that 4 units are in flight without padding.
+//     row per wave; 8 units in flight when rows have at least 8 units; rows
+//     of 24 units and more: 4 waves, 8 in flight and two rows per wave up to
+//     12 rows per CU, 8 in flight and one row per wave (two if the units
+//     are not a multiple of 8) from 24 rows per CU, two rows and 4 in
+//     flight between; one-unit rows (beyond 32 rows per CU) put 4 rows on
+//     each wave so that 4 units are in flight without padding.
 //   Rows of one unit (any format; FP32/FP16 only up to 32 rows per CU), of
 //     two units (FP32/FP16; INT4 up to 16 rows per CU; FP16 with FP32 x
 //     beyond that) and of three: x in registers (gemv_xreg), no staging.
@@ -199,10 +202,23 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         }
     } else if (fp) {
         p.variant = 2;
-        if (P >= 24) {            // very long rows: two per wave, fewer in flight each
+        if (P >= 24) {
+            // very long rows: 4 waves; up to 12 rows per CU two rows per
+            // wave, 8 in flight; from 24 rows per CU 8 in flight, one row
+            // per wave (two where a row's units are not a multiple of 8,
+            // which would pad every row's stream); in between two rows per
+            // wave, 4 in flight
             p.waves = 4;
-            p.D = 4;
-            p.rows = 2;
+            if (M <= 12 * cus) {
+                p.D = 8;
+                p.rows = 2;
+            } else if (M >= 24 * cus) {
+                p.D = 8;
+                p.rows = P % 8 == 0 ? 1 : 2;
+            } else {
+                p.D = 4;
+                p.rows = 2;
+            }
         } else if (P >= 4) {
             p.waves = P >= 16 ? 8 : 4;
             p.D = P >= 8 ? 8 : 4;
