@@ -93,6 +93,15 @@ void least_padding(int P, int* D, int* rows)
     *rows = order[best][1];
 }
 
+// Rows per wave (1 or 2) for rows of P units at D in flight: whichever pads
+// each wave's stream less, one row on a tie.
+int rows_for_depth(int P, int D)
+{
+    const int pad1 = (P + D - 1) / D * D - P;
+    const int pad2 = (2 * P + D - 1) / D * D - 2 * P;
+    return pad2 < 2 * pad1 ? 2 : 1;   // pad2 / 2P < pad1 / P
+}
+
 // Geometry for one call, chosen from sweeps on MI355X.  A row of nchunks
 // 16-byte chunks is P = ceil(nchunks / 64) units (one 1-KiB wave load each).
 //   FP32/FP16 (either accumulation), other rows: x read with each unit;
@@ -120,11 +129,12 @@ void least_padding(int P, int* D, int* rows)
 //     per CU): x read with each unit, 8 waves, 2 (two-unit rows) or 4 in
 //     flight -- the staging and its barrier would dominate such launches.
 //     Otherwise x is staged: rows of 8 units or more: 8 waves, 4 in flight,
-//     A first, a row per wave (rows of 8-16 units with 20-32 rows per CU:
-//     12 waves, at most 2 workgroups per CU); rows of 2 units: 8 waves, 2 in
-//     flight, split staging (staging loads, A prologue, LDS writes), at most
-//     3 workgroups per CU; rows of 3-7 units: 4 waves, split staging, at
-//     most 3 workgroups per CU.
+//     A first, a row per wave, or two where that pads less (rows_for_depth:
+//     16384 x 10240 29.4 -> 25.3 us); rows of 8-16 units with 20-32 rows
+//     per CU: 12 waves, at most 2 workgroups per CU; rows of 2 units: 8
+//     waves, 2 in flight, split staging (staging loads, A prologue, LDS
+//     writes), at most 3 workgroups per CU; rows of 3-7 units: 4 waves,
+//     split staging, at most 3 workgroups per CU.
 //     Staged x past 64 KiB (rows of 32 units and more): with two workgroups
 //     per CU fitting the device's LDS and over 4 x CUs rows, 4 waves, split
 //     staging, at most 2 workgroups per CU; otherwise 8 waves, x staged
@@ -146,7 +156,8 @@ void least_padding(int P, int* D, int* rows)
 //     every unit costs more cache bandwidth than staging it, once the staging
 //     (4N bytes per workgroup) is spread over enough rows: staged for rows of
 //     at least 12 units, or for 8192 rows and more; read with each unit
-//     otherwise.  Rows whose staged x passes 64 KiB stage it up to the
+//     otherwise (two rows per wave from 5 units).  Rows whose staged x
+//     passes 64 KiB stage it up to the
 //     device's LDS per workgroup (8 waves, 4 in flight, x before A, one
 //     workgroup per CU), reading x with each unit beyond that.
 // With a cap the grid stays below the row count and waves walk several
@@ -286,9 +297,13 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.cap = 1;
         } else {
             p.variant = 2;
+            // 4 waves; rows of 8 units or more: two per wave, 8 in flight;
+            // 4 units: one row, 4 in flight; 5-7 units: two rows (less
+            // padding: 2048 x 3072 4.37 -> 4.21 us); shorter: 4 units in
+            // flight over ceil(4 / P) rows
             p.waves = 4;
             p.D = P >= 8 ? 8 : 4;
-            p.rows = P >= 8 ? 2 : (P >= 4 ? 1 : (4 + P - 1) / P);
+            p.rows = P >= 8 ? 2 : (P == 4 ? 1 : (P > 4 ? 2 : (4 + P - 1) / P));
         }
     } else if (kind == kQ8) {
         p.variant = 1;
@@ -335,8 +350,10 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.waves = 12;
             p.cap = 2;
         } else if (P >= 8) {
-            // long rows: 8 waves, A first, one row per wave
+            // long rows: 8 waves, A first, one row per wave, or two where
+            // that pads less (rows of 9, 10, 13, 14 ... units)
             p.waves = 8;
+            p.rows = rows_for_depth(P, 4);
         } else if (P <= 2) {
             // rows of 2 units: 8 waves, 2 in flight, split staging, at most
             // 3 workgroups per CU (waves walk several rows)
