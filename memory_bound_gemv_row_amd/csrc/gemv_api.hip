@@ -71,8 +71,9 @@ struct Plan {
 // the padding re-reads units (a row of 12 units at 8 in flight streams 16:
 // FP16 8192x6144 19.9 us against 15.9 without padding).  The choice with
 // the least padding wins; ties go to 4 in flight and one row for rows under
-// 8 units (more waves), to 8 in flight otherwise.
-void least_padding(int P, int* D, int* rows)
+// 8 units (more waves), to 8 in flight otherwise.  Two rows per wave only
+// where the halved grid still gives every CU a workgroup (two_rows_fill).
+void least_padding(int P, bool two_rows_fill, int* D, int* rows)
 {
     static constexpr int kShort[4][2] = {{4, 1}, {4, 2}, {8, 1}, {8, 2}};
     static constexpr int kLong[4][2] = {{8, 1}, {8, 2}, {4, 1}, {4, 2}};
@@ -80,6 +81,8 @@ void least_padding(int P, int* D, int* rows)
     int best = 0;
     int64_t best_pad = -1, best_len = 1;
     for (int k = 0; k < 4; ++k) {
+        if (order[k][1] == 2 && !two_rows_fill)
+            continue;
         const int d = order[k][0], len = order[k][1] * P;
         const int64_t pad = (len + d - 1) / d * d - len;
         // pad / len < best_pad / best_len, compared without division
@@ -94,12 +97,20 @@ void least_padding(int P, int* D, int* rows)
 }
 
 // Rows per wave (1 or 2) for rows of P units at D in flight: whichever pads
-// each wave's stream less, one row on a tie.
-int rows_for_depth(int P, int D)
+// each wave's stream less, one row on a tie or where two rows per wave
+// would leave CUs without a workgroup (two_rows_fill false).
+int rows_for_depth(int P, int D, bool two_rows_fill)
 {
     const int pad1 = (P + D - 1) / D * D - P;
     const int pad2 = (2 * P + D - 1) / D * D - 2 * P;
-    return pad2 < 2 * pad1 ? 2 : 1;   // pad2 / 2P < pad1 / P
+    return two_rows_fill && pad2 < 2 * pad1 ? 2 : 1;   // pad2 / 2P < pad1 / P
+}
+
+// Whether M rows at two per wave, `waves` waves per workgroup, still give
+// each of `cus` CUs a workgroup.
+bool two_rows_fill(int64_t M, int waves, int cus)
+{
+    return (M + 2 * waves - 1) / (2 * waves) >= cus;
 }
 
 // Geometry for one call, chosen from sweeps on MI355X.  A row of nchunks
@@ -261,7 +272,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             }
         } else if (P >= 4) {
             p.waves = P >= 16 ? 8 : 4;
-            least_padding(P, &p.D, &p.rows);
+            least_padding(P, two_rows_fill(M, p.waves, cus), &p.D, &p.rows);
         } else {
             // rows of 1-3 units: enough rows per wave for 4 units in flight
             // (one row per wave would pad each wave's stream with re-reads)
@@ -273,10 +284,13 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         const bool fits = lds_bytes(kind, nchunks) <= kLdsBytes;
         p.rows = 1;
         if (fits && P >= 24) {
+            // two rows per wave where that pads less (8192 x 12800
+            // 35.36 -> 33.65 us, 4096 x 15360 22.89 -> 21.92)
             p.variant = 1;
             p.waves = 8;
             p.D = 4;
             p.stg = 2;
+            p.rows = rows_for_depth(P, 4, two_rows_fill(M, 8, cus));
         } else if (fits && P >= 12) {
             p.variant = 1;
             p.waves = 8;
@@ -303,7 +317,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             // flight over ceil(4 / P) rows
             p.waves = 4;
             p.D = P >= 8 ? 8 : 4;
-            p.rows = P >= 8 ? 2 : (P == 4 ? 1 : (P > 4 ? 2 : (4 + P - 1) / P));
+            p.rows = P >= 8 ? 2 : (P == 4 ? 1 : (P > 4 ? (two_rows_fill(M, 4, cus) ? 2 : 1) : (4 + P - 1) / P));
         }
     } else if (kind == kQ8) {
         p.variant = 1;
@@ -353,7 +367,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             // long rows: 8 waves, A first, one row per wave, or two where
             // that pads less (rows of 9, 10, 13, 14 ... units)
             p.waves = 8;
-            p.rows = rows_for_depth(P, 4);
+            p.rows = rows_for_depth(P, 4, two_rows_fill(M, 8, cus));
         } else if (P <= 2) {
             // rows of 2 units: 8 waves, 2 in flight, split staging, at most
             // 3 workgroups per CU (waves walk several rows)

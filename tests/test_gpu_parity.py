@@ -156,6 +156,19 @@ def test_long_fp_rows(gpu, oracle_mod, kind, M, N, D, rows):
     _check(oracle_mod, kind, ops, f"{kind} long rows M={M} N={N} {info}")
 
 
+@pytest.mark.parametrize("kind,M,N", [("q8", 4500, 9216 + 16), ("q8", 4200, 14336), ("f16x32", 9000, 12800 + 8),
+                                      ("f16x32", 2048 + 3, 3072 + 8), ("f16", 4096 + 5, 4608 + 8)])
+def test_two_rows_per_wave_where_that_pads_less(gpu, oracle_mod, kind, M, N):
+    # rows whose unit count does not divide by the loads in flight: two rows
+    # per wave (with enough rows to give every CU a workgroup), one padded
+    # sequence per wave (ragged last passes too)
+    info = binding.describe_launch(kind, M, N)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert info["rows_per_wave"] == 2, info
+    ops = inputs.make(kind, M, N, seed=M * 3 + N)
+    _check(oracle_mod, kind, ops, f"{kind} two rows per wave M={M} N={N} {info}")
+
+
 @pytest.mark.parametrize("M,N", [(20 * 256 + 5, 8192 + 16), (32 * 256, 16384), (24 * 256 + 3, 12288)])
 def test_int8_twelve_wave_workgroups(gpu, oracle_mod, M, N):
     # INT8 rows of 8-16 units, 20-32 rows per CU: 12-wave workgroups, at

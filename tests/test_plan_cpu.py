@@ -54,6 +54,8 @@ def test_every_plan_is_consistent(kind, dev):
             assert p["stage_order"] in (0, 1, 2), where
         else:
             assert p["lds_bytes"] == 0 and p["stage_order"] == -1, where
+        if p["variant"] in (1, 2) and M >= 8 * dev["cus"]:
+            assert p["grid"] >= dev["cus"], where                 # every CU gets a workgroup
         if p["variant"] == 5:
             assert 1 <= -(-(N // ELEMS_PER_CHUNK[kind]) // 64) <= 3, where   # rows of one to three units
         assert 1 <= p["units_in_flight"] <= 8, where
