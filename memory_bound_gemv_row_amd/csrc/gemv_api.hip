@@ -166,13 +166,16 @@ bool two_rows_fill(int64_t M, int waves, int cus)
 //   FP16 with FP32 x: x is twice the bytes of FP16 x, and reading it with
 //     every unit costs more cache bandwidth than staging it, once the staging
 //     (4N bytes per workgroup) is spread over enough rows: staged for rows of
-//     at least 12 units, or for 8192 rows and more; read with each unit
-//     otherwise (two rows per wave from 5 units).  Rows whose staged x
-//     passes 64 KiB stage it up to the
-//     device's LDS per workgroup (8 waves, 4 in flight, x before A, one
-//     workgroup per CU), reading x with each unit beyond that.
-// With a cap the grid stays below the row count and waves walk several
-// rows; otherwise every launch gives each CU work once M >= CUs.
+//     at least 12 units (24 and more: 8 waves, 4 in flight, split staging,
+//     two rows per wave where that pads less), or for 8192 rows and more;
+//     read with each unit otherwise (two rows per wave from 5 units).  Rows
+//     whose staged x passes 64 KiB stage it up to the device's LDS per
+//     workgroup (8 waves, 4 in flight, x before A, one workgroup per CU),
+//     reading x with each unit beyond that.
+// Two rows per wave are taken only where the halved grid still gives every
+// CU a workgroup.  With a cap the grid stays below the row count and waves
+// walk several rows; otherwise every launch gives each CU work once
+// M >= CUs.
 Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
 {
     Plan p{};
