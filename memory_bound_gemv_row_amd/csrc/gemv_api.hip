@@ -153,12 +153,15 @@ bool two_rows_fill(int64_t M, int waves, int cus)
 //     of two rows, 8 in flight) where only one workgroup fits and M <= 8 x
 //     CUs, or where the staged x would not fit at all.
 //   INT4, other rows, x staged: rows under 4 units: 8 waves, 2 in flight,
-//     split staging; longer rows: 4 waves, 4 in flight, x staged before A;
-//     at most 3 workgroups per CU.  Staged x past 64 KiB (rows over 16
-//     units): 8 waves, 4 in flight, x staged before A, one workgroup per
-//     CU.  x read with each unit (4 waves, 4 in flight) instead for M <= 4
-//     x CUs (any row length), or where the staged x would not fit the
-//     device's LDS.
+//     split staging, at most 3 workgroups per CU; longer rows: 4 in flight,
+//     x staged before A, 4 waves and at most 3 workgroups per CU -- but 8
+//     waves and at most 2 for rows of 14-16 units (fewer stagings of x:
+//     8192 x 28672 26.0 -> 22.3 us, 4096 x 28672 16.4 -> 13.5; shorter rows
+//     gained at some row counts and lost at others).  Staged x past 64 KiB
+//     (rows over 16 units): 8 waves, 4 in flight, x staged before A, one
+//     workgroup per CU.  x read with each unit (4 waves, 4 in flight)
+//     instead for M <= 4 x CUs (any row length), or where the staged x
+//     would not fit the device's LDS.
 //   INT8/INT4 rows of at most 32 chunks (half a wave load): the packed
 //     kernel, 64 / L rows per wave load, 8 waves; with up to 16 row groups
 //     per CU one group per wave, up to 32 two (both in flight), beyond that
@@ -404,13 +407,15 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.cap = 1;
     } else {
         // short INT4 rows: 8 waves, 2 units in flight, split staging;
-        // longer rows: 4 waves, 4 units, x staged before A
+        // longer rows: 4 units, x staged before A, 4 waves and at most 3
+        // workgroups per CU; rows of 14-16 units: 8 waves and at most 2
+        // workgroups per CU (fewer stagings of their 56-64 KiB of x)
         p.variant = 1;
-        p.waves = P < 4 ? 8 : 4;
+        p.waves = P < 4 || P >= 14 ? 8 : 4;
         p.D = P < 4 ? 2 : 4;
         p.rows = 1;
         p.stg = P < 4 ? 2 : 1;
-        p.cap = 3;
+        p.cap = P >= 14 ? 2 : 3;
     }
     p.lds = p.variant == 1 ? lds_bytes(kind, nchunks) : 0;
     p.block = p.waves * 64;
