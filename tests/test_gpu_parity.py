@@ -172,6 +172,18 @@ def test_two_rows_per_wave_where_that_pads_less(gpu, oracle_mod, kind, M, N):
     _check(oracle_mod, kind, ops, f"{kind} two rows per wave M={M} N={N} {info}")
 
 
+@pytest.mark.parametrize("kind,M,N,D", [("q4", 2048 + 3, 10240, 5), ("q4", 4096 + 5, 12288, 3),
+                                        ("q8", 14336 + 1, 5120 - 16, 5), ("q8", 3000, 5120, 5)])
+def test_depths_that_divide_the_row(gpu, oracle_mod, kind, M, N, D):
+    # INT4 rows of 5 and 6 units and INT8 rows of 5: 5 or 3 units in flight
+    # (waves walking one or several rows, a ragged last pass for INT8)
+    info = binding.describe_launch(kind, M, N)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert (info["variant"], info["units_in_flight"]) == (1, D), info
+    ops = inputs.make(kind, M, N, seed=M + 13 * N)
+    _check(oracle_mod, kind, ops, f"{kind} depth {D} M={M} N={N} {info}")
+
+
 @pytest.mark.parametrize("M,N", [(20 * 256 + 5, 8192 + 16), (32 * 256, 16384), (24 * 256 + 3, 12288)])
 def test_int8_twelve_wave_workgroups(gpu, oracle_mod, M, N):
     # INT8 rows of 8-16 units, 20-32 rows per CU: 12-wave workgroups, at
