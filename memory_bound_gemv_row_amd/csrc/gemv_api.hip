@@ -144,8 +144,9 @@ bool two_rows_fill(int64_t M, int waves, int cus)
 //     16384 x 10240 29.4 -> 25.3 us); rows of 8-16 units with 20-32 rows
 //     per CU: 12 waves, at most 2 workgroups per CU; rows of 2 units: 8
 //     waves, 2 in flight, split staging (staging loads, A prologue, LDS
-//     writes), at most 3 workgroups per CU; rows of 3-7 units: 4 waves,
-//     split staging, at most 3 workgroups per CU.
+//     writes), at most 3 workgroups per CU; rows of 4-5 units: 4 waves,
+//     split staging, at most 3 workgroups per CU; rows of 3, 6 or 7: 8
+//     waves, A first, at most 2 workgroups per CU.
 //     Staged x past 64 KiB (rows of 32 units and more): with two workgroups
 //     per CU fitting the device's LDS and over 4 x CUs rows, 4 waves, split
 //     staging, at most 2 workgroups per CU; otherwise 8 waves, x staged
@@ -388,12 +389,20 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.cap = 3;
         } else {
             // rows of 3-7 units, many of them: 4 waves, split staging, at
-            // most 3 workgroups per CU; rows of 5 units 5 in flight (no
-            // padding: 14336 x 5120 13.28 -> 12.86 us)
-            p.waves = 4;
-            p.stg = 2;
-            p.cap = 3;
-            p.D = P == 5 ? 5 : 4;
+            // most 3 workgroups per CU for rows of 4 units, and of 5 with 5
+            // in flight (no padding: 14336 x 5120 13.28 -> 12.86 us); rows
+            // of 3, 6 and 7 units: 8 waves, A first, at most 2 workgroups
+            // per CU (16384 x 6144 17.4 -> 16.2 us, 8192 x 6144 9.9 -> 9.0,
+            // 16384 x 3072 9.4 -> 9.0)
+            if (P == 4 || P == 5) {
+                p.waves = 4;
+                p.stg = 2;
+                p.cap = 3;
+                p.D = P;
+            } else {
+                p.waves = 8;
+                p.cap = 2;
+            }
         }
     } else if (const int lds = lds_bytes(kind, nchunks); lds > dev.lds_max || M <= 4 * cus) {
         // INT4 rows whose staged x would not fit a workgroup, or at most 4

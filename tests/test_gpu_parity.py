@@ -172,6 +172,18 @@ def test_two_rows_per_wave_where_that_pads_less(gpu, oracle_mod, kind, M, N):
     _check(oracle_mod, kind, ops, f"{kind} two rows per wave M={M} N={N} {info}")
 
 
+@pytest.mark.parametrize("M,N", [(16384 + 3, 6144), (9000, 7168 - 16), (12000, 3072 - 16)])
+def test_int8_rows_of_3_6_7_units(gpu, oracle_mod, M, N):
+    # many INT8 rows of 3, 6 or 7 units: 8 waves, A first, at most 2
+    # workgroups per CU, so waves walk several rows (ragged passes too)
+    info = binding.describe_launch("q8", M, N)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert (info["variant"], info["block"], info["stage_order"]) == (1, 512, 0), info
+        assert info["rows_per_wave"] >= 2, info
+    ops = inputs.make("q8", M, N, seed=M - N)
+    _check(oracle_mod, "q8", ops, f"q8 short staged rows M={M} N={N} {info}")
+
+
 @pytest.mark.parametrize("kind,M,N,D", [("q4", 2048 + 3, 10240, 5), ("q4", 4096 + 5, 12288, 3),
                                         ("q8", 14336 + 1, 5120 - 16, 5), ("q8", 3000, 5120, 5)])
 def test_depths_that_divide_the_row(gpu, oracle_mod, kind, M, N, D):
