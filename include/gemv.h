@@ -155,7 +155,7 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
  * 1-KiB loads in flight per wave, dynamic LDS bytes (x staged up to what
  * one workgroup may hold on the device), and the order in which x is staged
  * relative to the first loads of A.  The geometry is chosen per shape:
- * workgroups of 4 or 8 waves, 1 to 8 loads in flight, 1 to 4 rows (packed:
+ * workgroups of 4, 8 or 12 waves, 1 to 8 loads in flight, 1 to 4 rows (packed:
  * row groups) per wave, more where a grid cap makes waves walk further --
  * every launch keeps grid x block at or below 2^30 work-items (the llama.cpp
  * walkthrough's implementation note: the original kernel selects its block
