@@ -61,6 +61,28 @@ def test_every_plan_is_consistent(kind, dev):
         assert 1 <= p["units_in_flight"] <= 8, where
 
 
+def test_random_shapes_keep_the_invariants():
+    # seeded random row counts and lengths (log-uniform) on random devices
+    import numpy as np
+
+    rng = np.random.default_rng(2026)
+    for _ in range(3000):
+        kind = KINDS[rng.integers(len(KINDS))]
+        M = int(np.exp(rng.uniform(0, np.log(1 << 30))))
+        N = int(np.exp(rng.uniform(0, np.log(1 << 20))))
+        if kind == "q4":
+            N = max(128, N // 128 * 128)
+        dev = dict(cus=int(rng.choice([80, 104, 228, 256, 304])), lds_max=int(rng.choice([64, 160]) * 1024))
+        p = plan(kind, M, N, **dev)
+        where = (kind, M, N, dev, p)
+        assert 1 <= p["grid"] and p["grid"] * p["block"] <= 1 << 30, where
+        assert p["lds_bytes"] <= dev["lds_max"], where
+        if p["variant"] != 4:
+            assert p["grid"] * (p["block"] // 64) * p["rows_per_wave"] >= M, where
+        if p["variant"] in (1, 2) and M >= 8 * dev["cus"]:
+            assert p["grid"] >= dev["cus"], where
+
+
 def test_unaligned_operands_take_the_elementwise_kernel():
     for kind in KINDS:
         assert plan(kind, 4096, 4096, aligned=False)["variant"] == 3
