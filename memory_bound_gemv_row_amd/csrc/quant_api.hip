@@ -36,7 +36,8 @@ const void* q8_kernel(int P, int* waves)
 template <bool SSE>
 const void* row_kernel_q4_sse(int waves)
 {
-    return waves == 4 ? reinterpret_cast<const void*>(&quantize_q4_rows_kernel<4, 4, SSE>)
+    return waves == 2 ? reinterpret_cast<const void*>(&quantize_q4_rows_kernel<2, 4, SSE>)
+         : waves == 4 ? reinterpret_cast<const void*>(&quantize_q4_rows_kernel<4, 4, SSE>)
          : waves == 8 ? reinterpret_cast<const void*>(&quantize_q4_rows_kernel<8, 4, SSE>)
                       : reinterpret_cast<const void*>(&quantize_q4_rows_kernel<16, 4, SSE>);
 }
@@ -107,15 +108,17 @@ int gemv_quantize_q4(const float* W, uint8_t* q, uint16_t* scale, float* row_sse
         return launch(reinterpret_cast<const void*>(&quantize_elementwise_kernel<7>), grid4, 256, W, q, scale,
                       row_sse, M, N, stream);
     const int P = (N / 4 + 63) / 64;
-    if (P < 16) {
+    if (P <= 4) {
         // one wave per row, 4 waves per workgroup, 4 units in flight per wave
         const void* fn = row_sse != nullptr ? reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, true>)
                                             : reinterpret_cast<const void*>(&quantize_q4_kernel<4, 4, false>);
         return launch(fn, grid4, 256, W, q, scale, row_sse, M, N, stream);
     }
-    // a workgroup per row, 4 units in flight per wave, 4 to 16 waves so that
-    // each takes about 4 to 8 of the row's units
-    const int waves = P < 48 ? 4 : (P < 128 ? 8 : 16);
+    // a workgroup per row, 4 units in flight per wave, 2 to 16 waves so that
+    // each takes about 3 to 8 of the row's units (a wave per row pads rows
+    // of 5-15 units to a multiple of 4: 16384 x 1536 27.5 -> 22.6 us,
+    // 32768 x 1280 49.4 -> 36.2, 16384 x 3584 55.4 -> 45.6)
+    const int waves = P < 12 ? 2 : (P < 48 ? 4 : (P < 128 ? 8 : 16));
     return launch(row_kernel_q4(waves, row_sse != nullptr), gemv_device::capped_grid(M, waves * 64), waves * 64, W, q,
                   scale, row_sse, M, N, stream);
 }

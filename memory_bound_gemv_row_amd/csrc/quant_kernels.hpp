@@ -20,8 +20,8 @@
 //   * INT4 (a scale per 128 columns): a group is 32 lanes' 16-byte chunks,
 //     so one wave load holds two whole groups; the group maximum is a
 //     32-lane butterfly and every unit is quantised as soon as it arrives.
-//     Short rows: each wave streams whole rows with loads D units ahead,
-//     like the GEMV.  Rows of 16 units and more: a workgroup per row, its
+//     Rows of up to 4 units: each wave streams whole rows with loads D
+//     units ahead, like the GEMV.  Longer rows: a workgroup per row, its
 //     waves taking every WAVES-th unit (no group spans two waves, so they
 //     share nothing but the row's squared error, summed through LDS).
 #pragma once

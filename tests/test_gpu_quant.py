@@ -66,9 +66,10 @@ _NS = {
     # 16384 is the longest row held in registers, 16388 the first read twice;
     # N % 4 != 0 takes the element-wise path
     "q8": [1, 3, 4, 8, 252, 256, 260, 1000, 1024, 4100, 16384, 16388, 20000, 40000],
-    # up to 15 units a wave per row; from 16 (4096) a workgroup per row of
-    # 4, 8 (12416: 49 units) or 16 waves (32896: 129 units)
-    "q4": [128, 256, 384, 1024, 2176, 3968, 4096, 7296, 12416, 14336, 16384, 16512, 32896],
+    # up to 4 units a wave per row; beyond, a workgroup per row of 2 (1280:
+    # 5 units, 2176, 2816: 11), 4 (3072: 12, 3968, 4096), 8 (12416: 49
+    # units) or 16 waves (32896: 129 units)
+    "q4": [128, 256, 384, 1024, 1280, 2176, 2816, 3072, 3968, 4096, 7296, 12416, 14336, 16384, 16512, 32896],
 }
 
 
