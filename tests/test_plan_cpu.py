@@ -83,6 +83,19 @@ def test_random_shapes_keep_the_invariants():
             assert p["grid"] >= dev["cus"], where
 
 
+def test_fp_rows_pick_the_least_padding():
+    # FP16 rows of 4-23 units with rows enough to fill every CU at two rows
+    # per wave: each wave's unit sequence (rows x P) is padded to a multiple
+    # of the loads in flight by no more than the best of the four choices
+    for P in range(4, 24):
+        p = plan("f16", 16384, P * 512)
+        D, r = p["units_in_flight"], p["rows_per_wave"]
+        pad = lambda d, rr: (-(rr * P) % d) / (rr * P)
+        assert pad(D, r) == min(pad(d, rr) for d in (4, 8) for rr in (1, 2)), (P, p)
+    # too few rows to fill the CUs at two rows per wave: one row per wave
+    assert plan("f16", 1000, 6144)["rows_per_wave"] == 1
+
+
 def test_unaligned_operands_take_the_elementwise_kernel():
     for kind in KINDS:
         assert plan(kind, 4096, 4096, aligned=False)["variant"] == 3
