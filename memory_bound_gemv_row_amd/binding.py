@@ -167,6 +167,16 @@ def _need(t, name, dtypes, shape):
     return t.data_ptr()
 
 
+_INT_MAX = (1 << 31) - 1
+
+
+def _dims(*dims):
+    # the C ABI takes M and N as int: larger values would wrap in ctypes
+    for d in dims:
+        if not 0 <= d <= _INT_MAX:
+            raise ValueError(f"dimension {d} outside the C ABI's int range [0, 2^31 - 1]")
+
+
 def _out(out, M, device):
     import torch
 
@@ -180,6 +190,7 @@ def gemv_f32(A, x, out=None, stream=None):
     import torch
 
     M, N = A.shape
+    _dims(M, N)
     a = _need(A, "A", (torch.float32,), (M, N))
     xp = _need(x, "x", (torch.float32,), (N,))
     y = _out(out, M, A.device)
@@ -192,6 +203,7 @@ def gemv_f16(A, x, out=None, stream=None):
 
     h = (torch.float16, torch.int16, torch.uint16)
     M, N = A.shape
+    _dims(M, N)
     a = _need(A, "A", h, (M, N))
     xp = _need(x, "x", h, (N,))
     y = _out(out, M, A.device)
@@ -205,6 +217,7 @@ def gemv_f16x32(A, x, out=None, stream=None):
 
     h = (torch.float16, torch.int16, torch.uint16)
     M, N = A.shape
+    _dims(M, N)
     a = _need(A, "A", h, (M, N))
     xp = _need(x, "x", (torch.float32,), (N,))
     y = _out(out, M, A.device)
@@ -219,6 +232,7 @@ def gemv_f16_acc16(A, x, out=None, stream=None):
 
     h = (torch.float16, torch.int16, torch.uint16)
     M, N = A.shape
+    _dims(M, N)
     a = _need(A, "A", h, (M, N))
     xp = _need(x, "x", h, (N,))
     y = _out(out, M, A.device)
@@ -231,6 +245,7 @@ def gemv_q8(A, scale, x, out=None, stream=None):
 
     h = (torch.float16, torch.int16, torch.uint16)
     M, N = A.shape
+    _dims(M, N)
     a = _need(A, "A", (torch.int8,), (M, N))
     s = _need(scale, "scale", h, (M,))
     xp = _need(x, "x", h, (N,))
@@ -247,6 +262,7 @@ def gemv_q4(A, scale, x, out=None, stream=None):
     h = (torch.float16, torch.int16, torch.uint16)
     M, half = A.shape
     N = 2 * half
+    _dims(M, N)
     a = _need(A, "A", (torch.uint8,), (M, half))
     if N % 128:
         raise ValueError("INT4 needs N % 128 == 0")
@@ -263,6 +279,7 @@ def quantize_q8(W, with_error=True, stream=None):
     import torch
 
     M, N = W.shape
+    _dims(M, N)
     w = _need(W, "W", (torch.float32,), (M, N))
     q = torch.empty((M, N), dtype=torch.int8, device=W.device)
     s = torch.empty(M, dtype=torch.float16, device=W.device)
@@ -279,6 +296,7 @@ def quantize_q4(W, with_error=True, stream=None):
     import torch
 
     M, N = W.shape
+    _dims(M, N)
     if N % 128:
         raise ValueError("INT4 quantisation needs N % 128 == 0")
     w = _need(W, "W", (torch.float32,), (M, N))
@@ -296,6 +314,7 @@ def softmax_f16(x, out=None, stream=None):
 
     h = (torch.float16, torch.int16, torch.uint16)
     M, N = x.shape
+    _dims(M, N)
     xp = _need(x, "x", h, (M, N))
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)

@@ -340,7 +340,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.D = 4;
         p.rows = 1;
         const int lds = lds_bytes(kind, nchunks);
-        if (lds > dev.lds_max || (lds > kLdsBytes && 2 * lds > dev.lds_max && M <= 8 * cus)) {
+        if (lds > dev.lds_max || (lds >= kLdsBytes && 2 * lds > dev.lds_max && M <= 8 * cus)) {
             // staged x would not fit a workgroup, or only one workgroup
             // per CU and few rows to spread its staging over: x read with
             // each unit, 4 waves of two rows each, 8 units in flight
@@ -348,8 +348,8 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.waves = 4;
             p.D = 8;
             p.rows = 2;
-        } else if (lds > kLdsBytes) {
-            // long rows, staged x past 64 KiB: 4 waves, split
+        } else if (lds >= kLdsBytes) {
+            // long rows (32 units and more), staged x of 64 KiB or more: 4 waves, split
             // staging, at most 2 workgroups per CU when two fit and the
             // rows are many; else 8 waves, x staged before A, one
             // workgroup per CU

@@ -20,8 +20,8 @@
 //     loads (and packed short rows), loaded once per wave into registers.
 //   * Accumulation is FP32 in registers.  FP16 operands enter through
 //     v_dot2_f32_f16; INT8/INT4 codes are unpacked in registers to exact
-//     binary16 values (INT8 as offset subnormals, INT4 as exponent-biased
-//     integers, below) and enter the same way; the INT8 row scale multiplies
+//     binary16 integers (INT8 by a byte-select conversion, INT4 through an
+//     exponent bias, below) and enter the same way; the INT8 row scale multiplies
 //     the finished row sum, the INT4 group scale multiplies each 32-column
 //     partial (the reference weight is exactly q*s: "membound", section "The
 //     kernel decode actually runs: dequant GEMV").  FP16 weights with FP32 x
@@ -190,46 +190,45 @@ __device__ __forceinline__ float chunk_q4(u32x4 a, const u32x4 (&xp)[4], float s
     return __builtin_fmaf(s, __builtin_fmaf(acc_16, 0.0625f, acc_1), acc);
 }
 
-// INT8 decode (offset code).  Flipping the sign bit turns the
-// two's-complement code q into the unsigned byte q + 128, which placed in
-// the low mantissa bits of a binary16 with a zero exponent field reads as the
-// subnormal (q + 128) * 2^-24, exactly; v_dot2_f32_f16 multiplies it by x
-// exactly (at most 8 + 11 significant bits).  The offset is removed once
-// per row: sum_j q_j x_j = 2^24 * sum_j ((q_j + 128) 2^-24) x_j - 128 * sum_j x_j,
-// with sum_j x_j taken while x is staged.  (INT4 keeps its exponent-bias
-// decode: the same offset form for INT4 cancels a bias of 8 per weight
-// against per-chunk sums, and v_dot2_f32_f16, which is not correctly
-// rounded, then misses the 1e-4 gate at 14336-wide rows.)
+// INT8 -> exact binary16 pairs.  v_cvt_f16_i16 with an SDWA source select
+// converts one sign-extended byte of the word to binary16; the first
+// conversion writes the low half (clearing the high one), the second writes
+// the high half and keeps the low.  Every code is an integer of magnitude at
+// most 128, so each binary16 value is the code itself, and v_dot2_f32_f16
+// then forms each product q*x exactly: the row sum carries no offset to
+// cancel, whatever x holds (the reference weight is exactly q*s: "membound",
+// section "The kernel decode actually runs: dequant GEMV").
+__device__ __forceinline__ unsigned q8_pair_lo(unsigned w)
+{
+    unsigned r;
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
+        : "=&v"(r)
+        : "v"(w));
+    return r;
+}
 
-// INT8 chunk: acc + 2^-24 * sum (q + 128) x over 16
-// columns.  A byte permute places bytes 0,1 (and 2,3) of the XOR-ed word
-// under zero high bytes, giving the subnormal pairs (c, c+1) that match x's
-// natural pairs.
-__device__ __forceinline__ float q8_sub_chunk(u32x4 a, u32x4 x0, u32x4 x1, float acc)
+__device__ __forceinline__ unsigned q8_pair_hi(unsigned w)
+{
+    unsigned r;
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+        : "=&v"(r)
+        : "v"(w));
+    return r;
+}
+
+// INT8 chunk: acc + sum q x over 16 columns; bytes (2k, 2k+1) of the chunk
+// meet x's natural pairs.
+__device__ __forceinline__ float q8_chunk(u32x4 a, u32x4 x0, u32x4 x1, float acc)
 {
     const unsigned ws[4] = {a.x, a.y, a.z, a.w};
     const unsigned xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const unsigned w = ws[k] ^ 0x80808080u;
-        // v_perm_b32 selector: byte value 12 yields 0x00; 0..3 pick bytes of w
-        const unsigned p01 = __builtin_amdgcn_perm(0u, w, 0x0C010C00u);
-        const unsigned p23 = __builtin_amdgcn_perm(0u, w, 0x0C030C02u);
-        acc = __builtin_amdgcn_fdot2(as_h2(p01), as_h2(xs[2 * k]), acc, false);
-        acc = __builtin_amdgcn_fdot2(as_h2(p23), as_h2(xs[2 * k + 1]), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_h2(q8_pair_lo(ws[k])), as_h2(xs[2 * k]), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_h2(q8_pair_hi(ws[k])), as_h2(xs[2 * k + 1]), acc, false);
     }
-    return acc;
-}
-
-// acc + the sum of the 16 binary16 x values of two granules (v_dot2_f32_f16
-// against (1, 1): FP32 accumulation of exact binary16 values).
-__device__ __forceinline__ float x_sum_chunk(u32x4 x0, u32x4 x1, float acc)
-{
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    const unsigned xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        acc = __builtin_amdgcn_fdot2(as_h2(xs[k]), ones, acc, false);
     return acc;
 }
 
@@ -289,84 +288,6 @@ __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds
     }
 }
 
-// Chunks c0, c0 + NT, ..., c0 + (R-1) NT of stage_x_sums: all loads first
-// (2R granules in flight), then the sums in chunk order.
-template <int NT, int R>
-__device__ __forceinline__ void stage_sums_round(const u32x4* __restrict__ xg, u32x4* lds, int c0, int nchunks,
-                                                 int nchunks_pad, float& part)
-{
-    constexpr int G = Traits<kQ8>::kXGran;
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    u32x4 v[R][G];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int c = c0 + r * NT;
-#pragma unroll
-        for (int k = 0; k < G; ++k)
-            v[r][k] = c < nchunks ? xg[c * G + k] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int c = c0 + r * NT;
-        if (c >= nchunks_pad)
-            break;
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].x), ones, part, false);
-            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].y), ones, part, false);
-            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].z), ones, part, false);
-            part = __builtin_amdgcn_fdot2(as_h2(v[r][k].w), ones, part, false);
-            lds[c * G + k] = v[r][k];
-        }
-    }
-}
-
-// Staging for the INT8 decode: thread t stages whole chunks t, t + NT, ...
-// and accumulates the sum of all x (one partial per wave in lds_f[wave]).
-// Sums use v_dot2_f32_f16 against (1, 1): FP32 accumulation of exact
-// binary16 values; zero x (whole-pass padding) adds nothing.  Rows of more
-// chunks than threads load 4 chunks per thread at a time.
-template <int WAVES>
-__device__ __forceinline__ void stage_x_sums(const u32x4* __restrict__ xg, u32x4* lds, float* lds_f, int nchunks,
-                                             int nchunks_pad)
-{
-    constexpr int NT = WAVES * 64;
-    float part = 0.0f;
-    if (nchunks_pad <= NT) {
-        stage_sums_round<NT, 1>(xg, lds, threadIdx.x, nchunks, nchunks_pad, part);
-    } else {
-        for (int c0 = threadIdx.x; c0 < nchunks_pad; c0 += 4 * NT)
-            stage_sums_round<NT, 4>(xg, lds, c0, nchunks, nchunks_pad, part);
-    }
-    const float w = wave_sum(part);
-    if ((threadIdx.x & 63) == 0)
-        lds_f[threadIdx.x >> 6] = w;
-}
-
-// One thread's part of stage_x_sums when a single chunk per thread covers x:
-// v holds chunk c's granules (zero past the row end).
-template <int WAVES>
-__device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<kQ8>::kXGran], int c, u32x4* lds,
-                                                 float* lds_f, int nchunks_pad)
-{
-    constexpr int G = Traits<kQ8>::kXGran;
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    float sum = 0.0f;
-    if (c < nchunks_pad) {
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].x), ones, sum, false);
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].y), ones, sum, false);
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].z), ones, sum, false);
-            sum = __builtin_amdgcn_fdot2(as_h2(v[k].w), ones, sum, false);
-            lds[c * G + k] = v[k];
-        }
-    }
-    const float w = wave_sum(sum);
-    if ((threadIdx.x & 63) == 0)
-        lds_f[threadIdx.x >> 6] = w;
-}
-
 // ---------------------------------------------------------------- streaming kernel
 // Preconditions (checked by the host): N is a multiple of Traits<F>::kElems,
 // A and x are 16-byte aligned, M >= 1, and the launch provides
@@ -388,14 +309,12 @@ __device__ __forceinline__ void stage_chunk_sums(const u32x4 (&v)[Traits<kQ8>::k
 //
 //   XG  x granules are loaded with each unit (through L1/L2) instead of
 //       being staged in LDS: no staging and no barrier, at the cost of
-//       G x loads per A load.  INT8 then sums x per lane as it goes, for
-//       the offset-code decode's row correction.
+//       G x loads per A load.
 template <int F, bool XG>
 __host__ __device__ constexpr int stream_lds_words(int nchunks)
 {
-    // 16-byte granules of x for whole passes (zero past the row end), then
-    // (INT8) one float per wave (at most 16) for the partial sums of x.
-    return XG ? 0 : ((nchunks + 63) / 64) * 64 * Traits<F>::kXGran * 4 + (F == kQ8 ? 16 : 0);
+    // 16-byte granules of x for whole passes (zero past the row end)
+    return XG ? 0 : ((nchunks + 63) / 64) * 64 * Traits<F>::kXGran * 4;
 }
 
 // Buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes
@@ -411,8 +330,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 //   2  the staging loads, then the first D units of A, then the LDS writes:
 //      the staging loads are the older ones in the wave's in-order load
 //      counter, so the LDS writes wait only for them while A is in flight
-//      (when one round of at most 8 granules per thread stages all of x;
-//      otherwise as 1).
+//      (when one round of loads, two or eight granules per thread by
+//      format, stages all of x; otherwise as 1).
 template <int F>
 __host__ __device__ constexpr int default_stage_order()
 {
@@ -425,7 +344,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
 {
     using T = Traits<F>;
-    static_assert(WAVES <= 16, "the INT8 sum of x keeps one partial per wave");
+    static_assert(WAVES <= 16, "at most 1024 threads per workgroup");
     constexpr int kAux = NT ? 2 : 0;   // buffer-load cache policy: non-temporal
     constexpr int NT_ = WAVES * 64;
     constexpr int G = T::kXGran;       // x granules per unit
@@ -444,7 +363,6 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     const int nxg = nchunks * G;
     const int nxg_pad = P * 64 * G;             // staged granules, zero past the row end
     const u32x4* xg = reinterpret_cast<const u32x4*>(x);
-    float* lds_f = reinterpret_cast<float*>(lds_x + nxg_pad);
 
     // A unit's loads: the row's resource (wave-uniform), the pass offset
     // (wave-uniform) and the lane's fixed offset.  The whole offset goes in
@@ -498,9 +416,12 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 
     // With x staged in LDS the order of the prologue and the staging
     // matters (see default_stage_order).
-    constexpr int kRound = 8;                   // granules per thread in one staging round
-    const bool split = !XG && STG == 2 &&
-                       (F == kQ8 ? P * 64 <= NT_ : nxg_pad <= kRound * NT_);
+    // granules per thread in one staging round: the split order stages x in
+    // one round (INT8 and INT4 split only rows of at most 4 and 3 units, so
+    // two granules per thread cover them; FP16 with FP32 x, rows up to 32
+    // units, takes eight)
+    constexpr int kRound = (F == kQ8 || F == kQ4) ? 2 : 8;
+    const bool split = !XG && STG == 2 && nxg_pad <= kRound * NT_;
     bool issued = false;
     if ((XG || STG == 0) && units > 0) {
 #pragma unroll
@@ -508,54 +429,36 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             issue(d);
         issued = true;
     }
-    float xsum = 0.0f;   // INT8: sum of x over the row
     if constexpr (!XG) {
         if (split) {
-            if constexpr (F == kQ8) {
-                // one chunk (G granules) per thread: load, prologue, sum and write
-                const int c = threadIdx.x;
-                u32x4 v[G];
+            // every staging load is issued (granule 0 stands in past x's
+            // end and is zeroed when written): a load under a condition
+            // compiles to a branch per load, after which the compiler can
+            // no longer count the A loads in flight and waits for all of
+            // them in every unit
+            u32x4 v[kRound];
 #pragma unroll
-                for (int k = 0; k < G; ++k)
-                    v[k] = c < nchunks ? xg[c * G + k] : u32x4{0u, 0u, 0u, 0u};
-                if (units > 0) {
-#pragma unroll
-                    for (int d = 0; d < D; ++d)
-                        issue(d);
-                    issued = true;
-                }
-                stage_chunk_sums<WAVES>(v, c, lds_x, lds_f, P * 64);
-            } else {
-                u32x4 v[kRound];
-#pragma unroll
-                for (int k = 0; k < kRound; ++k) {
-                    const int g = threadIdx.x + k * NT_;
-                    v[k] = g < nxg ? xg[g] : u32x4{0u, 0u, 0u, 0u};
-                }
-                if (units > 0) {
-#pragma unroll
-                    for (int d = 0; d < D; ++d)
-                        issue(d);
-                    issued = true;
-                }
-#pragma unroll
-                for (int k = 0; k < kRound; ++k) {
-                    const int g = threadIdx.x + k * NT_;
-                    if (g < nxg_pad)
-                        lds_x[staged_index<F>(g / G, g % G, P * 64)] = (F == kQ4) ? q4_pair_x(v[k]) : v[k];
-                }
+            for (int k = 0; k < kRound; ++k) {
+                const int g = threadIdx.x + k * NT_;
+                v[k] = xg[g < nxg ? g : 0];
             }
-        } else if constexpr (F == kQ8) {
-            stage_x_sums<WAVES>(xg, lds_x, lds_f, nchunks, P * 64);
+            if (units > 0) {
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    issue(d);
+                issued = true;
+            }
+#pragma unroll
+            for (int k = 0; k < kRound; ++k) {
+                const int g = threadIdx.x + k * NT_;
+                const u32x4 vz = g < nxg ? v[k] : u32x4{0u, 0u, 0u, 0u};
+                if (g < nxg_pad)
+                    lds_x[staged_index<F>(g / G, g % G, P * 64)] = (F == kQ4) ? q4_pair_x(vz) : vz;
+            }
         } else {
             stage_x<F, NT_>(xg, lds_x, nxg, nxg_pad);
         }
         __syncthreads();
-        if constexpr (F == kQ8) {
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w)
-                xsum += lds_f[w];
-        }
     }
     if (units == 0)
         return;
@@ -566,7 +469,6 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     }
 
     float acc = 0.0f;
-    float xs = 0.0f;                                   // INT8 with XG: this lane's sum of x
     f16x2 acch = {(_Float16)0.0f, (_Float16)0.0f};   // FP16 accumulation only
     int c_row = wave_id, c_pass = 0;
     // One unit of arithmetic: a = the unit's 16 bytes of A per lane, xv = its
@@ -581,9 +483,7 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         } else if constexpr (F == kF16H) {
             acch = chunk_f16h(a, xv[0], acch);
         } else if constexpr (F == kQ8) {
-            acc = q8_sub_chunk(a, xv[0], xv[G - 1], acc);
-            if constexpr (XG)
-                xs = x_sum_chunk(xv[0], xv[G - 1], xs);
+            acc = q8_chunk(a, xv[0], xv[G - 1], acc);
         } else {
             const u32x4 xp[4] = {xv[0], xv[1 % G], xv[2 % G], xv[3 % G]};
             acc = chunk_q4(a, xp, half_bits_to_float(sraw), acc);
@@ -597,15 +497,9 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
                 acch = f16x2{(_Float16)0.0f, (_Float16)0.0f};
             }
             float t = wave_sum(acc);
-            if constexpr (F == kQ8 && XG) {
-                xsum = wave_sum(xs);
-                xs = 0.0f;
-            }
             if (lane == 0 && c_row < M) {
-                if constexpr (F == kQ8) {
-                    t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);   // remove the offset
+                if constexpr (F == kQ8)
                     t *= half_bits_to_float(sraw);   // this row's scale (see issue)
-                }
                 y[c_row] = t;
             }
             acc = 0.0f;
@@ -719,14 +613,7 @@ gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         issue(d);
 
     // x is older than every A load in the counter: ready before the first unit
-    float xsum = 0.0f;   // INT8: sum of x over the row
-    if constexpr (F == kQ8) {
-        float xs = 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            xs = x_sum_chunk(xr[k][0], xr[k][G - 1], xs);
-        xsum = wave_sum(xs);
-    } else if constexpr (F == kQ4) {
+    if constexpr (F == kQ4) {
 #pragma unroll
         for (int k = 0; k < K; ++k)
 #pragma unroll
@@ -748,7 +635,7 @@ gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         } else if constexpr (F == kF16H) {
             acch = chunk_f16h(buf[d], xr[pass][0], acch);
         } else if constexpr (F == kQ8) {
-            acc = q8_sub_chunk(buf[d], xr[pass][0], xr[pass][G - 1], acc);
+            acc = q8_chunk(buf[d], xr[pass][0], xr[pass][G - 1], acc);
         } else {
             acc = chunk_q4(buf[d], xr[pass], half_bits_to_float(sbuf[d]), acc);
         }
@@ -759,10 +646,8 @@ gemv_xreg(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
             }
             float t = wave_sum(acc);
             if (lane == 0 && c_row < M) {
-                if constexpr (F == kQ8) {
-                    t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);   // remove the offset
+                if constexpr (F == kQ8)
                     t *= half_bits_to_float(sbuf[d]);
-                }
                 y[c_row] = t;
             }
             acc = 0.0f;
@@ -845,8 +730,7 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         return;
     // x: this lane's chunk, G granules, straight into registers through a
     // resource of exactly x's bytes (zeros for lanes past the row end); no
-    // LDS and no barrier.  INT8 sums x over each row segment of L lanes
-    // (every segment holds all of x).
+    // LDS and no barrier.
     const auto xrsrc = make_rsrc(x, (uint32_t)nchunks * G * 16);
     u32x4 xv[G];
 #pragma unroll
@@ -879,9 +763,6 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     for (int d = 0; d < D; ++d)
         issue(d);
     // x arrives before the first A loads (older in the load counter)
-    float xsum = 0.0f;   // INT8: sum of x over the row
-    if constexpr (F == kQ8)
-        xsum = segment_sum(x_sum_chunk(xv[0], xv[G - 1], 0.0f), L);
     if constexpr (F == kQ4) {
 #pragma unroll
         for (int k = 0; k < G; ++k)
@@ -894,15 +775,13 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         if constexpr (F == kQ4) {
             acc = chunk_q4(buf[d], xv, half_bits_to_float(sbuf[d]), 0.0f);
         } else {
-            acc = q8_sub_chunk(buf[d], xv[0], xv[G - 1], 0.0f);
+            acc = q8_chunk(buf[d], xv[0], xv[G - 1], 0.0f);
         }
         float t = segment_sum(acc, L);
         if (c == 0 && c_g <= last && c_g * R + sub < M) {
             const int row = c_g * R + sub;
-            if constexpr (F == kQ8) {
-                t = __builtin_fmaf(t, 16777216.0f, -128.0f * xsum);   // remove the offset
+            if constexpr (F == kQ8)
                 t *= half_bits_to_float(sbuf[d]);
-            }
             y[row] = t;
         }
         c_g += nwaves;

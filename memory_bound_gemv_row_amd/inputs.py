@@ -107,6 +107,38 @@ def make_weights(M: int, N: int, seed: int = 0) -> np.ndarray:
     return rng.uniform(-1.0, 1.0, (M, N)).astype(np.float32)
 
 
+# Activation distributions beyond the workloads' zero-mean N(0, 1): decode
+# hidden states after an activation are non-negative or off-centre.
+X_DISTS = ("normal", "abs_normal", "shifted")
+
+
+def make_x_f16(N: int, dist: str = "normal", seed: int = 0) -> np.ndarray:
+    """binary16 x: ``normal`` N(0, 1), ``abs_normal`` |N(0, 1)|, ``shifted``
+    N(1, 1)."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal(N)
+    if dist == "normal":
+        v = z
+    elif dist == "abs_normal":
+        v = np.abs(z)
+    elif dist == "shifted":
+        v = z + 1.0
+    else:
+        raise ValueError(f"unknown x distribution {dist!r}")
+    return v.astype(np.float16)
+
+
+def make_gauss_weights(M: int, N: int, seed: int = 0, outlier: float = 0.0) -> np.ndarray:
+    """FP32 weights ~ N(0, 1), the quantiser's input for realistic codes.  With
+    ``outlier`` > 0 one weight per row (at a random column) is set to that
+    value, so that the row's absmax scale leaves most codes small."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((M, N)).astype(np.float32)
+    if outlier > 0 and N > 0:
+        W[np.arange(M), rng.integers(0, N, M)] = np.float32(outlier)
+    return W
+
+
 # Quantiser workloads: the INT8 and INT4 GEMV shapes, from FP32 weights.
 QUANT_WORKLOADS = [("q8", 8192, 8192), ("q8", 14336, 4096), ("q4", 4096, 14336), ("q4", 14336, 4096)]
 

@@ -148,7 +148,7 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("q8", 4096, 32768)["variant"] == 1
     assert binding.describe_launch("q4", 4096, 34816)["variant"] == 1
     assert binding.describe_launch("q4", 1024, 33280)["variant"] == 2
-    q8_beyond = (lds_max - 64) // 2048 * 1024 + 1024     # one unit past what fits
+    q8_beyond = lds_max // 2048 * 1024 + 1024            # one unit past what fits
     q4_beyond = lds_max // 4096 * 2048 + 2048
     assert binding.describe_launch("q8", 4096, q8_beyond)["variant"] == 2
     assert binding.describe_launch("q4", 4096, q4_beyond)["variant"] == 2

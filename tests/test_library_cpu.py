@@ -50,3 +50,22 @@ def test_status_strings(lib):
 def test_gfx950_code_object_is_embedded():
     blob = open(binding.LIB_PATH, "rb").read()
     assert b"gfx950" in blob
+
+
+def test_torch_wrappers_reject_dimensions_beyond_int():
+    # M and N cross the C ABI as int; a larger dimension must raise instead
+    # of wrapping (2^32 + 16 would become 16)
+    from types import SimpleNamespace
+
+    from memory_bound_gemv_row_amd import binding
+
+    big = SimpleNamespace(shape=((1 << 32) + 16, 4))
+    for fn in (binding.gemv_f32, binding.gemv_f16, binding.gemv_f16x32, binding.gemv_f16_acc16):
+        with pytest.raises(ValueError, match="int range"):
+            fn(big, None)
+    with pytest.raises(ValueError, match="int range"):
+        binding.gemv_q8(big, None, None)
+    with pytest.raises(ValueError, match="int range"):
+        binding.gemv_q4(SimpleNamespace(shape=(4, 1 << 31)), None, None)
+    with pytest.raises(ValueError, match="int range"):
+        binding.softmax_f16(SimpleNamespace(shape=(1, 1 << 31)))

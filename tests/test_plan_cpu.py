@@ -20,7 +20,7 @@ def plan(kind, M, N, cus=256, lds_max=160 * 1024, aligned=True):
 
 def staged_bytes(kind, N):
     nchunks = N // ELEMS_PER_CHUNK[kind]
-    return (nchunks + 63) // 64 * 64 * X_GRANULES[kind] * 16 + (64 if kind == "q8" else 0)
+    return (nchunks + 63) // 64 * 64 * X_GRANULES[kind] * 16
 
 
 _MS = [1, 7, 64, 255, 1000, 1024, 1025, 2048, 4096, 8192, 14336, 40000, 300000, (1 << 24) + 3]
@@ -123,13 +123,13 @@ def test_headline_shapes_on_mi355x():
 def test_long_rows_stage_x_up_to_the_device_limit():
     # INT8/INT4 and FP16-with-FP32-x rows whose staged x passes 64 KiB stage
     # it while it fits a workgroup; a 64-KiB device reads x with each unit
-    for kind, M, N in (("q8", 4096, 32768), ("q4", 4096, 34816), ("q4", 2048, 81920), ("f16x32", 4096, 24576)):
+    for kind, M, N in (("q8", 4096, 34816), ("q4", 4096, 34816), ("q4", 2048, 81920), ("f16x32", 4096, 24576)):
         assert staged_bytes(kind, N) > 64 * 1024
         p = plan(kind, M, N)
         assert p["variant"] == 1 and p["lds_bytes"] == staged_bytes(kind, N), (kind, M, N, p)
         assert plan(kind, M, N, lds_max=64 * 1024)["variant"] == 2, (kind, M, N)
     # one unit past what a workgroup may hold
-    assert plan("q8", 4096, 81920)["variant"] == 2
+    assert plan("q8", 4096, 81920)["variant"] == 1 and plan("q8", 4096, 81920 + 1024)["variant"] == 2
     assert plan("q4", 4096, 83968)["variant"] == 2
     assert plan("f16x32", 64, 40960 + 512)["variant"] == 2
 
