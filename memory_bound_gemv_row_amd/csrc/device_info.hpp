@@ -9,7 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include <mutex>
+#include <atomic>
 #include <stdint.h>
 
 namespace gemv_device {
@@ -33,25 +33,34 @@ inline int capped_grid(int64_t grid, int block)
 }
 
 // Properties of the current device; GEMV_E_DEVICE when there is none or its
-// attributes cannot be read.  Thread-safe; one cache for the whole library
-// (an inline function's statics are shared by every translation unit).
+// attributes cannot be read.  One cache for the whole library (an inline
+// function's statics are shared by every translation unit), filled on the
+// first call on each device and lock-free: a call reads two atomics.  Two
+// threads that both find a device's slot empty both query it and store the
+// same values; a slot is complete once its CU count is non-zero (stored last,
+// with release order).
 inline int current(Device* out)
 {
-    static std::mutex mutex;
-    static Device cache[kMaxDevices] = {};
+    struct Slot {
+        std::atomic<int> cus{0};
+        std::atomic<int> lds_max{0};
+    };
+    static Slot cache[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return GEMV_E_DEVICE;
-    std::lock_guard<std::mutex> lock(mutex);
-    if (cache[dev].cus == 0) {
-        int n = 0, lds = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0 ||
+    Slot& slot = cache[dev];
+    int cus = slot.cus.load(std::memory_order_acquire);
+    if (cus == 0) {
+        int lds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
             hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
             lds <= 0)
             return GEMV_E_DEVICE;
-        cache[dev] = {n, lds};
+        slot.lds_max.store(lds, std::memory_order_relaxed);
+        slot.cus.store(cus, std::memory_order_release);
     }
-    *out = cache[dev];
+    *out = Device{cus, slot.lds_max.load(std::memory_order_relaxed)};
     return GEMV_OK;
 }
 

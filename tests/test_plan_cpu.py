@@ -179,3 +179,29 @@ def test_describe_launch_for_rejects_bad_arguments():
         plan("f16", 16, 16, lds_max=0)
     lib = binding.load()
     assert lib.gemv_describe_launch_for(6, 16, 16, 1, 256, 163840, None) == 1
+
+
+def _acc16_terms(variant, N):
+    # binary16 running-sum terms per lane and row, by kernel: the element-wise
+    # kernel (3) adds one column per pass of 64 lanes; the streaming (2) and
+    # x-in-registers (5) kernels keep an (even, odd) pair per lane and add four
+    # column pairs of each 16-byte chunk, one chunk per 512-column pass
+    if variant == 3:
+        return -(-N // 64)
+    assert variant in (2, 5), variant      # any other kernel needs its own count here
+    return 4 * -(-N // 512)
+
+
+@pytest.mark.parametrize("dev", _DEVICES, ids=lambda d: f"{d['cus']}cu_{d['lds_max'] // 1024}k")
+def test_fp16_accumulation_plans_keep_the_gate_term_count(dev):
+    # the FP16-accumulation gate (oracle.metrics.acc16_bound) assumes at most
+    # k = max(ceil(N/64), 4) terms per binary16 sum; every plan the library can
+    # choose must keep within it, unaligned operands included
+    from oracle.metrics import acc16_bound  # noqa: F401  (the gate this pins)
+
+    for N in _NS + [1, 7, 9, 4100, 65536, 131072]:
+        k = max(-(-N // 64), 4)
+        for M in _MS:
+            for aligned in (True, False):
+                p = plan("f16_acc16", M, N, dev["cus"], dev["lds_max"], aligned)
+                assert _acc16_terms(p["variant"], N) <= k, (M, N, aligned, dev, p)

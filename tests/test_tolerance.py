@@ -210,3 +210,68 @@ def test_componentwise_fp32_bound_accepts_orders_and_catches_a_dropped_term():
         if N > 1:
             bad = ref - A[:, N // 2].astype(np.float64) * x[N // 2]
             assert within_fp32_bound("f32", ops, bad, ref) > 1.0
+
+
+def _dot2_f32(a0, b0, a1, b1, c):
+    """v_dot2_f32_f16 with two roundings (the pair sum, then the addend): the
+    products of binary16 operands are exact in FP32, and the instruction is
+    not correctly rounded, so the pessimistic order is emulated."""
+    s = (a0.astype(np.float64) * b0 + a1.astype(np.float64) * b1).astype(np.float32)
+    return (s.astype(np.float64) + c).astype(np.float32)
+
+
+def _q8_kernel_order(q, s, x, offset):
+    """Emulate the INT8 streaming kernel: lane l owns the 16-column chunks l,
+    l+64, ... of a row; each chunk enters a float32 running sum through eight
+    v_dot2_f32_f16 steps, then a 64-lane butterfly and the row scale.
+    offset=False: exact binary16 codes (the kernel's decode).  offset=True:
+    the biased decode (q + 128) 2^-24 with 128 sum(x) removed once per row,
+    a decode that cancels catastrophically for non-zero-mean x."""
+    M, N = q.shape
+    assert N % 1024 == 0
+    xh = x.astype(np.float32)
+    qc = q.reshape(M, N // 1024, 64, 16).astype(np.float32)
+    xc = xh.reshape(N // 1024, 64, 16)
+    if offset:
+        qc = (qc + 128) * np.float32(2.0 ** -24)
+    acc = np.zeros((M, 64), np.float32)
+    for p in range(N // 1024):
+        for k in range(8):
+            acc = _dot2_f32(qc[:, p, :, 2 * k], xc[p, :, 2 * k], qc[:, p, :, 2 * k + 1], xc[p, :, 2 * k + 1], acc)
+    t = _butterfly_f32(acc)
+    sf = s.astype(np.float32)
+    if offset:
+        xsum = np.float32(np.sum(xh.astype(np.float64)))
+        t = (t.astype(np.float64) * 2.0 ** 24 - 128.0 * xsum).astype(np.float32)
+    return (t * sf).astype(np.float32)
+
+
+@pytest.mark.parametrize("codes", ["uniform", "outlier"])
+def test_q8_exact_decode_error_does_not_depend_on_the_mean_of_x(codes):
+    # the INT8 reference weight is exactly q*s with FP32 accumulation
+    # ("membound", dequant GEMV section): with exact codes the error stays at
+    # FP32 level for zero-mean, non-negative and shifted x alike; the biased
+    # decode passes zero-mean x and fails the gate on the others
+    import oracle
+    from memory_bound_gemv_row_amd import inputs
+
+    M, N = 256, 8192
+    if codes == "uniform":
+        ops = inputs.make_q8(M, N, seed=3)
+        q, s = ops["A"], ops["scale"]
+    else:
+        oracle.build(force=False)
+        q, sb, _ = oracle.quantize_q8(inputs.make_gauss_weights(M, N, seed=3, outlier=25.0))
+        s = sb.view(np.float16)
+    errs = {}
+    for dist in inputs.X_DISTS:
+        x = inputs.make_x_f16(N, dist, seed=4)
+        ref = oracle.gemv_q8(q, s, x)
+        exact = parity_error(_q8_kernel_order(q, s, x, offset=False), ref)
+        biased = parity_error(_q8_kernel_order(q, s, x, offset=True), ref)
+        errs[dist] = (exact, biased)
+        assert exact < GATES["q8"] / 5, (codes, dist, exact)
+    spread = max(e for e, _ in errs.values()) / min(e for e, _ in errs.values())
+    assert spread < 4, errs
+    assert errs["abs_normal"][1] > GATES["q8"], errs
+    assert errs["shifted"][1] > GATES["q8"], errs
