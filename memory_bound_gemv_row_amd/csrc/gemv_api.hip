@@ -353,7 +353,7 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
             // staging, at most 2 workgroups per CU when two fit and the
             // rows are many; else 8 waves, x staged before A, one
             // workgroup per CU
-            const bool two = 2 * lds <= dev.lds_max && M > 4 * cus;
+            const bool two = 2 * (lds + kSplitSpareBytes) <= dev.lds_max && M > 4 * cus;
             p.waves = two ? 4 : 8;
             p.stg = two ? 2 : 1;
             p.cap = two ? 2 : 1;
@@ -440,6 +440,13 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.cap = P >= 14 ? 2 : 3;
     }
     p.lds = p.variant == 1 ? lds_bytes(kind, nchunks) : 0;
+    if (p.variant == 1 && p.stg == 2) {
+        // split staging writes past-the-end granules to spare slots
+        if (p.lds + kSplitSpareBytes <= dev.lds_max)
+            p.lds += kSplitSpareBytes;
+        else
+            p.stg = 1;
+    }
     p.block = p.waves * 64;
     const int64_t waves_needed = ((int64_t)M + p.rows - 1) / p.rows;
     int64_t grid = (waves_needed + p.waves - 1) / p.waves;

@@ -159,35 +159,38 @@ __device__ __forceinline__ float chunk_f16x32(u32x4 a, u32x4 x0, u32x4 x1, float
 // column c+k in bits [4k, 4k+4).  XOR with 0x8 per nibble turns a
 // two's-complement code q into q + 8 in 0..15.  Masking with 0x000F000F
 // keeps columns c and c+4 in the low mantissa bits of the two binary16
-// halves; under exponent bits 0x6400 they read 1024 + (q + 8), and
-// subtracting 1032 leaves q.  Mask 0x00F000F0 keeps columns c+1 and c+5 four
-// bits higher: 1024 + 16(q + 8), minus 1152, is 16q (exact), and the factor
-// 16 is removed once per chunk.  Shifting the word right by 8 gives columns
-// c+2, c+6 and c+3, c+7 the same way.  x is therefore staged with each
-// 8-column block reordered as (x0,x4), (x1,x5), (x2,x6), (x3,x7).
-__device__ __forceinline__ void q4_word(unsigned w, u32x4 xp, float& acc_1, float& acc_16)
+// halves; under exponent bits 0x6400 (2^10, unit spacing) they read
+// 1024 + (q + 8), and subtracting 1032 leaves q.  Mask 0x00F000F0 keeps
+// columns c+1 and c+5 four bits higher; under exponent bits 0x5400 (2^6,
+// spacing 1/16) they read 64 + (q + 8), and subtracting 72 leaves q.  Each
+// mask-and-XOR is one v_bitop3_b32 and each subtraction one v_pk_add_f16,
+// exact.  Shifting the word right by 8 gives columns c+2, c+6 and c+3, c+7
+// the same way.  x is therefore staged with each 8-column block reordered
+// as (x0,x4), (x1,x5), (x2,x6), (x3,x7).  All four pairs enter one FP32 sum.
+__device__ __forceinline__ float q4_word(unsigned w, u32x4 xp, float acc)
 {
-    const f16x2 b1 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const f16x2 b16 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-    // (w ^ 0x88888888) & mask | 0x64006400 written as one AND and one XOR:
-    // the XOR constant flips the nibble's sign bit (bit 3 or bit 7 of each
-    // half) and sets the exponent bits 0x6400, which the mask has cleared.
+    const f16x2 b_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const f16x2 b_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    // (w ^ 0x88888888) & mask | exponent bits, written as one AND and one
+    // XOR: the XOR constant flips the nibble's sign bit (bit 3 or bit 7 of
+    // each half) and sets the exponent bits, which the mask has cleared
     const unsigned w8 = w >> 8;
-    acc_1 = __builtin_amdgcn_fdot2(as_h2((w & 0x000F000Fu) ^ 0x64086408u) + b1, as_h2(xp.x), acc_1, false);
-    acc_16 = __builtin_amdgcn_fdot2(as_h2((w & 0x00F000F0u) ^ 0x64806480u) + b16, as_h2(xp.y), acc_16, false);
-    acc_1 = __builtin_amdgcn_fdot2(as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + b1, as_h2(xp.z), acc_1, false);
-    acc_16 = __builtin_amdgcn_fdot2(as_h2((w8 & 0x00F000F0u) ^ 0x64806480u) + b16, as_h2(xp.w), acc_16, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x000F000Fu) ^ 0x64086408u) + b_lo, as_h2(xp.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((w & 0x00F000F0u) ^ 0x54805480u) + b_hi, as_h2(xp.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + b_lo, as_h2(xp.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2((w8 & 0x00F000F0u) ^ 0x54805480u) + b_hi, as_h2(xp.w), acc, false);
+    return acc;
 }
 
 // INT4: 32 columns (all inside one 128-column group) and their group scale.
 __device__ __forceinline__ float chunk_q4(u32x4 a, const u32x4 (&xp)[4], float s, float acc)
 {
-    float acc_1 = 0.0f, acc_16 = 0.0f;
-    q4_word(a.x, xp[0], acc_1, acc_16);
-    q4_word(a.y, xp[1], acc_1, acc_16);
-    q4_word(a.z, xp[2], acc_1, acc_16);
-    q4_word(a.w, xp[3], acc_1, acc_16);
-    return __builtin_fmaf(s, __builtin_fmaf(acc_16, 0.0625f, acc_1), acc);
+    float part = 0.0f;
+    part = q4_word(a.x, xp[0], part);
+    part = q4_word(a.y, xp[1], part);
+    part = q4_word(a.z, xp[2], part);
+    part = q4_word(a.w, xp[3], part);
+    return __builtin_fmaf(s, part, acc);
 }
 
 // INT8 -> exact binary16 pairs.  v_cvt_f16_i16 with an SDWA source select
@@ -288,6 +291,54 @@ __device__ __forceinline__ void stage_x(const u32x4* __restrict__ xg, u32x4* lds
     }
 }
 
+// Split staging (see default_stage_order): rounds of split_round<F>()
+// granules per thread, granule g = g0 + k * NT for k < that.  Neither the loads
+// nor the LDS writes branch per granule: a load or store under a condition
+// compiles to a branch, after which the compiler no longer knows which loads
+// are in flight and waits for all of them, the A loads included, before the
+// write.  So every load is issued (granule 0 stands in past x's end and is
+// zeroed), and every write happens: granules past the zero-padded end go to
+// one spare granule per lane after the staged x (kSplitSpareBytes more LDS).
+// Granules per thread in a round: INT8 and INT4 split rows of a few units
+// (one to three granules per thread), FP16 with FP32 x rows up to 32 units
+// (up to eight); a larger round only adds loads of granule 0 and spare writes.
+template <int F>
+__host__ __device__ constexpr int split_round()
+{
+#ifdef GEMV_SPLIT_ROUND
+    return GEMV_SPLIT_ROUND;
+#else
+    return F == kF16X32 ? 8 : 2;
+#endif
+}
+constexpr int kSplitSpareBytes = 64 * 16;
+
+template <int F, int NT>
+__device__ __forceinline__ void split_round_load(const u32x4* __restrict__ xg, int g0, int nxg,
+                                                 u32x4 (&v)[split_round<F>()])
+{
+#pragma unroll
+    for (int k = 0; k < split_round<F>(); ++k) {
+        const int g = g0 + k * NT;
+        v[k] = xg[g < nxg ? g : 0];
+    }
+}
+
+template <int F, int NT>
+__device__ __forceinline__ void split_round_write(u32x4* lds, int g0, int nxg, int nxg_pad,
+                                                  const u32x4 (&v)[split_round<F>()])
+{
+    constexpr int G = Traits<F>::kXGran;
+    const int spare = nxg_pad + (threadIdx.x & 63);
+#pragma unroll
+    for (int k = 0; k < split_round<F>(); ++k) {
+        const int g = g0 + k * NT;
+        const u32x4 vz = g < nxg ? v[k] : u32x4{0u, 0u, 0u, 0u};
+        const int dst = g < nxg_pad ? staged_index<F>(g / G, g % G, nxg_pad / G) : spare;
+        lds[dst] = (F == kQ4) ? q4_pair_x(vz) : vz;
+    }
+}
+
 // ---------------------------------------------------------------- streaming kernel
 // Preconditions (checked by the host): N is a multiple of Traits<F>::kElems,
 // A and x are 16-byte aligned, M >= 1, and the launch provides
@@ -327,11 +378,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Order of the A prologue and the staging of x (with x in LDS):
 //   0  the first D units of A, then the staging (loads, LDS writes);
 //   1  the staging, then the first D units of A;
-//   2  the staging loads, then the first D units of A, then the LDS writes:
-//      the staging loads are the older ones in the wave's in-order load
-//      counter, so the LDS writes wait only for them while A is in flight
-//      (when one round of loads, two or eight granules per thread by
-//      format, stages all of x; otherwise as 1).
+//   2  the first round of staging loads, then the first D units of A, then
+//      the round's LDS writes and any further rounds: the first round's loads
+//      are the older ones in the wave's in-order load counter, so its LDS
+//      writes wait only for them while A is in flight (needs
+//      kSplitSpareBytes more LDS than the staged x).
 template <int F>
 __host__ __device__ constexpr int default_stage_order()
 {
@@ -359,7 +410,9 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     const int my_rows = wave_id < M ? (M - 1 - wave_id) / nwaves + 1 : 0;
     const int units = my_rows * P;
     const int units_pad = (units + D - 1) / D * D;
-    const int last_row = wave_id + (my_rows - 1) * nwaves;
+    // a wave without rows (past M) may issue its prologue on row 0 and
+    // discard it (split staging, below)
+    const int last_row = my_rows > 0 ? wave_id + (my_rows - 1) * nwaves : 0;
     const int nxg = nchunks * G;
     const int nxg_pad = P * 64 * G;             // staged granules, zero past the row end
     const u32x4* xg = reinterpret_cast<const u32x4*>(x);
@@ -416,12 +469,6 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
 
     // With x staged in LDS the order of the prologue and the staging
     // matters (see default_stage_order).
-    // granules per thread in one staging round: the split order stages x in
-    // one round (INT8 and INT4 split only rows of at most 4 and 3 units, so
-    // two granules per thread cover them; FP16 with FP32 x, rows up to 32
-    // units, takes eight)
-    constexpr int kRound = (F == kQ8 || F == kQ4) ? 2 : 8;
-    const bool split = !XG && STG == 2 && nxg_pad <= kRound * NT_;
     bool issued = false;
     if ((XG || STG == 0) && units > 0) {
 #pragma unroll
@@ -430,30 +477,24 @@ gemv_stream(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         issued = true;
     }
     if constexpr (!XG) {
-        if (split) {
-            // every staging load is issued (granule 0 stands in past x's
-            // end and is zeroed when written): a load under a condition
-            // compiles to a branch per load, after which the compiler can
-            // no longer count the A loads in flight and waits for all of
-            // them in every unit
-            u32x4 v[kRound];
+        if constexpr (STG == 2) {
+            // rounds of SR granules per thread; the A prologue goes
+            // out after the first round's loads, so the first round's LDS
+            // writes wait only for those older loads while A is in flight
+            constexpr int SR = split_round<F>();
+            u32x4 v[SR];
+            split_round_load<F, NT_>(xg, threadIdx.x, nxg, v);
+            // every wave issues the prologue here, without a branch: a branch
+            // around it leaves the compiler two paths with different loads in
+            // flight, and it then waits for the A loads before the LDS writes
 #pragma unroll
-            for (int k = 0; k < kRound; ++k) {
-                const int g = threadIdx.x + k * NT_;
-                v[k] = xg[g < nxg ? g : 0];
-            }
-            if (units > 0) {
-#pragma unroll
-                for (int d = 0; d < D; ++d)
-                    issue(d);
-                issued = true;
-            }
-#pragma unroll
-            for (int k = 0; k < kRound; ++k) {
-                const int g = threadIdx.x + k * NT_;
-                const u32x4 vz = g < nxg ? v[k] : u32x4{0u, 0u, 0u, 0u};
-                if (g < nxg_pad)
-                    lds_x[staged_index<F>(g / G, g % G, P * 64)] = (F == kQ4) ? q4_pair_x(vz) : vz;
+            for (int d = 0; d < D; ++d)
+                issue(d);
+            issued = true;
+            split_round_write<F, NT_>(lds_x, threadIdx.x, nxg, nxg_pad, v);
+            for (int g0 = threadIdx.x + SR * NT_; g0 - (int)threadIdx.x < nxg_pad; g0 += SR * NT_) {
+                split_round_load<F, NT_>(xg, g0, nxg, v);
+                split_round_write<F, NT_>(lds_x, g0, nxg, nxg_pad, v);
             }
         } else {
             stage_x<F, NT_>(xg, lds_x, nxg, nxg_pad);
