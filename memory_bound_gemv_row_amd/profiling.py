@@ -6,6 +6,8 @@ Usage (after the rocprofv3 runs named in each summary's header)::
     python -m memory_bound_gemv_row_amd.profiling counters <counter_collection.csv> <out.txt> <command>
     python -m memory_bound_gemv_row_amd.profiling traffic <fetch_counter_collection.csv> \
         <write_counter_collection.csv> <workload> <out.txt> <fetch command> <write command>
+    python -m memory_bound_gemv_row_amd.profiling table <workload> <out.txt> \
+        <run dir> <command> [<run dir> <command> ...]
 
 Traffic calibration: ``bench.py --profile`` launches, in order, a 1 GiB
 pure-read probe, the GEMV once, the probe again, and a 256 MiB copy.  The
@@ -131,9 +133,20 @@ def write_traffic_summary(fetch_csv, write_csv, workload, out, fetch_cmd, write_
     return t
 
 
+def _traced_op(names):
+    """The operation a trace profiles, from its kernel names."""
+    if any("quantize_" in n for n in names):
+        return "quant"
+    if any("softmax_f16" in n for n in names):
+        return "softmax"
+    return "gemv"
+
+
 def write_trace_summary(stats_csv, out, command):
     rows = _rows(stats_csv)
+    op = _traced_op([r["Name"] for r in rows])
     lines = [f"# rocprofv3 --kernel-trace --stats summary", f"command: {command}",
+             f"kernel_source_hash: {kernel_source_hash(op)}",
              "calls  avg_us  min_us  max_us  share%  kernel"]
     for r in rows:
         lines.append(f"{int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:8.3f} {float(r['MinNs']) / 1e3:7.3f} "
@@ -163,6 +176,122 @@ def write_counter_summary(csv_path, out, command):
         f.write("\n".join(lines) + "\n")
 
 
+def _agent(agent_csv):
+    """Num_Xcc, Cu_Count, Simd_Count and Max_Waves_Per_Cu of the profiled GPU."""
+    for r in _rows(agent_csv):
+        if r.get("Agent_Type", "").upper() == "GPU":
+            a = {k: int(r[k]) for k in ("Num_Xcc", "Cu_Count", "Simd_Count", "Max_Waves_Per_Cu", "Cu_Per_Engine")}
+            a["Shader_Engines"] = a["Cu_Count"] // a["Cu_Per_Engine"]
+            return a
+    raise ValueError(f"no GPU agent in {agent_csv}")
+
+
+def _mean_dispatches(csv_path, match, skip, largest=False):
+    """Mean of each counter over the dispatches whose kernel name contains
+    `match`, after the first `skip` of them (warm launches only); with
+    `largest`, only the dispatches of the largest grid (the full-size
+    probe, not the one-workgroup launch-floor probes)."""
+    per, grid = {}, {}
+    for r in _rows(csv_path):
+        if match in r["Kernel_Name"]:
+            i = int(r["Dispatch_Id"])
+            per.setdefault(i, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            per[i]["_kernel"] = r["Kernel_Name"]
+            grid[i] = int(r["Grid_Size"])
+    ids = sorted(per)
+    if largest and ids:
+        g = max(grid.values())
+        ids = [i for i in ids if grid[i] == g]
+    ids = ids[skip:]
+    if not ids:
+        raise ValueError(f"no dispatch of {match!r} after the first {skip} in {csv_path}")
+    keys = [k for k in per[ids[0]] if k != "_kernel"]
+    return {k: sum(per[i][k] for i in ids) / len(ids) for k in keys}, per[ids[0]]["_kernel"], len(ids)
+
+
+def derived_counters(c, agent):
+    """Figures from SQ/TCC readings of one dispatch.  SQ_BUSY_CYCLES is
+    summed over the shader engines (Cu_Count / Cu_Per_Engine of them), so the
+    kernel's busy cycles are T = SQ_BUSY_CYCLES / engines (GRBM_GUI_ACTIVE /
+    Num_Xcc also counts the dispatch's set-up, long next to a short kernel);
+    SQ_WAVE_CYCLES, SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_ANY count in units
+    of four cycles (a wave64 VALU instruction occupies its SIMD for four),
+    summed over the CUs:
+      waves per CU  4 SQ_WAVE_CYCLES / (Cu_Count T)   (occupancy; max Max_Waves_Per_Cu)
+      VALU busy     4 SQ_ACTIVE_INST_VALU / (Simd_Count T)
+      wait to issue SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of wave time waiting for an instruction to issue)
+      L2 hit rate   TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)"""
+    out = {}
+    if c.get("SQ_BUSY_CYCLES"):
+        T = c["SQ_BUSY_CYCLES"] / agent["Shader_Engines"]
+    else:
+        T = c.get("GRBM_GUI_ACTIVE", 0) / agent["Num_Xcc"]
+    if T and "SQ_WAVE_CYCLES" in c:
+        out["waves_per_cu"] = 4 * c["SQ_WAVE_CYCLES"] / (agent["Cu_Count"] * T)
+    if T and "SQ_ACTIVE_INST_VALU" in c:
+        out["valu_busy"] = 4 * c["SQ_ACTIVE_INST_VALU"] / (agent["Simd_Count"] * T)
+    if c.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in c:
+        out["waiting"] = c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
+    if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c and c["TCC_HIT_sum"] + c["TCC_MISS_sum"] > 0:
+        out["l2_hit"] = c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+    if c.get("SQ_WAVES") and "SQ_INSTS_VALU" in c:
+        out["valu_per_wave"] = c["SQ_INSTS_VALU"] / c["SQ_WAVES"]
+    if c.get("SQ_WAVES") and "SQ_INSTS_LDS" in c:
+        out["lds_per_wave"] = c["SQ_INSTS_LDS"] / c["SQ_WAVES"]
+    out["busy_us_at_2.4GHz"] = T / 2.4e3
+    return out
+
+
+def _fmt_derived(d, agent):
+    parts = []
+    if "waves_per_cu" in d:
+        parts.append(f"waves per CU {d['waves_per_cu']:.1f} of {agent['Max_Waves_Per_Cu']}")
+    if "valu_busy" in d:
+        parts.append(f"VALU busy {100 * d['valu_busy']:.1f}%")
+    if "waiting" in d:
+        parts.append(f"wait to issue {100 * d['waiting']:.1f}%")
+    if "l2_hit" in d:
+        parts.append(f"L2 hit rate {100 * d['l2_hit']:.1f}%")
+    if "valu_per_wave" in d:
+        parts.append(f"VALU per wave {d['valu_per_wave']:.0f}")
+    if "lds_per_wave" in d:
+        parts.append(f"LDS instr per wave {d['lds_per_wave']:.1f}")
+    parts.append(f"busy {d['busy_us_at_2.4GHz']:.2f} us at 2.4 GHz")
+    return "; ".join(parts)
+
+
+def write_counter_table(workload, out, passes, skip=4):
+    """One workload's counter passes (rocprofv3 --pmc of a short bench.py
+    run, each GEMV launch a dispatch of its own), averaged over the warm GEMV
+    dispatches, with derived figures (derived_counters), and the same figures
+    for the run's pure-read probe as a reference.
+
+    passes: [(run directory holding *counter_collection.csv and
+    *agent_info.csv, command), ...]."""
+    import glob
+
+    lines = [f"# rocprofv3 counters of the {workload} GEMV (mean over warm launches) and the same run's probe",
+             f"kernel_source_hash: {kernel_source_hash()}"]
+    gemv, probe, kname, n, agent = {}, {}, None, 0, None
+    for d, cmd in passes:
+        csv_path = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        agent = _agent(glob.glob(os.path.join(d, "*agent_info.csv"))[0])
+        vals, kname, n = _mean_dispatches(csv_path, "gemv_stream", skip) if "gemv_stream" in open(csv_path).read() \
+            else _mean_dispatches(csv_path, "gemv_", skip)
+        pvals, _, _ = _mean_dispatches(csv_path, "probe_read_kernel", 0, largest=True)
+        gemv.update(vals)
+        probe.update(pvals)
+        lines.append(f"command: {cmd}")
+    lines.append(f"agent: {agent}")
+    lines.append(f"kernel: {kname}  (mean of {n} warm dispatches)")
+    lines.append("readings: " + "  ".join(f"{k}={v:.0f}" for k, v in sorted(gemv.items())))
+    lines.append("derived: " + _fmt_derived(derived_counters(gemv, agent), agent))
+    lines.append("probe readings: " + "  ".join(f"{k}={v:.0f}" for k, v in sorted(probe.items())))
+    lines.append("probe derived: " + _fmt_derived(derived_counters(probe, agent), agent))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def read_traffic(path):
     """(bytes_per_launch, kernel_source_hash) from a traffic summary, or None."""
     try:
@@ -180,5 +309,9 @@ if __name__ == "__main__":
         write_counter_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         print(write_traffic_summary(*sys.argv[2:8]))
+    elif sys.argv[1] == "table":
+        # table <workload> <out.txt> <run dir 1> <cmd 1> [<run dir 2> <cmd 2> ...]
+        a = sys.argv[4:]
+        write_counter_table(sys.argv[2], sys.argv[3], list(zip(a[0::2], a[1::2])))
     else:
         raise SystemExit(__doc__)
