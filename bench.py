@@ -56,6 +56,10 @@ def parse():
                          "instead of the GEMV bench line")
     ap.add_argument("--plot-roofline", metavar="BENCH_JSON",
                     help="print an ASCII roofline chart from a saved bench line and exit (no GPU needed)")
+    ap.add_argument("--plan-sweep", type=int, default=0, metavar="COUNT",
+                    help="time the library's plan on COUNT seeded random shapes per format against the "
+                         "same-size pure-read probe, instead of the bench line")
+    ap.add_argument("--seed", type=int, default=0, help="seed of --plan-sweep's shapes")
     ap.add_argument("--profile", action="store_true",
                     help="launch each kernel exactly once after a cold flush (for counter collection)")
     return ap.parse_args()
@@ -384,6 +388,87 @@ def detail(rounds, launches=256):
     return out
 
 
+# ---------------------------------------------------------------- plan sweep
+SWEEP_KINDS = ("f32", "f16", "f16x32", "q8", "q4")
+SWEEP_MAX_WEIGHT_BYTES = 512 << 20
+
+
+def sweep_shapes(count, seed):
+    """`count` seeded shapes per format: M log-uniform on [256, 65536], N
+    log-uniform on [256, 32768] rounded to a multiple of 128 (INT4's group),
+    weights at most 512 MiB (redrawn otherwise)."""
+    import numpy as np
+
+    from memory_bound_gemv_row_amd import accounting
+
+    rng = np.random.default_rng(seed)
+    out = []
+    for kind in SWEEP_KINDS:
+        got = 0
+        while got < count:
+            M = int(round(2 ** rng.uniform(8, 16)))
+            N = max(128, int(round(2 ** rng.uniform(8, 15) / 128)) * 128)
+            if accounting.weight_bytes(kind, M, N) > SWEEP_MAX_WEIGHT_BYTES:
+                continue
+            out.append((kind, M, N))
+            got += 1
+    return out
+
+
+def zero_operands(kind, M, N):
+    """Operands of the right dtypes and shapes, all zero: the timing of the
+    streaming kernels does not depend on the values."""
+    import numpy as np
+
+    a = {"f32": (np.float32, N), "f16": (np.float16, N), "f16x32": (np.float16, N), "f16_acc16": (np.float16, N),
+         "q8": (np.int8, N), "q4": (np.uint8, N // 2)}[kind]
+    ops = {"A": np.zeros((M, a[1]), a[0]),
+           "x": np.zeros(N, np.float32 if kind in ("f32", "f16x32") else np.float16)}
+    if kind == "q8":
+        ops["scale"] = np.zeros(M, np.float16)
+    elif kind == "q4":
+        ops["scale"] = np.zeros((M, N // 128), np.float16)
+    return ops
+
+
+def plan_sweep(count, seed, rounds=3, launches=64):
+    """The library's own plan on seeded random shapes (sweep_shapes), each
+    against the pure-read probe over the same weight bytes launched the same
+    way (graph of `launches` launches over a >= 1 GiB ring, best of `rounds`):
+    how far each shape's plan sits from the floor of a launch that reads the
+    same bytes.  Prints one JSON line per shape and a per-format summary."""
+    import torch
+
+    from memory_bound_gemv_row_amd import binding
+
+    rows = []
+    for kind, M, N in sweep_shapes(count, seed):
+        ring = Ring(kind, M, N, zero_operands(kind, M, N))
+        g = graph_of(ring, launches)
+        pg, _ = probe_slice_graph(ring, launches)
+        g.replay()
+        pg.replay()
+        torch.cuda.synchronize()
+        tg = min(time_graph(g, launches) for _ in range(rounds))
+        tp = min(time_graph(pg, launches) for _ in range(rounds))
+        info = binding.describe_launch(kind, M, N, True)
+        row = {"kind": kind, "M": M, "N": N, "us": round(tg * 1e6, 3), "same_size_probe_us": round(tp * 1e6, 3),
+               "pct_of_same_size_probe": round(100 * tp / tg, 1), "plan": info}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        ring.free()
+        del g, pg
+        torch.cuda.empty_cache()
+    summary = {}
+    for kind in SWEEP_KINDS:
+        r = sorted((x for x in rows if x["kind"] == kind), key=lambda x: x["pct_of_same_size_probe"])
+        if r:
+            summary[kind] = {"shapes": len(r), "worst_pct": r[0]["pct_of_same_size_probe"],
+                             "median_pct": r[len(r) // 2]["pct_of_same_size_probe"],
+                             "worst_shape": f"{r[0]['M']}x{r[0]['N']}"}
+    print(json.dumps({"plan_sweep": summary, "seed": seed, "count": count}), flush=True)
+
+
 # ---------------------------------------------------------------- quantiser
 def quant_detail(rounds, launches=64, shapes=None):
     """The weight quantiser (FP32 -> INT8 / INT4 + per-row squared error) on
@@ -691,6 +776,8 @@ def main():
     binding.load()
     if args.op:
         return op_main(args)
+    if args.plan_sweep:
+        return plan_sweep(args.plan_sweep, args.seed)
     kind, M, N = args.kind, args.M, args.N
     ops = inputs.make(kind, M, N, seed=0)
     ring = Ring(kind, M, N, ops)

@@ -151,11 +151,13 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
  * kernel with x read from global memory, 3 = element-wise kernel, 4 = packed
  * kernel for INT8/INT4 rows of at most 32 16-byte chunks, several rows per
  * wave load, 5 = kernel for rows of one to three wave loads with each
- * lane's x in registers), grid and workgroup sizes, rows per wave (at most),
+ * lane's x in registers, 6 = split rows: few long rows, a workgroup of 2 to
+ * 16 waves per row whose wave sums meet in LDS), grid and workgroup sizes,
+ * rows per wave (at most),
  * 1-KiB loads in flight per wave, dynamic LDS bytes (x staged up to what
  * one workgroup may hold on the device), and the order in which x is staged
  * relative to the first loads of A.  The geometry is chosen per shape:
- * workgroups of 4, 8 or 12 waves, 1 to 8 loads in flight, 1 to 4 rows (packed:
+ * workgroups of 2 to 16 waves, 1 to 8 loads in flight, 1 to 4 rows (packed:
  * row groups) per wave, more where a grid cap makes waves walk further --
  * every launch keeps grid x block at or below 2^30 work-items (the llama.cpp
  * walkthrough's implementation note: the original kernel selects its block

@@ -53,7 +53,8 @@ int packed_rows_per_load(int nchunks) { return 64 / packed_lanes<kQ8>(nchunks); 
 
 struct Plan {
     int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise,
-                   // 4 packed short rows (INT8/INT4), 5 x in registers
+                   // 4 packed short rows (INT8/INT4), 5 x in registers,
+                   // 6 split rows (several waves per row)
     int grid;
     int block;
     int waves;     // per workgroup
@@ -62,8 +63,48 @@ struct Plan {
     int lds;
     int stg;       // order of A prologue and x staging (default_stage_order)
     int cap;       // at most cap workgroups per CU (0: no cap)
-    int xk;        // variant 5: units per row (K)
+    int xk;        // variant 5: units per row (K); variant 6: waves per row (S)
 };
+
+// Split rows (variant 6), chosen after the one-wave-per-row plan p0: where
+// p0 leaves the CUs short of waves (fewer than 4 per CU for FP32/FP16, 3
+// for INT8, 2 for INT4) and the rows are at least 4 units long (INT4: at
+// most 16, whose x, read with each unit, is four times the bytes of its
+// A), S waves share each row, S the least power of two that gives every CU
+// kSplitWavesPerCu waves (at most 16, and at least two units per wave);
+// each wave streams ceil(P / S) units, 2 or 4 in flight.
+// Graph-timed A/B against p0: FP16 64x65536 25.07 -> 6.16 us, INT8
+// 16x131072 37.79 -> 8.23, FP32 408x14592 13.29 -> 6.68, FP16 278x16896
+// 8.34 -> 5.42, FP16 1024x14336 7.89 -> 6.79, INT8 560x6656 4.02 -> 3.00,
+// INT4 363x8704 4.08 -> 3.32; where p0 already fills the CUs it won (FP16
+// 1792x4096 4.10 vs 4.13, FP32 1024x1024 2.52 vs 2.62, INT8 1143x16896
+// 6.83 vs 7.09), and INT4 rows of 18 units lost to it by 60 %.
+constexpr int kSplitWavesPerCu = 16;
+
+bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
+{
+    if (kind == kF16H || P < 4 || p0.variant == 3)
+        return false;
+    const int per_cu = kind == kQ8 ? 3 : (kind == kQ4 ? 2 : 4);
+    if ((int64_t)p0.grid * p0.waves >= (int64_t)per_cu * cus || (kind == kQ4 && P > 16))
+        return false;
+    const int64_t target = (int64_t)kSplitWavesPerCu * cus;
+    int S = 2;   // P >= 4: two units per wave at least
+    while (S < 16 && 4 * S <= P && (int64_t)M * S < target)
+        S *= 2;
+    const int per_wave = (P + S - 1) / S;
+    *p = Plan{};
+    p->variant = 6;
+    p->xk = S;
+    p->waves = S;
+    p->block = S * 64;
+    p->D = per_wave == 2 ? 2 : 4;   // at least two units per wave
+    p->rows = 1;
+    p->stg = -1;
+    p->lds = 0;
+    p->grid = M;
+    return true;
+}
 
 // Units in flight (4 or 8) and rows per wave (1 or 2) for rows of P units
 // (4 <= P < 24) read with x per unit, one row per wave otherwise: a wave
@@ -181,7 +222,7 @@ bool two_rows_fill(int64_t M, int waves, int cus)
 // CU a workgroup.  With a cap the grid stays below the row count and waves
 // walk several rows; otherwise every launch gives each CU work once
 // M >= CUs.
-Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
+Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
 {
     Plan p{};
     const int cus = dev.cus;
@@ -456,11 +497,41 @@ Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
     return p;
 }
 
+// The plan of a call: the one-wave-per-row plan (rows_plan), or split rows
+// where that leaves the CUs short of waves.
+Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
+{
+    const Plan p0 = rows_plan(kind, M, N, aligned, dev);
+    if (p0.variant == 3)
+        return p0;
+    const int nchunks = N / elems_per_chunk(kind);
+    Plan p{};
+    return split_plan(kind, M, (nchunks + 63) / 64, dev.cus, p0, &p) ? p : p0;
+}
+
 template <int F>
 const void* select_packed(const Plan& p)
 {
     return p.D == 1 ? reinterpret_cast<const void*>(&gemv_packed<F, 8, 1>)
                     : reinterpret_cast<const void*>(&gemv_packed<F, 8, 2>);
+}
+
+template <int F, int S>
+const void* select_split_d(const Plan& p)
+{
+    return p.D == 2 ? reinterpret_cast<const void*>(&gemv_split<F, S, 2>)
+                    : reinterpret_cast<const void*>(&gemv_split<F, S, 4>);
+}
+
+template <int F>
+const void* select_split(const Plan& p)
+{
+    switch (p.xk) {
+    case 2: return select_split_d<F, 2>(p);
+    case 4: return select_split_d<F, 4>(p);
+    case 8: return select_split_d<F, 8>(p);
+    default: return select_split_d<F, 16>(p);
+    }
 }
 
 template <int F>
@@ -526,6 +597,10 @@ const void* select_kernel(const Plan& p)
         return reinterpret_cast<const void*>(&gemv_elementwise<F>);
     if (p.variant == 5)
         return select_xreg<F>(p);
+    if constexpr (F != kF16H) {
+        if (p.variant == 6)
+            return select_split<F>(p);
+    }
     if constexpr (F == kQ8 || F == kQ4) {
         if (p.variant == 4)
             return select_packed<F>(p);

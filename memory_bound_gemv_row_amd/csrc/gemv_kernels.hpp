@@ -839,6 +839,127 @@ gemv_packed(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
         consume(d);
 }
 
+// ---------------------------------------------------------------- split rows (few, long rows)
+// When the rows are too few for one wave per row to fill the chip, a
+// workgroup of S waves takes one row: wave w streams the row's units w,
+// w + S, w + 2S, ... (one 16-byte chunk per lane and unit, as in
+// gemv_stream), D in flight; each wave reduces its 64 lane sums, the S wave
+// sums meet in LDS, and the first thread adds them in wave order and stores
+// y.  x is read with each unit through the caches (as gemv_stream's XG
+// form): the S waves of a row read disjoint parts of it.  The cross-wave step
+// is the LDS reduction of a row that spans waves ("membound", the llama.cpp
+// walkthrough's block-per-row kernel, and "cuda-gemv-optimization", the
+// shared-memory kernel: partial sums of one row meet in shared memory).
+//
+// Preconditions (checked by the host): N is a multiple of Traits<F>::kElems,
+// A and x are 16-byte aligned, 1 <= S <= units per row, the grid has one
+// workgroup per row (M <= 2^30 / (S * 64)).
+template <int F, int S, int D>
+__global__ void __launch_bounds__(S * 64)
+gemv_split(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
+           const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
+{
+    static_assert(F != kF16H, "FP16 accumulation keeps one wave per row");
+    using T = Traits<F>;
+    constexpr int G = T::kXGran;
+    constexpr bool kGlobal = F == kF32 || F == kF16;   // as gemv_stream: plain global loads
+    __shared__ float part[S];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = blockIdx.x;
+    if (row >= M)   // the whole workgroup: the grid has one workgroup per row
+        return;
+    const int nchunks = N / T::kElems;
+    const int P = (nchunks + 63) >> 6;
+    const int units = (P - w + S - 1) / S;      // passes w, w + S, ... < P (at least 1)
+    const int units_pad = (units + D - 1) / D * D;
+    const uint32_t row_bytes = (uint32_t)nchunks * 16;
+    const int groups = N / 128;                 // INT4 scales per row
+    const u32x4* xg = reinterpret_cast<const u32x4*>(x);
+    const uint8_t* arow = A + (int64_t)row * row_bytes;
+    const auto arsrc = make_rsrc(arow, row_bytes);
+    const auto xrsrc = make_rsrc(x, (uint32_t)nchunks * G * 16);
+    const auto srsrc = make_rsrc(scale + (int64_t)row * groups, (uint32_t)groups * 2);
+    constexpr int kAux = 2;                     // A: non-temporal
+
+    u32x4 buf[D];
+    u32x4 xbuf[D][G];
+    uint16_t sbuf[D];
+    // unit j (padded units re-read the wave's last unit and are not added)
+    auto issue = [&](int d, int j) {
+        const int pass = w + S * (j < units ? j : units - 1);
+        if constexpr (kGlobal) {
+            const int c = pass * 64 + lane;
+            const int cc = c < nchunks ? c : 0;
+            buf[d] = load16<true>(reinterpret_cast<const u32x4*>(arow) + cc);
+            xbuf[d][0] = xg[cc];
+        } else {
+            const int voff = lane * 16 + pass * 1024;
+            buf[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, voff, 0, kAux));
+#pragma unroll
+            for (int k = 0; k < G; ++k)
+                xbuf[d][k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, voff * G + k * 16, 0, 0));
+        }
+        if constexpr (F == kQ4)
+            sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (lane >> 2) * 2 + pass * 32, 0, 0);
+        else
+            sbuf[d] = 0;
+    };
+    float acc = 0.0f;
+    auto consume = [&](int d, int j) {
+        const int pass = w + S * (j < units ? j : units - 1);
+        const int cc = pass * 64 + lane;
+        const u32x4 a = buf[d];
+        u32x4 xv[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            xv[k] = (F == kQ4) ? q4_pair_x(xbuf[d][k]) : xbuf[d][k];
+        float t = acc;
+        if constexpr (F == kF32) {
+            t = chunk_f32(a, xv[0], t);
+        } else if constexpr (F == kF16) {
+            t = chunk_f16(a, xv[0], t);
+        } else if constexpr (F == kF16X32) {
+            t = chunk_f16x32(a, xv[0], xv[G - 1], t);
+        } else if constexpr (F == kQ8) {
+            t = q8_chunk(a, xv[0], xv[G - 1], t);
+        } else {
+            const u32x4 xp[4] = {xv[0], xv[1 % G], xv[2 % G], xv[3 % G]};
+            t = chunk_q4(a, xp, half_bits_to_float(sbuf[d]), t);
+        }
+        // a padded unit, or (global loads) a lane past the row end, adds nothing
+        const bool live = j < units && (!kGlobal || cc < nchunks);
+        acc = live ? t : acc;
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        issue(d, d);
+    for (int j0 = D; j0 < units_pad; j0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            consume(d, j0 - D + d);
+            issue(d, j0 + d);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        consume(d, units_pad - D + d);
+
+    const float t = wave_sum(acc);
+    if (lane == 0)
+        part[w] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float sum = part[0];
+#pragma unroll
+        for (int k = 1; k < S; ++k)
+            sum += part[k];
+        if constexpr (F == kQ8)
+            sum *= half_bits_to_float(scale[row]);
+        y[row] = sum;
+    }
+}
+
 // ---------------------------------------------------------------- element-wise kernel
 // Any N >= 0 and any alignment: one wave per row, lane l takes columns
 // l, l+64, ... with scalar loads (INT4: bytes l, l+64, ..., two columns

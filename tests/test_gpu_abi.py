@@ -182,9 +182,12 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 1
     assert binding.describe_launch("f16x32", 14336, 4096)["variant"] == 1
     assert binding.describe_launch("f16x32", 4096, 4096)["variant"] == 2
-    info = binding.describe_launch("f16x32", 64, 32768)
+    info = binding.describe_launch("f16x32", 4 * cus, 32768)
     assert info["variant"] == 1 and info["lds_bytes"] == 4 * 32768 <= lds_max, info
-    assert binding.describe_launch("f16x32", 64, lds_max // 4 + 512)["variant"] == 2
+    assert binding.describe_launch("f16x32", 16 * cus, lds_max // 4 + 512)["variant"] == 2
+    # few long rows: several waves per row (split rows), x read with each unit
+    info = binding.describe_launch("f16x32", 64, 32768)
+    assert info["variant"] == 6 and info["lds_bytes"] == 0 and info["grid"] == 64, info
     # few long INT8 rows stage x (one workgroup per CU); few INT4 rows of
     # four units or more read x with each unit
     assert binding.describe_launch("q8", 4 * cus, 8192)["stage_order"] == 1

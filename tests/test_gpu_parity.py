@@ -115,18 +115,18 @@ _LONG_ROWS = [
     ("q8", 1024, 32848, 1, 1),    # 66 KiB of staged x, few rows: one workgroup per CU
     ("q8", 3000, 32848, 1, 2),    # two workgroups per CU, waves walk two rows
     ("q8", 3000, 49168, 1, 1),    # 98 KiB: one workgroup per CU, waves walk two rows
-    ("q8", 1500, 49168, 2, -1),   # one workgroup per CU and few rows: x per unit
-    ("q8", 300, 81936, 2, -1),    # staged x would not fit a workgroup
+    ("q8", 2000, 49168, 2, -1),   # one workgroup per CU and few rows: x per unit
+    ("q8", 2200, 81936, 2, -1),   # staged x would not fit a workgroup
     ("q4", 3000, 34944, 1, 1),    # 72 KiB: one workgroup per CU
     ("q4", 1000, 34944, 2, -1),   # few rows: x per unit
     ("q4", 300, 82048, 2, -1),    # staged x would not fit a workgroup
     ("q8", 1000, 16400, 1, 1),    # rows of 17 units, few of them: staged, one workgroup per CU
     ("q4", 1000, 8320, 2, -1),    # few INT4 rows of 5 units: x per unit
-    ("f16x32", 700, 24584, 1, 1),  # 96 KiB of FP32 x: staged, one workgroup per CU
-    ("f16x32", 300, 40968, 2, -1),  # FP32 x would not fit a workgroup
+    ("f16x32", 1100, 24584, 1, 1),  # 96 KiB of FP32 x: staged, one workgroup per CU
+    ("f16x32", 2100, 40968, 2, -1),  # FP32 x would not fit a workgroup
     ("q4", 3000, 81920, 1, 1),    # staged x of exactly 160 KiB
     ("q8", 3000, 80848, 1, 1),    # 158 KiB, ragged last pass
-    ("f16x32", 700, 40960, 1, 1),  # 160 KiB of FP32 x
+    ("f16x32", 1100, 40960, 1, 1),  # 160 KiB of FP32 x
 ]
 
 

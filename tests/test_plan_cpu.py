@@ -37,8 +37,9 @@ def test_every_plan_is_consistent(kind, dev):
             continue
         p = plan(kind, M, N, **dev)
         where = (kind, M, N, dev, p)
-        assert p["variant"] in (1, 2, 3, 4, 5), where
-        assert 1 <= p["grid"] and p["block"] in (256, 512, 768), where
+        assert p["variant"] in (1, 2, 3, 4, 5, 6), where
+        assert 1 <= p["grid"] and p["block"] in (128, 256, 512, 768, 1024), where
+        assert p["block"] in (256, 512, 768) or p["variant"] == 6, where
         assert p["grid"] * p["block"] <= 1 << 30, where            # 32-bit work-item count
         aligned_path = N > 0 and N % ELEMS_PER_CHUNK[kind] == 0
         if not aligned_path:
@@ -60,6 +61,16 @@ def test_every_plan_is_consistent(kind, dev):
             assert p["grid"] >= dev["cus"], where                 # every CU gets a workgroup
         if p["variant"] == 5:
             assert 1 <= -(-(N // ELEMS_PER_CHUNK[kind]) // 64) <= 3, where   # rows of one to three units
+        if p["variant"] == 6:
+            # split rows: one workgroup of S waves per row, S a power of two
+            # from 2 to 16 and at most one wave per unit of the row, only
+            # where one wave per row leaves the CUs short of waves
+            S = p["block"] // 64
+            P = -(-(N // ELEMS_PER_CHUNK[kind]) // 64)
+            assert kind != "f16_acc16" and aligned_path, where
+            assert S in (2, 4, 8, 16) and S <= P and p["grid"] == M and p["rows_per_wave"] == 1, where
+            assert 2 * M <= 16 * dev["cus"], where
+            assert p["units_in_flight"] == (2 if -(-P // S) == 2 else 4), where
         assert 1 <= p["units_in_flight"] <= 8, where
 
 
@@ -134,7 +145,8 @@ def test_long_rows_stage_x_up_to_the_device_limit():
     # one unit past what a workgroup may hold
     assert plan("q8", 4096, 81920)["variant"] == 1 and plan("q8", 4096, 81920 + 1024)["variant"] == 2
     assert plan("q4", 4096, 83968)["variant"] == 2
-    assert plan("f16x32", 64, 40960 + 512)["variant"] == 2
+    assert plan("f16x32", 4096, 40960 + 512)["variant"] == 2
+    assert plan("f16x32", 64, 40960 + 512)["variant"] == 6     # few rows: split, x read with each unit
 
 
 def test_few_rows_rules():
