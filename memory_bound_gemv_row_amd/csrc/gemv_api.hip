@@ -67,25 +67,32 @@ struct Plan {
 };
 
 // Split rows (variant 6), chosen after the one-wave-per-row plan p0: where
-// p0 leaves the CUs short of waves (fewer than 4 per CU for FP32/FP16, 3
-// for INT8, 2 for INT4) and the rows are at least 4 units long (INT4: at
-// most 16, whose x, read with each unit, is four times the bytes of its
-// A), S waves share each row, S the least power of two that gives every CU
+// p0 leaves the CUs short of waves (fewer than 4 per CU for FP32/FP16 and
+// FP16 with FP32 x, 8 for FP32/FP16 rows of 16 units and more, 3 for INT8,
+// 2 for INT4) and the rows are at least 4 units long (INT4: at most 16,
+// whose x, read with each unit, is four times the bytes of its A), S waves
+// share each row, S the least power of two that gives every CU
 // kSplitWavesPerCu waves (at most 16, and at least two units per wave);
 // each wave streams ceil(P / S) units, 2 or 4 in flight.
 // Graph-timed A/B against p0: FP16 64x65536 25.07 -> 6.16 us, INT8
-// 16x131072 37.79 -> 8.23, FP32 408x14592 13.29 -> 6.68, FP16 278x16896
-// 8.34 -> 5.42, FP16 1024x14336 7.89 -> 6.79, INT8 560x6656 4.02 -> 3.00,
-// INT4 363x8704 4.08 -> 3.32; where p0 already fills the CUs it won (FP16
-// 1792x4096 4.10 vs 4.13, FP32 1024x1024 2.52 vs 2.62, INT8 1143x16896
-// 6.83 vs 7.09), and INT4 rows of 18 units lost to it by 60 %.
+// 16x131072 37.79 -> 8.23, FP32 408x14592 13.29 -> 6.68, FP32 2246x19200
+// 43.04 -> 29.95, FP16 278x16896 8.34 -> 5.42, FP16 1024x14336
+// 7.89 -> 6.79, INT8 560x6656 4.02 -> 3.00, INT4 363x8704 4.08 -> 3.32;
+// where p0 already fills the CUs it won (FP16 1792x4096 4.09 vs 4.19,
+// FP32 1024x1024 2.52 vs 2.66, FP16 1024x4096 3.09 vs 3.29, FP16 with FP32
+// x 1500x8192 6.63 vs 7.10, INT8 1500x10240 5.57 vs 6.18), and INT4 rows
+// of 18 units lost to it by 60 %.
 constexpr int kSplitWavesPerCu = 16;
 
 bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
 {
     if (kind == kF16H || P < 4 || p0.variant == 3)
         return false;
-    const int per_cu = kind == kQ8 ? 3 : (kind == kQ4 ? 2 : 4);
+    // FP32/FP16 rows of 16 units and more up to 8 waves per CU (x is one
+    // granule per unit); otherwise 4, INT8 3, INT4 2 (x per unit is two or
+    // four granules), FP16 with FP32 x 4
+    const bool fp = kind == kF32 || kind == kF16;
+    const int per_cu = fp && P >= 16 ? 8 : (kind == kQ8 ? 3 : (kind == kQ4 ? 2 : 4));
     if ((int64_t)p0.grid * p0.waves >= (int64_t)per_cu * cus || (kind == kQ4 && P > 16))
         return false;
     const int64_t target = (int64_t)kSplitWavesPerCu * cus;

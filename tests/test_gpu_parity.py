@@ -144,12 +144,13 @@ def test_long_rows_staged_or_per_unit(gpu, oracle_mod, kind, M, N, variant, stg)
 
 
 @pytest.mark.parametrize("kind,M,N,D,rows", [("f16", 8192, 14336 + 8, 8, 2), ("f32", 6144 + 3, 12288, 8, 1),
-                                             ("f16", 3000, 12288 + 8, 8, 2), ("f16", 4096 + 1, 14336, 4, 2),
+                                             ("f16_acc16", 3000, 12288 + 8, 8, 2), ("f16", 4096 + 1, 14336, 4, 2),
                                              ("f16_acc16", 6400, 16384, 8, 1), ("f16", 4096 + 7, 16384, 8, 1)])
 def test_long_fp_rows(gpu, oracle_mod, kind, M, N, D, rows):
     # FP32/FP16 rows of 24 units and more: 8 in flight and one row per wave
     # from 24 rows per CU or for multiples of 16 units (two where the units
-    # are not a multiple of 8), two rows per wave up to 12 per CU, 4 in
+    # are not a multiple of 8), two rows per wave up to 12 per CU (there
+    # FP32/FP16 split rows instead, FP16 accumulation keeps it), 4 in
     # flight between; ragged last passes
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     info = binding.describe_launch(kind, M, N)
