@@ -33,16 +33,19 @@ int elems_per_chunk(int kind)
     }
 }
 
-int lds_bytes(int kind, int nchunks)
+// Bytes of x one workgroup stages (whole passes, zero past the row end),
+// in 64 bits: rows near 2^30 elements would overflow an int.  FP32/FP16 (either
+// accumulation) read x with each unit and stage nothing.
+int64_t lds_bytes(int kind, int nchunks)
 {
+    int64_t granules = 0;   // 16-byte granules of x per chunk
     switch (kind) {
-    case kF32: return 4 * stream_lds_words<kF32, true>(nchunks);
-    case kF16: return 4 * stream_lds_words<kF16, true>(nchunks);
-    case kQ8: return 4 * stream_lds_words<kQ8, false>(nchunks);
-    case kF16X32: return 4 * stream_lds_words<kF16X32, false>(nchunks);
-    case kF16H: return 4 * stream_lds_words<kF16H, true>(nchunks);
-    default: return 4 * stream_lds_words<kQ4, false>(nchunks);
+    case kQ8: granules = Traits<kQ8>::kXGran; break;
+    case kQ4: granules = Traits<kQ4>::kXGran; break;
+    case kF16X32: granules = Traits<kF16X32>::kXGran; break;
+    default: break;
     }
+    return ((int64_t)nchunks + 63) / 64 * 64 * granules * 16;
 }
 
 // Packed short rows: INT8/INT4 rows of at most this many chunks share wave
@@ -340,7 +343,8 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.rows = (4 + P - 1) / P;
         }
     } else if (kind == kF16X32) {
-        const bool fits = lds_bytes(kind, nchunks) <= kLdsBytes;
+        const int64_t lds = lds_bytes(kind, nchunks);
+        const bool fits = lds <= kLdsBytes && lds <= dev.lds_max;
         p.rows = 1;
         if (fits && P >= 24) {
             // two rows per wave where that pads less (8192 x 12800
@@ -365,7 +369,7 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.waves = 4;
             p.D = 8;
             p.cap = 4;
-        } else if (lds_bytes(kind, nchunks) <= dev.lds_max && P > 32) {
+        } else if (lds <= dev.lds_max && P > 32) {
             // staged x past 64 KiB: 8 waves, 4 in flight, x staged before
             // A, one workgroup per CU
             p.variant = 1;
@@ -387,7 +391,7 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.variant = 1;
         p.D = 4;
         p.rows = 1;
-        const int lds = lds_bytes(kind, nchunks);
+        const int64_t lds = lds_bytes(kind, nchunks);
         if (lds > dev.lds_max || (lds >= kLdsBytes && 2 * lds > dev.lds_max && M <= 8 * cus)) {
             // staged x would not fit a workgroup, or only one workgroup
             // per CU and few rows to spread its staging over: x read with
@@ -456,7 +460,7 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
                 p.cap = 2;
             }
         }
-    } else if (const int lds = lds_bytes(kind, nchunks); lds > dev.lds_max || M <= 4 * cus) {
+    } else if (const int64_t lds = lds_bytes(kind, nchunks); lds > dev.lds_max || M <= 4 * cus) {
         // INT4 rows whose staged x would not fit a workgroup, or at most 4
         // rows per CU (of 4 units or more: shorter ones took x in
         // registers): x read with each unit, 4 waves, 4 in flight
@@ -487,7 +491,8 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.stg = P < 4 ? 2 : 1;
         p.cap = P >= 14 ? 2 : 3;
     }
-    p.lds = p.variant == 1 ? lds_bytes(kind, nchunks) : 0;
+    // staged plans were chosen only where x fits the device's LDS
+    p.lds = p.variant == 1 ? (int)lds_bytes(kind, nchunks) : 0;
     if (p.variant == 1 && p.stg == 2) {
         // split staging writes past-the-end granules to spare slots
         if (p.lds + kSplitSpareBytes <= dev.lds_max)
