@@ -24,8 +24,8 @@
  * Conventions: device pointers, caller-owned buffers, asynchronous on
  * `stream`, status codes from gemv.h (gemv_status), nothing allocated.
  * An infinite weight gives its row (INT8) or group (INT4) the largest
- * binary16 scale, 65504, and clipped codes; NaN weights are outside the rule
- * and give unspecified codes (and a NaN row_sse).
+ * binary16 scale, 65504, and clipped codes; a NaN weight has no code under
+ * the rule and gets code 0 (its row's row_sse is NaN).
  * row_sse, if not NULL, receives per row sum_j (q_ij * scale - w_ij)^2 in
  * FP32; RMSE = sqrt(sum_i row_sse[i] / (M * N)).  Results are deterministic.
  * The bandwidth path needs a 16-byte-aligned W (and, for INT8, N % 4 == 0

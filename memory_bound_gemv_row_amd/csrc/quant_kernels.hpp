@@ -102,11 +102,13 @@ __device__ __forceinline__ float div_by_qmax(float amax)
 
 // binary16 scale of a row or group: amax / qmax (correctly rounded binary32
 // quotient), rounded to nearest even binary16 by v_cvt_f16_f32 (binary16
-// subnormals kept), infinity clamped to 65504.
+// subnormals kept), infinity clamped to 65504.  The maxima skip NaN weights;
+// a row or group of NaN weights only has maximum 0 (v_max_f32 with 0 gives
+// 0 for NaN), so its scale is 0.
 template <int QMAX>
 __device__ __forceinline__ uint16_t scale_bits(float amax)
 {
-    const float s = div_by_qmax<QMAX>(amax);
+    const float s = div_by_qmax<QMAX>(fmaxf(amax, 0.0f));
     uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)s);
     if (b == 0x7C00u)
         b = 0x7BFFu;
@@ -128,14 +130,19 @@ __device__ __forceinline__ float half_to_float(uint16_t b) { return (float)__bui
 // half-integer, every value that close rounds to the same integer as q
 // does, so the fast result is exact; the rare weights near a half-integer
 // take the correctly rounded division.  Values with |t| >= 128 clip to QMAX
-// either way.
+// either way.  A NaN quotient (a NaN weight: the maxima skip NaN, so the
+// scale is finite, possibly zero) fails the comparison below, so it too
+// takes the rare path, which gives it code 0, as the oracle does; so does a
+// zero scale there; an infinite weight takes it as well and clips.
 template <int QMAX>
 __device__ __forceinline__ float code_of(float w, float sf, float inv)
 {
     float t = w * inv;
     const float frac = t - __builtin_floorf(t);
-    if (__builtin_expect(__builtin_fabsf(frac - 0.5f) < 0x1p-13f, 0) && sf != 0.0f)
-        t = w / sf;
+    if (__builtin_expect(!(__builtin_fabsf(frac - 0.5f) >= 0x1p-13f), 0)) {
+        const float tq = sf != 0.0f ? w / sf : 0.0f;
+        t = tq == tq ? tq : 0.0f;
+    }
     const float r = __builtin_rintf(t);
     return fminf(fmaxf(r, -(float)QMAX), (float)QMAX);
 }

@@ -40,8 +40,10 @@ def _compare(oracle, kind, W, label):
     if not np.array_equal(q, oq):
         bad = np.argwhere(q != oq)[:5]
         raise AssertionError((label, "codes differ at", bad.tolist()))
-    # an infinite weight makes its row's squared error infinite on both sides
+    # an infinite weight makes its row's squared error infinite on both
+    # sides, a NaN weight NaN
     assert np.array_equal(np.isinf(e), np.isinf(oe)), (label, "infinite errors")
+    assert np.array_equal(np.isnan(e), np.isnan(oe)), (label, "NaN errors")
     fin = np.isfinite(oe)
     e_f, oe_f = e[fin], oe[fin]
     denom = np.maximum(oe_f, 1e-30)
@@ -122,7 +124,7 @@ def test_near_ties_match_the_correctly_rounded_division(gpu, oracle_mod, kind, N
 
 @pytest.mark.parametrize("kind,N", [("q8", 512), ("q4", 512), ("q4", 4096)])
 def test_degenerate_rows(gpu, oracle_mod, kind, N):
-    M = 8
+    M = 10
     W = np.zeros((M, N), np.float32)
     W[1] = 1.0e7                                   # scale saturates at 65504, codes clip
     W[2, :] = np.linspace(-1e-4, 1e-4, N)          # binary16-subnormal scales
@@ -132,6 +134,9 @@ def test_degenerate_rows(gpu, oracle_mod, kind, N):
     W[6] = np.float32(3e-39) * np.sign(W[4])       # binary32-subnormal maximum
     W[7] = W[4]
     W[7, 200] = np.inf                             # infinite maximum: scale 65504, codes clip
+    W[8] = W[4]
+    W[8, ::37] = np.nan                            # NaN weights: skipped by the maxima, code 0
+    W[9] = np.nan                                  # all NaN: zero scales, codes 0
     _compare(oracle_mod, kind, W, f"{kind} degenerate N={N}")
 
 
