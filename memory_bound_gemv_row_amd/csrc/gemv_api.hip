@@ -12,6 +12,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
+
 namespace gemv {
 namespace {
 
@@ -162,6 +165,19 @@ int rows_for_depth(int P, int D, bool two_rows_fill)
 bool two_rows_fill(int64_t M, int waves, int cus)
 {
     return (M + 2 * waves - 1) / (2 * waves) >= cus;
+}
+
+// Workgroup size and grid of a plan whose waves walk rows: enough waves for
+// M rows at p->rows per wave, at most p->cap workgroups per CU (none: 0),
+// and at most 2^30 work-items.
+void finish_rows(int M, int cus, Plan* p)
+{
+    p->block = p->waves * 64;
+    const int64_t waves_needed = ((int64_t)M + p->rows - 1) / p->rows;
+    int64_t grid = (waves_needed + p->waves - 1) / p->waves;
+    if (p->cap > 0 && grid > (int64_t)p->cap * cus)
+        grid = (int64_t)p->cap * cus;
+    p->grid = gemv_device::capped_grid(grid, p->block);
 }
 
 // Geometry for one call, chosen from sweeps on MI355X.  A row of nchunks
@@ -500,25 +516,188 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
         else
             p.stg = 1;
     }
-    p.block = p.waves * 64;
-    const int64_t waves_needed = ((int64_t)M + p.rows - 1) / p.rows;
-    int64_t grid = (waves_needed + p.waves - 1) / p.waves;
-    if (p.cap > 0 && grid > (int64_t)p.cap * cus)
-        grid = (int64_t)p.cap * cus;
-    p.grid = gemv_device::capped_grid(grid, p.block);
+    finish_rows(M, cus, &p);
     return p;
 }
 
-// The plan of a call: the one-wave-per-row plan (rows_plan), or split rows
-// where that leaves the CUs short of waves.
-Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
+// FP32/FP16 cost model: the predicted time of a plan from its geometry.  A
+// launch has a fixed cost (the same for every plan; it matters only to the
+// margin below, which is relative).  A wave streams
+// U units -- its rows' units padded to a multiple of D, the padding being
+// re-reads that cost real traffic -- D at a time, so it waits about U/D + 1
+// memory latencies; the busiest CU runs ceil(grid / CUs) workgroups, in
+// turn where they outnumber the workgroups it holds at once; the chip
+// streams every unit (padding included) at the HBM rate, a CU streams its
+// units at a per-CU rate and issues a fixed cost per unit on its 4 SIMDs.
+// The four times overlap only in part and combine as a root sum of squares;
+// split rows add their LDS reduction.  The constants were fitted (weighted
+// least squares on log time, near-best plans weighted most) to the
+// graph-timed times of every candidate plan below on 52 seeded random
+// FP32/FP16 shapes on MI355X; they read as a launch cost of 1.69 us, a
+// latency of 0.34 us per round,
+// 8.9 TB/s for the chip, 47 GB/s per CU and 18 / 26 ns of issue per unit
+// and wave for FP32 / FP16.  On 32 further random shapes the plan the model
+// picks (within the margin below) is 3.4 % slower than the fastest
+// candidate (geometric mean; 10.5 % at worst for FP16, 17 % for FP32),
+// the measured rules alone 6.3 % (34 % at worst).
+struct FpCostModel {
+    double launch;        // s, fixed cost of a launch
+    double latency;       // s per memory round trip under load
+    double chip_bw;       // B/s, all CUs
+    double cu_bw;         // B/s, one CU
+    double split_cost;    // s, LDS reduction of a split row
+    double issue[2];      // s per unit and wave: FP32, FP16
+};
+constexpr FpCostModel kFpModel{1.691e-6, 3.412e-7, 8.946e12, 4.670e10, 1.814e-8, {1.788e-8, 2.597e-8}};
+
+// The model replaces the measured rules' plan only where it predicts a gain
+// above its own error on the rules' home ground: on the shapes the rules
+// were tuned on it ranks plans within 3-5 % of each other wrongly about as
+// often as rightly.
+constexpr double kModelMargin = 1.05;
+
+// The fitted shapes' range (row counts and lengths drawn log-uniform from
+// these): outside it the measured rules alone decide.
+constexpr int kModelRows[2] = {256, 65536};
+constexpr int kModelCols[2] = {256, 32768};
+
+// Waves one SIMD holds: the FP32/FP16 streaming kernels with 8 units in
+// flight use 68-69 VGPRs (7 waves of 512 registers); every other FP32/FP16
+// kernel uses at most 39 (8 waves, the hardware's limit).
+int fp_waves_per_simd(const Plan& p) { return p.variant == 2 && p.D == 8 ? 7 : 8; }
+
+double fp_cost(int kind, int64_t M, int64_t P, int cus, const Plan& p)
+{
+    const FpCostModel& m = kFpModel;
+    const int64_t waves = (int64_t)p.grid * p.waves;
+    int64_t U = 0, units = 0;
+    if (p.variant == 6) {
+        U = ((P + p.xk - 1) / p.xk + p.D - 1) / p.D * p.D;
+        units = waves * U;
+    } else {
+        // waves 0 .. nmax-1 walk rmax rows, the others rmin
+        const int64_t PP = p.variant == 5 ? p.xk : P;
+        const int64_t rmax = (M + waves - 1) / waves, rmin = M / waves, nmax = M - rmin * waves;
+        U = (rmax * PP + p.D - 1) / p.D * p.D;
+        const int64_t Umin = (rmin * PP + p.D - 1) / p.D * p.D;
+        units = nmax * U + (waves - nmax) * Umin;
+    }
+    const int held = std::min(fp_waves_per_simd(p) / ((p.waves + 3) / 4), 32);   // workgroups per CU
+    const int64_t wgs = (p.grid + cus - 1) / cus;                                 // on the busiest CU
+    const double rounds = std::max((double)wgs / held, 1.0) * ((double)U / p.D + 1.0);
+    const double cu_units = (double)wgs * p.waves * U;
+    const double t_chip = (double)units * 1024.0 / m.chip_bw;
+    const double t_cu = cu_units * 1024.0 / m.cu_bw;
+    const double t_lat = rounds * m.latency;
+    const double t_issue = cu_units * m.issue[kind == kF16 ? 1 : 0] / 4.0;
+    return m.launch + (p.variant == 6 ? m.split_cost : 0.0) +
+           std::sqrt(t_chip * t_chip + t_cu * t_cu + t_lat * t_lat + t_issue * t_issue);
+}
+
+// FP32/FP16: the measured rules' plan p0, or the candidate the cost model
+// ranks fastest where it predicts more than kModelMargin of a gain.
+// Candidates: the streaming kernel with 4 or 8 waves, 2, 4 or 8 units in
+// flight and 1, 2 or 4 rows per wave; rows of 1-3 units with x in
+// registers; split rows of S = 2-16 waves (each at least two units) with 2
+// or 4 in flight.
+Plan fp_model_plan(int kind, int M, int P, const Device& dev, const Plan& p0)
+{
+    double best_t = fp_cost(kind, M, P, dev.cus, p0);
+    const double rules_t = best_t;
+    Plan best = p0;
+    auto consider = [&](const Plan& c) {
+        const double t = fp_cost(kind, M, P, dev.cus, c);
+        if (t < best_t) {
+            best_t = t;
+            best = c;
+        }
+    };
+    auto rows_candidate = [&](int variant, int waves, int D, int rows, int cap, int xk) {
+        Plan c{};
+        c.variant = variant;
+        c.waves = waves;
+        c.D = D;
+        c.rows = rows;
+        c.cap = cap;
+        c.xk = xk;
+        c.stg = -1;
+        finish_rows(M, dev.cus, &c);
+        consider(c);
+    };
+    if (P == 1) {
+        for (int waves : {4, 8})
+            for (int D : {1, 2})
+                for (int rows : {1, 2})
+                    for (int cap : {0, 3})
+                        rows_candidate(5, waves, D, rows, cap, 1);
+    } else if (P == 2) {
+        for (int cap : {0, 3, 6})
+            rows_candidate(5, 4, 2, 1, cap, 2);
+    } else if (P == 3) {
+        for (int waves : {4, 8})
+            for (int cap : {0, 3})
+                rows_candidate(5, waves, 3, 1, cap, 3);
+    }
+    for (int waves : {4, 8})
+        for (int D : {2, 4, 8})
+            for (int rows : {1, 2, 4})
+                rows_candidate(2, waves, D, rows, 0, 0);
+    for (int S : {2, 4, 8, 16}) {
+        // one workgroup per row, no walking: the grid must hold every row
+        if (2 * S > P || (int64_t)M * S * 64 > gemv_device::kMaxWorkItems)
+            continue;
+        for (int D : {2, 4}) {
+            Plan c{};
+            c.variant = 6;
+            c.xk = S;
+            c.waves = S;
+            c.block = S * 64;
+            c.D = D;
+            c.rows = 1;
+            c.stg = -1;
+            c.grid = M;
+            consider(c);
+        }
+    }
+    return rules_t > kModelMargin * best_t ? best : p0;
+}
+
+Plan plan_uncached(int kind, int M, int N, bool aligned, const Device& dev)
 {
     const Plan p0 = rows_plan(kind, M, N, aligned, dev);
     if (p0.variant == 3)
         return p0;
-    const int nchunks = N / elems_per_chunk(kind);
-    Plan p{};
-    return split_plan(kind, M, (nchunks + 63) / 64, dev.cus, p0, &p) ? p : p0;
+    const int P = (N / elems_per_chunk(kind) + 63) / 64;
+    Plan p = p0;
+    Plan s{};
+    if (split_plan(kind, M, P, dev.cus, p0, &s))
+        p = s;
+    // the model only within the shapes it was fitted on
+    const bool fitted = M >= kModelRows[0] && M <= kModelRows[1] && N >= kModelCols[0] && N <= kModelCols[1];
+    return (kind == kF32 || kind == kF16) && fitted ? fp_model_plan(kind, M, P, dev, p) : p;
+}
+
+// The plan of a call: the one-wave-per-row plan (rows_plan), or split rows
+// where that leaves the CUs short of waves; for FP32/FP16 then the cost
+// model's choice where it predicts a clear gain.  Each host thread keeps
+// its last 16 plans, so repeated calls of a shape skip the search.
+Plan make_plan(int kind, int M, int N, bool aligned, const Device& dev)
+{
+    struct Entry {
+        int kind, M, N, cus, lds_max;
+        bool aligned, used;
+        Plan p;
+    };
+    constexpr int kEntries = 16;
+    static thread_local Entry cache[kEntries];
+    static thread_local unsigned next = 0;
+    for (const Entry& e : cache)
+        if (e.used && e.kind == kind && e.M == M && e.N == N && e.aligned == aligned && e.cus == dev.cus &&
+            e.lds_max == dev.lds_max)
+            return e.p;
+    const Plan p = plan_uncached(kind, M, N, aligned, dev);
+    cache[next++ % kEntries] = Entry{kind, M, N, dev.cus, dev.lds_max, aligned, true, p};
+    return p;
 }
 
 template <int F>

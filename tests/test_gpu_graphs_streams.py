@@ -87,3 +87,66 @@ def test_two_streams_at_once(gpu, oracle_mod):
     torch.cuda.synchronize()
     assert parity_error(ya.cpu().numpy(), oracle_mod.gemv_f16(a["A"], a["x"])) <= GATES["f16"]
     assert parity_error(yb.cpu().numpy(), oracle_mod.gemv_q4(b["A"], b["scale"], b["x"])) <= GATES["q4"]
+
+
+_FIRST_CALL_CAPTURED = r"""
+import sys
+import torch
+from memory_bound_gemv_row_amd import binding, inputs
+
+M, N = 1024, 4096
+f16 = inputs.make("f16", M, N, seed=8)
+A = torch.from_numpy(f16["A"]).cuda()
+x = torch.from_numpy(f16["x"]).cuda()
+W = torch.from_numpy(inputs.make_weights(256, 4096, seed=9)).cuda()
+X = torch.from_numpy(inputs.make_logits(64, 8192, seed=10)).cuda()
+y = torch.empty(M, device="cuda")
+qw = torch.empty((256, 4096), dtype=torch.int8, device="cuda")
+sw = torch.empty(256, dtype=torch.float16, device="cuda")
+ew = torch.empty(256, dtype=torch.float32, device="cuda")
+ys = torch.empty_like(X)
+outs = (y, qw, sw, ew, ys)
+torch.cuda.synchronize()
+
+def work():
+    h = torch.cuda.current_stream().cuda_stream
+    rc = (binding.gemv_f16_ptr(A.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, h),
+          binding.quantize_q8_ptr(W.data_ptr(), qw.data_ptr(), sw.data_ptr(), ew.data_ptr(), 256, 4096, h),
+          binding.softmax_f16_ptr(X.data_ptr(), ys.data_ptr(), 64, 8192, h))
+    assert rc == (0, 0, 0), rc
+
+# the process's first library calls are recorded into a graph
+g = torch.cuda.CUDAGraph()
+s = torch.cuda.Stream()
+s.wait_stream(torch.cuda.current_stream())
+with torch.cuda.stream(s):
+    with torch.cuda.graph(g, stream=s):
+        work()
+torch.cuda.current_stream().wait_stream(s)
+torch.cuda.synchronize()
+g.replay()
+torch.cuda.synchronize()
+got = [o.clone() for o in outs]
+for o in outs:
+    o.zero_()
+work()
+torch.cuda.synchronize()
+assert all(torch.equal(a, b) for a, b in zip(got, outs))
+print("first-call capture ok", flush=True)
+"""
+
+
+def test_first_call_inside_graph_capture(gpu):
+    # A fresh process whose first calls of the library (which reads the
+    # device's CU count and LDS size once) are captured into a graph: the
+    # capture must succeed and the replay match eager calls.
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("[graph] first call captured, fresh process")
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED], cwd=root, capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "first-call capture ok" in r.stdout

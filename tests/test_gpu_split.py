@@ -84,3 +84,30 @@ def test_split_rows_integer_inputs_bit_exact(gpu, oracle_mod, kind):
     y = run_gpu(kind, ops)
     ref = run_oracle(oracle_mod, kind, ops)
     assert np.array_equal(y.astype(np.float64), ref), (kind, np.max(np.abs(y - ref)))
+
+
+# Plans the FP32/FP16 cost model picks over the measured rules on MI355X:
+# (kind, M, N, (variant, block, units in flight, rows per wave)) -- split
+# rows at thousands of rows, two rows per wave with 2 in flight, and 4-wave
+# workgroups with 8 in flight for a few long rows
+_MODEL_CASES = [("f16", 4351, 9856, (6, 128, 2, 1)), ("f16", 2552, 9088, (6, 128, 2, 1)),
+                ("f16", 278, 16896, (6, 256, 4, 1)), ("f32", 902, 5248, (2, 256, 8, 1)),
+                ("f16", 16384, 2560, (2, 256, 2, 2)), ("f32", 11646, 1664, (2, 256, 2, 2))]
+
+
+@pytest.mark.parametrize("case", _MODEL_CASES, ids=lambda c: f"{c[0]}_{c[1]}x{c[2]}")
+def test_cost_model_plans_match_the_oracle(gpu, oracle_mod, case):
+    kind, M, N, want = case
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    info = binding.describe_launch(kind, M, N)
+    if cus == 256:
+        got = (info["variant"], info["block"], info["units_in_flight"], info["rows_per_wave"])
+        assert got == want, (kind, M, N, info)
+    ops = inputs.make(kind, M, N, seed=M + 7 * N)
+    label = f"{kind} model plan M={M} N={N} {info}"
+    say(f"[model] {label}")
+    y = run_gpu(kind, ops)
+    ref = run_oracle(oracle_mod, kind, ops)
+    rep = within_gate(oracle_mod, kind, ops, y, ref)
+    assert rep["ok"], (label, rep)
+    assert within_fp32_bound(kind, ops, y, ref) <= 1.0, label

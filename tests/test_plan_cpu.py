@@ -62,15 +62,20 @@ def test_every_plan_is_consistent(kind, dev):
         if p["variant"] == 5:
             assert 1 <= -(-(N // ELEMS_PER_CHUNK[kind]) // 64) <= 3, where   # rows of one to three units
         if p["variant"] == 6:
-            # split rows: one workgroup of S waves per row, S a power of two
-            # from 2 to 16 and at most one wave per unit of the row, only
-            # where one wave per row leaves the CUs short of waves
+            # split rows: one workgroup of S waves per row (the grid holds
+            # every row: the kernel does not walk), S a power of two from 2
+            # to 16 with at least two units per wave, 2 or 4 in flight
             S = p["block"] // 64
             P = -(-(N // ELEMS_PER_CHUNK[kind]) // 64)
             assert kind != "f16_acc16" and aligned_path, where
-            assert S in (2, 4, 8, 16) and S <= P and p["grid"] == M and p["rows_per_wave"] == 1, where
-            assert M <= 16 * dev["cus"], where          # the row plan had fewer than 8 waves per CU
-            assert p["units_in_flight"] == (2 if -(-P // S) == 2 else 4), where
+            assert S in (2, 4, 8, 16) and 2 * S <= P and p["grid"] == M and p["rows_per_wave"] == 1, where
+            assert M * p["block"] <= 1 << 30 and p["units_in_flight"] in (2, 4), where
+            if kind not in ("f32", "f16"):
+                # the rule alone: only where one wave per row leaves the CUs
+                # short of waves (fewer than 8 per CU), 2 in flight for two
+                # units per wave
+                assert M <= 16 * dev["cus"], where
+                assert p["units_in_flight"] == (2 if -(-P // S) == 2 else 4), where
         assert 1 <= p["units_in_flight"] <= 8, where
 
 
@@ -99,12 +104,14 @@ def test_random_shapes_keep_the_invariants():
 def test_fp_rows_pick_the_least_padding():
     # FP16 rows of 4-23 units with rows enough to fill every CU at two rows
     # per wave: each wave's unit sequence (rows x P) is padded to a multiple
-    # of the loads in flight by no more than the best of the four choices
+    # of the loads in flight by no more than the best of the rules' four
+    # choices (the cost model may take 2 in flight where that pads nothing)
     for P in range(4, 24):
         p = plan("f16", 16384, P * 512)
+        assert p["variant"] == 2, (P, p)
         D, r = p["units_in_flight"], p["rows_per_wave"]
         pad = lambda d, rr: (-(rr * P) % d) / (rr * P)
-        assert pad(D, r) == min(pad(d, rr) for d in (4, 8) for rr in (1, 2)), (P, p)
+        assert pad(D, r) <= min(pad(d, rr) for d in (4, 8) for rr in (1, 2)), (P, p)
     # too few rows to fill the CUs at two rows per wave: one row per wave
     assert plan("f16", 1000, 6144)["rows_per_wave"] == 1
 
@@ -220,3 +227,126 @@ def test_fp16_accumulation_plans_keep_the_gate_term_count(dev):
             for aligned in (True, False):
                 p = plan("f16_acc16", M, N, dev["cus"], dev["lds_max"], aligned)
                 assert _acc16_terms(p["variant"], N) <= k, (M, N, aligned, dev, p)
+
+
+# (variant, grid, block, units in flight, rows per wave) of the named
+# workloads on MI355X: the measured rules' plans, which the FP32/FP16 cost
+# model leaves in place (it predicts less than its margin of a gain there)
+_NAMED_PLANS = {
+    ("f16", 8192, 8192): (2, 1024, 512, 8, 1),
+    ("f16", 4096, 14336): (2, 512, 256, 4, 2),
+    ("f16", 14336, 4096): (2, 3584, 256, 8, 1),
+    ("f16", 4096, 4096): (2, 1024, 256, 8, 1),
+    ("f32", 1024, 1024): (2, 256, 256, 4, 1),
+    ("f32", 2048, 2048): (2, 512, 256, 8, 1),
+    ("f32", 4096, 4096): (2, 512, 512, 8, 1),
+    ("f32", 8192, 8192): (2, 2048, 256, 8, 1),
+    ("f16", 1792, 4096): (2, 448, 256, 8, 1),
+    ("f16", 14336, 512): (2, 448, 512, 4, 4),
+}
+
+
+def _geometry(p):
+    return (p["variant"], p["grid"], p["block"], p["units_in_flight"], p["rows_per_wave"])
+
+
+def test_named_workloads_keep_their_measured_plans():
+    for (kind, M, N), want in _NAMED_PLANS.items():
+        assert _geometry(plan(kind, M, N)) == want, (kind, M, N)
+
+
+def test_cost_model_replaces_plans_the_measurements_beat():
+    # Graph-timed times of every candidate plan on MI355X (us): the rules'
+    # plan, the cost model's, and the fastest candidate.
+    #   FP16 2552x9088: 8 waves, 4 in flight, 319 workgroups (63 CUs with two)
+    #     12.42; split rows, 2 waves per row, 2 in flight 9.88; best 9.62
+    #   FP16 4351x9856: 8 waves, 8 in flight, two rows per wave 21.33; split
+    #     rows, 2 waves, 2 in flight 16.24; best 15.94
+    #   FP16 278x16896: 16 waves per row, 4 in flight (each wave's 2-3 units
+    #     padded to 4) 5.54; 4 waves per row, 4 in flight 4.74; best 4.50
+    #   FP32 902x5248 and FP16 774x24704: 8 waves per row 6.22 and 10.43;
+    #     one wave per row, 4-wave workgroups, 8 in flight 4.97 and 8.43 (the
+    #     fastest of all candidates)
+    assert _geometry(plan("f16", 2552, 9088)) == (6, 2552, 128, 2, 1)
+    assert _geometry(plan("f16", 4351, 9856)) == (6, 4351, 128, 2, 1)
+    assert _geometry(plan("f16", 278, 16896)) == (6, 278, 256, 4, 1)
+    assert _geometry(plan("f32", 902, 5248)) == (2, 226, 256, 8, 1)
+    assert _geometry(plan("f16", 774, 24704)) == (2, 194, 256, 8, 1)
+    # the other formats keep the rules alone
+    assert plan("f16x32", 5484, 4608)["variant"] == 2
+    assert plan("f16_acc16", 2552, 9088)["variant"] == 2
+
+
+def test_plan_cache_gives_the_same_plans():
+    # each host thread keeps its last 16 plans: more shapes than that,
+    # interleaved across devices and in two orders, give the same plans
+    import numpy as np
+
+    rng = np.random.default_rng(7)
+    shapes = [(KINDS[rng.integers(len(KINDS))], int(rng.integers(1, 70000)), int(rng.integers(1, 300)) * 128)
+              for _ in range(60)]
+    devs = [MI355X, dict(cus=80, lds_max=64 * 1024)]
+    first = {(s, i): plan(*s, **d) for s in shapes for i, d in enumerate(devs)}
+    for s in reversed(shapes):
+        for i, d in reversed(list(enumerate(devs))):
+            assert plan(*s, **d) == first[(s, i)], (s, d)
+
+
+def _kernel_vgprs():
+    """VGPR counts of the built library's gfx950 kernels, read from the
+    code object's metadata: {demangled name: vgprs}."""
+    import os
+    import re
+    import shutil
+    import subprocess
+    import tempfile
+
+    from memory_bound_gemv_row_amd import build as hip_build
+
+    lib = hip_build.LIB
+    llvm = "/opt/rocm/llvm/bin"
+    tools = [shutil.which("objcopy"), shutil.which("c++filt"), os.path.join(llvm, "clang-offload-bundler"),
+             os.path.join(llvm, "llvm-readelf")]
+    if not os.path.exists(lib) or not all(t and os.path.exists(t) for t in tools):
+        pytest.skip("built library or code-object tools not available")
+    with tempfile.TemporaryDirectory() as d:
+        fat, dev, copy = os.path.join(d, "fat.bin"), os.path.join(d, "dev.o"), os.path.join(d, "copy.so")
+        # (objcopy rewrites its input unless given an output file)
+        subprocess.run([tools[0], "--dump-section", f".hip_fatbin={fat}", lib, copy], check=True)
+        subprocess.run([tools[2], "--unbundle", "--type=o", f"--input={fat}",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={dev}"], check=True)
+        notes = subprocess.run([tools[3], "--notes", dev], check=True, capture_output=True, text=True).stdout
+    out, name = {}, None
+    for line in notes.splitlines():
+        m = re.match(r"\s+\.name:\s+(\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.match(r"\s+\.vgpr_count:\s+(\d+)", line)
+        if m and name:
+            out[name] = int(m.group(1))
+    names = list(out)
+    plain = subprocess.run([tools[1]], input="\n".join(names), check=True, capture_output=True,
+                           text=True).stdout.splitlines()
+    return {p.split("(")[0]: out[n] for n, p in zip(names, plain)}
+
+
+def test_fp_kernel_occupancy_matches_the_cost_model():
+    # The FP32/FP16 cost model assumes 7 waves per SIMD for the streaming
+    # kernels with 8 units in flight and 8 for every other FP32/FP16 kernel
+    # it chooses from (512 VGPRs per SIMD lane, allocated in blocks of 8).
+    import re
+
+    vg = _kernel_vgprs()
+    seen = 0
+    for name, v in vg.items():
+        m = re.match(r"void gemv::gemv_(stream|xreg|split)<([01]), (\d+), (\d+)(.*)>$", name)
+        if not m:
+            continue
+        kernel, D = m.group(1), int(m.group(4))
+        if kernel == "stream" and not m.group(5).endswith("true, true, 0"):
+            continue
+        waves = min(8, 512 // (-(-v // 8) * 8))
+        want = 7 if kernel == "stream" and D == 8 else 8
+        assert waves == want, (name, v)
+        seen += 1
+    assert seen >= 40, seen
