@@ -88,20 +88,33 @@ struct Plan {
 // FP32 1024x1024 2.52 vs 2.66, FP16 1024x4096 3.09 vs 3.29, FP16 with FP32
 // x 1500x8192 6.63 vs 7.10, INT8 1500x10240 5.57 vs 6.18), and INT4 rows
 // of 18 units lost to it by 60 %.
+// INT8 (since its exact decode) splits up to 6 rows per CU, with S for 4
+// waves per CU and 2 units in flight: brute force over every plan on 17
+// such shapes put this 1.7 % from the fastest (geometric mean; 8 % at
+// worst), the rule above 10.5 % (24 %): INT8 1069x10368 5.61 -> 4.64 us,
+// 1453x4224 4.53 -> 3.88, 486x38592 7.97 -> 6.42.
 constexpr int kSplitWavesPerCu = 16;
 
 bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
 {
     if (kind == kF16H || P < 4 || p0.variant == 3)
         return false;
-    // FP32/FP16 rows of 16 units and more up to 8 waves per CU (x is one
-    // granule per unit); otherwise 4, INT8 3, INT4 2 (x per unit is two or
-    // four granules), FP16 with FP32 x 4
-    const bool fp = kind == kF32 || kind == kF16;
-    const int per_cu = fp && P >= 16 ? 8 : (kind == kQ8 ? 3 : (kind == kQ4 ? 2 : 4));
-    if ((int64_t)p0.grid * p0.waves >= (int64_t)per_cu * cus || (kind == kQ4 && P > 16))
-        return false;
-    const int64_t target = (int64_t)kSplitWavesPerCu * cus;
+    int64_t target = (int64_t)kSplitWavesPerCu * cus;
+    int depth = 0;   // 0: 2 for two units per wave, else 4
+    if (kind == kQ8) {
+        if (M > 6 * cus)
+            return false;
+        target = 4 * (int64_t)cus;
+        depth = 2;
+    } else {
+        // FP32/FP16 rows of 16 units and more up to 8 waves per CU (x is
+        // one granule per unit); otherwise 4, INT4 2 (x per unit is four
+        // granules), FP16 with FP32 x 4
+        const bool fp = kind == kF32 || kind == kF16;
+        const int per_cu = fp && P >= 16 ? 8 : (kind == kQ4 ? 2 : 4);
+        if ((int64_t)p0.grid * p0.waves >= (int64_t)per_cu * cus || (kind == kQ4 && P > 16))
+            return false;
+    }
     int S = 2;   // P >= 4: two units per wave at least
     while (S < 16 && 4 * S <= P && (int64_t)M * S < target)
         S *= 2;
@@ -111,7 +124,7 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
     p->xk = S;
     p->waves = S;
     p->block = S * 64;
-    p->D = per_wave == 2 ? 2 : 4;   // at least two units per wave
+    p->D = depth > 0 ? depth : (per_wave == 2 ? 2 : 4);   // at least two units per wave
     p->rows = 1;
     p->stg = -1;
     p->lds = 0;
@@ -207,14 +220,14 @@ void finish_rows(int M, int cus, Plan* p)
 //     x CUs, which stage x as below with 8 waves, x before A, one workgroup
 //     per CU): x read with each unit, 8 waves, 2 (two-unit rows) or 4 in
 //     flight -- the staging and its barrier would dominate such launches.
-//     Otherwise x is staged: rows of 8 units or more: 8 waves, 4 in flight,
-//     A first, a row per wave, or two where that pads less (rows_for_depth:
-//     16384 x 10240 29.4 -> 25.3 us); rows of 8-16 units with 20-32 rows
-//     per CU: 12 waves, at most 2 workgroups per CU; rows of 2 units: 8
-//     waves, 2 in flight, split staging (staging loads, A prologue, LDS
-//     writes), at most 3 workgroups per CU; rows of 4-5 units: 4 waves,
-//     split staging, at most 3 workgroups per CU; rows of 3, 6 or 7: 8
-//     waves, A first, at most 2 workgroups per CU.
+//     Otherwise x is staged: rows of 8 units or more: 4 waves, 4 in flight,
+//     split staging (staging loads, A prologue, LDS writes), two rows per
+//     wave for rows of 8-10 units where every CU still gets a workgroup,
+//     else one row and at most 2 workgroups per CU; rows of 2 units: 8
+//     waves, 2 in flight, split staging, at most 3 workgroups per CU; rows
+//     of 3-5 units: 4 waves, split staging, at most 3 workgroups per CU;
+//     rows of 6 or 7: 8 waves, A first, at most 2 workgroups per CU.  (Up
+//     to 6 rows per CU, rows of 4 units and more split instead: split_plan.)
 //     Staged x past 64 KiB (rows of 32 units and more): with two workgroups
 //     per CU fitting the device's LDS and over 4 x CUs rows, 4 waves, split
 //     staging, at most 2 workgroups per CU; otherwise 8 waves, x staged
@@ -442,16 +455,22 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             // each unit, 8 waves, 4 in flight
             p.variant = 2;
             p.waves = 8;
-        } else if (P >= 8 && P <= 16 && M >= 20 * cus && M <= 32 * cus) {
-            // rows of 8-16 units, 20-32 per CU: 12 waves, A first, at most 2
-            // workgroups per CU (half the staging of four 8-wave ones)
-            p.waves = 12;
-            p.cap = 2;
         } else if (P >= 8) {
-            // long rows: 8 waves, A first, one row per wave, or two where
-            // that pads less (rows of 9, 10, 13, 14 ... units)
-            p.waves = 8;
-            p.rows = rows_for_depth(P, 4, two_rows_fill(M, 8, cus));
+            // rows of 8-31 units, many of them: 4 waves, split staging; rows
+            // of 8-10 units two per wave with no cap where that still gives
+            // every CU a workgroup (8192 x 8192 12.11 -> 11.66 us), longer
+            // ones one per wave, at most 2 workgroups per CU.  Brute force
+            // over every plan on 27 such shapes: 3.8 % from the fastest
+            // (geometric mean), against 8.2 % for the earlier rule (8 waves,
+            // A first; 12 waves at 20-32 rows per CU), which the exact INT8
+            // decode left behind (6618 x 15104 20.37 -> 18.69 us)
+            p.waves = 4;
+            p.stg = 2;
+            if (P <= 10 && two_rows_fill(M, 4, cus)) {
+                p.rows = 2;
+            } else {
+                p.cap = 2;
+            }
         } else if (P <= 2) {
             // rows of 2 units: 8 waves, 2 in flight, split staging, at most
             // 3 workgroups per CU (waves walk several rows)
@@ -461,16 +480,16 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.cap = 3;
         } else {
             // rows of 3-7 units, many of them: 4 waves, split staging, at
-            // most 3 workgroups per CU for rows of 4 units, and of 5 with 5
-            // in flight (no padding: 14336 x 5120 13.28 -> 12.86 us); rows
-            // of 3, 6 and 7 units: 8 waves, A first, at most 2 workgroups
-            // per CU (16384 x 6144 17.4 -> 16.2 us, 8192 x 6144 9.9 -> 9.0,
-            // 16384 x 3072 9.4 -> 9.0)
-            if (P == 4 || P == 5) {
+            // most 3 workgroups per CU for rows of 3-5 units, 5 in flight for
+            // rows of 5 (no padding: 14336 x 5120 13.28 -> 12.86 us; rows of
+            // 3: 10225 x 2304 7.35 -> 6.21, 3564 x 2064 4.81 -> 3.72); rows of
+            // 6 and 7 units: 8 waves, A first, at most 2 workgroups per CU
+            // (16384 x 6144 17.4 -> 16.2 us, 8192 x 6144 9.9 -> 9.0)
+            if (P <= 5) {
                 p.waves = 4;
                 p.stg = 2;
                 p.cap = 3;
-                p.D = P;
+                p.D = P == 5 ? 5 : 4;
             } else {
                 p.waves = 8;
                 p.cap = 2;
@@ -749,10 +768,6 @@ const void* stream_kernel()
 template <int F, bool XG, int STG>
 const void* select_stream_stg(const Plan& p)
 {
-    if constexpr (F == kQ8 && !XG && STG == 0) {
-        if (p.waves == 12)
-            return stream_kernel<F, 12, 4, XG, STG>();
-    }
     // in-flight depths that divide rows of 5 or 6 units (4 waves)
     if constexpr ((F == kQ8 && !XG && STG == 2) || (F == kQ4 && !XG && STG == 1)) {
         if (p.waves == 4 && p.D == 5)

@@ -188,10 +188,11 @@ def test_describe_launch_fills_all_cus(gpu):
     # few long rows: several waves per row (split rows), x read with each unit
     info = binding.describe_launch("f16x32", 64, 32768)
     assert info["variant"] == 6 and info["lds_bytes"] == 0 and info["grid"] == 64, info
-    # few long INT8 rows stage x (one workgroup per CU); few INT4 rows of
-    # four units or more read x with each unit
-    assert binding.describe_launch("q8", 4 * cus, 8192)["stage_order"] == 1
-    assert binding.describe_launch("q8", 4 * cus + 1, 8192)["variant"] == 2
+    # few INT8 rows of four units or more (up to 6 per CU): split rows; a few
+    # more: x read with each unit; few INT4 rows of four units or more read
+    # x with each unit
+    assert binding.describe_launch("q8", 6 * cus, 8192)["variant"] == 6
+    assert binding.describe_launch("q8", 6 * cus + 1, 8192)["variant"] == 2
     assert binding.describe_launch("q4", 4 * cus, 8192)["variant"] == 2
     assert binding.describe_launch("q4", 4 * cus + 1, 8192)["variant"] == 1
 

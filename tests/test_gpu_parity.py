@@ -112,7 +112,7 @@ def test_quantised_x_paths_by_rows(gpu, oracle_mod, kind, N, small, large):
 # (kind, M, N, variant, stage order) on a device of 256 CUs whose workgroups
 # may hold 160 KiB of LDS; rows end in a ragged last pass
 _LONG_ROWS = [
-    ("q8", 1024, 32848, 1, 1),    # 66 KiB of staged x, few rows: one workgroup per CU
+    ("q8", 1024, 32848, 6, -1),   # 66 KiB of x, few rows: split rows, x read with each unit
     ("q8", 3000, 32848, 1, 2),    # two workgroups per CU, waves walk two rows
     ("q8", 3000, 49168, 1, 1),    # 98 KiB: one workgroup per CU, waves walk two rows
     ("q8", 2000, 49168, 2, -1),   # one workgroup per CU and few rows: x per unit
@@ -120,7 +120,7 @@ _LONG_ROWS = [
     ("q4", 3000, 34944, 1, 1),    # 72 KiB: one workgroup per CU
     ("q4", 1000, 34944, 2, -1),   # few rows: x per unit
     ("q4", 300, 82048, 2, -1),    # staged x would not fit a workgroup
-    ("q8", 1000, 16400, 1, 1),    # rows of 17 units, few of them: staged, one workgroup per CU
+    ("q8", 1000, 16400, 6, -1),   # rows of 17 units, few of them: split rows
     ("q4", 1000, 8320, 2, -1),    # few INT4 rows of 5 units: x per unit
     ("f16x32", 1100, 24584, 1, 1),  # 96 KiB of FP32 x: staged, one workgroup per CU
     ("f16x32", 2100, 40968, 2, -1),  # FP32 x would not fit a workgroup
@@ -162,7 +162,7 @@ def test_long_fp_rows(gpu, oracle_mod, kind, M, N, D, rows):
     _check(oracle_mod, kind, ops, f"{kind} long rows M={M} N={N} {info}")
 
 
-@pytest.mark.parametrize("kind,M,N", [("q8", 4500, 9216 + 16), ("q8", 4200, 14336), ("f16x32", 9000, 12800 + 8),
+@pytest.mark.parametrize("kind,M,N", [("q8", 4500, 9216 + 16), ("q8", 6000, 8192 + 16), ("f16x32", 9000, 12800 + 8),
                                       ("f16x32", 2048 + 3, 3072 + 8), ("f16_acc16", 4096 + 5, 4608 + 8)])
 def test_two_rows_per_wave_where_that_pads_less(gpu, oracle_mod, kind, M, N):
     # rows whose unit count does not divide by the loads in flight: two rows
@@ -175,13 +175,15 @@ def test_two_rows_per_wave_where_that_pads_less(gpu, oracle_mod, kind, M, N):
     _check(oracle_mod, kind, ops, f"{kind} two rows per wave M={M} N={N} {info}")
 
 
-@pytest.mark.parametrize("M,N", [(16384 + 3, 6144), (9000, 7168 - 16), (12000, 3072 - 16)])
-def test_int8_rows_of_3_6_7_units(gpu, oracle_mod, M, N):
-    # many INT8 rows of 3, 6 or 7 units: 8 waves, A first, at most 2
-    # workgroups per CU, so waves walk several rows (ragged passes too)
+@pytest.mark.parametrize("M,N,block,stg", [(16384 + 3, 6144, 512, 0), (9000, 7168 - 16, 512, 0),
+                                           (12000, 3072 - 16, 256, 2)])
+def test_int8_rows_of_3_6_7_units(gpu, oracle_mod, M, N, block, stg):
+    # many INT8 rows of 6 or 7 units: 8 waves, A first, at most 2 workgroups
+    # per CU; of 3 units: 4 waves, split staging, at most 3 per CU; waves
+    # walk several rows (ragged passes too)
     info = binding.describe_launch("q8", M, N)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert (info["variant"], info["block"], info["stage_order"]) == (1, 512, 0), info
+        assert (info["variant"], info["block"], info["stage_order"]) == (1, block, stg), info
         assert info["rows_per_wave"] >= 2, info
     ops = inputs.make("q8", M, N, seed=M - N)
     _check(oracle_mod, "q8", ops, f"q8 short staged rows M={M} N={N} {info}")
@@ -199,18 +201,19 @@ def test_depths_that_divide_the_row(gpu, oracle_mod, kind, M, N, D):
     _check(oracle_mod, kind, ops, f"{kind} depth {D} M={M} N={N} {info}")
 
 
-@pytest.mark.parametrize("M,N", [(20 * 256 + 5, 8192 + 16), (32 * 256, 16384), (24 * 256 + 3, 12288)])
-def test_int8_twelve_wave_workgroups(gpu, oracle_mod, M, N):
-    # INT8 rows of 8-16 units, 20-32 rows per CU: 12-wave workgroups, at
-    # most 2 per CU, so that beyond 24 rows per CU some waves walk two rows
-    # (ragged last pass too)
+@pytest.mark.parametrize("M,N,rows", [(20 * 256 + 5, 8192 + 16, 2), (32 * 256, 16384, 1), (24 * 256 + 3, 12288, 1)])
+def test_int8_long_rows_split_staging(gpu, oracle_mod, M, N, rows):
+    # INT8 rows of 8-31 units, many rows: 4-wave workgroups with split
+    # staging; rows of 8-10 units two per wave, longer ones at most 2
+    # workgroups per CU so that waves walk several rows (ragged last pass)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     info = binding.describe_launch("q8", M, N)
     if cus == 256:
-        assert (info["variant"], info["block"], info["stage_order"]) == (1, 768, 0), info
-        assert info["grid"] == min(-(-M // 12), 2 * cus), info
+        assert (info["variant"], info["block"], info["stage_order"]) == (1, 256, 2), info
+        want = -(-M // 8) if rows == 2 else min(-(-M // 4), 2 * cus)
+        assert info["grid"] == want, info
     ops = inputs.make("q8", M, N, seed=M ^ N)
-    _check(oracle_mod, "q8", ops, f"q8 12-wave M={M} N={N} {info}")
+    _check(oracle_mod, "q8", ops, f"q8 split staging M={M} N={N} {info}")
 
 
 @pytest.mark.parametrize("kind,M,N", [("f32", 8000, 252), ("f32", 9000, 260), ("f16", 14336, 1000),

@@ -70,7 +70,10 @@ def test_every_plan_is_consistent(kind, dev):
             assert kind != "f16_acc16" and aligned_path, where
             assert S in (2, 4, 8, 16) and 2 * S <= P and p["grid"] == M and p["rows_per_wave"] == 1, where
             assert M * p["block"] <= 1 << 30 and p["units_in_flight"] in (2, 4), where
-            if kind not in ("f32", "f16"):
+            if kind == "q8":
+                # INT8: up to 6 rows per CU, 2 in flight
+                assert M <= 6 * dev["cus"] and p["units_in_flight"] == 2, where
+            elif kind not in ("f32", "f16"):
                 # the rule alone: only where one wave per row leaves the CUs
                 # short of waves (fewer than 8 per CU), 2 in flight for two
                 # units per wave
@@ -161,10 +164,15 @@ def test_few_rows_rules():
     # few INT4 rows of four units or more: x per unit; one more row: staged
     assert plan("q4", 4 * cus, 8192)["variant"] == 2
     assert plan("q4", 4 * cus + 1, 8192)["variant"] == 1
-    # few long INT8 rows: staged, x before A, one workgroup per CU
+    # INT8 rows of four units or more, up to 6 rows per CU: split rows, S for
+    # 4 waves per CU, 2 in flight; a few more rows (up to 8 per CU, up to 16
+    # units): x read with each unit
     p = plan("q8", 4 * cus, 8192)
-    assert (p["variant"], p["stage_order"], p["block"]) == (1, 1, 512) and p["grid"] <= cus
-    assert plan("q8", 4 * cus + 1, 8192)["variant"] == 2
+    assert (p["variant"], p["block"], p["units_in_flight"], p["grid"]) == (6, 128, 2, 4 * cus)
+    p = plan("q8", 300, 38592)
+    assert (p["variant"], p["block"], p["units_in_flight"]) == (6, 256, 2)
+    assert plan("q8", 6 * cus, 8192)["variant"] == 6
+    assert plan("q8", 6 * cus + 1, 8192)["variant"] == 2
     # INT8 rows of 64 units with at most 8 rows per CU: x per unit, two rows a wave
     p = plan("q8", 2048, 65536)
     assert (p["variant"], p["units_in_flight"]) == (2, 8)
