@@ -181,6 +181,57 @@ int gemv_describe_launch(int kind, int M, int N, int aligned, gemv_launch_info* 
  * without a GPU.  GEMV_E_INVAL also for cus <= 0 or lds_max <= 0. */
 int gemv_describe_launch_for(int kind, int M, int N, int aligned, int cus, int lds_max, gemv_launch_info* info);
 
+/* An explicit launch plan, for plan searches and tuning: the choices the
+ * planner makes for a call (the llama.cpp walkthrough's implementation note:
+ * the block size is chosen at run time; here every choice can also be
+ * given).
+ *   variant          1 streaming kernel, x staged in LDS (INT8, INT4, FP16
+ *                    with FP32 x); 2 streaming kernel, x read with each
+ *                    unit; 4 packed short rows (INT8/INT4 rows of at most
+ *                    32 16-byte chunks); 5 x in registers (rows of exactly
+ *                    1-3 wave loads); 6 split rows (a workgroup per row)
+ *   waves            waves per workgroup (split rows: waves per row, 2-16)
+ *   units_in_flight  1-KiB wave loads in flight per wave
+ *   rows_per_wave    rows (packed: row groups) per wave the grid is sized
+ *                    for; waves walk whatever rows lie beyond (1 for split)
+ *   stage_order      variant 1: 0 A's first loads before x's staging, 1 x
+ *                    first, 2 staging loads / A's first loads / LDS writes;
+ *                    -1 otherwise
+ *   cap              at most this many workgroups per CU (0: no cap)
+ * Only combinations the library holds a kernel for are accepted. */
+typedef struct gemv_plan {
+    int variant;
+    int waves;
+    int units_in_flight;
+    int rows_per_wave;
+    int stage_order;
+    int cap;
+} gemv_plan;
+
+/* Whether `plan` can run `kind` at M x N on a device with `cus` compute
+ * units and `lds_max` bytes of LDS per workgroup, touching no device: fills
+ * `info` with the launch it makes and returns GEMV_OK, or returns
+ * GEMV_E_UNSUPPORTED for a plan the library holds no kernel for or that does
+ * not fit the shape (a staged x beyond lds_max, x in registers for rows not
+ * of 1-3 wave loads, split rows with fewer than two loads per wave or beyond
+ * 2^30 work-items, packed rows for FP formats or rows over 32 chunks, FP16
+ * accumulation outside variants 2 and 5), GEMV_E_INVAL for bad arguments
+ * (kind outside 0-5, M or N < 1, cus or lds_max <= 0, null pointers).  The
+ * shape must take the bandwidth path (N a multiple of a 16-byte chunk's
+ * elements, rows under 2 GiB, at most 2^30 rows). */
+int gemv_check_plan_for(int kind, int M, int N, int cus, int lds_max, const gemv_plan* plan,
+                        gemv_launch_info* info);
+
+/* Runs the GEMV of `kind` (operands as for gemv_f32 ... gemv_q4; `scale`
+ * ignored for FP formats) with `plan` instead of the planner's choice, on
+ * the current device; y is the same up to the summation order the plan
+ * implies (bit for bit where it sums each lane's chunks as the planner's
+ * plan does).  Checks as gemv_check_plan_for, plus GEMV_E_INVAL for A or x
+ * not 16-byte aligned.  Enqueues on `stream` and returns; GEMV_E_LAUNCH if
+ * the launch fails. */
+int gemv_launch_plan(int kind, const void* A, const uint16_t* scale, const void* x, float* y, int M, int N,
+                     const gemv_plan* plan, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

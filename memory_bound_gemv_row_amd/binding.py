@@ -34,6 +34,13 @@ class LaunchInfo(ctypes.Structure):
                 ("stage_order", ctypes.c_int)]
 
 
+class Plan(ctypes.Structure):
+    """gemv_plan: an explicit launch plan (variant, waves, units_in_flight,
+    rows_per_wave, stage_order, cap)."""
+    _fields_ = [("variant", ctypes.c_int), ("waves", ctypes.c_int), ("units_in_flight", ctypes.c_int),
+                ("rows_per_wave", ctypes.c_int), ("stage_order", ctypes.c_int), ("cap", ctypes.c_int)]
+
+
 def load():
     """Load the in-tree library (raises if it has not been built)."""
     global _lib
@@ -66,6 +73,10 @@ def load():
         lib.gemv_describe_launch.restype = i
         lib.gemv_describe_launch_for.argtypes = [i, i, i, i, i, i, ctypes.POINTER(LaunchInfo)]
         lib.gemv_describe_launch_for.restype = i
+        lib.gemv_check_plan_for.argtypes = [i, i, i, i, i, ctypes.POINTER(Plan), ctypes.POINTER(LaunchInfo)]
+        lib.gemv_check_plan_for.restype = i
+        lib.gemv_launch_plan.argtypes = [i, p, p, p, p, i, i, ctypes.POINTER(Plan), p]
+        lib.gemv_launch_plan.restype = i
         _lib = lib
         return lib
 
@@ -334,3 +345,24 @@ def probe_copy(src, dst, stream=None):
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst smaller than src")
     _check(probe_copy_ptr(src.data_ptr(), dst.data_ptr(), n, _stream(stream)), "gemv_probe_copy")
+
+
+def check_plan_for(kind: str, M: int, N: int, cus: int, lds_max: int, plan: tuple) -> dict | None:
+    """The launch an explicit plan (variant, waves, units_in_flight,
+    rows_per_wave, stage_order, cap) makes on a device of `cus` CUs and
+    `lds_max` bytes of LDS per workgroup, or None where the library holds no
+    kernel for it or it does not fit the shape; touches no device."""
+    _dims(M, N)
+    info = LaunchInfo()
+    rc = load().gemv_check_plan_for(KIND[kind], M, N, cus, lds_max, ctypes.byref(Plan(*plan)), ctypes.byref(info))
+    if rc == 2:
+        return None
+    _check(rc, "gemv_check_plan_for")
+    return {f: getattr(info, f) for f, _ in LaunchInfo._fields_}
+
+
+def launch_plan_ptr(kind: str, A: int, scale: int, x: int, y: int, M: int, N: int, plan: tuple,
+                    stream: int = 0) -> int:
+    """gemv_launch_plan on raw device pointers (scale 0 for FP formats)."""
+    _dims(M, N)
+    return load().gemv_launch_plan(KIND[kind], A, scale or None, x, y, M, N, ctypes.byref(Plan(*plan)), stream)

@@ -235,7 +235,7 @@ void finish_rows(int M, int cus, Plan* p)
 //     of two rows, 8 in flight) where only one workgroup fits and M <= 8 x
 //     CUs, or where the staged x would not fit at all.
 //   INT4, other rows, x staged: rows under 4 units: 8 waves, 2 in flight,
-//     split staging, at most 3 workgroups per CU; longer rows: 4 in flight,
+//     split staging, at most 4 workgroups per CU; longer rows: 4 in flight,
 //     x staged before A, 4 waves and at most 3 workgroups per CU -- but 8
 //     waves and at most 2 for rows of 14-16 units (fewer stagings of x:
 //     8192 x 28672 26.0 -> 22.3 us, 4096 x 28672 16.4 -> 13.5; shorter rows
@@ -246,14 +246,15 @@ void finish_rows(int M, int cus, Plan* p)
 //     would not fit the device's LDS.
 //   INT8/INT4 rows of at most 32 chunks (half a wave load): the packed
 //     kernel, 64 / L rows per wave load, 8 waves; with up to 16 row groups
-//     per CU one group per wave, up to 32 two (both in flight), beyond that
-//     four, two in flight.
+//     per CU one group per wave, beyond that two (both in flight).
 //   FP16 with FP32 x: x is twice the bytes of FP16 x, and reading it with
 //     every unit costs more cache bandwidth than staging it, once the staging
 //     (4N bytes per workgroup) is spread over enough rows: staged for rows of
 //     at least 12 units (24 and more: 8 waves, 4 in flight, split staging,
-//     two rows per wave where that pads less), or for 8192 rows and more;
-//     read with each unit otherwise (two rows per wave from 5 units).  Rows
+//     two rows per wave where that pads less), for rows of 4-11 units with
+//     more than 16 rows per CU (4 waves, split staging, at most 2
+//     workgroups per CU), or for 8192 rows and more; read with each unit
+//     otherwise (two rows per wave from 5 units).  Rows
 //     whose staged x passes 64 KiB stage it up to the device's LDS per
 //     workgroup (8 waves, 4 in flight, x before A, one workgroup per CU),
 //     reading x with each unit beyond that.
@@ -290,8 +291,11 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
         const int64_t per_cu = (groups + cus - 1) / cus;
         p.variant = 4;
         p.waves = 8;
+        // one group per wave up to 16 per CU, else two, both in flight
+        // (four groups per wave, two rounds of two, measured slower: INT4
+        // 40979 x 512 5.73 -> 4.79 us, INT8 30962 x 384 4.87 -> 4.67)
         p.D = per_cu <= 16 ? 1 : 2;
-        p.rows = per_cu <= 32 ? p.D : 4;
+        p.rows = p.D;
         p.stg = -1;   // x goes straight to registers
         p.lds = 0;
         p.block = p.waves * 64;
@@ -393,6 +397,18 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.D = P % 8 == 0 ? 8 : 4;
             p.stg = P % 8 == 0 ? 0 : 2;
             p.cap = 3;
+        } else if (fits && P >= 4 && M > 16 * cus) {
+            // rows of 4-11 units, many of them: staged x, 4 waves, 4 in
+            // flight, split staging, at most 2 workgroups per CU.  Brute
+            // force over every plan on 9 such shapes: 1.6 % from the fastest
+            // (geometric mean), against 11 % for x read with each unit below
+            // 8192 rows and A first above (5484 x 4608 13.25 -> 9.67 us,
+            // 9614 x 2048 9.00 -> 8.04)
+            p.variant = 1;
+            p.waves = 4;
+            p.D = 4;
+            p.stg = 2;
+            p.cap = 2;
         } else if (fits && M >= 8192) {
             p.variant = 1;
             p.waves = 4;
@@ -513,10 +529,12 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.stg = 1;
         p.cap = 1;
     } else {
-        // short INT4 rows: 8 waves, 2 units in flight, split staging;
-        // longer rows: 4 units, x staged before A, 4 waves and at most 3
-        // workgroups per CU; rows of 14-16 units: 8 waves and at most 2
-        // workgroups per CU (fewer stagings of their 56-64 KiB of x)
+        // short INT4 rows: 8 waves, 2 units in flight, split staging, at
+        // most 4 workgroups per CU (3 measured 1.7-4.8 % slower on seven
+        // shapes: 14336 x 4096 7.52 -> 7.30 us); longer rows: 4 units, x
+        // staged before A, 4 waves and at most 3 workgroups per CU; rows of
+        // 14-16 units: 8 waves and at most 2 workgroups per CU (fewer
+        // stagings of their 56-64 KiB of x)
         p.variant = 1;
         p.waves = P < 4 || P >= 14 ? 8 : 4;
         // rows of 5 and 6 units: 5 and 3 in flight, which divide them
@@ -524,7 +542,7 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
         p.D = P < 4 ? 2 : (P == 5 ? 5 : (P == 6 ? 3 : 4));
         p.rows = 1;
         p.stg = P < 4 ? 2 : 1;
-        p.cap = P >= 14 ? 2 : 3;
+        p.cap = P < 4 ? 4 : (P >= 14 ? 2 : 3);
     }
     // staged plans were chosen only where x fits the device's LDS
     p.lds = p.variant == 1 ? (int)lds_bytes(kind, nchunks) : 0;
@@ -969,10 +987,9 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
 namespace gemv {
 namespace {
 
-// gemv_describe_launch's report for a device of `dev`'s properties.
-void fill_launch_info(int kind, int M, int N, bool aligned, const Device& dev, gemv_launch_info* info)
+// The report of plan p for a call of M x N.
+void info_of_plan(int kind, int M, int N, const Plan& p, gemv_launch_info* info)
 {
-    const Plan p = make_plan(kind, M, N, aligned, dev);
     info->variant = p.variant;
     info->grid = p.grid;
     info->block = p.block;
@@ -988,6 +1005,102 @@ void fill_launch_info(int kind, int M, int N, bool aligned, const Device& dev, g
     info->units_in_flight = p.D;
     info->lds_bytes = p.lds;
     info->stage_order = p.variant == 1 ? p.stg : -1;
+}
+
+// gemv_describe_launch's report for a device of `dev`'s properties.
+void fill_launch_info(int kind, int M, int N, bool aligned, const Device& dev, gemv_launch_info* info)
+{
+    info_of_plan(kind, M, N, make_plan(kind, M, N, aligned, dev), info);
+}
+
+// An explicit plan (gemv_plan) checked against the kernels the library holds
+// and the shape, completed to a launch as the planner's plans are; GEMV_OK,
+// GEMV_E_INVAL or GEMV_E_UNSUPPORTED.
+int plan_from_user(int kind, int M, int N, const Device& dev, const gemv_plan& u, Plan* out)
+{
+    if (kind < 0 || kind > 5 || M < 1 || N < 1)
+        return GEMV_E_INVAL;
+    if (kind == kQ4 && N % 128 != 0)
+        return GEMV_E_UNSUPPORTED;
+    const int epc = elems_per_chunk(kind);
+    // the bandwidth path only (rows_plan's conditions for the element-wise kernel)
+    if (N % epc != 0 || (int64_t)(N / epc) * 16 >= ((int64_t)1 << 31) || M > (1 << 30))
+        return GEMV_E_UNSUPPORTED;
+    const int nchunks = N / epc;
+    const int P = (nchunks + 63) / 64;
+    const bool fp = kind == kF32 || kind == kF16 || kind == kF16H;
+    const bool intk = kind == kQ8 || kind == kQ4;
+    Plan p{};
+    p.variant = u.variant;
+    p.waves = u.waves;
+    p.D = u.units_in_flight;
+    p.rows = u.rows_per_wave;
+    p.stg = u.stage_order;
+    p.cap = u.cap;
+    if (p.rows < 1 || p.cap < 0)
+        return GEMV_E_UNSUPPORTED;
+    switch (p.variant) {
+    case 1:
+    case 2: {
+        const bool staged = p.variant == 1;
+        if (staged ? (fp || p.stg < 0 || p.stg > 2) : p.stg != -1)
+            return GEMV_E_UNSUPPORTED;   // FP32/FP16 read x with each unit
+        const bool common = (p.waves == 4 || p.waves == 8) && (p.D == 2 || p.D == 4 || p.D == 8);
+        // the depths instantiated for rows of 5 and 6 units
+        const bool d5 = staged && p.waves == 4 && p.D == 5 &&
+                        ((kind == kQ8 && p.stg == 2) || (kind == kQ4 && p.stg == 1));
+        const bool d3 = staged && p.waves == 4 && p.D == 3 && kind == kQ4 && p.stg == 1;
+        if (!(common || d5 || d3))
+            return GEMV_E_UNSUPPORTED;
+        if (staged) {
+            const int64_t lds = lds_bytes(kind, nchunks) + (p.stg == 2 ? kSplitSpareBytes : 0);
+            if (lds > dev.lds_max)
+                return GEMV_E_UNSUPPORTED;
+            p.lds = (int)lds;
+        }
+        finish_rows(M, dev.cus, &p);
+        break;
+    }
+    case 4: {
+        if (!intk || nchunks > kPackedMaxChunks || p.waves != 8 || (p.D != 1 && p.D != 2) || p.stg != -1)
+            return GEMV_E_UNSUPPORTED;
+        const int R = packed_rows_per_load(nchunks);
+        const int64_t groups = ((int64_t)M + R - 1) / R;
+        p.block = p.waves * 64;
+        const int64_t waves_needed = (groups + p.rows - 1) / p.rows;
+        int64_t grid = (waves_needed + p.waves - 1) / p.waves;
+        if (p.cap > 0 && grid > (int64_t)p.cap * dev.cus)
+            grid = (int64_t)p.cap * dev.cus;
+        p.grid = gemv_device::capped_grid(grid, p.block);
+        break;
+    }
+    case 5: {
+        if (P > 3 || p.stg != -1)
+            return GEMV_E_UNSUPPORTED;
+        p.xk = P;
+        const bool ok = P == 3   ? p.D == 3 && (p.waves == 4 || p.waves == 8)
+                        : P == 2 ? p.D == 2 && p.waves == 4
+                                 : (p.D == 1 || p.D == 2) && (p.waves == 4 || p.waves == 8);
+        if (!ok)
+            return GEMV_E_UNSUPPORTED;
+        finish_rows(M, dev.cus, &p);
+        break;
+    }
+    case 6: {
+        const int S = p.waves;
+        if (kind == kF16H || p.stg != -1 || p.cap != 0 || p.rows != 1 || !(S == 2 || S == 4 || S == 8 || S == 16) ||
+            2 * S > P || !(p.D == 2 || p.D == 4) || (int64_t)M * S * 64 > gemv_device::kMaxWorkItems)
+            return GEMV_E_UNSUPPORTED;
+        p.xk = S;
+        p.block = S * 64;
+        p.grid = M;
+        break;
+    }
+    default:
+        return GEMV_E_UNSUPPORTED;
+    }
+    *out = p;
+    return GEMV_OK;
 }
 
 int check_describe(int kind, int M, int N, const gemv_launch_info* info)
@@ -1023,6 +1136,39 @@ int gemv_describe_launch_for(int kind, int M, int N, int aligned, int cus, int l
         return GEMV_E_INVAL;
     gemv::fill_launch_info(kind, M, N, aligned != 0, gemv::Device{cus, lds_max}, info);
     return GEMV_OK;
+}
+
+int gemv_check_plan_for(int kind, int M, int N, int cus, int lds_max, const gemv_plan* plan, gemv_launch_info* info)
+{
+    if (plan == nullptr || info == nullptr || cus <= 0 || lds_max <= 0)
+        return GEMV_E_INVAL;
+    gemv::Plan p{};
+    if (int rc = gemv::plan_from_user(kind, M, N, gemv::Device{cus, lds_max}, *plan, &p); rc != GEMV_OK)
+        return rc;
+    gemv::info_of_plan(kind, M, N, p, info);
+    return GEMV_OK;
+}
+
+int gemv_launch_plan(int kind, const void* A, const uint16_t* scale, const void* x, float* y, int M, int N,
+                     const gemv_plan* plan, hipStream_t stream)
+{
+    if (plan == nullptr || A == nullptr || x == nullptr || y == nullptr ||
+        ((kind == gemv::kQ8 || kind == gemv::kQ4) && scale == nullptr))
+        return GEMV_E_INVAL;
+    if (!gemv::aligned16(A) || !gemv::aligned16(x))
+        return GEMV_E_INVAL;
+    gemv::Device dev{};
+    if (int rc = gemv_device::current(&dev); rc != GEMV_OK)
+        return rc;
+    gemv::Plan p{};
+    if (int rc = gemv::plan_from_user(kind, M, N, dev, *plan, &p); rc != GEMV_OK)
+        return rc;
+    const uint8_t* a8 = static_cast<const uint8_t*>(A);
+    const uint8_t* x8 = static_cast<const uint8_t*>(x);
+    void* args[] = {(void*)&a8, (void*)&scale, (void*)&x8, (void*)&y, (void*)&M, (void*)&N};
+    const hipError_t err = hipLaunchKernel(gemv::kernel_for(kind, p), dim3(p.grid), dim3(p.block), args,
+                                           (size_t)p.lds, stream);
+    return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
 }
 
 }  // extern "C"

@@ -66,6 +66,47 @@ int main(void)
         }
     }
     CHECK(plans > 70000);
+    /* explicit plans (gemv_check_plan_for): random plans, shapes and devices
+     * give a status and, when accepted, a launch within the limits */
+    long accepted = 0;
+    for (int it = 0; it < 200000; ++it) {
+        const int d = (int)(next() % 4);
+        const int kind = (int)(next() % 7) - (it % 50 == 0);   /* -1 and 6: invalid kinds */
+        const int M = (int)(next() % ((it % 3) == 0 ? (1u << 30) : 70000u));
+        int N = (int)(next() % ((it % 4) == 0 ? (1u << 30) : 140000u));
+        if (kind == 3 && it % 2)
+            N -= N % 128;
+        if (kind >= 0 && kind < 6 && it % 3)
+            N -= N % elems[kind];
+        /* fields drawn mostly from the accepted values, sometimes not */
+        static const int variants[] = {1, 2, 4, 5, 6, 2, 1, 0, 3, 7};
+        static const int waves[] = {4, 8, 2, 16, 4, 8, 12, 3, 0};
+        static const int depths[] = {4, 2, 8, 1, 3, 5, 4, 0, 6};
+        static const int rows[] = {1, 2, 4, 1, 0, -1};
+        static const int orders[] = {-1, 2, 1, 0, -1, 3, -2};
+        static const int caps[] = {0, 2, 3, 4, 0, 1, 6, -1};
+        const gemv_plan p = {variants[next() % 10], waves[next() % 9], depths[next() % 9], rows[next() % 6],
+                             orders[next() % 7], caps[next() % 8]};
+        gemv_launch_info info;
+        memset(&info, 0xAB, sizeof info);
+        const int rc = gemv_check_plan_for(kind, M, N, devices[d][0], devices[d][1], &p, &info);
+        CHECK(rc == GEMV_OK || rc == GEMV_E_UNSUPPORTED || rc == GEMV_E_INVAL);
+        if (rc != GEMV_OK)
+            continue;
+        ++accepted;
+        CHECK(info.variant == p.variant && info.units_in_flight == p.units_in_flight);
+        CHECK(info.grid >= 1 && (int64_t)info.grid * info.block <= ((int64_t)1 << 30));
+        CHECK(info.lds_bytes >= 0 && info.lds_bytes <= devices[d][1]);
+    }
+    CHECK(accepted > 100);
+    {
+        const gemv_plan ok = {2, 4, 4, 1, -1, 0};
+        gemv_launch_info info;
+        CHECK(gemv_check_plan_for(1, 4096, 4096, 256, 163840, NULL, &info) == GEMV_E_INVAL);
+        CHECK(gemv_check_plan_for(1, 4096, 4096, 256, 163840, &ok, NULL) == GEMV_E_INVAL);
+        CHECK(gemv_check_plan_for(1, 4096, 4096, 256, 163840, &ok, &info) == GEMV_OK);
+        CHECK(gemv_launch_plan(1, NULL, NULL, NULL, NULL, 4096, 4096, &ok, 0) == GEMV_E_INVAL);
+    }
     /* argument checks that return before any device call */
     gemv_launch_info info;
     CHECK(gemv_describe_launch_for(0, -1, 4, 1, 256, 163840, &info) == GEMV_E_INVAL);

@@ -243,13 +243,13 @@ def test_packed_short_rows_many_groups(gpu, oracle_mod, kind, N):
 
 @pytest.mark.parametrize("kind,N,M", [("q8", 512, 40000 + 1), ("q4", 1024, 40000 + 1), ("q4", 128, 140000 + 5),
                                       ("q8", 16, 600000 + 7)])
-def test_packed_waves_walk_several_groups(gpu, oracle_mod, kind, N, M):
-    # more than 32 row groups per CU: each wave walks four groups with two
-    # loads in flight (the steady-state loop), the last groups ragged
+def test_packed_waves_take_two_groups(gpu, oracle_mod, kind, N, M):
+    # more than 16 row groups per CU: each wave takes two groups, both in
+    # flight, the last groups ragged
     nchunks = N // (16 if kind == "q8" else 32)
     R = 64 // (1 << (nchunks - 1).bit_length())
     info = binding.describe_launch(kind, M, N)
-    assert info["variant"] == 4 and info["units_in_flight"] == 2 and info["rows_per_wave"] == 4 * R, info
+    assert info["variant"] == 4 and info["units_in_flight"] == 2 and info["rows_per_wave"] == 2 * R, info
     ops = inputs.make(kind, M, N, seed=M)
     _check(oracle_mod, kind, ops, f"{kind} packed multi-group M={M} N={N} {info}")
 

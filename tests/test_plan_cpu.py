@@ -280,9 +280,27 @@ def test_cost_model_replaces_plans_the_measurements_beat():
     assert _geometry(plan("f16", 278, 16896)) == (6, 278, 256, 4, 1)
     assert _geometry(plan("f32", 902, 5248)) == (2, 226, 256, 8, 1)
     assert _geometry(plan("f16", 774, 24704)) == (2, 194, 256, 8, 1)
-    # the other formats keep the rules alone
-    assert plan("f16x32", 5484, 4608)["variant"] == 2
+    # the other formats keep the measured rules alone
     assert plan("f16_acc16", 2552, 9088)["variant"] == 2
+    assert plan("f16x32", 2562, 14336)["variant"] == 1
+
+
+def test_rules_remeasured_by_brute_force():
+    # Rules the same brute-force search changed (graph-timed us, before ->
+    # after): FP16 with FP32 x, rows of 4-11 units, many rows: staged, 4
+    # waves, split staging, at most 2 workgroups per CU (5484x4608 13.25 ->
+    # 9.67); INT4 rows of 2-3 units: at most 4 workgroups per CU (14336x4096
+    # 7.52 -> 7.30); packed short rows beyond 16 groups per CU: two groups
+    # per wave (INT4 40979x512 5.73 -> 4.79); INT8 rows of 8-10 units: 4
+    # waves, two rows per wave, split staging (8192x8192 12.11 -> 11.65)
+    p = plan("f16x32", 5484, 4608)
+    assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 256, 2, 4, 512)
+    p = plan("q4", 14336, 4096)
+    assert (p["variant"], p["block"], p["stage_order"], p["grid"]) == (1, 512, 2, 4 * 256)
+    p = plan("q4", 40979, 512)
+    assert (p["variant"], p["units_in_flight"], p["rows_per_wave"]) == (4, 2, 2 * 4)
+    p = plan("q8", 8192, 8192)
+    assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 256, 2, 4, 1024)
 
 
 def test_plan_cache_gives_the_same_plans():
@@ -358,3 +376,72 @@ def test_fp_kernel_occupancy_matches_the_cost_model():
         assert waves == want, (name, v)
         seen += 1
     assert seen >= 40, seen
+
+
+# ---------------------------------------------------------------- explicit plans (gemv_check_plan_for)
+def check(kind, M, N, plan, cus=256, lds_max=160 * 1024):
+    return binding.check_plan_for(kind, M, N, cus, lds_max, plan)
+
+
+def test_planner_plans_as_explicit_plans():
+    # the planner's choices, written as explicit plans, make the same launch
+    for kind, M, N, p in (("f16", 8192, 8192, (2, 8, 8, 1, -1, 0)), ("q8", 8192, 8192, (1, 4, 4, 2, 2, 0)),
+                             ("q4", 14336, 4096, (1, 8, 2, 1, 2, 4)), ("f16", 2552, 9088, (6, 2, 2, 1, -1, 0)),
+                             ("q4", 14336, 512, (4, 8, 1, 1, -1, 0)), ("f16", 14336, 512, (2, 8, 4, 4, -1, 0)),
+                             ("f16x32", 5484, 4608, (1, 4, 4, 1, 2, 2)), ("q8", 1000, 16400, (6, 2, 2, 1, -1, 0))):
+        assert check(kind, M, N, p) == plan(kind, M, N), (kind, M, N, p)
+
+
+def test_explicit_plans_the_library_has_no_kernel_for():
+    for kind, M, N, p in (
+            ("f16", 4096, 4096, (1, 8, 8, 1, 0, 0)),     # FP16 reads x with each unit: no staged kernel
+            ("f16", 4096, 4096, (2, 12, 4, 1, -1, 0)),   # no 12-wave streaming kernel
+            ("f16", 4096, 4096, (2, 4, 3, 1, -1, 0)),    # 3 in flight: INT4 staged rows only
+            ("f16", 4096, 4096, (2, 4, 4, 1, 1, 0)),     # a stage order without staging
+            ("q8", 4096, 4096, (1, 4, 4, 1, 3, 0)),      # stage orders are 0-2
+            ("q8", 4096, 4096, (1, 4, 5, 1, 0, 0)),      # 5 in flight: INT8 split staging only
+            ("f16", 4096, 4096, (5, 4, 2, 1, -1, 0)),    # x in registers: rows of 1-3 units only
+            ("f16", 4096, 1024, (5, 8, 2, 1, -1, 0)),    # two-unit rows: 4 waves only
+            ("f16", 4096, 4096, (4, 8, 1, 1, -1, 0)),    # packed rows: INT8/INT4 only
+            ("q8", 4096, 1024, (4, 8, 1, 1, -1, 0)),     # packed rows: at most 32 chunks
+            ("f16", 4096, 4096, (6, 8, 2, 1, -1, 0)),    # split rows: at least two units per wave
+            ("f16", 4096, 4096, (6, 3, 2, 1, -1, 0)),    # waves per row: 2, 4, 8 or 16
+            ("f16", 4096, 8192, (6, 2, 8, 1, -1, 0)),    # split rows: 2 or 4 in flight
+            ("f16_acc16", 4096, 8192, (6, 2, 2, 1, -1, 0)),   # FP16 accumulation: variants 2 and 5
+            ("q8", 4096, 98304, (1, 4, 4, 1, 1, 0)),     # staged x beyond the LDS a workgroup may hold
+            ("f16", 4096, 4100, (2, 4, 4, 1, -1, 0)),    # not a multiple of the chunk: element-wise only
+            ("f16", 4096, 4096, (7, 4, 4, 1, -1, 0)), ("f16", 4096, 4096, (2, 4, 4, 0, -1, 0)),
+            ("f16", 4096, 4096, (2, 4, 4, 1, -1, -1))):
+        assert check(kind, M, N, p) is None, (kind, M, N, p)
+    with pytest.raises(GemvError):
+        check("f16", 0, 4096, (2, 4, 4, 1, -1, 0))
+    with pytest.raises(GemvError):
+        check("f16", 4096, 4096, (2, 4, 4, 1, -1, 0), cus=0)
+
+
+def test_every_candidate_plan_keeps_the_invariants():
+    # the plan search's candidates that the library accepts, over seeded
+    # shapes and devices: within the dispatch limit and the device's LDS,
+    # every row covered, split rows one workgroup per row
+    import numpy as np
+
+    import bench
+
+    rng = np.random.default_rng(11)
+    for _ in range(60):
+        kind = KINDS[rng.integers(len(KINDS))]
+        M = int(np.exp(rng.uniform(0, np.log(1 << 22))))
+        N = max(128, int(np.exp(rng.uniform(np.log(64), np.log(1 << 17)))) // 128 * 128)
+        dev = dict(cus=int(rng.choice([80, 256, 304])), lds_max=int(rng.choice([64, 160]) * 1024))
+        for p in bench.plan_candidates(kind, N):
+            info = check(kind, M, N, p, **dev)
+            if info is None:
+                continue
+            where = (kind, M, N, dev, p, info)
+            assert info["variant"] == p[0] and info["units_in_flight"] == p[2], where
+            assert 1 <= info["grid"] and info["grid"] * info["block"] <= 1 << 30, where
+            assert info["lds_bytes"] <= dev["lds_max"], where
+            if p[0] == 6:
+                assert info["grid"] == M and info["block"] == 64 * p[1], where
+            elif p[0] != 4:
+                assert info["grid"] * (info["block"] // 64) * info["rows_per_wave"] >= M, where
