@@ -519,8 +519,9 @@ def plan_search(count, seed, rounds=3, launches=48):
     gemv_check_plan_for) and the library's own plan, each as a graph of
     `launches` launches over a >= 1 GiB ring, best of `rounds`.  Prints one
     JSON line per shape (the library's plan, the fastest candidate, their
-    ratio) and a per-format summary: how far the planner's choice sits from
-    the best plan the library could have launched."""
+    ratio, every candidate's time) and a per-format summary: how far the
+    planner's choice sits from the best plan the library could have
+    launched."""
     import math
 
     import torch
@@ -562,7 +563,7 @@ def plan_search(count, seed, rounds=3, launches=48):
         info = binding.describe_launch(kind, M, N, True)
         row = {"kind": kind, "M": M, "N": N, "lib_us": round(t_lib * 1e6, 3), "best_us": round(best_t * 1e6, 3),
                "lib_over_best": round(t_lib / best_t, 4), "lib_plan": info, "best_plan": list(best_plan),
-               "candidates": len(cands)}
+               "candidates": len(cands), "all_us": [[list(p), round(t * 1e6, 3)] for t, p in cands]}
         rows.append(row)
         print(json.dumps(row), flush=True)
         ring.free()
@@ -851,8 +852,9 @@ def plan_search(count, seed, rounds=3, launches=48):
     gemv_check_plan_for) and the library's own plan, each as a graph of
     `launches` launches over a >= 1 GiB ring, best of `rounds`.  Prints one
     JSON line per shape (the library's plan, the fastest candidate, their
-    ratio) and a per-format summary: how far the planner's choice sits from
-    the best plan the library could have launched."""
+    ratio, every candidate's time) and a per-format summary: how far the
+    planner's choice sits from the best plan the library could have
+    launched."""
     import math
 
     import torch
@@ -894,7 +896,7 @@ def plan_search(count, seed, rounds=3, launches=48):
         info = binding.describe_launch(kind, M, N, True)
         row = {"kind": kind, "M": M, "N": N, "lib_us": round(t_lib * 1e6, 3), "best_us": round(best_t * 1e6, 3),
                "lib_over_best": round(t_lib / best_t, 4), "lib_plan": info, "best_plan": list(best_plan),
-               "candidates": len(cands)}
+               "candidates": len(cands), "all_us": [[list(p), round(t * 1e6, 3)] for t, p in cands]}
         rows.append(row)
         print(json.dumps(row), flush=True)
         ring.free()

@@ -285,17 +285,23 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
     }
     const int nchunks = N / epc;
     const int P = (nchunks + 63) / 64;
-    if ((kind == kQ8 || kind == kQ4) && nchunks <= kPackedMaxChunks) {
-        const int R = packed_rows_per_load(nchunks);
-        const int64_t groups = ((int64_t)M + R - 1) / R;
+    // row groups of a packed launch (rows of at most 32 chunks only)
+    const int64_t packed_groups = nchunks <= kPackedMaxChunks
+                                      ? ((int64_t)M + packed_rows_per_load(nchunks) - 1) / packed_rows_per_load(nchunks)
+                                      : 0;
+    if ((kind == kQ8 || kind == kQ4) && nchunks <= kPackedMaxChunks && packed_groups > 3 * (int64_t)cus) {
+        // more than 3 row groups per CU (fewer: x in registers, a wave per
+        // row, was 5-18 % faster on 12 such shapes)
+        const int64_t groups = packed_groups;
         const int64_t per_cu = (groups + cus - 1) / cus;
         p.variant = 4;
         p.waves = 8;
-        // one group per wave up to 16 per CU, else two, both in flight
-        // (four groups per wave, two rounds of two, measured slower: INT4
-        // 40979 x 512 5.73 -> 4.79 us, INT8 30962 x 384 4.87 -> 4.67)
+        // one group per wave up to 16 per CU, two (both in flight) up to 80,
+        // beyond that four, two rounds of two (four groups per wave lost
+        // below 80 per CU: INT4 40979 x 512 5.73 -> 4.79 us, INT8 30962 x
+        // 384 4.87 -> 4.67; won above: INT4 61267 x 896 9.28 -> 8.32)
         p.D = per_cu <= 16 ? 1 : 2;
-        p.rows = p.D;
+        p.rows = per_cu <= 80 ? p.D : 4;
         p.stg = -1;   // x goes straight to registers
         p.lds = 0;
         p.block = p.waves * 64;
@@ -341,7 +347,9 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.waves = 8;
             p.cap = 3;
         } else {
-            p.waves = kind == kF16X32 ? 4 : 8;
+            // 4 waves: with 8, few INT4 rows left most CUs idle (328 x 5248
+            // 3.42 -> 2.81 us)
+            p.waves = 4;
         }
     } else if (fp) {
         p.variant = 2;
@@ -379,7 +387,18 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
         const int64_t lds = lds_bytes(kind, nchunks);
         const bool fits = lds <= kLdsBytes && lds <= dev.lds_max;
         p.rows = 1;
-        if (fits && P >= 24) {
+        if (fits && P >= 12 && M > 8 * cus && M <= 14 * cus) {
+            // rows of 12 units and more, 8-14 rows per CU: 8 waves, 4 in
+            // flight, two rows per wave (fewer stagings of x), split staging,
+            // no cap.  Brute force over every plan on 7 such shapes (8-13
+            // rows per CU): at most 3.4 % from the fastest, against 2.6-19.5 %
+            // (2111 x 8704 11.21 -> 9.38 us, 3046 x 12672 15.93 -> 14.09)
+            p.variant = 1;
+            p.waves = 8;
+            p.D = 4;
+            p.stg = 2;
+            p.rows = 2;
+        } else if (fits && P >= 24) {
             // two rows per wave where that pads less (8192 x 12800
             // 35.36 -> 33.65 us, 4096 x 15360 22.89 -> 21.92)
             p.variant = 1;
@@ -397,13 +416,13 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.D = P % 8 == 0 ? 8 : 4;
             p.stg = P % 8 == 0 ? 0 : 2;
             p.cap = 3;
-        } else if (fits && P >= 4 && M > 16 * cus) {
-            // rows of 4-11 units, many of them: staged x, 4 waves, 4 in
+        } else if (fits && P >= 4 && M > 8 * cus) {
+            // rows of 4-11 units, more than 8 per CU: staged x, 4 waves, 4 in
             // flight, split staging, at most 2 workgroups per CU.  Brute
-            // force over every plan on 9 such shapes: 1.6 % from the fastest
-            // (geometric mean), against 11 % for x read with each unit below
+            // force over every plan on 11 such shapes: 1.4 % from the fastest
+            // (geometric mean), against 12 % for x read with each unit below
             // 8192 rows and A first above (5484 x 4608 13.25 -> 9.67 us,
-            // 9614 x 2048 9.00 -> 8.04)
+            // 3468 x 4480 10.23 -> 7.34, 9614 x 2048 9.00 -> 8.04)
             p.variant = 1;
             p.waves = 4;
             p.D = 4;
@@ -456,9 +475,10 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.cap = two ? 2 : 1;
         } else if (P == 2 && M <= 16 * cus) {
             // few rows of two units: x read with each unit (no staging, no
-            // barrier), 8 waves, 2 in flight
+            // barrier), 4 waves, 2 in flight (8 waves: 1.7 % slower on 7
+            // shapes, 2115 x 2048 3.24 -> 3.09 us)
             p.variant = 2;
-            p.waves = 8;
+            p.waves = 4;
             p.D = 2;
         } else if (P >= 8 && M <= 4 * cus) {
             // rows of 8-32 units, at most 4 per CU: 8 waves, x staged before
@@ -468,9 +488,10 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.cap = 1;
         } else if (P <= 16 && M <= 8 * cus) {
             // few rows (one GPU's share of a row-split matrix): x read with
-            // each unit, 8 waves, 4 in flight
+            // each unit, 4 in flight; 8 waves, 4 below 4 rows per CU (so
+            // that every CU gets a workgroup: 736 x 2560 2.97 -> 2.54 us)
             p.variant = 2;
-            p.waves = 8;
+            p.waves = M < 4 * cus ? 4 : 8;
         } else if (P >= 8) {
             // rows of 8-31 units, many of them: 4 waves, split staging; rows
             // of 8-10 units two per wave with no cap where that still gives
@@ -499,17 +520,12 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             // most 3 workgroups per CU for rows of 3-5 units, 5 in flight for
             // rows of 5 (no padding: 14336 x 5120 13.28 -> 12.86 us; rows of
             // 3: 10225 x 2304 7.35 -> 6.21, 3564 x 2064 4.81 -> 3.72); rows of
-            // 6 and 7 units: 8 waves, A first, at most 2 workgroups per CU
-            // (16384 x 6144 17.4 -> 16.2 us, 8192 x 6144 9.9 -> 9.0)
-            if (P <= 5) {
-                p.waves = 4;
-                p.stg = 2;
-                p.cap = 3;
-                p.D = P == 5 ? 5 : 4;
-            } else {
-                p.waves = 8;
-                p.cap = 2;
-            }
+            // 6 and 7 units at most 4 (against 8 waves, A first, at most 2:
+            // 4525 x 6912 8.94 -> 7.15 us, 5744 x 6400 9.35 -> 8.28)
+            p.waves = 4;
+            p.stg = 2;
+            p.cap = P <= 5 ? 3 : 4;
+            p.D = P == 5 ? 5 : 4;
         }
     } else if (const int64_t lds = lds_bytes(kind, nchunks); lds > dev.lds_max || M <= 4 * cus) {
         // INT4 rows whose staged x would not fit a workgroup, or at most 4

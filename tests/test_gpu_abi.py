@@ -181,7 +181,8 @@ def test_describe_launch_fills_all_cus(gpu):
     # hold
     assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 1
     assert binding.describe_launch("f16x32", 14336, 4096)["variant"] == 1
-    assert binding.describe_launch("f16x32", 4096, 4096)["variant"] == 2
+    assert binding.describe_launch("f16x32", 4096, 4096)["variant"] == 1
+    assert binding.describe_launch("f16x32", 8 * cus, 4096)["variant"] == 2   # 8 rows per CU: x per unit
     info = binding.describe_launch("f16x32", 4 * cus, 32768)
     assert info["variant"] == 1 and info["lds_bytes"] == 4 * 32768 <= lds_max, info
     assert binding.describe_launch("f16x32", 16 * cus, lds_max // 4 + 512)["variant"] == 2

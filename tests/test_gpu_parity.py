@@ -175,12 +175,12 @@ def test_two_rows_per_wave_where_that_pads_less(gpu, oracle_mod, kind, M, N):
     _check(oracle_mod, kind, ops, f"{kind} two rows per wave M={M} N={N} {info}")
 
 
-@pytest.mark.parametrize("M,N,block,stg", [(16384 + 3, 6144, 512, 0), (9000, 7168 - 16, 512, 0),
+@pytest.mark.parametrize("M,N,block,stg", [(16384 + 3, 6144, 256, 2), (9000, 7168 - 16, 256, 2),
                                            (12000, 3072 - 16, 256, 2)])
 def test_int8_rows_of_3_6_7_units(gpu, oracle_mod, M, N, block, stg):
-    # many INT8 rows of 6 or 7 units: 8 waves, A first, at most 2 workgroups
-    # per CU; of 3 units: 4 waves, split staging, at most 3 per CU; waves
-    # walk several rows (ragged passes too)
+    # many INT8 rows of 3, 6 or 7 units: 4 waves, split staging, at most 3
+    # (rows of 3 units) or 4 workgroups per CU; waves walk several rows
+    # (ragged passes too)
     info = binding.describe_launch("q8", M, N)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert (info["variant"], info["block"], info["stage_order"]) == (1, block, stg), info
@@ -232,9 +232,10 @@ def test_x_in_registers_many_rows(gpu, oracle_mod, kind, M, N):
 @pytest.mark.parametrize("kind,N", [("q8", 16), ("q8", 48), ("q8", 272), ("q8", 512),
                                     ("q4", 128), ("q4", 384), ("q4", 640), ("q4", 1024)])
 def test_packed_short_rows_many_groups(gpu, oracle_mod, kind, N):
-    # rows of at most 32 chunks share wave loads: enough rows for every wave
-    # of a full grid, and a last group only partly filled
-    M = 14336 + 3
+    # rows of at most 32 chunks share wave loads (with more than 3 row
+    # groups per CU): enough rows for every wave of a full grid, and a last
+    # group only partly filled
+    M = 14336 + 3 if N > 16 else 65536 + 3
     info = binding.describe_launch(kind, M, N)
     assert info["variant"] == 4, info
     ops = inputs.make(kind, M, N, seed=N)

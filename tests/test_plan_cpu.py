@@ -23,6 +23,12 @@ def staged_bytes(kind, N):
     return (nchunks + 63) // 64 * 64 * X_GRANULES[kind] * 16
 
 
+def _fewer_stagings(kind, M, p, cus):
+    # FP16 with FP32 x, 8-14 rows per CU: two rows per wave staged, fewer
+    # workgroups than CUs (fewer stagings of x measured faster)
+    return kind == "f16x32" and p["variant"] == 1 and p["rows_per_wave"] >= 2 and M <= 14 * cus
+
+
 _MS = [1, 7, 64, 255, 1000, 1024, 1025, 2048, 4096, 8192, 14336, 40000, 300000, (1 << 24) + 3]
 _NS = [0, 3, 8, 16, 128, 256, 512, 1000, 1024, 1536, 2048, 4096, 8192, 14336, 16384, 20480, 32768, 34816, 49152,
        65536, 81920, 98304]
@@ -57,7 +63,7 @@ def test_every_plan_is_consistent(kind, dev):
             assert p["stage_order"] in (0, 1, 2), where
         else:
             assert p["lds_bytes"] == 0 and p["stage_order"] == -1, where
-        if p["variant"] in (1, 2) and M >= 8 * dev["cus"]:
+        if p["variant"] in (1, 2) and M >= 8 * dev["cus"] and not _fewer_stagings(kind, M, p, dev["cus"]):
             assert p["grid"] >= dev["cus"], where                 # every CU gets a workgroup
         if p["variant"] == 5:
             assert 1 <= -(-(N // ELEMS_PER_CHUNK[kind]) // 64) <= 3, where   # rows of one to three units
@@ -100,7 +106,7 @@ def test_random_shapes_keep_the_invariants():
         assert p["lds_bytes"] <= dev["lds_max"], where
         if p["variant"] != 4:
             assert p["grid"] * (p["block"] // 64) * p["rows_per_wave"] >= M, where
-        if p["variant"] in (1, 2) and M >= 8 * dev["cus"]:
+        if p["variant"] in (1, 2) and M >= 8 * dev["cus"] and not _fewer_stagings(kind, M, p, dev["cus"]):
             assert p["grid"] >= dev["cus"], where
 
 
