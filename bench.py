@@ -815,103 +815,6 @@ def ascii_roofline(study, width=72, height=22):
     return "\n".join(lines)
 
 
-def plan_candidates(kind, N):
-    """Every explicit plan (variant, waves, units in flight, rows per wave,
-    stage order, cap) the library holds a kernel for at row length N, over
-    the ranges its planner chooses from; gemv_check_plan_for drops those that
-    do not fit a given shape and device."""
-    epc = {"f32": 4, "f16": 8, "f16_acc16": 8, "f16x32": 8, "q8": 16, "q4": 32}[kind]
-    nchunks = N // epc
-    P = -(-nchunks // 64)
-    fp = kind in ("f32", "f16", "f16_acc16")
-    out = []
-    if P == 1:
-        out += [(5, w, d, r, -1, cap) for w in (4, 8) for d in (1, 2) for r in (1, 2) for cap in (0, 3)]
-    elif P == 2:
-        out += [(5, 4, 2, 1, -1, cap) for cap in (0, 3, 6)]
-    elif P == 3:
-        out += [(5, w, 3, 1, -1, cap) for w in (4, 8) for cap in (0, 3)]
-    if kind in ("q8", "q4") and nchunks <= 32:
-        out += [(4, 8, d, r, -1, 0) for d, r in ((1, 1), (1, 2), (2, 2), (2, 4), (1, 4))]
-    out += [(2, w, d, r, -1, 0) for w in (4, 8) for d in (2, 4, 8) for r in ((1, 2, 4) if fp else (1, 2))]
-    if not fp:
-        out += [(1, w, d, r, stg, cap) for w in (4, 8) for d in (2, 4, 8) for stg in (0, 1, 2)
-                for r, cap in ((1, 0), (2, 0), (1, 1), (1, 2), (1, 3), (1, 4))]
-        if kind == "q8":
-            out += [(1, 4, 5, 1, 2, cap) for cap in (0, 2, 3)]
-        if kind == "q4":
-            out += [(1, 4, d, 1, 1, cap) for d in (3, 5) for cap in (0, 2, 3)]
-    if kind != "f16_acc16":
-        out += [(6, S, d, 1, -1, 0) for S in (2, 4, 8, 16) if 2 * S <= P for d in (2, 4)]
-    return out
-
-
-def plan_search(count, seed, rounds=3, launches=48):
-    """Brute force over the plans: on each seeded random shape
-    (sweep_shapes), every candidate plan that fits (plan_candidates,
-    gemv_check_plan_for) and the library's own plan, each as a graph of
-    `launches` launches over a >= 1 GiB ring, best of `rounds`.  Prints one
-    JSON line per shape (the library's plan, the fastest candidate, their
-    ratio, every candidate's time) and a per-format summary: how far the
-    planner's choice sits from the best plan the library could have
-    launched."""
-    import math
-
-    import torch
-
-    from memory_bound_gemv_row_amd import binding
-
-    props = torch.cuda.get_device_properties(0)
-    cus, lds_max = props.multi_processor_count, props.shared_memory_per_block
-    rows = []
-    for kind, M, N in sweep_shapes(count, seed):
-        ring = Ring(kind, M, N, zero_operands(kind, M, N))
-        sh = torch.cuda.current_stream().cuda_stream
-        for i in range(16):   # warm the clocks before the first timing
-            ring.launch(i, sh)
-        torch.cuda.synchronize()
-
-        def timed(launch_one):
-            g = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                with torch.cuda.graph(g, stream=s):
-                    for i in range(launches):
-                        launch_one(i, torch.cuda.current_stream().cuda_stream)
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            return min(time_graph(g, launches) for _ in range(rounds))
-
-        t_lib = timed(ring.launch)
-        cands = []
-        for plan in plan_candidates(kind, N):
-            if binding.check_plan_for(kind, M, N, cus, lds_max, plan) is None:
-                continue
-            cands.append((timed(lambda i, h, plan=plan: ring.launch_plan(i, h, plan)), plan))
-        t_lib = min(t_lib, timed(ring.launch))   # again after the candidates: the better of the two
-        best_t, best_plan = min(cands)
-        info = binding.describe_launch(kind, M, N, True)
-        row = {"kind": kind, "M": M, "N": N, "lib_us": round(t_lib * 1e6, 3), "best_us": round(best_t * 1e6, 3),
-               "lib_over_best": round(t_lib / best_t, 4), "lib_plan": info, "best_plan": list(best_plan),
-               "candidates": len(cands), "all_us": [[list(p), round(t * 1e6, 3)] for t, p in cands]}
-        rows.append(row)
-        print(json.dumps(row), flush=True)
-        ring.free()
-        torch.cuda.empty_cache()
-    summary = {}
-    for kind in SWEEP_KINDS:
-        r = sorted((x for x in rows if x["kind"] == kind), key=lambda x: x["lib_over_best"])
-        if r:
-            geo = math.exp(sum(math.log(x["lib_over_best"]) for x in r) / len(r))
-            summary[kind] = {"shapes": len(r), "geomean_lib_over_best": round(geo, 4),
-                             "median_lib_over_best": r[len(r) // 2]["lib_over_best"],
-                             "worst_lib_over_best": r[-1]["lib_over_best"], "worst_shape": f"{r[-1]['M']}x{r[-1]['N']}"}
-    print(json.dumps({"plan_search": summary, "seed": seed, "count": count}), flush=True)
-
-
 # ---------------------------------------------------------------- quantiser / softmax on their own
 def op_main(args):
     """--op: the quantiser or the softmax at one shape.  With --profile: one
