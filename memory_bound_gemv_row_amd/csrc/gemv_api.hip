@@ -73,9 +73,9 @@ struct Plan {
 };
 
 // Split rows (variant 6), chosen after the one-wave-per-row plan p0: where
-// p0 leaves the CUs short of waves (fewer than 4 per CU for FP32/FP16 and
-// FP16 with FP32 x, 8 for FP32/FP16 rows of 16 units and more, 3 for INT8,
-// 2 for INT4) and the rows are at least 4 units long (INT4: at most 16,
+// p0 leaves the CUs short of waves (fewer than 4 per CU for FP32/FP16, 8
+// for FP32/FP16 rows of 16 units and more, 2 for INT4) and the rows are at
+// least 4 units long (INT4: at most 16,
 // whose x, read with each unit, is four times the bytes of its A), S waves
 // share each row, S the least power of two that gives every CU
 // kSplitWavesPerCu waves (at most 16, and at least two units per wave);
@@ -85,9 +85,9 @@ struct Plan {
 // 43.04 -> 29.95, FP16 278x16896 8.34 -> 5.42, FP16 1024x14336
 // 7.89 -> 6.79, INT8 560x6656 4.02 -> 3.00, INT4 363x8704 4.08 -> 3.32;
 // where p0 already fills the CUs it won (FP16 1792x4096 4.09 vs 4.19,
-// FP32 1024x1024 2.52 vs 2.66, FP16 1024x4096 3.09 vs 3.29, FP16 with FP32
-// x 1500x8192 6.63 vs 7.10, INT8 1500x10240 5.57 vs 6.18), and INT4 rows
-// of 18 units lost to it by 60 %.
+// FP32 1024x1024 2.52 vs 2.66, FP16 1024x4096 3.09 vs 3.29), and INT4 rows
+// of 18 units lost to it by 60 %.  INT8 and FP16 with FP32 x have rules of
+// their own (below), which the brute-force search measured.
 // INT8 (since its exact decode) splits up to 6 rows per CU, with S for 4
 // waves per CU and 2 units in flight: brute force over every plan on 17
 // such shapes put this 1.7 % from the fastest (geometric mean; 8 % at
@@ -106,6 +106,17 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
             return false;
         target = 4 * (int64_t)cus;
         depth = 2;
+    } else if (kind == kF16X32) {
+        // up to 7 rows per CU (rows of 16 units and more: 5, above which
+        // staged x measured up to 26 % faster: 1702 x 23168 19.79 -> 15.05
+        // us), two waves per row (the fewest), 4 in flight below 2 rows per
+        // CU, else 2, where S for 16 waves per CU was up to 31 % from the
+        // fastest plan (1492 x 5120 6.26 -> 5.11 us, 410 x 24448 7.80 ->
+        // 6.74, 977 x 27392 15.19 -> 11.92)
+        if (M > (P < 16 ? 7 : 5) * cus)
+            return false;
+        target = 0;
+        depth = M < 2 * cus ? 4 : 2;
     } else {
         // FP32/FP16 rows of 16 units and more up to 8 waves per CU (x is
         // one granule per unit); otherwise 4, INT4 2 (x per unit is four
@@ -161,16 +172,6 @@ void least_padding(int P, bool two_rows_fill, int* D, int* rows)
     }
     *D = order[best][0];
     *rows = order[best][1];
-}
-
-// Rows per wave (1 or 2) for rows of P units at D in flight: whichever pads
-// each wave's stream less, one row on a tie or where two rows per wave
-// would leave CUs without a workgroup (two_rows_fill false).
-int rows_for_depth(int P, int D, bool two_rows_fill)
-{
-    const int pad1 = (P + D - 1) / D * D - P;
-    const int pad2 = (2 * P + D - 1) / D * D - 2 * P;
-    return two_rows_fill && pad2 < 2 * pad1 ? 2 : 1;   // pad2 / 2P < pad1 / P
 }
 
 // Whether M rows at two per wave, `waves` waves per workgroup, still give
@@ -384,8 +385,9 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.rows = (4 + P - 1) / P;
         }
     } else if (kind == kF16X32) {
+        // (up to 7 rows per CU of 4 units and more: split rows, split_plan)
         const int64_t lds = lds_bytes(kind, nchunks);
-        const bool fits = lds <= kLdsBytes && lds <= dev.lds_max;
+        const bool fits = lds <= dev.lds_max;
         p.rows = 1;
         if (fits && P >= 12 && M > 8 * cus && M <= 14 * cus) {
             // rows of 12 units and more, 8-14 rows per CU: 8 waves, 4 in
@@ -398,49 +400,34 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
             p.D = 4;
             p.stg = 2;
             p.rows = 2;
-        } else if (fits && P >= 24) {
-            // two rows per wave where that pads less (8192 x 12800
-            // 35.36 -> 33.65 us, 4096 x 15360 22.89 -> 21.92)
+        } else if (fits && P == 16) {
+            // rows of 16 units: 8 waves, 8 in flight, A first, at most 3
+            // workgroups per CU (8192 x 8192 22.45 us, against 22.66 for
+            // the rule below)
             p.variant = 1;
             p.waves = 8;
-            p.D = 4;
-            p.stg = 2;
-            p.rows = rows_for_depth(P, 4, two_rows_fill(M, 8, cus));
-        } else if (fits && P >= 12) {
-            // 8 waves, at most 3 workgroups per CU; 8 in flight, A first,
-            // for rows of 16 units, else 4 in flight with split staging (a
-            // row of 12 or 20 units would pad to 16 or 24: 4096 x 6144
-            // 11.61 -> 9.30 us, 4096 x 10240 16.51 -> 14.35)
-            p.variant = 1;
-            p.waves = 8;
-            p.D = P % 8 == 0 ? 8 : 4;
-            p.stg = P % 8 == 0 ? 0 : 2;
+            p.D = 8;
+            p.stg = 0;
             p.cap = 3;
-        } else if (fits && P >= 4 && M > 8 * cus) {
-            // rows of 4-11 units, more than 8 per CU: staged x, 4 waves, 4 in
-            // flight, split staging, at most 2 workgroups per CU.  Brute
-            // force over every plan on 11 such shapes: 1.4 % from the fastest
-            // (geometric mean), against 12 % for x read with each unit below
-            // 8192 rows and A first above (5484 x 4608 13.25 -> 9.67 us,
-            // 3468 x 4480 10.23 -> 7.34, 9614 x 2048 9.00 -> 8.04)
+        } else if (fits && P >= 4) {
+            // staged x, 4 waves, split staging; rows of 11 units and more 8
+            // in flight, shorter ones 4; at most 2 workgroups per CU, one
+            // for rows of 16 units and more.  Brute force over every plan
+            // on 120 seeded random shapes (these rules and the split rows
+            // together): 2.3 % from the fastest (geometric mean; 9.5 % at
+            // worst), against 4.1 % (31 %) for the rules before, which took
+            // 8 waves for rows of 12 units and more (12815 x 14720 63.57 ->
+            // 57.20 us, 4137 x 19968 32.51 -> 30.01)
             p.variant = 1;
             p.waves = 4;
-            p.D = 4;
             p.stg = 2;
-            p.cap = 2;
+            p.D = P >= 11 ? 8 : 4;
+            p.cap = P >= 16 ? 1 : 2;
         } else if (fits && M >= 8192) {
             p.variant = 1;
             p.waves = 4;
             p.D = 8;
             p.cap = 4;
-        } else if (lds <= dev.lds_max && P > 32) {
-            // staged x past 64 KiB: 8 waves, 4 in flight, x staged before
-            // A, one workgroup per CU
-            p.variant = 1;
-            p.waves = 8;
-            p.D = 4;
-            p.stg = 1;
-            p.cap = 1;
         } else {
             p.variant = 2;
             // 4 waves; rows of 8 units or more: two per wave, 8 in flight;

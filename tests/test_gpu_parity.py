@@ -76,16 +76,16 @@ def test_many_passes_and_row_groups(gpu, oracle_mod, kind, N):
     _check(oracle_mod, kind, ops, f"{kind} tiles N={N}")
 
 
-@pytest.mark.parametrize("kind,N", [("q8", 2048), ("q8", 4096 + 16), ("q4", 2048 + 128), ("q4", 14336),
-                                    ("f16x32", 1024), ("f16x32", 8192 + 8)])
-def test_waves_walk_several_rows(gpu, oracle_mod, kind, N):
-    # grids capped per CU: each wave walks two or three rows, the last ones
+@pytest.mark.parametrize("kind,N,walk", [("q8", 2048, 2), ("q8", 4096 + 16, 2), ("q4", 2048 + 128, 2), ("q4", 14336, 2),
+                                         ("f16x32", 1024, 2), ("f16x32", 8192 + 8, 4)])
+def test_waves_walk_several_rows(gpu, oracle_mod, kind, N, walk):
+    # grids capped per CU: each wave walks `walk` rows and more, the last ones
     # ragged across waves
     # (the cap can depend on M, so settle M against the plan it gets)
     M = 1 << 20
     for _ in range(4):
         probe = binding.describe_launch(kind, M, N)
-        M = probe["grid"] * probe["block"] // 64 * 2 + 37
+        M = probe["grid"] * probe["block"] // 64 * walk + 37
     info = binding.describe_launch(kind, M, N)
     assert info["rows_per_wave"] >= 3, info
     ops = inputs.make(kind, M, N, seed=11)
@@ -122,11 +122,12 @@ _LONG_ROWS = [
     ("q4", 300, 82048, 2, -1),    # staged x would not fit a workgroup
     ("q8", 1000, 16400, 6, -1),   # rows of 17 units, few of them: split rows
     ("q4", 1000, 8320, 2, -1),    # few INT4 rows of 5 units: x per unit
-    ("f16x32", 1100, 24584, 1, 1),  # 96 KiB of FP32 x: staged, one workgroup per CU
+    ("f16x32", 4100, 24584, 1, 2),  # 96 KiB of FP32 x: staged, one workgroup per CU
+    ("f16x32", 1100, 24584, 6, -1),  # few rows of 49 units: two waves per row
     ("f16x32", 2100, 40968, 2, -1),  # FP32 x would not fit a workgroup
     ("q4", 3000, 81920, 1, 1),    # staged x of exactly 160 KiB
     ("q8", 3000, 80848, 1, 1),    # 158 KiB, ragged last pass
-    ("f16x32", 1100, 40960, 1, 1),  # 160 KiB of FP32 x
+    ("f16x32", 4100, 40960, 1, 1),  # 160 KiB of FP32 x: no room for split staging's spare granules
 ]
 
 
@@ -162,7 +163,7 @@ def test_long_fp_rows(gpu, oracle_mod, kind, M, N, D, rows):
     _check(oracle_mod, kind, ops, f"{kind} long rows M={M} N={N} {info}")
 
 
-@pytest.mark.parametrize("kind,M,N", [("q8", 4500, 9216 + 16), ("q8", 6000, 8192 + 16), ("f16x32", 9000, 12800 + 8),
+@pytest.mark.parametrize("kind,M,N", [("q8", 4500, 9216 + 16), ("q8", 6000, 8192 + 16), ("f16x32", 3000, 12800 + 8),
                                       ("f16x32", 2048 + 3, 3072 + 8), ("f16_acc16", 4096 + 5, 4608 + 8)])
 def test_two_rows_per_wave_where_that_pads_less(gpu, oracle_mod, kind, M, N):
     # rows whose unit count does not divide by the loads in flight: two rows
