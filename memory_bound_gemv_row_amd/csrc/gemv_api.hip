@@ -115,16 +115,26 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
         // 6.74, 977 x 27392 15.19 -> 11.92)
         if (M > (P < 16 ? 7 : 5) * cus)
             return false;
-        target = 0;
+        if (M >= cus)
+            target = 0;   // (below one row per CU: enough waves to fill the chip)
         depth = M < 2 * cus ? 4 : 2;
     } else {
         // FP32/FP16 rows of 16 units and more up to 8 waves per CU (x is
         // one granule per unit); otherwise 4, INT4 2 (x per unit is four
-        // granules), FP16 with FP32 x 4
+        // granules)
         const bool fp = kind == kF32 || kind == kF16;
         const int per_cu = fp && P >= 16 ? 8 : (kind == kQ4 ? 2 : 4);
         if ((int64_t)p0.grid * p0.waves >= (int64_t)per_cu * cus || (kind == kQ4 && P > 16))
             return false;
+        if (fp && M >= 2 * cus) {
+            // FP32/FP16 from two rows per CU: two waves per row, 4 in flight
+            // (with the cost model after it, 144 random shapes put the
+            // picks 3.6 % (FP32) and 2.9 % (FP16) from the fastest plan,
+            // against 3.9 % and 3.4 % with S for 16 waves per CU: FP16
+            // 696 x 9600 5.27 -> 4.51 us, FP32 686 x 4864 5.17 -> 4.49)
+            target = 0;
+            depth = 4;
+        }
     }
     int S = 2;   // P >= 4: two units per wave at least
     while (S < 16 && 4 * S <= P && (int64_t)M * S < target)
@@ -563,12 +573,15 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
 // FP32/FP16 cost model: the predicted time of a plan from its geometry.  A
 // launch has a fixed cost (the same for every plan; it matters only to the
 // margin below, which is relative).  A wave streams
-// U units -- its rows' units padded to a multiple of D, the padding being
-// re-reads that cost real traffic -- D at a time, so it waits about U/D + 1
-// memory latencies; the busiest CU runs ceil(grid / CUs) workgroups, in
-// turn where they outnumber the workgroups it holds at once; the chip
-// streams every unit (padding included) at the HBM rate, a CU streams its
-// units at a per-CU rate and issues a fixed cost per unit on its 4 SIMDs.
+// U units -- its rows' units padded to a multiple of D -- D at a time, so
+// it waits about U/D + 1 memory latencies; the busiest CU runs
+// ceil(grid / CUs) workgroups, in turn where they outnumber the workgroups
+// it holds at once (its 4 SIMDs hold waves-per-SIMD x 4 waves, so that
+// many / waves workgroups); the chip streams every unit at the HBM rate, a
+// walking wave's padding included (it re-reads its last row from the
+// start), a split row's not (its padded loads repeat the wave's own last
+// unit, served from the caches); a CU streams its units at a per-CU rate
+// and issues a fixed cost per unit on its 4 SIMDs.
 // The four times overlap only in part and combine as a root sum of squares;
 // split rows add their LDS reduction.  The constants were fitted (weighted
 // least squares on log time, near-best plans weighted most) to the
@@ -579,7 +592,13 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
 // and wave for FP32 / FP16.  On 32 further random shapes the plan the model
 // picks (within the margin below) is 3.4 % slower than the fastest
 // candidate (geometric mean; 10.5 % at worst for FP16, 17 % for FP32),
-// the measured rules alone 6.3 % (34 % at worst).
+// the measured rules alone 6.3 % (34 % at worst).  The two corrections
+// above (the fit predates them: it held 8 two-wave workgroups per CU, and
+// counted split rows' padding as traffic) take the picks on 144 random
+// shapes from 4.3 % to 3.9 % (FP32) and 3.9 % to 3.4 % (FP16) behind the
+// fastest plan (FP16 18048 x 3456 22.32 -> 19.49 us, 10463 x 3200 13.75
+// -> 11.65: two waves per row); refitting the constants in the corrected
+// form made held-out picks worse in five of six folds, so they stay.
 struct FpCostModel {
     double launch;        // s, fixed cost of a launch
     double latency;       // s per memory round trip under load
@@ -613,7 +632,7 @@ double fp_cost(int kind, int64_t M, int64_t P, int cus, const Plan& p)
     int64_t U = 0, units = 0;
     if (p.variant == 6) {
         U = ((P + p.xk - 1) / p.xk + p.D - 1) / p.D * p.D;
-        units = waves * U;
+        units = M * P;   // padding re-reads the wave's last unit from cache
     } else {
         // waves 0 .. nmax-1 walk rmax rows, the others rmin
         const int64_t PP = p.variant == 5 ? p.xk : P;
@@ -622,7 +641,7 @@ double fp_cost(int kind, int64_t M, int64_t P, int cus, const Plan& p)
         const int64_t Umin = (rmin * PP + p.D - 1) / p.D * p.D;
         units = nmax * U + (waves - nmax) * Umin;
     }
-    const int held = std::min(fp_waves_per_simd(p) / ((p.waves + 3) / 4), 32);   // workgroups per CU
+    const int held = std::min(4 * fp_waves_per_simd(p) / p.waves, 32);   // workgroups per CU
     const int64_t wgs = (p.grid + cus - 1) / cus;                                 // on the busiest CU
     const double rounds = std::max((double)wgs / held, 1.0) * ((double)U / p.D + 1.0);
     const double cu_units = (double)wgs * p.waves * U;

@@ -187,10 +187,13 @@ def test_describe_launch_fills_all_cus(gpu):
     assert info["variant"] == 1 and info["lds_bytes"] == 4 * 32768 + 1024 <= lds_max, info   # x and spare granules
     assert binding.describe_launch("f16x32", 16 * cus, lds_max // 4 + 512)["variant"] == 2
     # few long rows (up to 5 per CU for rows of 16 units and more, 7 for
-    # shorter ones): two waves per row (split rows), x read with each unit
-    for M, N in ((64, 32768), (4 * cus, 32768), (5 * cus, 32768), (7 * cus, 4096)):
+    # shorter ones): split rows, x read with each unit; two waves per row
+    # from one row per CU, below that enough waves to fill the chip
+    for M, N in ((cus, 32768), (4 * cus, 32768), (5 * cus, 32768), (7 * cus, 4096)):
         info = binding.describe_launch("f16x32", M, N)
         assert info["variant"] == 6 and info["block"] == 128 and info["lds_bytes"] == 0 and info["grid"] == M, info
+    info = binding.describe_launch("f16x32", 64, 32768)
+    assert info["variant"] == 6 and info["grid"] * info["block"] // 64 >= 4 * cus, info
     assert binding.describe_launch("f16x32", 6 * cus, 32768)["variant"] == 1
     # few INT8 rows of four units or more (up to 6 per CU): split rows; a few
     # more: x read with each unit; few INT4 rows of four units or more read

@@ -59,9 +59,10 @@ def test_split_rows_match_the_oracle(gpu, oracle_mod, kind):
     if cus == 256:
         # the cases reach every waves-per-row value and both depths (INT4,
         # split only for rows of at most 16 units, up to 4 waves per row;
-        # INT8 splits with 2 in flight; FP16 with FP32 x two waves per row,
-        # its other splits run as explicit plans in test_gpu_plans)
-        want = {2, 4} if kind == "q4" else ({2} if kind == "f16x32" else {2, 4, 8, 16})
+        # INT8 splits with 2 in flight; FP16 with FP32 x two waves per row
+        # from one row per CU, 8 or 16 for fewer rows, its 4-wave split
+        # running as an explicit plan in test_gpu_plans)
+        want = {2, 4} if kind == "q4" else ({2, 8, 16} if kind == "f16x32" else {2, 4, 8, 16})
         depths = {2} if kind == "q8" else {2, 4}
         assert {s for s, _ in seen} == want and {d for _, d in seen} == depths, seen
 
@@ -94,7 +95,7 @@ def test_split_rows_integer_inputs_bit_exact(gpu, oracle_mod, kind):
 # rows at thousands of rows, two rows per wave with 2 in flight, and 4-wave
 # workgroups with 8 in flight for a few long rows
 _MODEL_CASES = [("f16", 4351, 9856, (6, 128, 2, 1)), ("f16", 2552, 9088, (6, 128, 2, 1)),
-                ("f16", 278, 16896, (6, 256, 4, 1)), ("f32", 902, 5248, (2, 256, 8, 1)),
+                ("f16", 278, 16896, (6, 256, 4, 1)), ("f32", 902, 5248, (6, 128, 4, 1)),
                 ("f16", 16384, 2560, (2, 256, 2, 2)), ("f32", 11646, 1664, (2, 256, 2, 2))]
 
 
