@@ -129,7 +129,7 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
         if (fp && M >= 2 * cus) {
             // FP32/FP16 from two rows per CU: two waves per row, 4 in flight
             // (with the cost model after it, 144 random shapes put the
-            // picks 3.6 % (FP32) and 2.9 % (FP16) from the fastest plan,
+            // picks 3.5 % (FP32) and 2.9 % (FP16) from the fastest plan,
             // against 3.9 % and 3.4 % with S for 16 waves per CU: FP16
             // 696 x 9600 5.27 -> 4.51 us, FP32 686 x 4864 5.17 -> 4.49)
             target = 0;
@@ -596,8 +596,8 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
 // above (the fit predates them: it held 8 two-wave workgroups per CU, and
 // counted split rows' padding as traffic) take the picks on 144 random
 // shapes from 4.3 % to 3.9 % (FP32) and 3.9 % to 3.4 % (FP16) behind the
-// fastest plan (FP16 18048 x 3456 22.32 -> 19.49 us, 10463 x 3200 13.75
-// -> 11.65: two waves per row); refitting the constants in the corrected
+// fastest plan (FP16 799 x 9344 5.87 -> 4.93 us, 10463 x 3200 13.75 ->
+// 11.65: two waves per row); refitting the constants in the corrected
 // form made held-out picks worse in five of six folds, so they stay.
 struct FpCostModel {
     double launch;        // s, fixed cost of a launch
