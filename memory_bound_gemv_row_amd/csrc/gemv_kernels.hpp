@@ -256,8 +256,8 @@ __device__ __forceinline__ u32x4 q4_pair_x(u32x4 v)
 // keeps the chunks of each pass together and splits them by granule: the
 // four reads of a unit are 1 KiB apart, an offset the LDS instruction holds,
 // so planes cost no address arithmetic (14336 x 4096: 1.4 M bank-conflict
-// cycles per launch to none, median 7.68 -> 7.19 us; 4096 x 14336 8.06 ->
-// 7.94).  INT8 keeps x's natural order (two granules per chunk, 2-way
+// cycles per launch to 0.2 M, all of them the staging writes', median 7.68
+// -> 7.19 us; 4096 x 14336 8.06 -> 7.94).  INT8 keeps x's natural order (two granules per chunk, 2-way
 // conflicts): neither kind of plane measured faster for it.
 template <int F>
 __device__ __forceinline__ int staged_index(int c, int k, int nchunks_pad)

@@ -8,6 +8,8 @@ Usage (after the rocprofv3 runs named in each summary's header)::
         <write_counter_collection.csv> <workload> <out.txt> <fetch command> <write command>
     python -m memory_bound_gemv_row_amd.profiling table <workload> <out.txt> \
         <run dir> <command> [<run dir> <command> ...]
+    python -m memory_bound_gemv_row_amd.profiling search <plan-search jsonl> <seed> <out.txt>
+    python -m memory_bound_gemv_row_amd.profiling sweep <plan-sweep jsonl> <seed> <out.txt>
 
 Traffic calibration: ``bench.py --profile`` launches, in order, a 1 GiB
 pure-read probe, the GEMV once, the probe again, and a 256 MiB copy.  The
@@ -20,6 +22,7 @@ from __future__ import annotations
 
 import csv
 import hashlib
+import json
 import os
 import re
 import sys
@@ -292,6 +295,65 @@ def write_counter_table(workload, out, passes, skip=4):
         f.write("\n".join(lines) + "\n")
 
 
+def _bench_lines(src, key):
+    rows, summary = [], None
+    with open(src) as f:
+        for line in f:
+            if not line.startswith("{"):
+                continue
+            d = json.loads(line)
+            if key in d:
+                summary = d[key]
+            else:
+                rows.append(d)
+    return rows, summary
+
+
+def write_search_summary(src, seed, out):
+    """Text summary of `bench.py --plan-search 24 --seed <seed>` output (JSON
+    lines in `src`): per shape the library's plan against the fastest of
+    every plan the library holds a kernel for."""
+    rows, summ = _bench_lines(src, "plan_search")
+    with open(out, "w") as f:
+        f.write("# bench.py --plan-search: the library's plan against every plan it holds a kernel for "
+                "(gemv_launch_plan), graph-timed, best of 3\n")
+        f.write(f"command: python3 bench.py --plan-search 24 --seed {seed} > {os.path.basename(src)}\n")
+        f.write(f"summary by: python3 -m memory_bound_gemv_row_amd.profiling search {os.path.basename(src)} {seed} "
+                f"{os.path.basename(out)}\n")
+        f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
+        f.write("summary (library plan / fastest candidate: geometric mean, median, worst): " + "; ".join(
+            f"{k} {v['geomean_lib_over_best']:.3f} / {v['median_lib_over_best']:.3f} / {v['worst_lib_over_best']:.3f} "
+            f"(worst {v['worst_shape']})" for k, v in summ.items()) + "\n")
+        f.write("kind    M       N     lib_us   best_us  lib/best  candidates  library plan (variant grid block "
+                "in-flight stage)  fastest (variant waves in-flight rows stage cap)\n")
+        for r in sorted(rows, key=lambda r: (r["kind"], r["lib_over_best"])):
+            p = r["lib_plan"]
+            f.write(f"{r['kind']:6s} {r['M']:6d} {r['N']:6d} {r['lib_us']:9.3f} {r['best_us']:9.3f} "
+                    f"{r['lib_over_best']:7.3f} {r['candidates']:6d}      {p['variant']} {p['grid']} {p['block']} "
+                    f"{p['units_in_flight']} {p['stage_order']}      {' '.join(map(str, r['best_plan']))}\n")
+
+
+def write_sweep_summary(src, seed, out):
+    """Text summary of `bench.py --plan-sweep 24 --seed <seed>` output: each
+    shape's plan against the pure-read probe over the same bytes."""
+    rows, summ = _bench_lines(src, "plan_sweep")
+    with open(out, "w") as f:
+        f.write("# bench.py --plan-sweep: each shape's plan against the pure-read probe over the same bytes "
+                "(graph-timed, best of 3)\n")
+        f.write(f"command: python3 bench.py --plan-sweep 24 --seed {seed} > {os.path.basename(src)}\n")
+        f.write(f"summary by: python3 -m memory_bound_gemv_row_amd.profiling sweep {os.path.basename(src)} {seed} "
+                f"{os.path.basename(out)}\n")
+        f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
+        f.write("summary (worst / median % of the same-size probe): " + "; ".join(
+            f"{k} {v['worst_pct']} / {v['median_pct']} (worst {v['worst_shape']})" for k, v in summ.items()) + "\n")
+        f.write("kind    M       N        us   probe_us  %probe  variant grid block units_in_flight stage\n")
+        for r in sorted(rows, key=lambda r: (r["kind"], r["pct_of_same_size_probe"])):
+            p = r["plan"]
+            f.write(f"{r['kind']:6s} {r['M']:6d} {r['N']:6d} {r['us']:9.3f} {r['same_size_probe_us']:9.3f} "
+                    f"{r['pct_of_same_size_probe']:6.1f}  {p['variant']} {p['grid']} {p['block']} "
+                    f"{p['units_in_flight']} {p['stage_order']}\n")
+
+
 def read_traffic(path):
     """(bytes_per_launch, kernel_source_hash) from a traffic summary, or None."""
     try:
@@ -313,5 +375,9 @@ if __name__ == "__main__":
         # table <workload> <out.txt> <run dir 1> <cmd 1> [<run dir 2> <cmd 2> ...]
         a = sys.argv[4:]
         write_counter_table(sys.argv[2], sys.argv[3], list(zip(a[0::2], a[1::2])))
+    elif sys.argv[1] == "search":
+        write_search_summary(sys.argv[2], sys.argv[3], sys.argv[4])   # <bench jsonl> <seed> <out.txt>
+    elif sys.argv[1] == "sweep":
+        write_sweep_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     else:
         raise SystemExit(__doc__)
