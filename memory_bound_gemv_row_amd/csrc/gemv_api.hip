@@ -544,18 +544,29 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
     } else {
         // short INT4 rows: 8 waves, 2 units in flight, split staging, at
         // most 4 workgroups per CU (3 measured 1.7-4.8 % slower on seven
-        // shapes: 14336 x 4096 7.52 -> 7.30 us); longer rows: 4 units, x
-        // staged before A, 4 waves and at most 3 workgroups per CU; rows of
-        // 14-16 units: 8 waves and at most 2 workgroups per CU (fewer
-        // stagings of their 56-64 KiB of x)
+        // shapes: 14336 x 4096 7.52 -> 7.30 us); rows of 5-9 units: 4
+        // units in flight (5 and 3 for rows of 5 and 6 units, which divide
+        // them: 2048 x 10240 5.65 -> 5.08 us, 2048 x 12288 5.65 -> 5.42), x
+        // staged before A, 4 waves and at most 3 workgroups per CU.  With x
+        // in per-pass planes (staged_index), brute force over every plan on
+        // 72 seeded random shapes moved rows of 10 units and more, and many
+        // rows of 4, to 8 waves, 4 in flight, split staging and 1 (2 for
+        // rows of 4) workgroups per CU: the picks from 1.9 % to 1.0 % behind
+        // the fastest plan (geometric mean; 12.2 % to 6.8 % at worst;
+        // 5832 x 25088 17.2 -> 15.4 us, 4096 x 8192 5.77 -> 5.49)
         p.variant = 1;
-        p.waves = P < 4 || P >= 14 ? 8 : 4;
-        // rows of 5 and 6 units: 5 and 3 in flight, which divide them
-        // (2048 x 10240 5.65 -> 5.08 us, 2048 x 12288 5.65 -> 5.42)
-        p.D = P < 4 ? 2 : (P == 5 ? 5 : (P == 6 ? 3 : 4));
         p.rows = 1;
-        p.stg = P < 4 ? 2 : 1;
-        p.cap = P < 4 ? 4 : (P >= 14 ? 2 : 3);
+        if (P >= 10 || (P == 4 && M > 8 * cus)) {
+            p.waves = 8;
+            p.D = 4;
+            p.stg = 2;
+            p.cap = P >= 10 ? 1 : 2;
+        } else {
+            p.waves = P < 4 ? 8 : 4;
+            p.D = P < 4 ? 2 : (P == 5 ? 5 : (P == 6 ? 3 : 4));
+            p.stg = P < 4 ? 2 : 1;
+            p.cap = P < 4 ? 4 : 3;
+        }
     }
     // staged plans were chosen only where x fits the device's LDS
     p.lds = p.variant == 1 ? (int)lds_bytes(kind, nchunks) : 0;
