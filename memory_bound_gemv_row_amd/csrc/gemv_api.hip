@@ -365,15 +365,22 @@ Plan rows_plan(int kind, int M, int N, bool aligned, const Device& dev)
     } else if (fp) {
         p.variant = 2;
         if (P >= 24) {
-            // very long rows: 4 waves; up to 12 rows per CU two rows per
-            // wave, 8 in flight; from 24 rows per CU 8 in flight, one row
-            // per wave (two where a row's units are not a multiple of 8,
-            // which would pad every row's stream); in between two rows per
-            // wave, 4 in flight
+            // very long rows: 4 waves; up to 11 rows per CU two rows per
+            // wave, 8 in flight (few enough waves that split_plan takes
+            // over: two waves per row); from 11 to 16 rows per CU four rows
+            // per wave, 8 in flight, so that the grid gives every CU one
+            // workgroup (four_rows_rule), except rows of a multiple of 16
+            // units (FP16 4096 x 32768 42.31 us against 43.18 with four);
+            // from 24 rows per CU 8 in flight, one row per wave (two where a
+            // row's units are not a multiple of 8, which would pad every
+            // row's stream); in between two rows per wave, 4 in flight
             p.waves = 4;
-            if (M <= 12 * cus) {
+            if (M <= 11 * cus) {
                 p.D = 8;
                 p.rows = 2;
+            } else if (M <= 16 * cus && P % 16 != 0) {
+                p.D = 8;
+                p.rows = 4;
             } else if (M >= 24 * cus || P % 16 == 0) {
                 // (between 12 and 24 rows per CU only rows of a multiple of
                 // 16 units measured faster so: FP16 4096 x 32768 44.5 ->
@@ -732,10 +739,21 @@ Plan fp_model_plan(int kind, int M, int P, const Device& dev, const Plan& p0)
     return rules_t > kModelMargin * best_t ? best : p0;
 }
 
+// FP32/FP16 rows of 24 units and more, 11-16 rows per CU: 4 waves of four
+// rows each, 8 in flight, one workgroup per CU (rows_plan), a measured rule
+// that neither split_plan nor the cost model replaces.  Brute force over
+// every plan on 16 seeded random shapes there: the fastest plan on 13 (9 %
+// behind at worst, 2856 x 28928 at 11.2 rows per CU), where the split rows
+// and the cost model's picks were 0-15 % behind (FP32 3912 x 6784 19.52 ->
+// 16.97 us, 3494 x 10880 27.41 -> 24.45, FP16 3656 x 26752 33.70 -> 30.18);
+// past 16 rows per CU some CUs get two workgroups and it falls 37-58 %
+// behind.
+bool four_rows_rule(const Plan& p) { return (p.variant == 2 && p.rows == 4 && p.waves == 4 && p.D == 8); }
+
 Plan plan_uncached(int kind, int M, int N, bool aligned, const Device& dev)
 {
     const Plan p0 = rows_plan(kind, M, N, aligned, dev);
-    if (p0.variant == 3)
+    if (p0.variant == 3 || ((kind == kF32 || kind == kF16) && four_rows_rule(p0)))
         return p0;
     const int P = (N / elems_per_chunk(kind) + 63) / 64;
     Plan p = p0;

@@ -145,13 +145,14 @@ def test_long_rows_staged_or_per_unit(gpu, oracle_mod, kind, M, N, variant, stg)
 
 
 @pytest.mark.parametrize("kind,M,N,D,rows", [("f16_acc16", 8192, 14336 + 8, 8, 2), ("f32", 6144 + 3, 12288, 8, 1),
-                                             ("f16_acc16", 3000, 12288 + 8, 8, 2), ("f16_acc16", 4096 + 1, 14336, 4, 2),
+                                             ("f16_acc16", 3000, 12288 + 8, 8, 4), ("f16_acc16", 4096 + 1, 14336, 4, 2),
                                              ("f16_acc16", 6400, 16384, 8, 1), ("f16_acc16", 4096 + 7, 16384, 8, 1)])
 def test_long_fp_rows(gpu, oracle_mod, kind, M, N, D, rows):
     # The measured rules for rows of 24 units and more: 8 in flight and one
     # row per wave from 24 rows per CU or for multiples of 16 units (two
-    # where the units are not a multiple of 8), two rows per wave up to 12
-    # per CU, 4 in flight between; ragged last passes.  FP16 accumulation
+    # where the units are not a multiple of 8), two rows per wave up to 11
+    # per CU, four from 11 to 16 (rows not a multiple of 16 units), 4 in
+    # flight between; ragged last passes.  FP16 accumulation
     # keeps these rules; FP32/FP16 take the cost model's plan where it
     # predicts a clear gain (its plans are checked in test_gpu_split.py)
     cus = torch.cuda.get_device_properties(0).multi_processor_count

@@ -23,6 +23,14 @@ def staged_bytes(kind, N):
     return (nchunks + 63) // 64 * 64 * X_GRANULES[kind] * 16
 
 
+def _four_rows(kind, M, N, cus):
+    # FP rows of 24 units and more at 11-16 rows per CU: four rows per wave,
+    # one 4-wave workgroup per CU at most (some CUs idle below 16 rows per
+    # CU: measured faster than filling them)
+    P = -(-(N // ELEMS_PER_CHUNK[kind]) // 64) if N else 0
+    return kind in ("f32", "f16", "f16_acc16") and P >= 24 and P % 16 and 11 * cus < M <= 16 * cus
+
+
 def _fewer_stagings(kind, M, p, cus):
     # FP16 with FP32 x, 8-14 rows per CU: two rows per wave staged, fewer
     # workgroups than CUs (fewer stagings of x measured faster)
@@ -63,7 +71,8 @@ def test_every_plan_is_consistent(kind, dev):
             assert p["stage_order"] in (0, 1, 2), where
         else:
             assert p["lds_bytes"] == 0 and p["stage_order"] == -1, where
-        if p["variant"] in (1, 2) and M >= 8 * dev["cus"] and not _fewer_stagings(kind, M, p, dev["cus"]):
+        if (p["variant"] in (1, 2) and M >= 8 * dev["cus"] and not _fewer_stagings(kind, M, p, dev["cus"])
+                and not _four_rows(kind, M, N, dev["cus"])):
             assert p["grid"] >= dev["cus"], where                 # every CU gets a workgroup
         if p["variant"] == 5:
             assert 1 <= -(-(N // ELEMS_PER_CHUNK[kind]) // 64) <= 3, where   # rows of one to three units
@@ -111,7 +120,8 @@ def test_random_shapes_keep_the_invariants():
         assert p["lds_bytes"] <= dev["lds_max"], where
         if p["variant"] != 4:
             assert p["grid"] * (p["block"] // 64) * p["rows_per_wave"] >= M, where
-        if p["variant"] in (1, 2) and M >= 8 * dev["cus"] and not _fewer_stagings(kind, M, p, dev["cus"]):
+        if (p["variant"] in (1, 2) and M >= 8 * dev["cus"] and not _fewer_stagings(kind, M, p, dev["cus"])
+                and not _four_rows(kind, M, N, dev["cus"])):
             assert p["grid"] >= dev["cus"], where
 
 
@@ -253,7 +263,7 @@ def test_fp16_accumulation_plans_keep_the_gate_term_count(dev):
 # model leaves in place (it predicts less than its margin of a gain there)
 _NAMED_PLANS = {
     ("f16", 8192, 8192): (2, 1024, 512, 8, 1),
-    ("f16", 4096, 14336): (2, 512, 256, 4, 2),
+    ("f16", 4096, 14336): (2, 256, 256, 8, 4),
     ("f16", 14336, 4096): (2, 3584, 256, 8, 1),
     ("f16", 4096, 4096): (2, 1024, 256, 8, 1),
     ("f32", 1024, 1024): (2, 256, 256, 4, 1),
