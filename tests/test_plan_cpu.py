@@ -326,6 +326,38 @@ def test_rules_remeasured_by_brute_force():
     assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 256, 2, 4, 1024)
 
 
+def test_rules_from_the_random_shape_search():
+    # Rules the brute-force search over seeded random shapes changed
+    # (graph-timed us, before -> after):
+    #   FP32/FP16 rows of 24 units and more, 11-16 rows per CU: 4 waves of
+    #     four rows, 8 in flight, one workgroup per CU, kept from split rows
+    #     and the cost model (FP32 3912x6784 19.27 -> 16.83, FP16
+    #     3656x26752 33.58 -> 29.89)
+    #   FP32/FP16 split rows from two rows per CU: two waves per row, 4 in
+    #     flight (FP16 10463x3200 13.25 -> 11.43)
+    #   INT4 rows of 10 units and more: 8 waves, split staging, one
+    #     workgroup per CU; many rows of 4 units: two (5832x25088 17.59 ->
+    #     16.10, 4096x8192 5.70 -> 5.45)
+    #   FP16 with FP32 x: split rows of two waves up to 5-7 rows per CU
+    #     (977x27392 15.08 -> 11.83); staged, 4 waves, 8 in flight, one
+    #     workgroup per CU for rows of 16 units and more (12815x14720 63.45
+    #     -> 57.50)
+    for kind, M, N in (("f32", 3912, 6784), ("f16", 3656, 26752)):
+        p = plan(kind, M, N)
+        assert (p["variant"], p["block"], p["units_in_flight"], p["rows_per_wave"]) == (2, 256, 8, 4), (kind, M, N, p)
+        assert p["grid"] == -(-M // 16) <= 256, (kind, M, N, p)
+    p = plan("f16", 10463, 3200)
+    assert (p["variant"], p["block"], p["units_in_flight"], p["grid"]) == (6, 128, 4, 10463)
+    p = plan("q4", 5832, 25088)
+    assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 512, 2, 4, 256)
+    p = plan("q4", 4096, 8192)
+    assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 512, 2, 4, 512)
+    p = plan("f16x32", 977, 27392)
+    assert (p["variant"], p["block"], p["units_in_flight"], p["grid"]) == (6, 128, 2, 977)
+    p = plan("f16x32", 12815, 14720)
+    assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 256, 2, 8, 256)
+
+
 def test_plan_cache_gives_the_same_plans():
     # each host thread keeps its last 16 plans: more shapes than that,
     # interleaved across devices and in two orders, give the same plans
