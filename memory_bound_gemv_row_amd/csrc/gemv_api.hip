@@ -109,15 +109,16 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
     } else if (kind == kF16X32) {
         // up to 7 rows per CU (rows of 16 units and more: 5, above which
         // staged x measured up to 26 % faster: 1702 x 23168 19.79 -> 15.05
-        // us), two waves per row (the fewest), 4 in flight below 2 rows per
-        // CU, else 2, where S for 16 waves per CU was up to 31 % from the
+        // us), two waves per row (the fewest), 4 in flight below 3.5 rows
+        // per CU, else 2 (512 x 25984: 9.77 us at 2 in flight, 7.60 at 4),
+        // where S for 16 waves per CU was up to 31 % from the
         // fastest plan (1492 x 5120 6.26 -> 5.11 us, 410 x 24448 7.80 ->
         // 6.74, 977 x 27392 15.19 -> 11.92)
         if (M > (P < 16 ? 7 : 5) * cus)
             return false;
         if (M >= cus)
             target = 0;   // (below one row per CU: enough waves to fill the chip)
-        depth = M < 2 * cus ? 4 : 2;
+        depth = 2 * M < 7 * cus ? 4 : 2;
     } else {
         // FP32/FP16 rows of 16 units and more up to 8 waves per CU (x is
         // one granule per unit); otherwise 4, INT4 2 (x per unit is four
@@ -128,12 +129,14 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
             return false;
         if (fp && M >= 2 * cus) {
             // FP32/FP16 from two rows per CU: two waves per row, 4 in flight
-            // (with the cost model after it, 144 random shapes put the
-            // picks 3.5 % (FP32) and 2.9 % (FP16) from the fastest plan,
-            // against 3.9 % and 3.4 % with S for 16 waves per CU: FP16
-            // 696 x 9600 5.27 -> 4.51 us, FP32 686 x 4864 5.17 -> 4.49)
+            // below 4 rows per CU, else 2 (with the cost model after it,
+            // 144 random shapes put the picks 3.5 % (FP32) and 2.9 % (FP16)
+            // from the fastest plan, against 3.9 % and 3.4 % with S for 16
+            // waves per CU: FP16 696 x 9600 5.27 -> 4.51 us, FP32 686 x 4864
+            // 5.17 -> 4.49; 2 in flight from 4 rows per CU: FP32 1345 x
+            // 9344 11.20 -> 9.70)
             target = 0;
-            depth = 4;
+            depth = M < 4 * cus ? 4 : 2;
         }
     }
     int S = 2;   // P >= 4: two units per wave at least
