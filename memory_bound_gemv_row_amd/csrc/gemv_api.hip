@@ -109,8 +109,9 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
     } else if (kind == kF16X32) {
         // up to 7 rows per CU (rows of 16 units and more: 5, above which
         // staged x measured up to 26 % faster: 1702 x 23168 19.79 -> 15.05
-        // us), two waves per row (the fewest), 4 in flight below 3.5 rows
-        // per CU, else 2 (512 x 25984: 9.77 us at 2 in flight, 7.60 at 4),
+        // us), two waves per row (the fewest), 4 in flight below 3 rows per
+        // CU, else 2 (512 x 25984: 9.67 us at 2 in flight, 7.42 at 4; 800 x
+        // 16384: 7.15 at 2, 7.75 at 4),
         // where S for 16 waves per CU was up to 31 % from the
         // fastest plan (1492 x 5120 6.26 -> 5.11 us, 410 x 24448 7.80 ->
         // 6.74, 977 x 27392 15.19 -> 11.92)
@@ -118,7 +119,7 @@ bool split_plan(int kind, int M, int P, int cus, const Plan& p0, Plan* p)
             return false;
         if (M >= cus)
             target = 0;   // (below one row per CU: enough waves to fill the chip)
-        depth = 2 * M < 7 * cus ? 4 : 2;
+        depth = M < 3 * cus ? 4 : 2;
     } else {
         // FP32/FP16 rows of 16 units and more up to 8 waves per CU (x is
         // one granule per unit); otherwise 4, INT4 2 (x per unit is four

@@ -90,10 +90,10 @@ def test_every_plan_is_consistent(kind, dev):
                 assert M <= 6 * dev["cus"] and p["units_in_flight"] == 2, where
             elif kind == "f16x32":
                 # FP16 with FP32 x: up to 7 rows per CU, two waves per row
-                # from one row per CU, 4 in flight below 3.5 rows per CU,
-                # else 2
+                # from one row per CU, 4 in flight below 3 rows per CU, else
+                # 2
                 assert M <= 7 * dev["cus"] and (S == 2 or M < dev["cus"]), where
-                assert p["units_in_flight"] == (4 if 2 * M < 7 * dev["cus"] else 2), where
+                assert p["units_in_flight"] == (4 if M < 3 * dev["cus"] else 2), where
             elif kind not in ("f32", "f16"):
                 # the rule alone: only where one wave per row leaves the CUs
                 # short of waves (fewer than 8 per CU), 2 in flight for two
