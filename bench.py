@@ -510,6 +510,13 @@ def plan_candidates(kind, N):
             out += [(1, 4, d, 1, 1, cap) for d in (3, 5) for cap in (0, 2, 3)]
     if kind != "f16_acc16":
         out += [(6, S, d, 1, -1, 0) for S in (2, 4, 8, 16) if 2 * S <= P for d in (2, 4)]
+    if kind in ("q8", "q4", "f16x32"):
+        # row slabs: S waves own P / S passes each (one or two)
+        for S in sorted({P, P // 2}):
+            if not (1 <= S <= 16 and P % S == 0 and P // S <= 2):
+                continue
+            out += [(7, S, d, r, -1, cap) for d in (4, 8) for r in (4, 8) for cap in sorted({0, max(1, 32 // S)})
+                    if (r * (P // S)) % d == 0]
     return out
 
 

@@ -60,16 +60,20 @@ int packed_rows_per_load(int nchunks) { return 64 / packed_lanes<kQ8>(nchunks); 
 struct Plan {
     int variant;   // 1 stream + LDS x, 2 stream + global x, 3 element-wise,
                    // 4 packed short rows (INT8/INT4), 5 x in registers,
-                   // 6 split rows (several waves per row)
+                   // 6 split rows (several waves per row),
+                   // 7 row slabs (INT8/INT4/FP16 with FP32 x: waves own
+                   // passes, x slices in registers)
     int grid;
     int block;
     int waves;     // per workgroup
-    int rows;      // rows per wave (upper bound); variant 4: row groups per wave
+    int rows;      // rows per wave (upper bound); variant 4: row groups per wave;
+                   // variant 7: rows per slab (R)
     int D;         // units in flight per wave
     int lds;
     int stg;       // order of A prologue and x staging (default_stage_order)
     int cap;       // at most cap workgroups per CU (0: no cap)
-    int xk;        // variant 5: units per row (K); variant 6: waves per row (S)
+    int xk;        // variant 5: units per row (K); variant 6: waves per row (S);
+                   // variant 7: passes per wave (Q)
 };
 
 // Split rows (variant 6), chosen after the one-wave-per-row plan p0: where
@@ -754,12 +758,78 @@ Plan fp_model_plan(int kind, int M, int P, const Device& dev, const Plan& p0)
 // behind.
 bool four_rows_rule(const Plan& p) { return (p.variant == 2 && p.rows == 4 && p.waves == 4 && p.D == 8); }
 
+// Row slabs (variant 7, gemv_slab) for INT8, INT4 and FP16 with FP32 x,
+// whose x the streaming kernel stages in LDS once per workgroup or reads
+// with every unit.  A slab plan takes S = P waves per workgroup (S = P / 2,
+// two passes per wave, for rows of 17-32 units), 4 rows per slab, 4 loads
+// in flight (8 with two passes per wave).  Where it is taken: FP16 with FP32
+// x for rows of 2 units and more, and one-unit rows from 14 rows per CU;
+// INT4 rows of 3-16 units save 6 (3-7 units at any row count, longer rows
+// up to 12 rows per CU); INT8 rows of 9 units and more between 2 and 100
+// rows per CU.  Slabs of 8 rows where two passes per wave give the busiest
+// CU no more rows than slabs of 4 (fewer workgroups, each loading its x
+// once).  INT4 caps the grid at 32 waves per CU, so that workgroups walk
+// several slabs with x loaded once.  Graph-timed on four seeds of 24 random
+// shapes per format (bench-style ring over >= 1 GiB), against the rules
+// before: geometric mean 0.957 / 0.945 (FP16 with FP32 x, seeds 0-1 / 2-3),
+// 0.968 / 0.964 (INT4), 0.990 / 0.988 (INT8), with no INT shape slower by
+// more than 3 %: INT4 4096 x 14336 8.08 -> 7.84 us, FP16 with FP32 x
+// 8192 x 8192 22.82 -> 22.02, INT8 2295 x 24576 14.51 -> 12.21, INT4
+// 569 x 8320 4.16 -> 3.25.  Rows of 2 units (INT4 14336 x 4096 7.30 ->
+// 7.74), INT8 rows of 4-8 units (14336 x 4096 10.74 -> 11.15, 8192 x 8192
+// 12.39 -> 12.74) and INT4 rows of 6 units (5113 x 10880 8.17 -> 8.79)
+// stay with the streaming kernel.
+bool slab_plan(int kind, int M, int P, int cus, Plan* p)
+{
+    const int64_t rows = M;
+    bool take = false;
+    if (kind == kF16X32)
+        take = rows >= cus && (P >= 2 || rows >= 14 * (int64_t)cus);
+    else if (kind == kQ4)
+        take = rows >= cus && P >= 3 && P <= 16 && P != 6 && (P <= 7 || rows <= 12 * (int64_t)cus);
+    else if (kind == kQ8)
+        take = P >= 9 && rows >= 2 * (int64_t)cus && rows <= 100 * (int64_t)cus;
+    if (!take || P > 32 || (P > 16 && P % 2 != 0))
+        return false;
+    const int S = P <= 16 ? P : P / 2;
+    const int Q = P / S;
+    int R = 4;
+    if (Q == 2) {
+        // rows on the busiest CU: whole slabs, grid of one slab per workgroup
+        auto busiest = [&](int r) { return ((rows + r - 1) / r + cus - 1) / cus * r; };
+        if (busiest(8) <= busiest(4))
+            R = 8;
+    }
+    *p = Plan{};
+    p->variant = 7;
+    p->waves = S;
+    p->block = S * 64;
+    p->xk = Q;
+    p->rows = R;
+    p->D = Q == 2 ? 8 : 4;
+    p->stg = -1;
+    p->lds = 0;
+    int64_t grid = (rows + R - 1) / R;
+    if (kind == kQ4) {
+        const int64_t cap = (int64_t)(32 / S > 1 ? 32 / S : 1) * cus;
+        if (grid > cap) {
+            grid = cap;
+            p->cap = 32 / S > 1 ? 32 / S : 1;
+        }
+    }
+    p->grid = gemv_device::capped_grid(grid, p->block);
+    return true;
+}
+
 Plan plan_uncached(int kind, int M, int N, bool aligned, const Device& dev)
 {
     const Plan p0 = rows_plan(kind, M, N, aligned, dev);
     if (p0.variant == 3 || ((kind == kF32 || kind == kF16) && four_rows_rule(p0)))
         return p0;
     const int P = (N / elems_per_chunk(kind) + 63) / 64;
+    Plan sl{};
+    if (slab_plan(kind, M, P, dev.cus, &sl))
+        return sl;
     Plan p = p0;
     Plan s{};
     if (split_plan(kind, M, P, dev.cus, p0, &s))
@@ -815,6 +885,28 @@ const void* select_split(const Plan& p)
     case 8: return select_split_d<F, 8>(p);
     default: return select_split_d<F, 16>(p);
     }
+}
+
+template <int F, int Q, int R>
+const void* select_slab_r(const Plan& p)
+{
+    if constexpr (R * Q >= 8) {
+        if (p.D == 8)
+            return reinterpret_cast<const void*>(&gemv_slab<F, Q, 8, R>);
+    }
+    return reinterpret_cast<const void*>(&gemv_slab<F, Q, 4, R>);
+}
+
+template <int F, int Q>
+const void* select_slab_q(const Plan& p)
+{
+    return p.rows == 4 ? select_slab_r<F, Q, 4>(p) : select_slab_r<F, Q, 8>(p);
+}
+
+template <int F>
+const void* select_slab(const Plan& p)
+{
+    return p.xk == 2 ? select_slab_q<F, 2>(p) : select_slab_q<F, 1>(p);
 }
 
 template <int F>
@@ -884,6 +976,10 @@ const void* select_kernel(const Plan& p)
         if (p.variant == 4)
             return select_packed<F>(p);
     }
+    if constexpr (F == kQ8 || F == kQ4 || F == kF16X32) {
+        if (p.variant == 7)
+            return select_slab<F>(p);
+    }
     if constexpr (F == kF32 || F == kF16 || F == kF16H)
         return select_stream<F, true>(p);
     else
@@ -903,6 +999,18 @@ const void* kernel_for(int kind, const Plan& p)
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Enqueue plan p on `stream`.
+int launch_planned(int kind, const Plan& p, const void* A, const uint16_t* scale, const void* x, float* y, int M,
+                   int N, hipStream_t stream)
+{
+    const uint8_t* a8 = static_cast<const uint8_t*>(A);
+    const uint8_t* x8 = static_cast<const uint8_t*>(x);
+    void* args[] = {(void*)&a8, (void*)&scale, (void*)&x8, (void*)&y, (void*)&M, (void*)&N};
+    const hipError_t err = hipLaunchKernel(kernel_for(kind, p), dim3(p.grid), dim3(p.block), args,
+                                           (size_t)p.lds, stream);
+    return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
+}
 
 int launch(int kind, const void* A, const uint16_t* scale, const void* x, float* y, int M, int N,
            hipStream_t stream)
@@ -924,12 +1032,7 @@ int launch(int kind, const void* A, const uint16_t* scale, const void* x, float*
         return rc;
     const bool aligned = aligned16(A) && aligned16(x);
     const Plan p = make_plan(kind, M, N, aligned, dev);
-    const uint8_t* a8 = static_cast<const uint8_t*>(A);
-    const uint8_t* x8 = static_cast<const uint8_t*>(x);
-    void* args[] = {(void*)&a8, (void*)&scale, (void*)&x8, (void*)&y, (void*)&M, (void*)&N};
-    const hipError_t err = hipLaunchKernel(kernel_for(kind, p), dim3(p.grid), dim3(p.block), args,
-                                           (size_t)p.lds, stream);
-    return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
+    return launch_planned(kind, p, A, scale, x, y, M, N, stream);
 }
 
 // Probe geometry: enough 256-thread workgroups to give every CU 8 of them.
@@ -1054,6 +1157,10 @@ void info_of_plan(int kind, int M, int N, const Plan& p, gemv_launch_info* info)
         const int64_t R = packed_rows_per_load(N / elems_per_chunk(kind));
         const int64_t groups = ((int64_t)M + R - 1) / R;
         info->rows_per_wave = waves > 0 ? (int)((groups + waves - 1) / waves * R) : 0;
+    } else if (p.variant == 7) {
+        // R rows of every slab the workgroup takes
+        const int64_t slabs = ((int64_t)M + p.rows - 1) / p.rows;
+        info->rows_per_wave = p.grid > 0 ? (int)((slabs + p.grid - 1) / p.grid * p.rows) : 0;
     } else {
         info->rows_per_wave = waves > 0 ? (int)(((int64_t)M + waves - 1) / waves) : 0;
     }
@@ -1151,6 +1258,21 @@ int plan_from_user(int kind, int M, int N, const Device& dev, const gemv_plan& u
         p.grid = M;
         break;
     }
+    case 7: {
+        // S = waves waves per slab, Q = P / S passes per wave (1 or 2)
+        const int S = p.waves;
+        if (!(kind == kQ8 || kind == kQ4 || kind == kF16X32) || p.stg != -1 || S < 1 || S > 16 || P % S != 0 ||
+            P / S > 2 || !(p.D == 4 || p.D == 8) || !(p.rows == 4 || p.rows == 8) || p.rows * (P / S) % p.D != 0)
+            return GEMV_E_UNSUPPORTED;
+        p.xk = P / S;
+        p.block = S * 64;
+        p.lds = 0;
+        int64_t grid = ((int64_t)M + p.rows - 1) / p.rows;
+        if (p.cap > 0 && grid > (int64_t)p.cap * dev.cus)
+            grid = (int64_t)p.cap * dev.cus;
+        p.grid = gemv_device::capped_grid(grid, p.block);
+        break;
+    }
     default:
         return GEMV_E_UNSUPPORTED;
     }
@@ -1218,12 +1340,7 @@ int gemv_launch_plan(int kind, const void* A, const uint16_t* scale, const void*
     gemv::Plan p{};
     if (int rc = gemv::plan_from_user(kind, M, N, dev, *plan, &p); rc != GEMV_OK)
         return rc;
-    const uint8_t* a8 = static_cast<const uint8_t*>(A);
-    const uint8_t* x8 = static_cast<const uint8_t*>(x);
-    void* args[] = {(void*)&a8, (void*)&scale, (void*)&x8, (void*)&y, (void*)&M, (void*)&N};
-    const hipError_t err = hipLaunchKernel(gemv::kernel_for(kind, p), dim3(p.grid), dim3(p.block), args,
-                                           (size_t)p.lds, stream);
-    return err == hipSuccess ? GEMV_OK : GEMV_E_LAUNCH;
+    return gemv::launch_planned(kind, p, A, scale, x, y, M, N, stream);
 }
 
 }  // extern "C"

@@ -970,6 +970,195 @@ gemv_split(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
     }
 }
 
+// ---------------------------------------------------------------- row slabs, x slices in registers
+// Sums of eight values over the 64 lanes at once: on return lane l holds the
+// sum of v[l >> 3].  A butterfly that halves the values at each step instead
+// of reducing each one separately: v_permlane32_swap pairs v[i] with v[i+4]
+// across the wave's halves (lanes 0-31 keep rows 0-3, lanes 32-63 rows 4-7),
+// v_permlane16_swap pairs the remaining values across 16-lane rows, a select
+// and a DPP rotation by 8 across half rows, then three DPP adds within each
+// 8-lane group: 18 instructions for eight sums, where eight wave_sum calls
+// take about 70.
+__device__ __forceinline__ float wave_sum8(const float (&v)[8])
+{
+    float b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v[i]),
+                                                        __builtin_bit_cast(unsigned, v[i + 4]), false, false);
+        b[i] = as_f(p[0]) + as_f(p[1]);
+    }
+    float c[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, b[i]),
+                                                        __builtin_bit_cast(unsigned, b[i + 2]), false, false);
+        c[i] = as_f(p[0]) + as_f(p[1]);
+    }
+    // c[0] holds rows 0, 2, 4, 6 and c[1] rows 1, 3, 5, 7 in the four 16-lane
+    // rows; lanes with bit 3 set keep c[1]
+    const bool odd = (threadIdx.x & 8) != 0;
+    const float keep = odd ? c[1] : c[0];
+    const float give = odd ? c[0] : c[1];
+    float r = keep + dpp_mov<0x128>(give);   // row_ror:8: the other half row
+    r += dpp_mov<0xB1>(r);    // lane ^ 1
+    r += dpp_mov<0x4E>(r);    // lane ^ 2
+    r += dpp_mov<0x141>(r);   // row_half_mirror: the other quad
+    return r;
+}
+
+// The same for four values: on return lane l holds the sum of v[l >> 4]
+// (10 instructions).
+__device__ __forceinline__ float wave_sum4(const float (&v)[4])
+{
+    float b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v[i]),
+                                                        __builtin_bit_cast(unsigned, v[i + 2]), false, false);
+        b[i] = as_f(p[0]) + as_f(p[1]);
+    }
+    // b[0] holds rows 0 and 2, b[1] rows 1 and 3 in the wave's halves
+    const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, b[0]),
+                                                    __builtin_bit_cast(unsigned, b[1]), false, false);
+    float r = as_f(p[0]) + as_f(p[1]);
+    r += dpp_mov<0x128>(r);   // row_ror:8: the other half row
+    r += dpp_mov<0xB1>(r);    // lane ^ 1
+    r += dpp_mov<0x4E>(r);    // lane ^ 2
+    r += dpp_mov<0x141>(r);   // row_half_mirror: the other quad
+    return r;
+}
+
+// Long INT8/INT4 and FP16-with-FP32-x rows, whose x every workgroup of
+// gemv_stream would stage in LDS: a workgroup of S waves takes R = 4 or 8
+// consecutive rows (a slab) at a time, and wave w owns the passes w, w + S, ...,
+// w + (Q - 1) S of every row of the slab (S * Q = P units per row).  Lane l's
+// chunks are then the same in every row, so each wave loads its lanes' x for
+// its Q passes into registers once (as gemv_xreg does for a whole row) and
+// streams the slab's R Q units, D in flight, into one FP32 sum per row, with
+// no x staging and no LDS read of x.  The wave then reduces its R row sums
+// at once (wave_sum8, wave_sum4) and leaves them in LDS; the slab's first R threads
+// add the S wave sums of their row in wave order (deterministic) and store
+// y: the cross-wave step of a row that spans waves, as in gemv_split, once
+// per slab.  Units past the slab's last row are padding: they re-read that
+// row's units and are not stored.
+//
+// Preconditions (checked by the host): F is kQ8, kQ4 or kF16X32; the row is
+// P = ceil(N / kElems / 64) = S * Q units with blockDim.x = 64 S, S <= 16;
+// A and x 16-byte aligned; 1 <= M <= 2^30.  No dynamic LDS.
+template <int F, int Q, int D, int kSlabRows>
+__global__ void __launch_bounds__(1024)
+gemv_slab(const uint8_t* __restrict__ A, const uint16_t* __restrict__ scale,
+          const uint8_t* __restrict__ x, float* __restrict__ y, int M, int N)
+{
+    static_assert(F == kQ8 || F == kQ4 || F == kF16X32, "formats that would stage x");
+    static_assert(kSlabRows == 4 || kSlabRows == 8, "rows per slab");
+    static_assert((kSlabRows * Q) % D == 0 && D % Q == 0, "load slots must map to fixed rows and passes");
+    using T = Traits<F>;
+    constexpr int G = T::kXGran;
+    constexpr int U = kSlabRows * Q;            // units per wave and slab
+    constexpr int kAux = 2;                     // A: non-temporal
+    __shared__ float part[16 * kSlabRows];      // [wave][row of the slab]
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = blockDim.x >> 6;
+    const int nchunks = N / T::kElems;
+    const uint32_t row_bytes = (uint32_t)nchunks * 16;
+    const int groups = N / 128;                 // INT4 scales per row
+    const int nslabs = (M + kSlabRows - 1) / kSlabRows;
+
+    // this lane's x granules for passes w + q S (zeros past the row end)
+    const auto xrsrc = make_rsrc(x, (uint32_t)nchunks * G * 16);
+    u32x4 xr[Q][G];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            xr[q][g] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, (((w + q * S) * 64 + lane) * G + g) * 16, 0, 0));
+    bool paired = false;   // INT4: x reordered for q4_word once, after the first A loads
+
+    for (int slab = blockIdx.x; slab < nslabs; slab += gridDim.x) {
+        const int row0 = slab * kSlabRows;
+        const int rows = M - row0 < kSlabRows ? M - row0 : kSlabRows;
+        // INT8: the slab's row scales, one per thread of the first 8 (zeros
+        // past the slab), loaded before A so that they are the oldest loads
+        float srow = 0.0f;
+        if constexpr (F == kQ8)
+            srow = half_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(
+                make_rsrc(scale + row0, (uint32_t)rows * 2), (int)threadIdx.x * 2, 0, 0));
+
+        u32x4 buf[D];
+        uint16_t sbuf[D];
+        // unit j: slab row j / Q (padding re-reads the last row), pass w + (j % Q) S
+        auto issue = [&](int d, int j) {
+            const int r = j / Q;
+            const int row = row0 + (r < rows ? r : rows - 1);
+            const int pass = w + (j % Q) * S;
+            const auto rsrc = make_rsrc(A + (int64_t)row * row_bytes, row_bytes);
+            buf[d] = __builtin_bit_cast(u32x4,
+                                        __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane * 16 + pass * 1024, 0, kAux));
+            if constexpr (F == kQ4) {
+                const auto srsrc = make_rsrc(scale + (int64_t)row * groups, (uint32_t)groups * 2);
+                sbuf[d] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, (lane >> 2) * 2 + pass * 32, 0, 0);
+            } else {
+                sbuf[d] = 0;
+            }
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            issue(d, d);
+        if constexpr (F == kQ4) {
+            // x is older than every A load in the counter
+            if (!paired) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        xr[q][g] = q4_pair_x(xr[q][g]);
+                paired = true;
+            }
+        }
+
+        float acc[kSlabRows];
+#pragma unroll
+        for (int r = 0; r < kSlabRows; ++r)
+            acc[r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int d = j % D, q = j % Q, r = j / Q;
+            if constexpr (F == kF16X32)
+                acc[r] = chunk_f16x32(buf[d], xr[q][0], xr[q][G - 1], acc[r]);
+            else if constexpr (F == kQ8)
+                acc[r] = q8_chunk(buf[d], xr[q][0], xr[q][G - 1], acc[r]);
+            else
+                acc[r] = chunk_q4(buf[d], xr[q], half_bits_to_float(sbuf[d]), acc[r]);
+            if (j + D < U)
+                issue(d, j + D);
+        }
+        // lane l holds row l / (64 / R)
+        constexpr int kShift = kSlabRows == 8 ? 3 : 4;
+        float t;
+        if constexpr (kSlabRows == 8)
+            t = wave_sum8(acc);
+        else
+            t = wave_sum4(acc);
+        if ((lane & ((1 << kShift) - 1)) == 0 && (lane >> kShift) < rows)
+            part[w * kSlabRows + (lane >> kShift)] = t;
+
+        __syncthreads();
+        if ((int)threadIdx.x < rows) {
+            float sum = part[threadIdx.x];
+            for (int k = 1; k < S; ++k)
+                sum += part[k * kSlabRows + threadIdx.x];
+            if constexpr (F == kQ8)
+                sum *= srow;
+            y[row0 + threadIdx.x] = sum;
+        }
+        __syncthreads();   // part is reused by the next slab
+    }
+}
+
 // ---------------------------------------------------------------- element-wise kernel
 // Any N >= 0 and any alignment: one wave per row, lane l takes columns
 // l, l+64, ... with scalar loads (INT4: bytes l, l+64, ..., two columns

@@ -56,7 +56,7 @@ int main(void)
             if (!(info.grid >= (M > 0) && info.block >= 64 && info.block <= 1024 && info.block % 64 == 0))
                 fprintf(stderr, "kind %d M %d N %d aligned %d device %d/%d: variant %d grid %d block %d\n", kind, M, N,
                         aligned, devices[d][0], devices[d][1], info.variant, info.grid, info.block);
-            CHECK(info.variant >= 1 && info.variant <= 6);
+            CHECK(info.variant >= 1 && info.variant <= 7);
             CHECK(info.grid >= (M > 0) && info.block >= 64 && info.block <= 1024 && info.block % 64 == 0);
             CHECK((int64_t)info.grid * info.block <= ((int64_t)1 << 30));
             CHECK(info.units_in_flight >= 1 && info.units_in_flight <= 8);
@@ -82,7 +82,7 @@ int main(void)
         static const int variants[] = {1, 2, 4, 5, 6, 2, 1, 0, 3, 7};
         static const int waves[] = {4, 8, 2, 16, 4, 8, 12, 3, 0};
         static const int depths[] = {4, 2, 8, 1, 3, 5, 4, 0, 6};
-        static const int rows[] = {1, 2, 4, 1, 0, -1};
+        static const int rows[] = {1, 2, 4, 8, 0, -1};
         static const int orders[] = {-1, 2, 1, 0, -1, 3, -2};
         static const int caps[] = {0, 2, 3, 4, 0, 1, 6, -1};
         const gemv_plan p = {variants[next() % 10], waves[next() % 9], depths[next() % 9], rows[next() % 6],

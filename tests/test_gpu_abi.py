@@ -145,14 +145,14 @@ def test_describe_launch_fills_all_cus(gpu):
     # workgroup's LDS and the rows are many, else x read with each unit
     lds_max = props.shared_memory_per_block
     assert binding.describe_launch("q8", 4096, 31744)["variant"] == 1
-    assert binding.describe_launch("q8", 4096, 32768)["variant"] == 1
+    assert binding.describe_launch("q8", 4096, 34816)["variant"] == 1   # (rows of 32 units: row slabs)
     assert binding.describe_launch("q4", 4096, 34816)["variant"] == 1
     assert binding.describe_launch("q4", 1024, 33280)["variant"] == 2
     q8_beyond = lds_max // 2048 * 1024 + 1024            # one unit past what fits
     q4_beyond = lds_max // 4096 * 2048 + 2048
     assert binding.describe_launch("q8", 4096, q8_beyond)["variant"] == 2
     assert binding.describe_launch("q4", 4096, q4_beyond)["variant"] == 2
-    for kind, M, N in (("q8", 4096, 32768), ("q4", 4096, 34816), ("q8", 1024, 32768)):
+    for kind, M, N in (("q8", 4096, 34816), ("q4", 4096, 34816), ("q8", 1024, 32768)):
         info = binding.describe_launch(kind, M, N)
         assert info["variant"] == 2 or info["lds_bytes"] <= lds_max, (kind, M, N, info)
     # INT8/INT4 rows of at most 32 chunks: the packed short-row kernel
@@ -167,8 +167,12 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("f16", 4096, 512)["variant"] == 5
     assert binding.describe_launch("f16", 14336, 1024)["variant"] == 5
     assert binding.describe_launch("f32", 14336, 256)["variant"] == 2
-    assert binding.describe_launch("f16x32", 14336, 512)["variant"] == 5
-    assert binding.describe_launch("f16x32", 4096, 1024)["variant"] == 2
+    assert binding.describe_launch("f16x32", 3000, 512)["variant"] == 5
+    assert binding.describe_launch("f16x32", 200, 1024)["variant"] == 2
+    # FP16 with FP32 x from one row per CU (one-unit rows from 14 per CU):
+    # row slabs, x slices in registers
+    assert binding.describe_launch("f16x32", 14336, 512)["variant"] == 7
+    assert binding.describe_launch("f16x32", 4096, 1024)["variant"] == 7
     assert binding.describe_launch("f16", 14336, 1536)["variant"] == 5
     assert binding.describe_launch("q8", 4096, 3072)["variant"] == 1   # INT8 three-unit rows stay staged
     # more than 2^30 rows: the row-walking kernels' int cursors could wrap,
@@ -176,32 +180,33 @@ def test_describe_launch_fills_all_cus(gpu):
     for kind in ("f16", "q8", "q4"):
         assert binding.describe_launch(kind, (1 << 30) + 1, 128)["variant"] == 3
         assert binding.describe_launch(kind, 1 << 30, 128)["variant"] != 3
-    # FP16 A with FP32 x: x staged in LDS for long rows or many rows, read
-    # with each unit otherwise, and never staged beyond what a workgroup may
-    # hold
-    assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 1
-    assert binding.describe_launch("f16x32", 14336, 4096)["variant"] == 1
-    assert binding.describe_launch("f16x32", 4096, 4096)["variant"] == 1
-    assert binding.describe_launch("f16x32", 8 * cus, 4096)["variant"] == 1   # 8 rows per CU: staged too
+    # FP16 A with FP32 x: row slabs for rows of up to 16 units (and an even
+    # count up to 32); longer rows staged in LDS for many rows, read with
+    # each unit otherwise, and never staged beyond what a workgroup may hold
+    assert binding.describe_launch("f16x32", 8192, 8192)["variant"] == 7
+    assert binding.describe_launch("f16x32", 14336, 4096)["variant"] == 7
+    assert binding.describe_launch("f16x32", 4096, 4096)["variant"] == 7
+    assert binding.describe_launch("f16x32", 8 * cus, 4096)["variant"] == 7
     info = binding.describe_launch("f16x32", 16 * cus, 32768)
     assert info["variant"] == 1 and info["lds_bytes"] == 4 * 32768 + 1024 <= lds_max, info   # x and spare granules
     assert binding.describe_launch("f16x32", 16 * cus, lds_max // 4 + 512)["variant"] == 2
-    # few long rows (up to 5 per CU for rows of 16 units and more, 7 for
-    # shorter ones): split rows, x read with each unit; two waves per row
-    # from one row per CU, below that enough waves to fill the chip
-    for M, N in ((cus, 32768), (4 * cus, 32768), (5 * cus, 32768), (7 * cus, 4096)):
+    # few long rows (up to 5 per CU for rows of 16 units and more; shorter
+    # ones from one row per CU take row slabs): split rows, x read with each
+    # unit; two waves per row from one row per CU, below that enough waves
+    # to fill the chip
+    for M, N in ((cus, 32768), (4 * cus, 32768), (5 * cus, 32768), (cus, 4096 * 9)):
         info = binding.describe_launch("f16x32", M, N)
         assert info["variant"] == 6 and info["block"] == 128 and info["lds_bytes"] == 0 and info["grid"] == M, info
     info = binding.describe_launch("f16x32", 64, 32768)
     assert info["variant"] == 6 and info["grid"] * info["block"] // 64 >= 4 * cus, info
     assert binding.describe_launch("f16x32", 6 * cus, 32768)["variant"] == 1
     # few INT8 rows of four units or more (up to 6 per CU): split rows; a few
-    # more: x read with each unit; few INT4 rows of four units or more read
-    # x with each unit
+    # more: x read with each unit; few INT4 rows of six units (others take
+    # row slabs) read x with each unit
     assert binding.describe_launch("q8", 6 * cus, 8192)["variant"] == 6
     assert binding.describe_launch("q8", 6 * cus + 1, 8192)["variant"] == 2
-    assert binding.describe_launch("q4", 4 * cus, 8192)["variant"] == 2
-    assert binding.describe_launch("q4", 4 * cus + 1, 8192)["variant"] == 1
+    assert binding.describe_launch("q4", 4 * cus, 12288)["variant"] == 2
+    assert binding.describe_launch("q4", 4 * cus + 1, 12288)["variant"] == 1
 
 
 def test_launches_stay_within_the_dispatch_limit(gpu):

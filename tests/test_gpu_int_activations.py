@@ -8,9 +8,10 @@ and accumulate in FP32 ("membound", section "The kernel decode actually
 runs: dequant GEMV": the reference weight is exactly q*s, FP32 accumulate),
 so the error must not depend on the mean of x or on where the codes sit.
 Every case runs at the shapes that reach each INT8/INT4 plan: staged x
-(8192^2, 14336x4096, 4096x14336), x read per unit (1792x4096), x in registers
-(rows of one or two units: 4096x1024, 4096x2048) and packed short rows
-(14336x512).  Codes made from Gaussian weights come from the oracle's
+(8192^2, 14336x4096), x read per unit (1792x4096), x in registers (rows of
+one or two units: 4096x1024, 4096x2048), packed short rows (14336x512) and
+row slabs (INT4 4096x14336; INT8 rows of 10 units, one pass per wave, and
+of 24, two passes per wave).  Codes made from Gaussian weights come from the oracle's
 quantiser, never from the GPU's.
 """
 import numpy as np
@@ -23,7 +24,7 @@ from gpu_util import run_gpu, run_oracle, say, within_fp32_bound, within_gate
 pytestmark = pytest.mark.gpu
 
 _SHAPES = {
-    "q8": [(8192, 8192), (14336, 4096), (1792, 4096), (4096, 1024), (14336, 512)],
+    "q8": [(8192, 8192), (14336, 4096), (1792, 4096), (4096, 1024), (14336, 512), (1913, 10240), (2295, 24576)],
     "q4": [(4096, 14336), (14336, 4096), (1792, 4096), (4096, 2048), (14336, 512)],
 }
 _WEIGHTS = ("codes", "gauss", "outlier")

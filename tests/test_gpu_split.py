@@ -34,7 +34,7 @@ def _n(kind, units, ragged):
 # (M, units per row, ragged): waves per row S from 2 to 16 on 256 CUs, two
 # units per wave (2 in flight) and more (4 in flight, padded)
 _CASES = [(1, 40, True), (3, 33, False), (17, 20, True), (300, 9, True), (300, 4, False), (700, 16, True),
-          (700, 5, False), (1100, 30, True)]
+          (700, 5, False), (1100, 30, True), (17, 12, False), (200, 10, True), (100, 4, True)]
 
 
 @pytest.mark.parametrize("kind", ["f32", "f16", "f16x32", "q8", "q4"])
@@ -58,12 +58,13 @@ def test_split_rows_match_the_oracle(gpu, oracle_mod, kind):
         assert within_fp32_bound(kind, ops, y, ref) <= 1.0, label
     if cus == 256:
         # the cases reach every waves-per-row value and both depths (INT4,
-        # split only for rows of at most 16 units, up to 4 waves per row;
-        # INT8 splits with 2 in flight; FP16 with FP32 x two waves per row
-        # from one row per CU, 8 or 16 for fewer rows, its 4-wave split
-        # running as an explicit plan in test_gpu_plans)
-        want = {2, 4} if kind == "q4" else ({2, 8, 16} if kind == "f16x32" else {2, 4, 8, 16})
-        depths = {2} if kind == "q8" else {2, 4}
+        # split only for rows of at most 16 units and fewer rows than CUs,
+        # up to 4 waves per row; INT8 splits with 2 in flight; FP16 with
+        # FP32 x splits only fewer rows than CUs, 4 in flight: from one row
+        # per CU its rows take row slabs, and its 2-deep split runs as an
+        # explicit plan in test_gpu_plans)
+        want = {2, 4} if kind == "q4" else {2, 4, 8, 16}
+        depths = {2} if kind == "q8" else ({4} if kind == "f16x32" else {2, 4})
         assert {s for s, _ in seen} == want and {d for _, d in seen} == depths, seen
 
 

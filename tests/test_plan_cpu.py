@@ -51,9 +51,9 @@ def test_every_plan_is_consistent(kind, dev):
             continue
         p = plan(kind, M, N, **dev)
         where = (kind, M, N, dev, p)
-        assert p["variant"] in (1, 2, 3, 4, 5, 6), where
-        assert 1 <= p["grid"] and p["block"] in (128, 256, 512, 768, 1024), where
-        assert p["block"] in (256, 512, 768) or p["variant"] == 6, where
+        assert p["variant"] in (1, 2, 3, 4, 5, 6, 7), where
+        assert 1 <= p["grid"] and p["block"] % 64 == 0 and 64 <= p["block"] <= 1024, where
+        assert p["block"] in (256, 512, 768) or p["variant"] in (6, 7), where
         assert p["grid"] * p["block"] <= 1 << 30, where            # 32-bit work-item count
         aligned_path = N > 0 and N % ELEMS_PER_CHUNK[kind] == 0
         if not aligned_path:
@@ -100,7 +100,30 @@ def test_every_plan_is_consistent(kind, dev):
                 # units per wave
                 assert M <= 16 * dev["cus"], where
                 assert p["units_in_flight"] == (2 if -(-P // S) == 2 else 4), where
+        if p["variant"] == 7:
+            _check_slab(kind, M, N, dev, p, where)
         assert 1 <= p["units_in_flight"] <= 8, where
+
+
+def _check_slab(kind, M, N, dev, p, where):
+    # row slabs: S waves per workgroup own one or two passes each of every
+    # row (S = P, or P / 2 for rows of 17-32 units), slabs of 4 or 8 rows,
+    # 4 in flight (8 with two passes per wave); the grid's slabs cover M
+    cus = dev["cus"]
+    S = p["block"] // 64
+    P = -(-(N // ELEMS_PER_CHUNK[kind]) // 64)
+    assert kind in ("q8", "q4", "f16x32") and N % ELEMS_PER_CHUNK[kind] == 0, where
+    assert S == (P if P <= 16 else P // 2) and P % S == 0 and P <= 32, where
+    assert p["units_in_flight"] == (4 if S == P else 8), where
+    assert p["rows_per_wave"] % 4 == 0 and p["grid"] * p["rows_per_wave"] >= M, where
+    assert p["lds_bytes"] == 0 and p["stage_order"] == -1, where
+    if kind == "f16x32":
+        assert M >= cus and (P >= 2 or M >= 14 * cus), where
+    elif kind == "q4":
+        assert M >= cus and 3 <= P <= 16 and P != 6 and (P <= 7 or M <= 12 * cus), where
+        assert p["grid"] <= max(1, 32 // S) * cus, where        # at most 32 waves per CU
+    else:
+        assert P >= 9 and 2 * cus <= M <= 100 * cus, where
 
 
 def test_random_shapes_keep_the_invariants():
@@ -119,7 +142,9 @@ def test_random_shapes_keep_the_invariants():
         where = (kind, M, N, dev, p)
         assert 1 <= p["grid"] and p["grid"] * p["block"] <= 1 << 30, where
         assert p["lds_bytes"] <= dev["lds_max"], where
-        if p["variant"] != 4:
+        if p["variant"] == 7:
+            _check_slab(kind, M, N, dev, p, where)
+        elif p["variant"] != 4:
             assert p["grid"] * (p["block"] // 64) * p["rows_per_wave"] >= M, where
         if (p["variant"] in (1, 2) and M >= 8 * dev["cus"] and not _fewer_stagings(kind, M, p, dev["cus"])
                 and not _four_rows(kind, M, N, dev["cus"])):
@@ -157,12 +182,42 @@ def test_huge_shapes_take_the_elementwise_kernel():
 
 
 def test_headline_shapes_on_mi355x():
-    # FP16 and FP32 read x with each unit; INT8/INT4 stage it; all fill every CU
+    # FP16 and FP32 read x with each unit; INT8 and INT4 14336x4096 stage it;
+    # INT4 4096x14336 and FP16 with FP32 x take row slabs (x slices in
+    # registers); all fill every CU
     for kind, M, N, variant in (("f16", 8192, 8192, 2), ("f16", 4096, 14336, 2), ("f16", 14336, 4096, 2),
                                 ("f32", 8192, 8192, 2), ("q8", 8192, 8192, 1), ("q8", 14336, 4096, 1),
-                                ("q4", 4096, 14336, 1), ("q4", 14336, 4096, 1)):
+                                ("q4", 4096, 14336, 7), ("q4", 14336, 4096, 1), ("f16x32", 8192, 8192, 7),
+                                ("f16x32", 4096, 14336, 7), ("f16x32", 14336, 4096, 7)):
         p = plan(kind, M, N)
         assert p["variant"] == variant and p["grid"] >= 256, (kind, M, N, p)
+
+
+def test_slab_plans_of_the_named_shapes():
+    # (variant, block = 64 S, loads in flight, rows per slab, grid)
+    def geo(p):
+        return (p["variant"], p["block"], p["units_in_flight"], p["rows_per_wave"], p["grid"])
+
+    # INT4 4096x14336: 7 passes, 7 waves, one pass each, slabs of 4 rows
+    assert geo(plan("q4", 4096, 14336)) == (7, 448, 4, 4, 1024)
+    # FP16 with FP32 x: 16 passes, 16 waves; 28 passes: 14 waves of two
+    # passes, 8 in flight, slabs of 8 rows (slabs of 4 would give the
+    # busiest CU as many rows in twice the workgroups)
+    assert geo(plan("f16x32", 8192, 8192)) == (7, 1024, 4, 4, 2048)
+    assert geo(plan("f16x32", 4096, 14336)) == (7, 896, 8, 8, 512)
+    # rows of 17-32 units with slabs of 4 rows where those load the busiest
+    # CU less (INT8 2295x24576: 3 slabs of 4 rows against 2 of 8)
+    assert geo(plan("q8", 2295, 24576)) == (7, 768, 8, 4, 574)
+    # INT4: at most 32 waves per CU, workgroups walk the slabs beyond
+    p = plan("q4", 300000, 8192)
+    assert (p["variant"], p["block"], p["grid"]) == (7, 256, 8 * 256) and p["rows_per_wave"] >= 300000 / (8 * 256)
+    # where the streaming kernel stays: INT4 rows of 2 or 6 units, INT8 rows
+    # under 9 units, long INT4 rows beyond 12 rows per CU, INT8 beyond 100,
+    # fewer rows than CUs
+    for kind, M, N in (("q4", 14336, 4096), ("q4", 5113, 10880), ("q8", 14336, 4096), ("q8", 8192, 8192),
+                       ("q4", 9681, 21504), ("q8", 33708, 13184), ("q4", 255, 8192), ("f16x32", 255, 8192),
+                       ("q8", 511, 24576)):
+        assert plan(kind, M, N)["variant"] != 7, (kind, M, N)
 
 
 def test_long_rows_stage_x_up_to_the_device_limit():
@@ -183,9 +238,10 @@ def test_long_rows_stage_x_up_to_the_device_limit():
 
 def test_few_rows_rules():
     cus = 256
-    # few INT4 rows of four units or more: x per unit; one more row: staged
-    assert plan("q4", 4 * cus, 8192)["variant"] == 2
-    assert plan("q4", 4 * cus + 1, 8192)["variant"] == 1
+    # few INT4 rows of four units or more (rows of 6 units: the others take
+    # row slabs): x per unit; one more row: staged
+    assert plan("q4", 4 * cus, 12288)["variant"] == 2
+    assert plan("q4", 4 * cus + 1, 12288)["variant"] == 1
     # INT8 rows of four units or more, up to 6 rows per CU: split rows, S for
     # 4 waves per CU, 2 in flight; a few more rows (up to 8 per CU, up to 16
     # units): x read with each unit
@@ -304,9 +360,10 @@ def test_cost_model_replaces_plans_the_measurements_beat():
     assert _geometry(plan("f16", 278, 16896)) == (6, 278, 256, 4, 1)
     assert _geometry(plan("f32", 902, 5248)) == (6, 902, 128, 4, 1)
     assert _geometry(plan("f16", 774, 24704)) == (6, 774, 128, 4, 1)
-    # the other formats keep the measured rules alone
+    # the other formats keep the measured rules alone (FP16 with FP32 x:
+    # row slabs)
     assert plan("f16_acc16", 2552, 9088)["variant"] == 2
-    assert plan("f16x32", 2562, 14336)["variant"] == 1
+    assert plan("f16x32", 2562, 14336)["variant"] == 7
 
 
 def test_rules_remeasured_by_brute_force():
@@ -317,8 +374,9 @@ def test_rules_remeasured_by_brute_force():
     # 7.52 -> 7.30); packed short rows beyond 16 groups per CU: two groups
     # per wave (INT4 40979x512 5.73 -> 4.79); INT8 rows of 8-10 units: 4
     # waves, two rows per wave, split staging (8192x8192 12.11 -> 11.65)
+    # (FP16 with FP32 x 5484x4608 has since taken row slabs)
     p = plan("f16x32", 5484, 4608)
-    assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 256, 2, 4, 512)
+    assert (p["variant"], p["block"], p["units_in_flight"], p["grid"]) == (7, 576, 4, 1371)
     p = plan("q4", 14336, 4096)
     assert (p["variant"], p["block"], p["stage_order"], p["grid"]) == (1, 512, 2, 4 * 256)
     p = plan("q4", 40979, 512)
@@ -351,8 +409,9 @@ def test_rules_from_the_random_shape_search():
     assert (p["variant"], p["block"], p["units_in_flight"], p["grid"]) == (6, 128, 4, 10463)
     p = plan("q4", 5832, 25088)
     assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 512, 2, 4, 256)
+    # (INT4 4096x8192, rows of 4 units, has since taken row slabs)
     p = plan("q4", 4096, 8192)
-    assert (p["variant"], p["block"], p["stage_order"], p["units_in_flight"], p["grid"]) == (1, 512, 2, 4, 512)
+    assert (p["variant"], p["block"], p["units_in_flight"], p["grid"]) == (7, 256, 4, 1024)
     p = plan("f16x32", 977, 27392)
     assert (p["variant"], p["block"], p["units_in_flight"], p["grid"]) == (6, 128, 2, 977)
     p = plan("f16x32", 12815, 14720)
@@ -444,7 +503,9 @@ def test_planner_plans_as_explicit_plans():
     for kind, M, N, p in (("f16", 8192, 8192, (2, 8, 8, 1, -1, 0)), ("q8", 8192, 8192, (1, 4, 4, 2, 2, 0)),
                              ("q4", 14336, 4096, (1, 8, 2, 1, 2, 4)), ("f16", 2552, 9088, (6, 2, 2, 1, -1, 0)),
                              ("q4", 14336, 512, (4, 8, 1, 1, -1, 0)), ("f16", 14336, 512, (2, 8, 4, 4, -1, 0)),
-                             ("f16x32", 5484, 4608, (1, 4, 4, 1, 2, 2)), ("q8", 1000, 16400, (6, 2, 2, 1, -1, 0))):
+                             ("f16x32", 5484, 4608, (7, 9, 4, 4, -1, 0)), ("q8", 1000, 16400, (6, 2, 2, 1, -1, 0)),
+                             ("q4", 4096, 14336, (7, 7, 4, 4, -1, 0)), ("f16x32", 4096, 14336, (7, 14, 8, 8, -1, 0)),
+                             ("q4", 300000, 8192, (7, 4, 4, 4, -1, 8))):
         assert check(kind, M, N, p) == plan(kind, M, N), (kind, M, N, p)
 
 
@@ -466,6 +527,14 @@ def test_explicit_plans_the_library_has_no_kernel_for():
             ("f16_acc16", 4096, 8192, (6, 2, 2, 1, -1, 0)),   # FP16 accumulation: variants 2 and 5
             ("q8", 4096, 98304, (1, 4, 4, 1, 1, 0)),     # staged x beyond the LDS a workgroup may hold
             ("f16", 4096, 4100, (2, 4, 4, 1, -1, 0)),    # not a multiple of the chunk: element-wise only
+            ("f16", 4096, 4096, (7, 4, 4, 4, -1, 0)),    # row slabs: INT8, INT4, FP16 with FP32 x only
+            ("q8", 4096, 8192, (7, 3, 4, 4, -1, 0)),     # slabs: S waves own P / S passes (P = 8)
+            ("q8", 4096, 8192, (7, 2, 4, 4, -1, 0)),     # ... one or two passes per wave
+            ("q8", 4096, 8192, (7, 8, 2, 4, -1, 0)),     # ... 4 or 8 in flight
+            ("q8", 4096, 8192, (7, 8, 8, 4, -1, 0)),     # ... that divide the slab's units
+            ("q8", 4096, 8192, (7, 8, 4, 2, -1, 0)),     # ... slabs of 4 or 8 rows
+            ("q8", 4096, 8192, (7, 8, 4, 4, 2, 0)),      # ... nothing staged
+            ("q8", 4096, 17408, (7, 17, 4, 4, -1, 0)),   # ... at most 16 waves
             ("f16", 4096, 4096, (7, 4, 4, 1, -1, 0)), ("f16", 4096, 4096, (2, 4, 4, 0, -1, 0)),
             ("f16", 4096, 4096, (2, 4, 4, 1, -1, -1))):
         assert check(kind, M, N, p) is None, (kind, M, N, p)
@@ -499,5 +568,7 @@ def test_every_candidate_plan_keeps_the_invariants():
             assert info["lds_bytes"] <= dev["lds_max"], where
             if p[0] == 6:
                 assert info["grid"] == M and info["block"] == 64 * p[1], where
+            elif p[0] == 7:
+                assert info["block"] == 64 * p[1] and info["grid"] * info["rows_per_wave"] >= M, where
             elif p[0] != 4:
                 assert info["grid"] * (info["block"] // 64) * info["rows_per_wave"] >= M, where
