@@ -152,8 +152,11 @@ int gemv_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream
  * kernel for INT8/INT4 rows of at most 32 16-byte chunks, several rows per
  * wave load, 5 = kernel for rows of one to three wave loads with each
  * lane's x in registers, 6 = split rows: few long rows, a workgroup of 2 to
- * 16 waves per row whose wave sums meet in LDS), grid and workgroup sizes,
- * rows per wave (at most),
+ * 16 waves per row whose wave sums meet in LDS, 7 = row slabs: INT8, INT4
+ * and FP16 with FP32 x, a workgroup of S waves takes 4 or 8 rows at a time,
+ * each wave one or two passes of every row with its slice of x in
+ * registers, the wave sums of a row meeting in LDS), grid and workgroup
+ * sizes, rows per wave (at most; row slabs: the rows each workgroup takes),
  * 1-KiB loads in flight per wave, dynamic LDS bytes (x staged up to what
  * one workgroup may hold on the device), and the order in which x is staged
  * relative to the first loads of A.  The geometry is chosen per shape:
@@ -189,11 +192,17 @@ int gemv_describe_launch_for(int kind, int M, int N, int aligned, int cus, int l
  *                    with FP32 x); 2 streaming kernel, x read with each
  *                    unit; 4 packed short rows (INT8/INT4 rows of at most
  *                    32 16-byte chunks); 5 x in registers (rows of exactly
- *                    1-3 wave loads); 6 split rows (a workgroup per row)
- *   waves            waves per workgroup (split rows: waves per row, 2-16)
- *   units_in_flight  1-KiB wave loads in flight per wave
+ *                    1-3 wave loads); 6 split rows (a workgroup per row);
+ *                    7 row slabs (INT8, INT4, FP16 with FP32 x: S waves own
+ *                    P / S = 1 or 2 passes each of every row, P the wave
+ *                    loads per row, S <= 16)
+ *   waves            waves per workgroup (split rows: waves per row, 2-16;
+ *                    row slabs: S)
+ *   units_in_flight  1-KiB wave loads in flight per wave (row slabs: 4 or 8,
+ *                    dividing the slab's units per wave)
  *   rows_per_wave    rows (packed: row groups) per wave the grid is sized
- *                    for; waves walk whatever rows lie beyond (1 for split)
+ *                    for; waves walk whatever rows lie beyond (1 for split;
+ *                    row slabs: rows per slab, 4 or 8)
  *   stage_order      variant 1: 0 A's first loads before x's staging, 1 x
  *                    first, 2 staging loads / A's first loads / LDS writes;
  *                    -1 otherwise
@@ -214,7 +223,8 @@ typedef struct gemv_plan {
  * GEMV_E_UNSUPPORTED for a plan the library holds no kernel for or that does
  * not fit the shape (a staged x beyond lds_max, x in registers for rows not
  * of 1-3 wave loads, split rows with fewer than two loads per wave or beyond
- * 2^30 work-items, packed rows for FP formats or rows over 32 chunks, FP16
+ * 2^30 work-items, packed rows for FP formats or rows over 32 chunks, row
+ * slabs for FP32/FP16 or with S not dividing P into one or two passes, FP16
  * accumulation outside variants 2 and 5), GEMV_E_INVAL for bad arguments
  * (kind outside 0-5, M or N < 1, cus or lds_max <= 0, null pointers).  The
  * shape must take the bandwidth path (N a multiple of a 16-byte chunk's

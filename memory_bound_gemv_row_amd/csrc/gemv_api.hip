@@ -761,43 +761,57 @@ bool four_rows_rule(const Plan& p) { return (p.variant == 2 && p.rows == 4 && p.
 // Row slabs (variant 7, gemv_slab) for INT8, INT4 and FP16 with FP32 x,
 // whose x the streaming kernel stages in LDS once per workgroup or reads
 // with every unit.  A slab plan takes S = P waves per workgroup (S = P / 2,
-// two passes per wave, for rows of 17-32 units), 4 rows per slab, 4 loads
-// in flight (8 with two passes per wave).  Where it is taken: FP16 with FP32
-// x for rows of 2 units and more, and one-unit rows from 14 rows per CU;
-// INT4 rows of 3-16 units save 6 (3-7 units at any row count, longer rows
-// up to 12 rows per CU); INT8 rows of 9 units and more between 2 and 100
-// rows per CU.  Slabs of 8 rows where two passes per wave give the busiest
-// CU no more rows than slabs of 4 (fewer workgroups, each loading its x
-// once).  INT4 caps the grid at 32 waves per CU, so that workgroups walk
-// several slabs with x loaded once.  Graph-timed on four seeds of 24 random
-// shapes per format (bench-style ring over >= 1 GiB), against the rules
-// before: geometric mean 0.957 / 0.945 (FP16 with FP32 x, seeds 0-1 / 2-3),
-// 0.968 / 0.964 (INT4), 0.990 / 0.988 (INT8), with no INT shape slower by
-// more than 3 %: INT4 4096 x 14336 8.08 -> 7.84 us, FP16 with FP32 x
-// 8192 x 8192 22.82 -> 22.02, INT8 2295 x 24576 14.51 -> 12.21, INT4
-// 569 x 8320 4.16 -> 3.25.  Rows of 2 units (INT4 14336 x 4096 7.30 ->
-// 7.74), INT8 rows of 4-8 units (14336 x 4096 10.74 -> 11.15, 8192 x 8192
-// 12.39 -> 12.74) and INT4 rows of 6 units (5113 x 10880 8.17 -> 8.79)
-// stay with the streaming kernel.
-bool slab_plan(int kind, int M, int P, int cus, Plan* p)
+// two passes per wave, for rows of 17-32 units and INT8 rows of an even
+// count from 10), 4 rows per slab, 4 loads in flight (8 with two passes
+// per wave).  Where it is taken: FP16 with FP32 x from one row per CU, for
+// rows of 2 units and more, and one-unit rows from 14 rows per CU; INT4
+// rows of 3-16 units but 6, from one row per CU (rows of 8 units and more
+// only up to 12 rows per CU), and one-unit rows of more than 32 chunks
+// (past the packed kernel) from 4 rows per CU; INT8 rows of 9 units and
+// more between 2 and 100 rows per CU.  Slabs of 8 rows where two passes
+// per wave give the busiest CU no more rows than slabs of 4 (fewer
+// workgroups, each loading its x once) and every CU still a slab.  INT4 caps the grid at 32 waves per
+// CU, so that workgroups walk several slabs with x loaded once.
+// Graph-timed on four seeds of 24 random shapes per format (bench-style
+// ring over >= 1 GiB), against the rules before: geometric mean 0.957 /
+// 0.945 (FP16 with FP32 x, seeds 0-1 / 2-3), 0.968 / 0.964 (INT4), 0.990 /
+// 0.988 (INT8), with no INT shape slower by more than 3 %: INT4 4096 x
+// 14336 8.08 -> 7.84 us, FP16 with FP32 x 8192 x 8192 22.82 -> 22.02,
+// INT8 2295 x 24576 14.51 -> 12.21, INT4 569 x 8320 4.16 -> 3.25.  Rows of
+// 2 units (INT4 14336 x 4096 7.30 -> 7.74), INT8 rows of 4-8 units (14336 x
+// 4096 10.74 -> 11.15, 8192 x 8192 12.39 -> 12.74) and INT4 rows of 6
+// units (5113 x 10880 8.17 -> 8.79) stay with the streaming kernel.  A
+// fifth seed, held out (the plan search, every candidate timed): INT4 0.937
+// and FP16 with FP32 x 0.962 of the previous planner's times, INT8 1.001;
+// its INT4 one-unit rows past the packed kernel (51636 x 1408 10.34 ->
+// 9.18 us, 26708 x 1536 7.20 -> 6.53) and INT8 rows of 16 units (4039 x
+// 15616 12.47 at one pass per wave, 11.57-11.86 at two) gave the last two
+// rules, which the four training seeds support too (INT4 22965 x 2048
+// 7.27 -> 6.73; INT8 2567 x 15616 10.71 -> 9.04 at two passes, 9.16 at
+// one).
+bool slab_plan(int kind, int M, int nchunks, int cus, Plan* p)
 {
+    const int P = (nchunks + 63) / 64;
     const int64_t rows = M;
     bool take = false;
     if (kind == kF16X32)
         take = rows >= cus && (P >= 2 || rows >= 14 * (int64_t)cus);
     else if (kind == kQ4)
-        take = rows >= cus && P >= 3 && P <= 16 && P != 6 && (P <= 7 || rows <= 12 * (int64_t)cus);
+        take = (rows >= cus && P >= 3 && P <= 16 && P != 6 && (P <= 7 || rows <= 12 * (int64_t)cus)) ||
+               (P == 1 && nchunks > kPackedMaxChunks && rows >= 4 * (int64_t)cus);
     else if (kind == kQ8)
         take = P >= 9 && rows >= 2 * (int64_t)cus && rows <= 100 * (int64_t)cus;
     if (!take || P > 32 || (P > 16 && P % 2 != 0))
         return false;
-    const int S = P <= 16 ? P : P / 2;
+    // two passes per wave for rows of 17-32 units, and for INT8 rows of an
+    // even count from 10 units
+    const int S = P > 16 || (kind == kQ8 && P >= 10 && P % 2 == 0) ? P / 2 : P;
     const int Q = P / S;
     int R = 4;
     if (Q == 2) {
         // rows on the busiest CU: whole slabs, grid of one slab per workgroup
         auto busiest = [&](int r) { return ((rows + r - 1) / r + cus - 1) / cus * r; };
-        if (busiest(8) <= busiest(4))
+        if ((rows + 7) / 8 >= cus && busiest(8) <= busiest(4))
             R = 8;
     }
     *p = Plan{};
@@ -828,7 +842,7 @@ Plan plan_uncached(int kind, int M, int N, bool aligned, const Device& dev)
         return p0;
     const int P = (N / elems_per_chunk(kind) + 63) / 64;
     Plan sl{};
-    if (slab_plan(kind, M, P, dev.cus, &sl))
+    if (slab_plan(kind, M, N / elems_per_chunk(kind), dev.cus, &sl))
         return sl;
     Plan p = p0;
     Plan s{};

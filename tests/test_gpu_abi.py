@@ -160,7 +160,8 @@ def test_describe_launch_fills_all_cus(gpu):
     assert binding.describe_launch("q4", 14336, 1024)["variant"] == 4
     # one-unit rows just past that: x in registers; two-unit rows: staged
     assert binding.describe_launch("q8", 14336, 528)["variant"] == 5
-    assert binding.describe_launch("q4", 14336, 1152)["variant"] == 5
+    assert binding.describe_launch("q4", 1000, 1152)["variant"] == 5
+    assert binding.describe_launch("q4", 14336, 1152)["variant"] == 7   # from 4 rows per CU: row slabs
     assert binding.describe_launch("q8", 14336, 1040)["variant"] == 1
     assert binding.describe_launch("q4", 14336, 2176)["variant"] == 1
     # FP rows of one unit (up to 32 rows per CU) and of two units: x in registers

@@ -8,10 +8,10 @@ and accumulate in FP32 ("membound", section "The kernel decode actually
 runs: dequant GEMV": the reference weight is exactly q*s, FP32 accumulate),
 so the error must not depend on the mean of x or on where the codes sit.
 Every case runs at the shapes that reach each INT8/INT4 plan: staged x
-(8192^2, 14336x4096), x read per unit (1792x4096), x in registers (rows of
-one or two units: 4096x1024, 4096x2048), packed short rows (14336x512) and
-row slabs (INT4 4096x14336; INT8 rows of 10 units, one pass per wave, and
-of 24, two passes per wave).  Codes made from Gaussian weights come from the oracle's
+(8192^2, 14336x4096), x read per unit (1792x4096), x in registers (INT8
+rows of one unit: 4096x1024), packed short rows (14336x512) and row slabs
+(INT4 4096x14336 and one-unit rows of 64 chunks, 4096x2048; INT8 rows of 10
+and of 24 units, two passes per wave).  Codes made from Gaussian weights come from the oracle's
 quantiser, never from the GPU's.
 """
 import numpy as np

@@ -94,11 +94,12 @@ def test_waves_walk_several_rows(gpu, oracle_mod, kind, N, walk):
 
 @pytest.mark.parametrize("kind,N,small,large", [("q8", 1024, 5, 5), ("q8", 1008, 5, 5), ("q8", 2048, 2, 1),
                                                 ("q8", 4096, 2, 1), ("q8", 8192 - 16, 2, 1),
-                                                ("q4", 2048, 5, 5), ("q4", 4096, 5, 1), ("q4", 2176, 5, 1)])
+                                                ("q4", 2048, 7, 7), ("q4", 4096, 5, 1), ("q4", 2176, 5, 1)])
 def test_quantised_x_paths_by_rows(gpu, oracle_mod, kind, N, small, large):
     # INT8/INT4 take x in registers (variant 5: rows of one unit, and few
     # INT4 rows of two), read with each unit (2) for few longer rows, and
-    # staged in LDS (1) for many: each plan at the same row length, with a
+    # staged in LDS (1) for many; INT4 one-unit rows of more than 32 chunks
+    # from 4 rows per CU take row slabs (7): each plan at the same row length, with a
     # ragged last workgroup (and, for many one-unit rows, waves walking
     # several rows two loads deep)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -226,7 +227,7 @@ def test_int8_long_rows_split_staging(gpu, oracle_mod, M, N, rows):
 
 @pytest.mark.parametrize("kind,M,N", [("f32", 8000, 252), ("f32", 9000, 260), ("f16", 14336, 1000),
                                       ("f16x32", 3000, 512), ("f16x32", 3000, 504), ("f16_acc16", 6000, 1024),
-                                      ("q8", 14336, 1008), ("q4", 14336, 2048), ("f16", 14336, 1528),
+                                      ("q8", 14336, 1008), ("q4", 900, 2048), ("f16", 14336, 1528),
                                       ("f32", 4096, 768), ("q4", 200, 6144)])
 def test_x_in_registers_many_rows(gpu, oracle_mod, kind, M, N):
     # rows of one or two wave loads with x held in registers, enough rows

@@ -113,14 +113,17 @@ def _check_slab(kind, M, N, dev, p, where):
     S = p["block"] // 64
     P = -(-(N // ELEMS_PER_CHUNK[kind]) // 64)
     assert kind in ("q8", "q4", "f16x32") and N % ELEMS_PER_CHUNK[kind] == 0, where
-    assert S == (P if P <= 16 else P // 2) and P % S == 0 and P <= 32, where
-    assert p["units_in_flight"] == (4 if S == P else 8), where
+    two = P > 16 or (kind == "q8" and P >= 10 and P % 2 == 0)   # two passes per wave
+    assert S == (P // 2 if two else P) and P % S == 0 and P <= 32, where
+    assert p["units_in_flight"] == (8 if two else 4), where
     assert p["rows_per_wave"] % 4 == 0 and p["grid"] * p["rows_per_wave"] >= M, where
     assert p["lds_bytes"] == 0 and p["stage_order"] == -1, where
     if kind == "f16x32":
         assert M >= cus and (P >= 2 or M >= 14 * cus), where
     elif kind == "q4":
-        assert M >= cus and 3 <= P <= 16 and P != 6 and (P <= 7 or M <= 12 * cus), where
+        nchunks = N // ELEMS_PER_CHUNK[kind]
+        assert ((M >= cus and 3 <= P <= 16 and P != 6 and (P <= 7 or M <= 12 * cus))
+                or (P == 1 and nchunks > 32 and M >= 4 * cus)), where
         assert p["grid"] <= max(1, 32 // S) * cus, where        # at most 32 waves per CU
     else:
         assert P >= 9 and 2 * cus <= M <= 100 * cus, where
@@ -211,6 +214,13 @@ def test_slab_plans_of_the_named_shapes():
     # INT4: at most 32 waves per CU, workgroups walk the slabs beyond
     p = plan("q4", 300000, 8192)
     assert (p["variant"], p["block"], p["grid"]) == (7, 256, 8 * 256) and p["rows_per_wave"] >= 300000 / (8 * 256)
+    # INT8 rows of an even count from 10 units: two passes per wave
+    assert geo(plan("q8", 4039, 15616)) == (7, 512, 8, 8, 505)
+    assert geo(plan("q8", 1913, 10240)) == (7, 320, 8, 4, 479)
+    # INT4 one-unit rows past the packed kernel (more than 32 chunks), from
+    # 4 rows per CU: one wave per slab, at most 32 per CU
+    assert geo(plan("q4", 51636, 1408)) == (7, 64, 4, 4 * 2, 32 * 256) and plan("q4", 1023, 1408)["variant"] != 7
+    assert plan("q4", 51636, 1024)["variant"] == 4
     # where the streaming kernel stays: INT4 rows of 2 or 6 units, INT8 rows
     # under 9 units, long INT4 rows beyond 12 rows per CU, INT8 beyond 100,
     # fewer rows than CUs
@@ -260,9 +270,10 @@ def test_short_rows_rules():
     # INT8/INT4 rows of at most 32 chunks: the packed kernel
     assert plan("q8", 14336, 512)["variant"] == 4
     assert plan("q4", 14336, 1024)["variant"] == 4
-    # one unit just past: x in registers
+    # one unit just past: x in registers (INT4 from 4 rows per CU: row slabs)
     assert plan("q8", 14336, 528)["variant"] == 5
-    assert plan("q4", 14336, 1152)["variant"] == 5
+    assert plan("q4", 1000, 1152)["variant"] == 5
+    assert plan("q4", 14336, 1152)["variant"] == 7
     # FP16 rows of one and two units: x in registers
     assert plan("f16", 4096, 512)["variant"] == 5
     assert plan("f16", 14336, 1024)["variant"] == 5
