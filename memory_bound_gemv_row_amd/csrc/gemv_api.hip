@@ -768,7 +768,7 @@ bool four_rows_rule(const Plan& p) { return (p.variant == 2 && p.rows == 4 && p.
 // rows of 3-16 units but 6, from one row per CU (rows of 8 units and more
 // only up to 12 rows per CU), and one-unit rows of more than 32 chunks
 // (past the packed kernel) from 4 rows per CU; INT8 rows of 9 units and
-// more between 2 and 100 rows per CU.  Slabs of 8 rows where two passes
+// more between 2 and 12 rows per CU.  Slabs of 8 rows where two passes
 // per wave give the busiest CU no more rows than slabs of 4 (fewer
 // workgroups, each loading its x once) and every CU still a slab.  INT4 caps the grid at 32 waves per
 // CU, so that workgroups walk several slabs with x loaded once.
@@ -788,7 +788,13 @@ bool four_rows_rule(const Plan& p) { return (p.variant == 2 && p.rows == 4 && p.
 // 15616 12.47 at one pass per wave, 11.57-11.86 at two) gave the last two
 // rules, which the four training seeds support too (INT4 22965 x 2048
 // 7.27 -> 6.73; INT8 2567 x 15616 10.71 -> 9.04 at two passes, 9.16 at
-// one).
+// one).  A sixth seed, held out after that: row slabs 0.913 (INT4, 6
+// shapes) and 0.974 (FP16 with FP32 x, 18 shapes) of the fastest plan of
+// the other kernels, but INT8 1.070 (7 shapes), its losses all past 12 rows
+// per CU (5559 x 13312 16.69 against 13.78, 12805 x 12672 31.52 against
+// 26.20, 4008 x 18432 14.33 against 13.52): INT8 row slabs stop at 12 rows
+// per CU (all six seeds: 0.988-1.003 of the streaming kernels' best over
+// every INT8 shape, where up to 100 rows per CU read 0.986-1.018).
 bool slab_plan(int kind, int M, int nchunks, int cus, Plan* p)
 {
     const int P = (nchunks + 63) / 64;
@@ -800,7 +806,7 @@ bool slab_plan(int kind, int M, int nchunks, int cus, Plan* p)
         take = (rows >= cus && P >= 3 && P <= 16 && P != 6 && (P <= 7 || rows <= 12 * (int64_t)cus)) ||
                (P == 1 && nchunks > kPackedMaxChunks && rows >= 4 * (int64_t)cus);
     else if (kind == kQ8)
-        take = P >= 9 && rows >= 2 * (int64_t)cus && rows <= 100 * (int64_t)cus;
+        take = P >= 9 && rows >= 2 * (int64_t)cus && rows <= 12 * (int64_t)cus;
     if (!take || P > 32 || (P > 16 && P % 2 != 0))
         return false;
     // two passes per wave for rows of 17-32 units, and for INT8 rows of an
