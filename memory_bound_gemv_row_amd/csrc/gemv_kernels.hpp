@@ -11,13 +11,16 @@
 //     wave-wide load instruction moves 1 KiB of contiguous bytes: the
 //     coalesced mapping "column = lane + width * pass" at 16-byte
 //     granularity ("membound", stage 3: 128-bit loads).  Rows shorter than
-//     half a wave load share wave loads (gemv_packed).
+//     half a wave load share wave loads (gemv_packed); few long rows, and
+//     INT8/INT4/FP16-with-FP32-x rows in slabs of 4 or 8, spread one row's
+//     passes over the waves of a workgroup (gemv_split, gemv_slab).
 //   * D such 1-KiB units are issued before any is consumed, so each wave
 //     keeps D KiB of A in flight.
 //   * x reaches the lanes one of three ways, by shape: staged once per
 //     workgroup in LDS ("membound", stage 2 stages x in shared memory), read
-//     through the caches with each unit, or, for rows of one to three wave
-//     loads (and packed short rows), loaded once per wave into registers.
+//     through the caches with each unit, or loaded once per wave into
+//     registers: for rows of one to three wave loads, packed short rows, and
+//     in row slabs each wave's slice of x for the passes it owns.
 //   * Accumulation is FP32 in registers.  FP16 operands enter through
 //     v_dot2_f32_f16; INT8/INT4 codes are unpacked in registers to exact
 //     binary16 integers (INT8 by a byte-select conversion, INT4 through an
@@ -31,6 +34,8 @@
 //     LDS round trip and no atomics ("Making GEMV Fast", section "How does
 //     warpReduceSum work?", and the llama.cpp walkthrough's butterfly, both
 //     on 32-wide warps; here the butterfly spans 64 lanes).  Lane 0 stores.
+//     Row slabs reduce four or eight rows' partials at once with lane
+//     permutes, and a row whose passes span waves meets in LDS.
 //
 // No MFMA: at batch 1 each weight is used once, so the work is a stream of
 // about one FMA per weight, bounded by HBM bandwidth, not a contraction.
