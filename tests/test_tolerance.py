@@ -275,3 +275,88 @@ def test_q8_exact_decode_error_does_not_depend_on_the_mean_of_x(codes):
     assert spread < 4, errs
     assert errs["abs_normal"][1] > GATES["q8"], errs
     assert errs["shifted"][1] > GATES["q8"], errs
+
+
+# ---------------------------------------------------------------- row-slab order
+def _slab_butterfly(v):
+    """The row-slab reduction of one row's 64 lane sums: FP32 adds of lane
+    pairs at xor distances 32 and 16 (the two lane-permute swaps), 8 (a
+    rotation by 8 within 16 lanes), then 1, 2 and 4 within each group of 8."""
+    v = v.astype(np.float32)
+    idx = np.arange(64)
+    for d in (32, 16, 8, 1, 2, 4):
+        v = (v + v[:, idx ^ d]).astype(np.float32)
+    return v[:, 0]
+
+
+def _slab_order(kind, W, s, x, S, drop_wave=None):
+    """Emulate gemv_slab: wave w of S owns passes w, w + S, ...; lane l of
+    that wave sums its chunk of each pass in FP32 (INT8/INT4 products exact,
+    each v_dot2_f32_f16 step with two roundings; FP16 weights with FP32 x one
+    rounding per v_fma_mix_f32 step); the wave's 64 lane sums meet in the
+    slab butterfly, the S wave sums are added in wave order, and INT8 takes
+    its row scale last.  W holds exact weight values (codes for INT8/INT4).
+    drop_wave leaves one wave's sum out (a planted mistake)."""
+    M, N = W.shape
+    E = {"q8": 16, "q4": 32, "f16x32": 8}[kind]
+    P = N // (64 * E)
+    assert N == P * 64 * E and P % S == 0
+    Wc = W.reshape(M, P, 64, E).astype(np.float64)
+    xc = x.astype(np.float64).reshape(P, 64, E)
+    waves = []
+    for w in range(S):
+        acc = np.zeros((M, 64), np.float32)
+        for p in range(w, P, S):
+            if kind == "f16x32":
+                for k in range(E):
+                    acc = (acc.astype(np.float64) + Wc[:, p, :, k] * xc[p, :, k]).astype(np.float32)
+            elif kind == "q8":
+                for k in range(0, E, 2):
+                    acc = _dot2_f32(Wc[:, p, :, k], xc[p, :, k], Wc[:, p, :, k + 1], xc[p, :, k + 1], acc)
+            else:
+                part = np.zeros((M, 64), np.float32)
+                for word in range(4):
+                    for j in range(4):   # pairs (x_j, x_{j+4}) of the word's 8 columns
+                        c0, c1 = 8 * word + j, 8 * word + j + 4
+                        part = _dot2_f32(Wc[:, p, :, c0], xc[p, :, c0], Wc[:, p, :, c1], xc[p, :, c1], part)
+                # a lane's 32 columns lie in one 128-column group: (p * 64 + l) // 4
+                sg = s.astype(np.float64)[:, (p * 64 + np.arange(64)) // 4]
+                acc = (acc.astype(np.float64) + sg * part.astype(np.float64)).astype(np.float32)
+        if w != drop_wave:
+            waves.append(_slab_butterfly(acc))
+    t = waves[0]
+    for v in waves[1:]:
+        t = (t + v).astype(np.float32)
+    if kind == "q8":
+        t = (t.astype(np.float64) * s.astype(np.float64)).astype(np.float32)
+    return t
+
+
+@pytest.mark.parametrize("kind,N,S", [("q8", 24576, 12), ("q4", 14336, 7), ("f16x32", 8192, 16)])
+def test_slab_order_within_the_gate(kind, N, S):
+    # The row-slab kernel's order (passes split over the waves, the batched
+    # butterfly, wave sums added in LDS) on the workloads' value
+    # distributions and, for INT8/INT4, non-zero-mean activations: its
+    # floored error stays far inside the gate, as the streaming kernel's
+    # does; leaving one wave's sum out fails it
+    import oracle
+    from memory_bound_gemv_row_amd import inputs
+    from qpack import unpack_int4
+
+    oracle.build(force=False)
+    M = 48
+    ops = inputs.make(kind, M, N, seed=7)
+    for dist in (inputs.X_DISTS if kind != "f16x32" else ("normal",)):
+        x = ops["x"] if kind == "f16x32" else inputs.make_x_f16(N, dist, seed=8)
+        if kind == "q8":
+            W, s = ops["A"], ops["scale"]
+            ref = oracle.gemv_q8(ops["A"], s, x)
+        elif kind == "q4":
+            W, s = unpack_int4(ops["A"]), ops["scale"]
+            ref = oracle.gemv_q4(ops["A"], s, x)
+        else:
+            W, s = ops["A"], None
+            ref = oracle.gemv_f16x32(ops["A"], x)
+        err = parity_error(_slab_order(kind, W, s, x, S), ref)
+        assert err < GATES[kind] / 5, (kind, dist, err)
+        assert parity_error(_slab_order(kind, W, s, x, S, drop_wave=S // 2), ref) > GATES[kind], (kind, dist)
