@@ -731,6 +731,13 @@ Plan fp_model_plan(int kind, int M, int P, const Device& dev, const Plan& p0)
         // one workgroup per row, no walking: the grid must hold every row
         if (2 * S > P || (int64_t)M * S * 64 > gemv_device::kMaxWorkItems)
             continue;
+        // from two rows per CU split rows keep the rules' two waves per row:
+        // on three seeds of random shapes the model's 4-16 waves per row
+        // there lost to two in 9 of 11 shapes (FP32 1399 x 28288 29.53 ->
+        // 26.76 us, 581 x 23168 12.95 -> 11.58, FP16 1071 x 29440 13.84 ->
+        // 12.65; the two it won by 0.8-1.6 %)
+        if (S > 2 && M >= 2 * (int64_t)dev.cus)
+            continue;
         for (int D : {2, 4}) {
             Plan c{};
             c.variant = 6;

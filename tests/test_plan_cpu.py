@@ -372,6 +372,14 @@ def test_cost_model_replaces_plans_the_measurements_beat():
     assert _geometry(plan("f16", 278, 16896)) == (6, 278, 256, 4, 1)
     assert _geometry(plan("f32", 902, 5248)) == (6, 902, 128, 4, 1)
     assert _geometry(plan("f16", 774, 24704)) == (6, 774, 128, 4, 1)
+    # From two rows per CU the model keeps split rows at two waves: its
+    # 4-16 waves per row lost there in 9 of 11 measured shapes (FP32
+    # 1399x28288 29.53 -> 26.76, 581x23168 12.95 -> 11.58, FP16 1071x29440
+    # 13.84 -> 12.65); below that many waves per row still pay.
+    assert _geometry(plan("f32", 1399, 28288)) == (6, 1399, 128, 4, 1)
+    assert _geometry(plan("f32", 581, 23168)) == (6, 581, 128, 4, 1)
+    assert _geometry(plan("f16", 1071, 29440)) == (6, 1071, 128, 4, 1)
+    assert plan("f16", 400, 29440)["block"] > 128
     # the other formats keep the measured rules alone (FP16 with FP32 x:
     # row slabs)
     assert plan("f16_acc16", 2552, 9088)["variant"] == 2
