@@ -63,6 +63,9 @@ def parse():
                     help="time every plan the library holds a kernel for (gemv_launch_plan) on COUNT seeded "
                          "random shapes per format against the library's own plan, instead of the bench line")
     ap.add_argument("--seed", type=int, default=0, help="seed of --plan-sweep's and --plan-search's shapes")
+    ap.add_argument("--plan-search-named", action="store_true",
+                    help="the plan search of --plan-search on the named workloads and the shard shapes "
+                         "(every shape and format of the detail table) instead of random shapes")
     ap.add_argument("--profile", action="store_true",
                     help="launch each kernel exactly once after a cold flush (for counter collection)")
     return ap.parse_args()
@@ -520,7 +523,7 @@ def plan_candidates(kind, N):
     return out
 
 
-def plan_search(count, seed, rounds=3, launches=48):
+def plan_search(count, seed, rounds=3, launches=48, shapes=None):
     """Brute force over the plans: on each seeded random shape
     (sweep_shapes), every candidate plan that fits (plan_candidates,
     gemv_check_plan_for) and the library's own plan, each as a graph of
@@ -528,7 +531,7 @@ def plan_search(count, seed, rounds=3, launches=48):
     JSON line per shape (the library's plan, the fastest candidate, their
     ratio, every candidate's time) and a per-format summary: how far the
     planner's choice sits from the best plan the library could have
-    launched."""
+    launched.  `shapes` replaces the random shapes when given."""
     import math
 
     import torch
@@ -538,7 +541,7 @@ def plan_search(count, seed, rounds=3, launches=48):
     props = torch.cuda.get_device_properties(0)
     cus, lds_max = props.multi_processor_count, props.shared_memory_per_block
     rows = []
-    for kind, M, N in sweep_shapes(count, seed):
+    for kind, M, N in shapes or sweep_shapes(count, seed):
         ring = Ring(kind, M, N, zero_operands(kind, M, N))
         sh = torch.cuda.current_stream().cuda_stream
         for i in range(16):   # warm the clocks before the first timing
@@ -576,14 +579,14 @@ def plan_search(count, seed, rounds=3, launches=48):
         ring.free()
         torch.cuda.empty_cache()
     summary = {}
-    for kind in SWEEP_KINDS:
+    for kind in dict.fromkeys(x["kind"] for x in rows):
         r = sorted((x for x in rows if x["kind"] == kind), key=lambda x: x["lib_over_best"])
         if r:
             geo = math.exp(sum(math.log(x["lib_over_best"]) for x in r) / len(r))
             summary[kind] = {"shapes": len(r), "geomean_lib_over_best": round(geo, 4),
                              "median_lib_over_best": r[len(r) // 2]["lib_over_best"],
                              "worst_lib_over_best": r[-1]["lib_over_best"], "worst_shape": f"{r[-1]['M']}x{r[-1]['N']}"}
-    print(json.dumps({"plan_search": summary, "seed": seed, "count": count}), flush=True)
+    print(json.dumps({"plan_search": summary, "seed": None if shapes else seed, "count": len(rows)}), flush=True)
 
 
 # ---------------------------------------------------------------- quantiser
@@ -897,6 +900,9 @@ def main():
         return plan_sweep(args.plan_sweep, args.seed)
     if args.plan_search:
         return plan_search(args.plan_search, args.seed)
+    if args.plan_search_named:
+        named = [(k, M, N) for _, M, N, kinds in DETAIL_SHAPES for k in kinds]
+        return plan_search(0, None, rounds=5, launches=64, shapes=named)
     kind, M, N = args.kind, args.M, args.N
     ops = inputs.make(kind, M, N, seed=0)
     ring = Ring(kind, M, N, ops)

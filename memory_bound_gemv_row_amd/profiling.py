@@ -8,7 +8,7 @@ Usage (after the rocprofv3 runs named in each summary's header)::
         <write_counter_collection.csv> <workload> <out.txt> <fetch command> <write command>
     python -m memory_bound_gemv_row_amd.profiling table <workload> <out.txt> \
         <run dir> <command> [<run dir> <command> ...]
-    python -m memory_bound_gemv_row_amd.profiling search <plan-search jsonl> <seed> <out.txt>
+    python -m memory_bound_gemv_row_amd.profiling search <plan-search jsonl> <seed|named> <out.txt>
     python -m memory_bound_gemv_row_amd.profiling sweep <plan-sweep jsonl> <seed> <out.txt>
 
 Traffic calibration: ``bench.py --profile`` launches, in order, a 1 GiB
@@ -314,10 +314,12 @@ def write_search_summary(src, seed, out):
     lines in `src`): per shape the library's plan against the fastest of
     every plan the library holds a kernel for."""
     rows, summ = _bench_lines(src, "plan_search")
+    named = seed == "named"
     with open(out, "w") as f:
         f.write("# bench.py --plan-search: the library's plan against every plan it holds a kernel for "
-                "(gemv_launch_plan), graph-timed, best of 3\n")
-        f.write(f"command: python3 bench.py --plan-search 24 --seed {seed} > {os.path.basename(src)}\n")
+                f"(gemv_launch_plan), graph-timed, best of {5 if named else 3}\n")
+        run = "--plan-search-named" if named else f"--plan-search 24 --seed {seed}"
+        f.write(f"command: python3 bench.py {run} > {os.path.basename(src)}\n")
         f.write(f"summary by: python3 -m memory_bound_gemv_row_amd.profiling search {os.path.basename(src)} {seed} "
                 f"{os.path.basename(out)}\n")
         f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
